@@ -1,0 +1,397 @@
+"""Checks that pin the CPU oracle to facts fixed outside itself.
+
+Each ``pin_*`` function takes the oracle package ``o`` and raises
+AssertionError when the oracle disagrees with: a worked example printed on the
+pages (stored under tests/golden/ with its citation), a closed form that the
+definitions imply, an invariant, a library routine in a special case, or brute
+force on tiny inputs. ``test_oracle_pins.py`` runs them against the oracle;
+``test_oracle_mutations.py`` plants plausible mistakes in the oracle and checks
+that some pin fails for every one of them.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import torch
+
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+F32 = np.float32
+
+
+def golden(name: str) -> dict:
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def ulp32(x) -> np.ndarray:
+    x = np.abs(np.asarray(x, dtype=np.float32))
+    return np.spacing(x).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Worked examples printed on the pages
+# ---------------------------------------------------------------------------
+def pin_weight_example(o):
+    g = golden("weight_rtn_example.json")
+    w = np.array(g["w_rows_in_channels_cols_out_channels"], dtype=F32)
+    wq, sw = o.quantize_weights_per_channel(o.fold_weights(w, np.ones(w.shape[0], F32)))
+    assert wq.shape == (w.shape[1], w.shape[0])
+    assert np.array_equal(wq.T.astype(np.int64), np.array(g["q_expected"])), wq.T
+    assert np.allclose(sw, g["scale_printed"], rtol=1e-3, atol=0)
+    recon = wq.T.astype(np.float64) * sw.astype(np.float64)[None, :]
+    assert np.allclose(np.round(recon, 4), g["reconstructed_expected"], atol=1.01e-4)
+    x = np.array(g["x"], dtype=np.float64)
+    assert np.allclose(x @ w.astype(np.float64), g["output_original_printed"], atol=5e-4)
+    assert np.allclose(x @ recon, g["output_reconstructed_expected"], atol=6e-4)
+
+
+def pin_act_example(o):
+    g = golden("act_per_token_example.json")
+    xq, dx = o.quantize_activations(np.array([g["x"]], dtype=F32))
+    assert np.array_equal(xq[0].astype(np.int64), g["q_expected"]), xq
+    assert abs(float(dx[0]) - g["scale_printed"]) < 5e-4
+
+
+def pin_smoothed_example(o):
+    g = golden("smoothed_act_example.json")
+    act = (np.array(g["normalized"], dtype=F32) * np.array(g["gamma"], dtype=F32)).astype(F32)
+    assert np.array_equal(act, np.array(g["activation_expected"], dtype=F32))
+    s = np.array(g["smoothing"], dtype=F32)
+    xh = o.smooth_activations(act[None, :], s)[0]
+    assert np.all(np.abs(xh - np.array(g["smoothed_activation_expected"], dtype=F32))
+                  <= ulp32(g["smoothed_activation_expected"]))
+    xq, _ = o.quantize_activations(act[None, :], s)
+    assert np.array_equal(xq[0].astype(np.int64), g["q_expected"]), xq
+    # Without smoothing the same activation collapses to the unsmoothed example.
+    xq0, _ = o.quantize_activations(act[None, :])
+    assert np.array_equal(xq0[0].astype(np.int64), golden("act_per_token_example.json")["q_expected"])
+
+
+def pin_per_tensor_crush(o):
+    g = golden("per_tensor_crush.json")
+    r60 = g["range_60"]
+    row = np.array([[r60["absmax"]] + r60["values"]], dtype=F32)
+    xq, dx = o.quantize_activations(row)
+    assert np.array_equal(xq[0, 1:].astype(np.int64), r60["q_expected"])
+    assert abs(float(dx[0]) - r60["step_about"]) < 0.05
+    r40 = g["range_40"]
+    bulk = np.linspace(r40["bulk_lo"], r40["bulk_hi"], 40001).astype(F32)
+    xq, _ = o.quantize_activations(np.concatenate([[F32(r40["absmax"])], bulk])[None, :])
+    assert len(np.unique(xq[0, 1:])) == r40["distinct_levels_expected"]
+    # The per-tensor baseline behaves the same way on a whole matrix.
+    x = np.tile(bulk[None, :401], (3, 1))
+    x[1, 7] = F32(r40["absmax"])
+    w = np.eye(401, dtype=F32)
+    y = o.per_tensor_int8_linear(x, w)
+    assert len(np.unique(np.round(y[0] / (40.0 / 127), 6))) <= r40["distinct_levels_expected"]
+
+
+def pin_trace_shapes(o):
+    g = golden("llm_int8_trace_shapes.json")
+    m, k = g["m"], g["k"]
+    rng = np.random.default_rng(1234)
+    x = np.clip(rng.standard_normal((m, k)), -2, 2).astype(np.float16).astype(F32)
+    cols = np.sort(rng.choice(k, g["n_outliers"], replace=False))
+    x[:, cols] *= F32(20.0)
+    mask = o.detect_outliers(x, g["threshold"])
+    assert int(mask.sum()) == g["n_outliers"] and np.array_equal(np.flatnonzero(mask), cols)
+    assert int((~mask).sum()) == g["regular_cols"]
+    n = 96  # output columns kept small: the shapes of the split do not depend on n
+    w16 = (rng.standard_normal((k, n)) * 0.02).astype(np.float16).astype(F32)
+    wq, sw = o.quantize_weights_per_channel(w16)
+    r = o.int8_decomp_linear(x, wq, sw, w16, g["threshold"])
+    assert r["acc"].shape == (m, n) and r["acc"].dtype == np.int32
+    assert r["y"].shape == (m, n) and r["y"].dtype == np.float16
+    assert r["count"] == g["n_outliers"]
+    assert np.all(r["xq"][:, cols] == 0)
+    assert g["k"] * g["n"] // 2**20 == g["int8_weight_mib"] and 2 * g["k"] * g["n"] // 2**20 == g["fp16_weight_mib"]
+
+
+# ---------------------------------------------------------------------------
+# Calibration and the smoothing factor
+# ---------------------------------------------------------------------------
+def pin_calibration(o):
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((37, 29)).astype(F32)
+    x[:, 3] *= -50
+    ref = np.array([max(abs(float(x[t, j])) for t in range(x.shape[0])) for j in range(x.shape[1])], F32)
+    a = o.calibrate_absmax(x)
+    assert np.array_equal(a, ref)
+    # running maximum over batches equals one pass over all rows
+    a2 = o.calibrate_absmax(x[20:], o.calibrate_absmax(x[:20]))
+    assert np.array_equal(a2, ref)
+    assert np.array_equal(o.calibrate_absmax(-x), ref)
+    assert np.array_equal(o.weight_row_absmax(x.T), ref)
+
+
+def pin_smoothing_closed_forms(o):
+    rng = np.random.default_rng(11)
+    k = 300
+    a = np.abs(rng.standard_normal(k)).astype(F32) + F32(0.05)
+    a[[5, 77]] = F32(61.0), F32(45.5)
+    w = (np.abs(rng.standard_normal(k)) * 0.05).astype(F32) + F32(1e-3)
+    for alpha in (0.3, 0.5, 0.8):
+        s = o.smoothing_factors(a, w, alpha).astype(np.float64)
+        prod = a.astype(np.float64) * w.astype(np.float64)
+        xmax = a / s                        # largest smoothed activation of channel j
+        wmax = s * w                        # largest folded weight of row j
+        assert np.all(np.abs(xmax / prod ** (1 - alpha) - 1) < 2.5e-7), alpha
+        assert np.all(np.abs(wmax / prod ** alpha - 1) < 2.5e-7), alpha
+        if alpha == 0.5:
+            assert np.all(np.abs(xmax / wmax - 1) < 2.5e-7)
+    assert np.array_equal(o.smoothing_factors(a, w, 1.0), a)
+    inv = (np.float32(1.0) / w).astype(F32)
+    assert np.all(np.abs(o.smoothing_factors(a, w, 0.0) - inv) <= np.spacing(inv))
+    # outlier channels get large s, the rest stay moderate
+    s = o.smoothing_factors(a, w, 0.8)
+    assert s[5] > 10 * np.median(s) and s[77] > 10 * np.median(s)
+    # channels without signal are left alone
+    z = o.smoothing_factors(np.array([0, 1, 0], F32), np.array([1, 0, 0], F32), 0.5)
+    assert np.array_equal(z, np.ones(3, F32))
+
+
+def pin_smoothing_identity(o):
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((9, 64)).astype(F32)
+    w = rng.standard_normal((64, 40)).astype(F32)
+    s = np.ldexp(1.0, rng.integers(-6, 7, size=64)).astype(F32)  # powers of two: exact scaling
+    xh = o.smooth_activations(x, s).astype(np.float64)
+    wf = o.fold_weights(w, s).astype(np.float64)
+    prods_smoothed = xh[:, :, None] * wf[None, :, :]
+    prods_plain = x.astype(np.float64)[:, :, None] * w.astype(np.float64)[None, :, :]
+    assert np.array_equal(prods_smoothed, prods_plain)
+    # a general s keeps the product within binary32 rounding of the two scalings
+    s2 = (np.abs(rng.standard_normal(64)) * 5 + 0.1).astype(F32)
+    y = o.smooth_activations(x, s2).astype(np.float64) @ o.fold_weights(w, s2).astype(np.float64)
+    y0 = x.astype(np.float64) @ w.astype(np.float64)
+    bound = (np.abs(x).astype(np.float64) @ np.abs(w).astype(np.float64)) * 2 ** -22
+    assert np.all(np.abs(y - y0) <= bound)
+    # direction: the outlier channel of the activation shrinks, its weight row grows
+    a = o.calibrate_absmax(x * np.where(np.arange(64) == 9, 40.0, 1.0).astype(F32))
+    sf = o.smoothing_factors(a, o.weight_row_absmax(w), 0.5)
+    assert sf[9] > 1
+    assert np.abs(o.smooth_activations(x, sf)[:, 9]).max() < np.abs(x[:, 9]).max()
+    assert np.abs(o.fold_weights(w, sf)[9]).max() > np.abs(w[9]).max()
+
+
+# ---------------------------------------------------------------------------
+# Quantisation invariants
+# ---------------------------------------------------------------------------
+def _check_rtn(values, q, scale, axis):
+    v = values.astype(np.float64)
+    sc = np.expand_dims(scale.astype(np.float64), axis)
+    nz = scale > 0
+    qa = np.abs(q.astype(np.int64))
+    top = qa.max(axis=axis)
+    assert np.all(top[nz] == 127), top
+    assert np.all(qa <= 127)
+    err = np.abs(v - q.astype(np.float64) * sc)
+    assert np.all(err <= sc * (0.5 + 2 ** -20) + 1e-30)
+    assert np.all(q.take(np.flatnonzero(~nz), axis=1 - axis) == 0)
+
+
+def pin_quant_invariants(o):
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((33, 130)).astype(F32)
+    x[:, 17] *= 60
+    x[4] = 0
+    s = (np.abs(rng.standard_normal(130)) + 0.5).astype(F32)
+    xq, dx = o.quantize_activations(x, s)
+    assert xq.dtype == np.int8 and dx.dtype == np.float32 and xq.shape == x.shape
+    _check_rtn(o.smooth_activations(x, s), xq, dx, 1)
+    assert dx[4] == 0 and np.all(xq[4] == 0)
+    xqn, dxn = o.quantize_activations(-x, s)
+    assert np.array_equal(xqn, -xq) and np.array_equal(dxn, dx)
+    w = (rng.standard_normal((130, 70)) * 0.02).astype(F32)
+    w[:, 3] = 0
+    wq, sw = o.quantize_weights_per_channel(w)
+    assert wq.shape == (70, 130)
+    _check_rtn(w, wq.T, sw, 0)
+    assert sw[3] == 0
+    # With a unit scale (largest magnitude 127) the quantiser is plain
+    # round-half-to-even of the values, which Python's round() computes.
+    ties = np.array([127.0, 0.5, 1.5, 2.5, -0.5, -2.5, 3.49, -126.5, 125.5, 0.0], F32)
+    expect = np.array([round(float(v)) for v in ties], np.int64)
+    xq1, dx1 = o.quantize_activations(ties[None, :])
+    assert dx1[0] == 1 and np.array_equal(xq1[0].astype(np.int64), expect)
+    wq1, sw1 = o.quantize_weights_per_channel(ties[:, None])
+    assert sw1[0] == 1 and np.array_equal(wq1[0].astype(np.int64), expect)
+
+
+# ---------------------------------------------------------------------------
+# GEMM by brute force
+# ---------------------------------------------------------------------------
+def pin_gemm_bruteforce(o):
+    rng = np.random.default_rng(9)
+    for (m, n, k) in [(1, 1, 1), (3, 5, 7), (8, 8, 128), (5, 2, 64)]:
+        xq = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+        wq = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+        acc = o.int8_matmul(xq, wq)
+        ref = [[sum(int(xq[i, t]) * int(wq[j, t]) for t in range(k)) for j in range(n)] for i in range(m)]
+        assert acc.dtype == np.int32 and np.array_equal(acc.astype(np.int64), np.array(ref, dtype=np.int64))
+    k = 14336
+    xq = np.full((2, k), 127, np.int8)
+    xq[1] = -127
+    wq = np.full((3, k), 127, np.int8)
+    wq[1, ::2] = -127
+    acc = o.int8_matmul(xq, wq)
+    assert int(acc[0, 0]) == 127 * 127 * k == 231225344
+    assert int(acc[1, 0]) == -231225344 and int(acc[0, 1]) == 0
+    wq[2] = -127
+    assert int(o.int8_matmul(xq, wq)[1, 2]) == 231225344
+    # int32 headroom: K = 133144 fits, K = 133145 does not
+    assert int(o.int8_matmul(np.full((1, 133144), 127, np.int8), np.full((1, 133144), 127, np.int8))[0, 0]) \
+        == 127 * 127 * 133144
+    try:
+        o.int8_matmul(np.full((1, 133145), 127, np.int8), np.full((1, 133145), 127, np.int8))
+    except OverflowError:
+        pass
+    else:
+        raise AssertionError("accumulator overflow not detected")
+
+
+# ---------------------------------------------------------------------------
+# Dequantisation and output rounding
+# ---------------------------------------------------------------------------
+def pin_rounding_vs_torch(o):
+    rng = np.random.default_rng(21)
+    v = (rng.standard_normal(200000) * np.exp(rng.uniform(-30, 30, 200000))).astype(F32)
+    # exact ties in bf16 and fp16 (half-way bit patterns) in both parities
+    u = rng.integers(0, 2**31, size=4000, dtype=np.uint64).astype(np.uint32) & np.uint32(0x7F7F0000)
+    ties = (u | np.uint32(0x8000)).view(np.float32)
+    v = np.concatenate([v, ties, -ties, np.array([0.0, -0.0, 1.0, 65504.0, 1e-8], F32)])
+    tb = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(o.f32_to_bf16_bits(v), tb)
+    assert np.array_equal(o.round_bf16(v), torch.from_numpy(v).to(torch.bfloat16).float().numpy())
+    small = v[np.abs(v) < 60000]
+    th = torch.from_numpy(small).to(torch.float16).numpy()
+    assert np.array_equal(o.round_f16(small).view(np.uint16), th.view(np.uint16))
+
+
+def pin_f16_from_f64(o):
+    """The oracle's final fp16 sum rounds a binary64 value once; check that
+    cast against the nearest-value search over all finite fp16 values."""
+    allh = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)  # non-negative finite
+    rng = np.random.default_rng(4)
+    idx = rng.integers(1, len(allh) - 1, size=3000)
+    mids = (allh[idx] + allh[idx + 1]) / 2
+    vals = np.concatenate([mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                           rng.uniform(0, 60000, 3000)])
+    got = vals.astype(np.float16).astype(np.float64)
+    pos = np.searchsorted(allh, vals)
+    lo, hi = allh[np.maximum(pos - 1, 0)], allh[np.minimum(pos, len(allh) - 1)]
+    lo_bits = np.maximum(pos - 1, 0)
+    d_lo, d_hi = vals - lo, hi - vals
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (lo_bits % 2 == 1))
+    ref = np.where(vals == hi, hi, np.where(pick_hi, hi, lo))
+    assert np.array_equal(got, ref)
+    # and the oracle's decomposition sum uses exactly this cast
+    a = np.array([1.0, 2048.0], np.float16)
+    b = np.array([2.0 ** -11, 1.0], np.float16)
+    r = o.int8_decomp_linear  # noqa: F841 (existence)
+    assert np.array_equal((a.astype(np.float64) + b.astype(np.float64)).astype(np.float16),
+                          np.array([1.0, 2048.0], np.float16))
+
+
+def pin_dequant(o):
+    rng = np.random.default_rng(13)
+    acc = rng.integers(-231225344, 231225345, size=(17, 23)).astype(np.int32)
+    acc[0, :3] = [16777217, -16777219, 0]
+    dx = workloads.positive_scales(17, 1)
+    dw = workloads.positive_scales(23, 2)
+    y = o.dequantize(acc, dx, dw, "f32")
+    exact = acc.astype(np.float64) * dx.astype(np.float64)[:, None] * dw.astype(np.float64)[None, :]
+    assert np.all(np.abs(y - exact) <= 3 * ulp32(exact) + 1e-45)
+    assert np.array_equal(acc.astype(F32), torch.from_numpy(acc).float().numpy())
+    yb = o.dequantize(acc, dx, dw, "bf16")
+    assert yb.dtype == np.uint16
+    assert np.array_equal(yb, torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    yh = o.dequantize(acc, dx, dw, "f16")
+    assert np.array_equal(yh, torch.from_numpy(y).to(torch.float16).numpy())
+    # the per-row scale multiplies rows, the per-column scale columns
+    ones = np.ones((2, 3), np.int32)
+    yy = o.dequantize(ones, np.array([1, 2], F32), np.array([4, 8, 16], F32), "f32")
+    assert np.array_equal(yy, np.array([[4, 8, 16], [8, 16, 32]], F32))
+
+
+# ---------------------------------------------------------------------------
+# Error ordering on the tiny configuration
+# ---------------------------------------------------------------------------
+def rel_err(y, ref):
+    return float(np.linalg.norm(np.asarray(y, np.float64) - ref) / np.linalg.norm(ref))
+
+
+def tiny_errors(o, alpha):
+    c = workloads.linear_case("tiny")
+    ref = c.x.astype(np.float64) @ c.w.astype(np.float64)
+    a = o.calibrate_absmax(c.x_calib)
+    s, wq, sw = o.smooth_fold_quantize(a, c.w, alpha)
+    y_s, _, _, _ = o.smoothquant_linear(c.x, s, wq, sw, "f32")
+    wq1, sw1 = o.quantize_weights_per_channel(c.w)
+    y_u, _, _, _ = o.smoothquant_linear(c.x, None, wq1, sw1, "f32")
+    y_t = o.per_tensor_int8_linear(c.x, c.w)
+    return rel_err(y_s, ref), rel_err(y_u, ref), rel_err(y_t, ref)
+
+
+def pin_error_ordering(o):
+    e_s5, e_u, e_t = tiny_errors(o, 0.5)
+    e_s8, _, _ = tiny_errors(o, 0.8)
+    assert e_s5 < e_u < e_t, (e_s5, e_u, e_t)
+    assert e_s8 < e_u, (e_s8, e_u)
+    assert e_s5 < 0.02 and e_t > 0.04
+
+
+# ---------------------------------------------------------------------------
+# LLM.int8() decomposition
+# ---------------------------------------------------------------------------
+def pin_llm_int8(o):
+    c = workloads.decomp_case(seed=3, m=96, k=256, n=80, n_outlier_cols=3)
+    wq, sw = o.quantize_weights_per_channel(c.w)
+    ref = c.x.astype(np.float64) @ c.w.astype(np.float64)
+    r = o.int8_decomp_linear(c.x, wq, sw, c.w, 6.0)
+    assert r["count"] == 3 and np.array_equal(np.flatnonzero(r["mask"]), c.channels)
+    # the split is linear: the decomposed layer is close to the exact product
+    e_dec = rel_err(r["y"], ref)
+    y_plain = o.w8a8_linear(*o.quantize_activations(c.x), wq, sw, "f16")
+    e_plain = rel_err(y_plain, ref)
+    e_tensor = rel_err(o.per_tensor_int8_linear(c.x, c.w), ref)
+    assert e_dec < 0.5 * e_plain and e_dec < 0.25 * e_tensor and e_dec < 0.02, (e_dec, e_plain, e_tensor)
+    # infinite threshold: no outliers, the plain per-row int8 path in fp16
+    r_inf = o.int8_decomp_linear(c.x, wq, sw, c.w, np.inf)
+    assert r_inf["count"] == 0 and np.array_equal(r_inf["y"], y_plain)
+    assert np.all(r_inf["y_out"] == 0)
+    # threshold below every magnitude: all columns take the fp16 route -> an fp16 GEMM
+    xz = np.where(c.x == 0, np.float16(1.0), c.x.astype(np.float16)).astype(F32)
+    r0 = o.int8_decomp_linear(xz, wq, sw, c.w, 0.0)
+    assert r0["count"] == c.k and np.all(r0["xq"] == 0) and np.all(r0["y_int"] == 0)
+    ref0 = xz.astype(np.float64) @ c.w.astype(np.float64)
+    bound = np.abs(ref0) * 2 ** -11 + (np.abs(xz).astype(np.float64) @ np.abs(c.w).astype(np.float64)) \
+        * c.k * 2 ** -24 + 2 ** -24
+    assert np.all(np.abs(r0["y"].astype(np.float64) - ref0) <= bound)
+    # the threshold is strict
+    x = c.x.copy()
+    x[:, c.channels] = np.clip(x[:, c.channels], -5.5, 5.5)
+    x[0, 10] = 6.0
+    x[1, 11] = np.float32(np.float16(6.0) + np.float16(2 ** -8))
+    m = o.detect_outliers(x, 6.0)
+    assert not m[10] and m[11] and int(m.sum()) == 1
+    # the int8 side keeps near-full resolution on the regular columns
+    _check_rtn(np.where(r["mask"][None, :], F32(0), c.x), r["xq"], r["x_scale"], 1)
+    # the fp16 partial alone is the outlier slice's product, within fp16 rounding
+    ref_o = c.x[:, c.channels].astype(np.float64) @ c.w[c.channels].astype(np.float64)
+    assert np.all(np.abs(r["y_out"].astype(np.float64) - ref_o) <= np.abs(ref_o) * 2 ** -10 + 2 ** -24)
+    # and the output is the fp16 sum of the two partials
+    assert np.all(np.abs(r["y"].astype(np.float64) - r["y_int"].astype(np.float64) - r["y_out"].astype(np.float64))
+                  <= np.abs(r["y"].astype(np.float64)) * 2 ** -11 + 2 ** -24)
+
+
+ALL_PINS = [
+    pin_weight_example, pin_act_example, pin_smoothed_example, pin_per_tensor_crush, pin_trace_shapes,
+    pin_calibration, pin_smoothing_closed_forms, pin_smoothing_identity, pin_quant_invariants,
+    pin_gemm_bruteforce, pin_rounding_vs_torch, pin_f16_from_f64, pin_dequant, pin_error_ordering,
+    pin_llm_int8,
+]

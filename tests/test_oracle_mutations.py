@@ -1,0 +1,222 @@
+"""Plant plausible mistakes in the CPU oracle and check that a pin catches each.
+
+Every mutant replaces one oracle function by a copy with one mistake (a dropped
+term, a wrong sign or exponent, a transposed operand, a wrong rounding). The
+test passes only if at least one pin in ``oracle_pins.ALL_PINS`` fails on the
+mutant, which shows the pins constrain every part of the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import llm_int8 as o_int8
+from oracle import numerics as o_num
+from oracle import smoothquant as o_sq
+from tests import oracle_pins
+
+F32 = np.float32
+
+
+def _smooth_swapped(a, w, alpha):
+    a64, w64 = np.asarray(a, np.float64), np.asarray(w, np.float64)
+    ok = (a64 > 0) & (w64 > 0)
+    with np.errstate(all="ignore"):
+        s = np.power(a64, 1 - alpha) / np.power(w64, alpha)
+    return np.where(ok, s, 1.0).astype(F32)
+
+
+def _smooth_product(a, w, alpha):
+    a64, w64 = np.asarray(a, np.float64), np.asarray(w, np.float64)
+    ok = (a64 > 0) & (w64 > 0)
+    with np.errstate(all="ignore"):
+        s = np.power(a64, alpha) * np.power(w64, 1 - alpha)
+    return np.where(ok, s, 1.0).astype(F32)
+
+
+def _smooth_zero_not_one(a, w, alpha):
+    a64, w64 = np.asarray(a, np.float64), np.asarray(w, np.float64)
+    with np.errstate(all="ignore"):
+        s = np.power(a64, alpha) / np.power(w64, 1 - alpha)
+    return np.nan_to_num(s, nan=0.0, posinf=0.0).astype(F32)
+
+
+def _fold_divides(w, s):
+    return (np.asarray(w, F32) / np.asarray(s, F32)[:, None]).astype(F32)
+
+
+def _smooth_act_multiplies(x, s):
+    x = np.asarray(x, F32)
+    return x.copy() if s is None else (x * np.asarray(s, F32)[None, :]).astype(F32)
+
+
+def _quant_w_per_row(wf):
+    wf = np.asarray(wf, F32)
+    rowmax = np.abs(wf).max(axis=1).astype(F32)
+    scale = (rowmax / F32(127)).astype(F32)
+    with np.errstate(all="ignore"):
+        q = np.clip(np.rint((wf / scale[:, None]).astype(F32)), -127, 127)
+    q = np.where(scale[:, None] > 0, q, 0)
+    return np.ascontiguousarray(q.T.astype(np.int8)), scale[: wf.shape[1]] if wf.shape[1] <= wf.shape[0] \
+        else np.resize(scale, wf.shape[1])
+
+
+def _quant_w_qmax128(wf):
+    wf = np.asarray(wf, F32)
+    colmax = np.abs(wf).max(axis=0).astype(F32)
+    scale = (colmax / F32(128)).astype(F32)
+    with np.errstate(all="ignore"):
+        q = np.clip(np.rint((wf / scale[None, :]).astype(F32)), -127, 127)
+    q = np.where(scale[None, :] > 0, q, 0)
+    return np.ascontiguousarray(q.T.astype(np.int8)), scale
+
+
+def _quant_w_no_transpose(wf):
+    wq, sw = o_sq.__dict__["_orig_quantize_weights_per_channel"](wf)
+    return np.ascontiguousarray(wq.T).reshape(wq.shape), sw
+
+
+def _quant_act_trunc(x, s=None):
+    xh = o_sq.smooth_activations(x, s)
+    scale = (np.abs(xh).max(axis=1).astype(F32) / F32(127)).astype(F32)
+    with np.errstate(all="ignore"):
+        q = np.clip(np.trunc((xh / scale[:, None]).astype(F32)), -127, 127)
+    return np.where(scale[:, None] > 0, q, 0).astype(np.int8), scale
+
+
+def _quant_act_half_away(x, s=None):
+    xh = o_sq.smooth_activations(x, s)
+    scale = (np.abs(xh).max(axis=1).astype(F32) / F32(127)).astype(F32)
+    with np.errstate(all="ignore"):
+        r = (xh / scale[:, None]).astype(F32)
+    q = np.clip(np.sign(r) * np.floor(np.abs(r) + 0.5), -127, 127)
+    return np.where(scale[:, None] > 0, q, 0).astype(np.int8), scale
+
+
+def _quant_act_per_tensor(x, s=None):
+    xh = o_sq.smooth_activations(x, s)
+    scale = np.full(xh.shape[0], F32(np.abs(xh).max() / F32(127)), F32)
+    with np.errstate(all="ignore"):
+        q = np.clip(np.rint((xh / scale[:, None]).astype(F32)), -127, 127)
+    return np.where(scale[:, None] > 0, q, 0).astype(np.int8), scale
+
+
+def _quant_act_ignores_s(x, s=None):
+    return o_sq.__dict__["_orig_quantize_activations"](x, None)
+
+
+def _gemm_reversed_k(xq, wq):
+    return o_sq.__dict__["_orig_int8_matmul"](xq, np.ascontiguousarray(np.asarray(wq)[:, ::-1]))
+
+
+def _gemm_no_overflow_check(xq, wq):
+    return (np.asarray(xq, np.float64) @ np.asarray(wq, np.float64).T).astype(np.int64).astype(np.int32)
+
+
+def _dequant_drops_w_scale(acc, x_scale, w_scale, out="bf16"):
+    y = (np.asarray(acc, np.int32).astype(F32) * np.asarray(x_scale, F32)[:, None]).astype(F32)
+    return o_num.round_to(y, out)
+
+
+def _dequant_swaps_scales(acc, x_scale, w_scale, out="bf16"):
+    acc = np.asarray(acc, np.int32)
+    xs = np.resize(np.asarray(w_scale, F32), acc.shape[0])
+    ws = np.resize(np.asarray(x_scale, F32), acc.shape[1])
+    y = (acc.astype(F32) * xs[:, None]).astype(F32)
+    return o_num.round_to((y * ws[None, :]).astype(F32), out)
+
+
+def _bf16_truncates(x):
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def _calib_signed_max(x_rows, prior=None):
+    x = np.asarray(x_rows, F32)
+    a = x.max(axis=0)
+    return (np.maximum(a, prior) if prior is not None else a).astype(F32)
+
+
+def _calib_ignores_prior(x_rows, prior=None):
+    return np.abs(np.asarray(x_rows, F32)).max(axis=0).astype(F32)
+
+
+def _row_absmax_by_column(w):
+    w = np.abs(np.asarray(w, F32))
+    return np.resize(w.max(axis=0), w.shape[0]).astype(F32)
+
+
+def _detect_ge(x, threshold):
+    return np.abs(np.asarray(x, F32)).max(axis=0) >= F32(threshold)
+
+
+def _rows_regular_all_cols(x, mask):
+    xf = np.asarray(x, F32)
+    scale = (np.abs(xf).max(axis=1).astype(F32) / F32(127)).astype(F32)
+    with np.errstate(all="ignore"):
+        q = np.clip(np.rint((np.where(mask[None, :], 0, xf) / scale[:, None]).astype(F32)), -127, 127)
+    return np.where(scale[:, None] > 0, q, 0).astype(np.int8), scale
+
+
+def _outlier_product_drops_last(x, w16, mask):
+    m = mask.copy()
+    idx = np.flatnonzero(m)
+    if len(idx):
+        m[idx[-1]] = False
+    return o_int8.__dict__["_orig_fp16_outlier_product"](x, w16, m)
+
+
+def _outlier_product_wrong_row(x, w16, mask):
+    return o_int8.__dict__["_orig_fp16_outlier_product"](x, np.roll(np.asarray(w16), 1, axis=0), mask)
+
+
+MUTANTS = {
+    "s_exponents_swapped": (o_sq, "smoothing_factors", _smooth_swapped),
+    "s_product_not_quotient": (o_sq, "smoothing_factors", _smooth_product),
+    "s_zero_channel_not_one": (o_sq, "smoothing_factors", _smooth_zero_not_one),
+    "fold_divides_weight": (o_sq, "fold_weights", _fold_divides),
+    "activation_multiplied_by_s": (o_sq, "smooth_activations", _smooth_act_multiplies),
+    "weight_scale_per_row": (o_sq, "quantize_weights_per_channel", _quant_w_per_row),
+    "weight_qmax_128": (o_sq, "quantize_weights_per_channel", _quant_w_qmax128),
+    "weight_not_transposed": (o_sq, "quantize_weights_per_channel", _quant_w_no_transpose),
+    "act_truncates": (o_sq, "quantize_activations", _quant_act_trunc),
+    "act_round_half_away": (o_sq, "quantize_activations", _quant_act_half_away),
+    "act_per_tensor_scale": (o_sq, "quantize_activations", _quant_act_per_tensor),
+    "act_ignores_smoothing": (o_sq, "quantize_activations", _quant_act_ignores_s),
+    "gemm_wrong_k_index": (o_sq, "int8_matmul", _gemm_reversed_k),
+    "gemm_no_overflow_guard": (o_sq, "int8_matmul", _gemm_no_overflow_check),
+    "dequant_drops_weight_scale": (o_sq, "dequantize", _dequant_drops_w_scale),
+    "dequant_swaps_scales": (o_sq, "dequantize", _dequant_swaps_scales),
+    "bf16_truncates": (o_num, "f32_to_bf16_bits", _bf16_truncates),
+    "calib_drops_abs": (o_sq, "calibrate_absmax", _calib_signed_max),
+    "calib_ignores_running_max": (o_sq, "calibrate_absmax", _calib_ignores_prior),
+    "weight_rowmax_wrong_axis": (o_sq, "weight_row_absmax", _row_absmax_by_column),
+    "detect_not_strict": (o_int8, "detect_outliers", _detect_ge),
+    "row_scale_includes_outliers": (o_int8, "quantize_rows_regular", _rows_regular_all_cols),
+    "fp16_slice_drops_column": (o_int8, "fp16_outlier_product", _outlier_product_drops_last),
+    "fp16_slice_wrong_weight_row": (o_int8, "fp16_outlier_product", _outlier_product_wrong_row),
+}
+
+
+def _plant(monkeypatch, module, name, fn):
+    monkeypatch.setitem(module.__dict__, "_orig_" + name, getattr(module, name))
+    monkeypatch.setattr(module, name, fn)
+    if hasattr(oracle, name):
+        monkeypatch.setattr(oracle, name, fn)
+    # functions re-exported through another submodule's namespace
+    for mod in (o_sq, o_int8, o_num):
+        if mod is not module and name in mod.__dict__:
+            monkeypatch.setitem(mod.__dict__, name, fn)
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_some_pin_catches(mutant, monkeypatch):
+    module, name, fn = MUTANTS[mutant]
+    _plant(monkeypatch, module, name, fn)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(oracle)
+        except Exception as e:  # AssertionError, or a shape error the mistake causes
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin catches mutant {mutant}"
