@@ -1,0 +1,210 @@
+"""Benchmark of the W8A8 linear layer on one MI355X.
+
+A step is one pass of the run-time path over one batch: per-token int8
+quantisation of X (with the smoothing divide) followed by the int8 MFMA GEMM
+with the fused dequantisation epilogue to bf16. The default workload is the
+Llama-3.1-8B-shaped fused QKV projection in prefill, M=2048 tokens, K=4096,
+N=6144, bf16 in and out, alpha 0.5. Calibration and the weight fold are
+load-time steps; they run once before the timed region and are reported
+beside the step, not inside it.
+
+Prints one JSON line. ``value`` is end-to-end TOP/s, 2*M*N*K per step over the
+timed steps; ``roofline`` rates the GEMM kernel (the dominant one) against the
+dense int8 MFMA peak with its mean duration from HIP events recorded around
+each launch in the timed region; ``cpu_baseline`` times the CPU oracle on a
+bounded sample of rows of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W8A8 linear TOPS (quant+int8 GEMM+dequant), 8B shapes, % int8 MFMA peak"
+PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, TOP/s
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, GB/s
+PROFILE_PMC = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="qkv_prefill",
+                   help="qkv_prefill (default), gateup_prefill, down_prefill, decode_up, decode_down, tiny")
+    p.add_argument("--m", type=int, default=None, help="override the token count (decode workloads)")
+    p.add_argument("--alpha", type=float, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle time budget")
+    return p.parse_args()
+
+
+def kernel_source_hash(name: str) -> str:
+    path = os.path.join(ROOT, "w8a8_int8_quantization_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def pmc_traffic(workload: str, kernel_file: str):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, if current."""
+    try:
+        with open(PROFILE_PMC) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = d.get(workload)
+    if not e or e.get("source_sha256_16") != kernel_source_hash(kernel_file):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(c, s_ref, budget_s: float):
+    """The CPU oracle's run-time path (quantise, int8 GEMM, dequantise) on row chunks of X."""
+    import numpy as np
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    _, wq, sw = oracle.smooth_fold_quantize(None, c.w, c.alpha, s=s_ref)
+    rows, t_total = 0, 0.0
+    chunk = 64
+    while rows < c.m and t_total < budget_s:
+        r1 = min(c.m, rows + chunk)
+        t0 = time.perf_counter()
+        oracle.smoothquant_linear(c.x[rows:r1], s_ref, wq, sw, c.y_dtype)
+        t_total += time.perf_counter() - t0
+        rows = r1
+        chunk = min(chunk * 2, 512)
+    tops = 2.0 * rows * c.n * c.k / t_total / 1e12
+    return {"value": tops, "unit": "TOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {c.m} rows of X (all N={c.n} outputs, K={c.k}), "
+                      f"{t_total:.1f} s of numpy/BLAS work"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the W8A8 linear layer is built and measured on a single "
+              "MI355X (no sharding or collectives in this library); use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads
+    import w8a8_int8_quantization_amd as sq
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    c = workloads.linear_case(args.workload, m=args.m, alpha=args.alpha)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    to = lambda a, dt: torch.from_numpy(a).to(tdt[dt]).to(dev)
+    xc, x, w = to(c.x_calib, c.x_dtype), to(c.x, c.x_dtype), to(c.w, c.w_dtype)
+    out_dt = tdt[c.y_dtype]
+    print(f"[bench] workload {c.name} M={c.m} K={c.k} N={c.n} alpha={c.alpha}", file=sys.stderr, flush=True)
+
+    # ---- load-time steps (once, timed separately)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    e0, e1, e2 = ev(), ev(), ev()
+    absmax = torch.zeros(c.k, dtype=torch.float32, device=dev)
+    e0.record()
+    sq.sq_calibrate_absmax(xc, absmax)
+    e1.record()
+    s, wq, sw = sq.sq_smooth_fold_weights(w, c.alpha, absmax=absmax)
+    e2.record()
+    torch.cuda.synchronize()
+    prep = {"calibrate_ms": e0.elapsed_time(e1), "smooth_fold_ms": e1.elapsed_time(e2),
+            "calib_rows": int(c.x_calib.shape[0])}
+
+    xq = torch.empty((c.m, c.k), dtype=torch.int8, device=dev)
+    dx = torch.empty(c.m, dtype=torch.float32, device=dev)
+    y = torch.empty((c.m, c.n), dtype=out_dt, device=dev)
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        sq.sq_quant_act_per_token(x, s, xq=xq, x_scale=dx)
+        if evs:
+            evs[1].record()
+        sq.sq_w8a8_linear(xq, dx, wq, sw, y=y, out_dtype=out_dt)
+        if evs:
+            evs[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps, events around each kernel
+    evs = [[ev(), ev(), ev()] for _ in range(args.steps)]
+    t_start, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    ops = 2.0 * c.m * c.n * c.k
+    ms_per_step = total_ms / args.steps
+    value = ops / (ms_per_step * 1e-3) / 1e12
+    gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
+    in_bytes = {"f32": 4, "bf16": 2}[c.x_dtype]
+    quant_bytes = c.m * c.k * in_bytes + 4 * c.k + c.m * c.k + 4 * c.m
+    gemm_bytes = c.m * c.k + c.n * c.k + 4 * c.m + 4 * c.n + c.m * c.n * {"f32": 4, "bf16": 2}[c.y_dtype]
+    decode = c.m <= 64
+    traffic = pmc_traffic(c.name if args.m is None else f"{c.name}_m{c.m}", "gemm.hip")
+    if decode:
+        roof = {"bound": "hbm", "achieved": gemm_bytes / (gemm_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "kernel": "gemm_i8", "bytes_per_launch": gemm_bytes}
+    else:
+        roof = {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                "kernel": "gemm_i8", "ops_per_launch": ops}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic
+    roof["launch_us"] = gemm_ms * 1e3
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "TOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": f"{c.name}: X {c.x_dtype} [{c.m} x {c.k}] -> W [{c.k} x {c.n}], "
+                               f"{c.y_dtype} out, alpha {c.alpha}", "M": c.m, "K": c.k, "N": c.n,
+                   "x_dtype": c.x_dtype, "y_dtype": c.y_dtype, "alpha": c.alpha},
+        "pct_int8_peak": 100.0 * value / PEAK_INT8_TOPS,
+        "gemm_only_tops": gemm_tops,
+        "gemm_us": gemm_ms * 1e3,
+        "quant_us": quant_ms * 1e3,
+        "quant_gbs": quant_bytes / (quant_ms * 1e-3) / 1e9,
+        "quant_frac_hbm": quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "step_gbs_algorithmic": (quant_bytes + gemm_bytes) / (ms_per_step * 1e-3) / 1e9,
+        "load_time": prep,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        s_ref = oracle.smoothing_factors(oracle.calibrate_absmax(c.x_calib), oracle.weight_row_absmax(c.w),
+                                         c.alpha)
+        result["cpu_baseline"] = cpu_baseline(c, s_ref, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

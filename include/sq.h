@@ -1,0 +1,248 @@
+/*
+ * sq.h - C ABI of the SmoothQuant W8A8 linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * The library implements, as HIP kernels, the run-time and load-time steps of
+ * a W8A8 int8 linear layer with SmoothQuant smoothing, and the LLM.int8()
+ * vectorwise decomposition. The pages defining the operations:
+ *
+ *   [W8A8]  "Half the Size, Better Performance, Same Accuracy: Understanding
+ *           W8A8 INT8 LLM Quantization"
+ *   [CALIB] "How does SmoothQuant int8 LLM calibration work and what steps do
+ *           technicians need to follow for accurate deployment?"
+ *   [INT8]  the LLM.int8() page (aicassindra.com, "quant_llm_int8")
+ *
+ * Conventions shared by every entry point:
+ *
+ *  - Pointers to tensors are DEVICE pointers, allocated and owned by the
+ *    caller. The library never allocates, frees or keeps device memory; where
+ *    an entry point needs scratch memory the caller passes a workspace of at
+ *    least the size the matching *_workspace_size() returns (NULL is allowed
+ *    when that size is 0).
+ *  - Matrices are row-major with an explicit leading dimension in elements.
+ *    W is [K x N] (rows are input channels, columns output channels) as on
+ *    the pages; the int8 weight Wq is stored transposed, [N x K], so both
+ *    GEMM operands are contiguous along K.
+ *  - Every call is asynchronous on the given stream (NULL = the default
+ *    stream): it returns once the work is enqueued. Results are visible after
+ *    the stream is synchronised. Calls are stateless and may be made from any
+ *    host thread.
+ *  - All arguments are validated before anything is enqueued, so a call that
+ *    returns an error has done no work. SQ_ERR_HIP reports a failed launch;
+ *    sq_last_hip_error() returns the HIP error code of the latest such
+ *    failure on the calling thread.
+ *  - Shape rules: M, N, T >= 0 (a zero size is a valid no-op); K >= 64 and
+ *    K % 64 == 0. Tensor pointers must be 16-byte aligned and leading
+ *    dimensions must keep every row 16-byte aligned.
+ *  - Inputs containing NaN or infinity are outside the contract (no check is
+ *    made, to keep the kernels at memory speed).
+ */
+#ifndef SQ_H_
+#define SQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t without pulling in the HIP headers. */
+typedef struct ihipStream_t* sq_stream_t;
+
+typedef enum sq_status {
+  SQ_OK = 0,
+  SQ_ERR_NULL = 1,      /* a required pointer is NULL */
+  SQ_ERR_DTYPE = 2,     /* element type not supported by this entry point */
+  SQ_ERR_SHAPE = 3,     /* negative size, K not a positive multiple of 64, ld < row length */
+  SQ_ERR_ALIGN = 4,     /* pointer or row not 16-byte aligned */
+  SQ_ERR_RANGE = 5,     /* value out of range: alpha outside [0,1], K beyond int32 headroom, bad flags */
+  SQ_ERR_WORKSPACE = 6, /* workspace missing or smaller than *_workspace_size() */
+  SQ_ERR_HIP = 7        /* a HIP launch failed; see sq_last_hip_error() */
+} sq_status;
+
+typedef enum sq_dtype {
+  SQ_F32 = 0,  /* IEEE binary32 */
+  SQ_BF16 = 1, /* bfloat16 */
+  SQ_F16 = 2,  /* IEEE binary16 */
+  SQ_I32 = 3,  /* int32 (raw GEMM accumulator output) */
+  SQ_I8 = 4
+} sq_dtype;
+
+/* Largest K for which the int32 accumulator cannot overflow:
+ * 127 * 127 * K < 2^31  <=>  K <= 133144. */
+#define SQ_MAX_K_INT32 133144
+
+/* Flags of sq_smooth_fold_weights. */
+#define SQ_SMOOTH_COMPUTE 0u /* compute s from absmax and W, write it to `smooth` */
+#define SQ_SMOOTH_GIVEN 1u   /* read s from `smooth` (not written) */
+#define SQ_SMOOTH_NONE 2u    /* s = 1 (plain per-channel weight quantisation); `smooth` and `absmax` may be NULL */
+
+const char* sq_status_string(sq_status status);
+int sq_last_hip_error(void);
+/* Library version as 10000*major + 100*minor + patch. */
+int sq_version(void);
+
+/*
+ * Calibration: per-input-channel activation absmax, as a running maximum.
+ * [W8A8] "How the smoothing factor is computed" (A_j is the largest activation
+ * seen in channel j over the calibration samples); [CALIB] "The Technical
+ * Workflow for Int8 Quantization Deployment" (maximum absolute value per
+ * channel).
+ *
+ *   absmax[j] = max(absmax[j], max_{0<=t<T} |x[t*ldx + j]|)   for 0 <= j < K
+ *
+ * x:      [T x ldx] of type xt (SQ_F32, SQ_BF16 or SQ_F16), read only.
+ * absmax: [K] binary32, read and written. The caller zero-fills it once before
+ *         the first calibration batch and then calls once per batch. Entries
+ *         stay non-negative.
+ * The result is exact (a maximum), independent of launch order.
+ */
+sq_status sq_calibrate_absmax(const void* x, sq_dtype xt, int64_t t, int64_t k, int64_t ldx,
+                              float* absmax, sq_stream_t stream);
+
+/*
+ * Load-time weight preparation: smoothing factor, fold, per-output-channel
+ * symmetric int8 quantisation.
+ * [W8A8] "How the smoothing factor is computed" (s_j from the activation
+ * absmax A_j, the largest weight magnitude W_j of row j and alpha; row j of W
+ * is multiplied by s_j); "How the Model Was Compressed" and "Why Naive Weight
+ * Quantization Doesn't Work" (scale = max|column| / 127, q = round(w/scale),
+ * one scale per output channel).
+ *
+ *   W_j   = max_n |w[j][n]|
+ *   s_j   = fl32( A_j^alpha / W_j^(1-alpha) )   powers and quotient in binary64;
+ *           s_j = 1 when A_j == 0 or W_j == 0              (SQ_SMOOTH_COMPUTE)
+ *   W'_jn = fl32(s_j * w[j][n])
+ *   sw_n  = fl32(max_j |W'_jn| / 127)
+ *   wq[n][j] = clamp(round_half_even(fl32(W'_jn / sw_n)), -127, 127); 0 when sw_n == 0
+ *
+ * absmax:  [K] binary32 (from sq_calibrate_absmax); unused with SQ_SMOOTH_GIVEN/NONE.
+ * w:       [K x ldw] of type wt (SQ_F32, SQ_BF16 or SQ_F16). Unlike the other
+ *          inputs, W may have any leading dimension >= N (16-byte aligned rows
+ *          are read with vector loads, others element by element); the
+ *          pointer must be aligned to the element size.
+ * alpha:   migration strength in [0, 1] ([CALIB]); unused unless SQ_SMOOTH_COMPUTE.
+ * flags:   one of SQ_SMOOTH_COMPUTE, SQ_SMOOTH_GIVEN, SQ_SMOOTH_NONE.
+ * smooth:  [K] binary32; written (COMPUTE), read (GIVEN) or unused (NONE, may be NULL).
+ * wq:      [N x K] int8 output (K-contiguous).
+ * w_scale: [N] binary32 output.
+ * ws:      workspace of sq_smooth_fold_workspace_size(k, n) bytes.
+ */
+size_t sq_smooth_fold_workspace_size(int64_t k, int64_t n);
+sq_status sq_smooth_fold_weights(const float* absmax, const void* w, sq_dtype wt, int64_t k, int64_t n,
+                                 int64_t ldw, double alpha, uint32_t flags, float* smooth, int8_t* wq,
+                                 float* w_scale, void* ws, size_t ws_bytes, sq_stream_t stream);
+
+/*
+ * Run-time per-token dynamic int8 activation quantisation with the
+ * smoothing divide fused in.
+ * [W8A8] "How the Model Was Compressed" (one scale per token over all its
+ * channels, computed at run time); "Why Activation Quantization Is Hard"
+ * (scale = max|x| / 127, q = round(x/scale)); "How the smoothing factor is
+ * computed" (the activation side is divided by s).
+ *
+ *   xh_ij = fl32(x_ij / s_j)          (x_ij itself when smooth == NULL)
+ *   d_i   = fl32(max_j |xh_ij| / 127)
+ *   xq_ij = clamp(round_half_even(fl32(xh_ij / d_i)), -127, 127); 0 when d_i == 0
+ *
+ * Every division is correctly rounded binary32, as in IEEE-754.
+ * x: [M x ldx] of type xt (SQ_F32, SQ_BF16 or SQ_F16). smooth: [K] or NULL.
+ * xq: [M x K] int8 output. x_scale: [M] binary32 output.
+ */
+sq_status sq_quant_act_per_token(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx,
+                                 const float* smooth, int8_t* xq, float* x_scale, sq_stream_t stream);
+
+/*
+ * int8 x int8 -> int32 GEMM with the fused per-token x per-output-channel
+ * dequantisation epilogue, on the gfx950 int8 matrix cores.
+ * [INT8] "The architecture: every piece explained" (int32 accumulation; the
+ * accumulator is scaled by the outer product of row and column scales);
+ * [W8A8] "Performance After Quantization", Inter-Token Latency (the int8
+ * matmul output is converted back to bf16).
+ *
+ *   acc_in = sum_k xq[i][k] * wq[n][k]                       exact int32
+ *   y[i][n] = out( fl32( fl32( fl32(acc_in) * x_scale_i ) * w_scale_n ) )
+ *
+ * out() is round-to-nearest-even to yt = SQ_BF16, SQ_F16 or SQ_F32; yt =
+ * SQ_I32 writes acc itself (scales unused, may be NULL).
+ * xq: [M x K], wq: [N x K] (K-contiguous, rows 16-byte aligned), y: [M x ldy].
+ * K must not exceed SQ_MAX_K_INT32.
+ * ws: workspace of sq_w8a8_linear_workspace_size(m, n, k) bytes.
+ */
+size_t sq_w8a8_linear_workspace_size(int64_t m, int64_t n, int64_t k);
+sq_status sq_w8a8_linear(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
+                         int64_t m, int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy,
+                         void* ws, size_t ws_bytes, sq_stream_t stream);
+
+/*
+ * The whole run-time path in one call: sq_quant_act_per_token followed by
+ * sq_w8a8_linear on the same stream, with Xq and the row scales held in the
+ * workspace. The results equal those of the two calls made separately.
+ * ws: workspace of sq_w8a8_linear_dyn_workspace_size(m, n, k) bytes.
+ */
+size_t sq_w8a8_linear_dyn_workspace_size(int64_t m, int64_t n, int64_t k);
+sq_status sq_w8a8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const float* smooth,
+                             const int8_t* wq, const float* w_scale, int64_t m, int64_t n, int64_t k,
+                             void* y, sq_dtype yt, int64_t ldy, void* ws, size_t ws_bytes,
+                             sq_stream_t stream);
+
+/*
+ * LLM.int8() outlier detection over the feature columns of X.
+ * [INT8] "The architecture: every piece explained", top row (a column is an
+ * outlier when some |x| in it exceeds the threshold; 6.0 is the usual value).
+ *
+ *   mask[c] = (max_i |x[i][c]| > threshold) ? 1 : 0          (strictly greater)
+ *   idx[0 .. count-1] = the outlier columns in ascending order; *count = their number
+ *
+ * x: [M x ldx] SQ_F16 or SQ_BF16 or SQ_F32. mask: [K] uint8 output. idx: [K]
+ * int32 output (only the first *count entries are defined). count: one int32
+ * in device memory. ws: sq_outlier_detect_workspace_size(k) bytes.
+ */
+size_t sq_outlier_detect_workspace_size(int64_t k);
+sq_status sq_outlier_detect(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, float threshold,
+                            uint8_t* mask, int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
+                            sq_stream_t stream);
+
+/*
+ * LLM.int8() row-wise (vectorwise) int8 quantisation of the regular columns.
+ * [INT8] "End-to-end flow" (each row's scale is its absolute maximum over the
+ * regular features only).
+ *
+ *   d_i   = fl32(max_{c : mask[c]==0} |x_ic| / 127)
+ *   xq_ic = mask[c] ? 0 : clamp(round_half_even(fl32(x_ic / d_i)), -127, 127); 0 when d_i == 0
+ *
+ * Setting the outlier columns of Xq to zero gives the same int8 product as
+ * removing them from X and from W.
+ */
+sq_status sq_quant_act_rows_masked(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx,
+                                   const uint8_t* mask, int8_t* xq, float* x_scale, sq_stream_t stream);
+
+/*
+ * LLM.int8() decomposed linear layer, fp16 in and out.
+ * [INT8] "The architecture: every piece explained" and "End-to-end flow":
+ * detection, column split, int8 path with row scales over the regular
+ * columns and load-time column scales of W, fp16 path over the outlier slice,
+ * element-wise sum of the two fp16 partial products.
+ *
+ *   y_int  = fp16( fl32( fl32(fl32(acc_in) * d_i) * w_scale_n ) )
+ *   y_out  = fp16( sum over outlier columns c in ascending order of x_ic * w16[c][n] ),
+ *            each product and each partial sum rounded to binary32
+ *   y[i][n] = fp16( y_int + y_out )        (the exact sum of the two fp16 values, rounded once)
+ *
+ * x: [M x ldx] SQ_F16. wq: [N x K] int8 and w_scale: [N] from
+ * sq_smooth_fold_weights(..., SQ_SMOOTH_NONE) on the same fp16 W. w16: [K x
+ * ldw16] fp16 weights (only the outlier rows are read). y: [M x ldy] fp16.
+ * n_outliers: one int32 in device memory, the number of outlier columns found.
+ * ws: sq_int8_decomp_workspace_size(m, n, k) bytes.
+ */
+size_t sq_int8_decomp_workspace_size(int64_t m, int64_t n, int64_t k);
+sq_status sq_int8_decomp_linear(const void* x, int64_t ldx, const int8_t* wq, const float* w_scale,
+                                const void* w16, int64_t ldw16, int64_t m, int64_t n, int64_t k,
+                                float threshold, void* y, int64_t ldy, int32_t* n_outliers,
+                                void* ws, size_t ws_bytes, sq_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQ_H_ */

@@ -25,7 +25,7 @@ Readings (listed with reasons in the design notes):
 """
 from __future__ import annotations
 
-from typing import Dict
+from typing import Dict, Optional
 
 import numpy as np
 
@@ -63,13 +63,18 @@ def fp16_outlier_product(x: np.ndarray, w16: np.ndarray, mask: np.ndarray) -> np
 
 
 def int8_decomp_linear(x: np.ndarray, wq: np.ndarray, w_scale: np.ndarray,
-                       w16: np.ndarray, threshold: float = 6.0) -> Dict[str, np.ndarray]:
+                       w16: np.ndarray, threshold: float = 6.0,
+                       mask: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """The decomposed linear layer. Returns every intermediate by name.
 
     x: [M x K] fp16 values; wq: [N x K] int8 (per-column scales over all K
     rows, made at load time); w_scale: [N]; w16: [K x N] fp16 weights.
+    ``mask`` replaces the detection step when the outlier columns are already
+    known (for example from all rows of a matrix whose rows are evaluated one
+    subset at a time; every later step is row-independent).
     """
-    mask = detect_outliers(x, threshold)
+    if mask is None:
+        mask = detect_outliers(x, threshold)
     xq, dx = quantize_rows_regular(x, mask)
     acc = int8_matmul(xq, wq)
     y = (acc.astype(F32) * dx[:, None]).astype(F32)

@@ -1,0 +1,124 @@
+// Device-side helpers shared by the gfx950 kernels of the W8A8 library.
+//
+// Storage formats: bf16 and fp16 values travel as uint16_t bit patterns;
+// 16-byte vectors carry 8 of them, or 4 binary32 values.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sq.h"
+
+namespace sqk {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kQMax = 127;
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// binary32 -> bf16, round to nearest, ties to even (NaN is outside the contract).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// binary32 -> binary16 with the hardware conversion (round to nearest even).
+// The empty asm pins f as a rounded binary32 value: without it the compiler
+// folds "multiply, then convert to half" into one v_fma_mix instruction that
+// rounds the exact product straight to binary16, which differs from rounding
+// to binary32 first whenever the binary32 product sits on a binary16 tie.
+__device__ __forceinline__ uint32_t f32_to_f16(float f) {
+  asm volatile("" : "+v"(f));
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Element types of the activation / weight inputs.
+struct F32In {
+  static constexpr int kVec = 4;  // elements per 16-byte vector
+  static constexpr int kBytes = 4;
+  __device__ __forceinline__ static float load1(const uint8_t* p) { return *reinterpret_cast<const float*>(p); }
+  __device__ __forceinline__ static void unpack(const u32x4& v, float* o) {
+    o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+  }
+};
+struct BF16In {
+  static constexpr int kVec = 8;
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static float load1(const uint8_t* p) {
+    return bf16_to_f32(*reinterpret_cast<const uint16_t*>(p));
+  }
+  __device__ __forceinline__ static void unpack(const u32x4& v, float* o) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+struct F16In {
+  static constexpr int kVec = 8;
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static float load1(const uint8_t* p) {
+    return f16_to_f32(*reinterpret_cast<const uint16_t*>(p));
+  }
+  __device__ __forceinline__ static void unpack(const u32x4& v, float* o) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = f16_to_f32(w[i] & 0xFFFFu);
+      o[2 * i + 1] = f16_to_f32(w[i] >> 16);
+    }
+  }
+};
+
+// ---------------------------------------------------------------- loads
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void store16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// ---------------------------------------------------------------- reductions
+// Maximum over the 64 lanes of a wavefront (every lane receives it).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Maximum over a workgroup of kThreads threads; `red` holds kThreads/64 floats of LDS.
+template <int kThreads>
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int wid = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wid] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+// Running maximum of non-negative binary32 values: their bit patterns order like the values.
+__device__ __forceinline__ void atomic_max_nonneg(float* addr, float v) {
+  atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
+}
+
+// ---------------------------------------------------------------- rounding
+// round-half-to-even to an integer, then clamp to the symmetric int8 range.
+__device__ __forceinline__ int quant_rne_clamp(float q) {
+  float r = __builtin_rintf(q);
+  r = fminf(fmaxf(r, -(float)kQMax), (float)kQMax);
+  return (int)r;
+}
+
+}  // namespace sqk

@@ -1,0 +1,42 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+// Each returns the HIP error of its launches; arguments are validated by the
+// C-ABI layer before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sq.h"
+
+namespace sqh {
+
+// Extra inputs of the LLM.int8() epilogue: the fp16 outlier slice.
+struct DecompArgs {
+  const uint16_t* x;    // [M x ldx] fp16 activations
+  int64_t ldx;
+  const uint16_t* w16;  // [K x ldw] fp16 weights
+  int64_t ldw;
+  const int32_t* idx;   // ascending outlier columns
+  const int32_t* count; // number of outlier columns (device)
+};
+
+hipError_t fill_u32(void* p, uint32_t value, int64_t count, hipStream_t s);
+
+hipError_t absmax_cols(const void* x, sq_dtype xt, int64_t t, int64_t k, int64_t ldx, float* absmax,
+                       hipStream_t s);
+
+hipError_t outlier_select(const float* colmax, int64_t k, float threshold, uint8_t* mask, int32_t* idx,
+                          int32_t* count, hipStream_t s);
+
+hipError_t fold_weights(const float* absmax, const void* w, sq_dtype wt, int64_t k, int64_t n, int64_t ldw,
+                        double alpha, uint32_t flags, float* smooth, int8_t* wq, float* w_scale,
+                        float* colmax_ws, hipStream_t s);
+
+hipError_t quant_rows(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, const float* smooth,
+                      const uint8_t* mask, int8_t* xq, float* x_scale, hipStream_t s);
+
+hipError_t gemm_i8(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
+                   int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec,
+                   hipStream_t s);
+
+}  // namespace sqh
