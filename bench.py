@@ -44,7 +44,22 @@ def parse():
     p.add_argument("--alpha", type=float, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle time budget")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run a plain device-to-device copy of 512 MiB (5 times), the known-size "
+                        "reference that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
     return p.parse_args()
+
+
+def copy_probe():
+    import torch
+    n = 512 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
 
 
 def kernel_source_hash(name: str) -> str:
@@ -98,6 +113,10 @@ def main():
         print("bench.py runs on one GPU only: the W8A8 linear layer is built and measured on a single "
               "MI355X (no sharding or collectives in this library); use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe()
+        return
 
     import numpy as np
     import torch

@@ -105,6 +105,66 @@ def test_quant_act(dtype, m, k, smooth):
     assert np.array_equal(host(xq), xq_ref)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("k", [64, 192, 4096, 4160, 8192, 14336, 16384])
+@pytest.mark.parametrize("smooth", [False, True])
+def test_quant_act_prefill_kernel(dtype, k, smooth):
+    """Row counts >= 64 run the row-per-wave kernel with Markstein quotients."""
+    if dtype == "f32" and k > 8192:
+        pytest.skip("covered by the workgroup-per-row kernel")
+    m = 133
+    log("quant wave", dtype, k, smooth)
+    c = workloads.random_linear_case(m=m, k=k, n=64, seed=k + m + int(smooth), dtype=dtype, calib_rows=64,
+                                     model="silu_gated" if k > 8192 else "gaussian_outlier")
+    x = c.x.copy()
+    x[3] = 0
+    s_ref = None
+    if smooth:
+        s_ref = oracle.smoothing_factors(oracle.calibrate_absmax(c.x_calib), oracle.weight_row_absmax(c.w), 0.5)
+    xq, dx = sq.sq_quant_act_per_token(to_dev(x, dtype), None if s_ref is None else torch.from_numpy(s_ref).to(dev()))
+    xq_ref, dx_ref = oracle.quantize_activations(x, s_ref)
+    assert np.array_equal(host(dx), dx_ref)
+    assert np.array_equal(host(xq), xq_ref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quant_act_range_fallbacks(dtype):
+    """Rows and smoothing factors outside the fast-division bounds take IEEE division
+    and still match the oracle bit for bit: tiny rows, huge rows, rows mixing tiny
+    and normal values, and smoothing factors far from 1."""
+    m, k = 96, 512
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    x[0] *= np.float32(1e-35)                     # whole row tiny: d < 2^-30
+    x[1] *= np.float32(1e25)                      # huge row: max > 2^50
+    x[2, ::3] *= np.float32(1e-30)                # tiny entries inside a normal row
+    x[3, 5] = np.float32(3e-39)                   # a subnormal entry
+    x[4] = 0
+    x[5, :7] = [1e-20, -2e-25, 5e-30, 1e-38, 2e-40, -7e-42, 0]
+    xr = oracle.round_bf16(x) if dtype == "bf16" else x
+    for s_ref in (None, np.exp(rng.uniform(-2, 2, k)).astype(np.float32)):
+        xq, dx = sq.sq_quant_act_per_token(to_dev(xr, dtype), None if s_ref is None else torch.from_numpy(s_ref).to(dev()))
+        xq_ref, dx_ref = oracle.quantize_activations(xr, s_ref)
+        assert np.array_equal(host(dx), dx_ref) and np.array_equal(host(xq), xq_ref)
+    # smoothing factors outside [2^-20, 2^20] switch the whole launch to IEEE division
+    s_bad = np.exp(rng.uniform(-2, 2, k)).astype(np.float32)
+    s_bad[17] = np.float32(1e-8)
+    s_bad[18] = np.float32(3e7)
+    xq, dx = sq.sq_quant_act_per_token(to_dev(xr, dtype), torch.from_numpy(s_bad).to(dev()))
+    xq_ref, dx_ref = oracle.quantize_activations(xr, s_bad)
+    assert np.array_equal(host(dx), dx_ref) and np.array_equal(host(xq), xq_ref)
+
+
+@pytest.mark.parametrize("k,nout", [(512, 3), (4096, 8), (8192, 0)])
+def test_quant_rows_masked_prefill_kernel(k, nout):
+    cfg = workloads.decomp_case(seed=k + nout, m=200, k=k, n=64, n_outlier_cols=nout)
+    xh = to_dev(cfg.x, "f16")
+    mask_ref = oracle.detect_outliers(cfg.x, 6.0)
+    xq, dx = sq.sq_quant_act_rows_masked(xh, torch.from_numpy(mask_ref.astype(np.uint8)).to(dev()))
+    xq_ref, dx_ref = oracle.quantize_rows_regular(cfg.x, mask_ref)
+    assert np.array_equal(host(xq), xq_ref) and np.array_equal(host(dx), dx_ref)
+
+
 def test_quant_act_ties_and_padding():
     """Exact .5 quotients round to even; a padded leading dimension is honoured."""
     k = 128
@@ -119,8 +179,11 @@ def test_quant_act_ties_and_padding():
 
 
 # --------------------------------------------------------------------------- int8 GEMM
+# Small shapes run the 128 x 128 kernel; from about a million outputs on, the
+# 256-row kernel (BN 256 or 192), including ragged M and N tails.
 GEMM_SHAPES = [(1, 1, 64), (3, 5, 64), (16, 512, 256), (100, 72, 192), (129, 257, 320), (256, 256, 512),
-               (300, 130, 4096), (77, 1000, 1088), (1, 4096, 14336), (64, 200, 14336)]
+               (300, 130, 4096), (77, 1000, 1088), (1, 4096, 14336), (64, 200, 14336),
+               (1000, 1100, 384), (513, 2050, 1024), (2048, 768, 256), (256, 4096, 128), (777, 1536, 4160)]
 
 
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
@@ -148,7 +211,8 @@ def test_gemm_extremes():
 
 
 @pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("m,n,k", [(5, 64, 128), (129, 257, 320), (200, 300, 4096)])
+@pytest.mark.parametrize("m,n,k", [(5, 64, 128), (129, 257, 320), (200, 300, 4096), (1000, 1100, 384),
+                                   (512, 2048, 256)])
 def test_gemm_dequant(out, m, n, k):
     log("gemm dequant", out, m, n, k)
     xq = workloads.uniform_int8((m, k), seed=3 * m + n, stream=2)
@@ -163,8 +227,8 @@ def test_gemm_dequant(out, m, n, k):
     log("  exact fraction", frac)
 
 
-def test_gemm_padded_output():
-    m, n, k = 40, 50, 256
+@pytest.mark.parametrize("m,n,k", [(40, 50, 256), (700, 1500, 256)])
+def test_gemm_padded_output(m, n, k):
     xq = workloads.uniform_int8((m, k), seed=1, stream=4)
     wq = workloads.uniform_int8((n, k), seed=1, stream=5)
     dx = workloads.positive_scales(m, seed=2)
@@ -205,7 +269,7 @@ def test_linear_dyn_equals_two_calls(m, k, n):
 
 # --------------------------------------------------------------------------- LLM.int8()
 @pytest.mark.parametrize("m,k,n,nout", [(64, 256, 96, 3), (130, 512, 200, 0), (257, 1024, 333, 9),
-                                        (96, 256, 64, 256)])
+                                        (96, 256, 64, 256), (1030, 512, 1100, 5), (600, 256, 2000, 40)])
 def test_int8_decomp_small(m, k, n, nout):
     log("decomp", m, k, n, nout)
     cfg = workloads.decomp_case(seed=m + n, m=m, k=k, n=n, n_outlier_cols=min(nout, k))

@@ -1,0 +1,393 @@
+// Large-tile int8 MFMA GEMM for prefill-sized problems, with the fused
+// dequantisation epilogue (and the LLM.int8() fp16 outlier slice).
+//
+// The LLM.int8() page, "The architecture: every piece explained": int8 x int8
+// products accumulated in int32, scaled by the outer product of the row
+// (token) and column (output channel) scales; the fp16 outlier slice is added
+// to the dequantised product. "Half the Size, Better Performance, Same
+// Accuracy: Understanding W8A8 INT8 LLM Quantization", "Performance After
+// Quantization" (Inter-Token Latency): the result goes back to bf16.
+//
+// Design for gfx950 (256 CUs, 160 KiB LDS per CU, 64-wide waves):
+//  * one 256-thread workgroup per CU computes a 256 x BN output tile
+//    (BN = 256, or 192 when that fills the 256 CUs better); 4 waves in a 2 x 2
+//    grid, each owning 128 x BN/2 outputs = 4 x BN/64 blocks of
+//    v_mfma_i32_32x32x32_i8 with int32 accumulators in AGPRs. A 128-row wave
+//    tile needs 64 B of LDS reads per clock per CU at full MFMA rate, half of
+//    what a 64-row tile needs.
+//  * K advances 128 bytes per stage through a double-buffered LDS (2 x 64
+//    KiB) filled by gfx950's direct global-to-LDS transfers (global_load_lds,
+//    16 bytes per lane): no registers stage the tiles, every tile row is one
+//    full 128-byte line per stage (full-line requests: the L1 sustains only
+//    a bounded number of requests in flight, so 64-byte requests halve the
+//    bandwidth), and each stage's transfers start a full stage (~2000 MFMA
+//    cycles) before it is consumed. Completion is tracked with explicit vmcnt
+//    waits and one barrier per stage.
+//  * LDS rows are 128 bytes; the eight 16-byte chunks of row r are XOR-
+//    swizzled with r & 7, and each transfer lane fetches the chunk that
+//    belongs at its fixed LDS slot, so the MFMA fragment reads are free of
+//    bank conflicts.
+//  * The MFMA A operand is the Wq fragment and B the Xq fragment, so a lane's
+//    four consecutive accumulator registers are four consecutive output
+//    columns of one token: the epilogue writes 8-byte (bf16/fp16) or 16-byte
+//    (fp32/int32) vectors.
+//  * Workgroups are dispatched round-robin over the 8 XCDs; the tile order
+//    gives each XCD a contiguous range of tiles, grouped 4 tile-rows at a time,
+//    so that tiles sharing Xq and Wq panels run under the same L2.
+#include "sq_common.hpp"
+#include "sq_launch.hpp"
+
+namespace sqk {
+
+constexpr int kBigBM = 256;
+constexpr int kBigBK = 128;    // k bytes per pipeline stage: one 128-byte line per tile row
+constexpr int kBigStages = 2;  // LDS double buffer
+constexpr int kGroupM = 4;
+
+enum BigOut { kBigF32 = 0, kBigBF16 = 1, kBigF16 = 2, kBigI32 = 3, kBigDecomp = 4 };
+
+// Byte offset of 16-byte chunk c (0..7) of tile row r in a stage (128-byte
+// rows). The chunk index is XOR-ed with r & 7, so the MFMA fragment reads (32
+// consecutive rows x one chunk per half-wave) spread over all banks; without
+// it every lane of a half-wave would hit the same bank group.
+__device__ __forceinline__ int big_swz(int r) { return r & 7; }
+__device__ __forceinline__ int big_lds_off(int r, int c) { return r * kBigBK + ((c ^ big_swz(r)) << 4); }
+
+template <int BN>
+struct BigCfg {
+  static constexpr int kWN = BN / 2;
+  static constexpr int kFN = kWN / 32;
+  static constexpr int kFM = 4;
+  static constexpr int kStageA = kBigBM * kBigBK;
+  static constexpr int kStage = (kBigBM + BN) * kBigBK;
+  // 1 KiB direct-to-LDS transfers (8 rows each) per wave and stage
+  static constexpr int kDmaA = kBigBM / 8 / 4;
+  static constexpr int kDmaB = BN / 8 / 4;
+  static constexpr int kDma = kDmaA + kDmaB;
+};
+
+struct BigEpi {
+  const float* x_scale;
+  const float* w_scale;
+  void* y;
+  int64_t ldy;
+  sqh::DecompArgs dec;
+};
+
+// s_waitcnt vmcnt(n) with the lgkm and exp counters left alone (gfx9 encoding).
+template <int kN>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((kN & 0xF) | ((kN >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int kOut>
+__device__ __forceinline__ void store4(void* y, int64_t off, const float* v, const int* a, bool vec, int nvalid) {
+  if (kOut == kBigI32) {
+    int32_t* p = reinterpret_cast<int32_t*>(y) + off;
+    if (vec) {
+      *reinterpret_cast<int4*>(p) = make_int4(a[0], a[1], a[2], a[3]);
+    } else {
+      for (int e = 0; e < nvalid; ++e) p[e] = a[e];
+    }
+  } else if (kOut == kBigF32) {
+    float* p = reinterpret_cast<float*>(y) + off;
+    if (vec) {
+      *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+      for (int e = 0; e < nvalid; ++e) p[e] = v[e];
+    }
+  } else {
+    uint32_t h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = kOut == kBigBF16 ? f32_to_bf16(v[e]) : f32_to_f16(v[e]);
+    uint16_t* p = reinterpret_cast<uint16_t*>(y) + off;
+    if (vec) {
+      *reinterpret_cast<uint2*>(p) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    } else {
+      for (int e = 0; e < nvalid; ++e) p[e] = (uint16_t)h[e];
+    }
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int BN, int kOut, bool kVec>
+__global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
+                                                          int M, int N, int K, BigEpi ep) {
+  using C = BigCfg<BN>;
+  __shared__ __attribute__((aligned(1024))) int8_t smem[kBigStages * C::kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+
+  // ---- tile schedule: contiguous tile ranges per XCD, grouped along M
+  const int nbm = (M + kBigBM - 1) / kBigBM;
+  const int nbn = (N + BN - 1) / BN;
+  const int total = nbm * nbn;
+  int t = blockIdx.x;
+  const int full = total & ~7;
+  if (t < full) t = (t & 7) * (full >> 3) + (t >> 3);
+  const int in_group = kGroupM * nbn;
+  const int first_m = (t / in_group) * kGroupM;
+  const int gm = min(nbm - first_m, kGroupM);
+  const int tm = first_m + (t % in_group) % gm;
+  const int tn = (t % in_group) / gm;
+  const int m0 = tm * kBigBM, n0 = tn * BN;
+
+  // ---- direct-to-LDS transfers: lane L of a 1 KiB transfer fills LDS bytes
+  // [16L, 16L+16) of an 8-row block, i.e. row L/8, physical chunk L%8, so it
+  // fetches the logical chunk (L%8) ^ swizzle(row) of that row from HBM; the
+  // 8 lanes of a row read one whole 128-byte line.
+  const int8_t* src[C::kDma];
+  int dst[C::kDma];
+#pragma unroll
+  for (int i = 0; i < C::kDma; ++i) {
+    const bool is_a = i < C::kDmaA;
+    const int blk = (is_a ? i : i - C::kDmaA) * 4 + wid;  // 8-row block within the operand tile
+    const int r = blk * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ big_swz(r);
+    if (is_a) {
+      src[i] = A + (int64_t)min(m0 + r, M - 1) * K + c * 16;
+      dst[i] = blk * 1024;
+    } else {
+      src[i] = B + (int64_t)min(n0 + r, N - 1) * K + c * 16;
+      dst[i] = C::kStageA + blk * 1024;
+    }
+  }
+  const int nk = K / kBigBK;
+  auto issue = [&](int kt) {
+    int8_t* stage = smem + (kt % kBigStages) * C::kStage;
+    const int64_t koff = (int64_t)kt * kBigBK;
+#pragma unroll
+    for (int i = 0; i < C::kDma; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + koff), (lds_void*)(stage + dst[i]), 16, 0, 0);
+  };
+
+  v16i acc[C::kFN][C::kFM];
+#pragma unroll
+  for (int j = 0; j < C::kFN; ++j)
+#pragma unroll
+    for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0;
+
+  issue(0);
+  if (nk > 1) issue(1);
+
+  const int frow = lane & 31;
+  const int fhalf = lane >> 5;
+  // Fragments of one 32-k substep: Xq blocks for this wave's 128 tokens and
+  // Wq blocks for its BN/2 output channels.
+  auto read_frags = [&](const int8_t* stage, int ks, v4i* xf, v4i* wf) {
+    const int c = 2 * ks + fhalf;
+#pragma unroll
+    for (int i = 0; i < C::kFM; ++i)
+      xf[i] = *reinterpret_cast<const v4i*>(stage + big_lds_off(wm * 128 + 32 * i + frow, c));
+#pragma unroll
+    for (int j = 0; j < C::kFN; ++j)
+      wf[j] = *reinterpret_cast<const v4i*>(stage + C::kStageA + big_lds_off(wn * C::kWN + 32 * j + frow, c));
+  };
+  auto mfmas = [&](const v4i* xf, const v4i* wf) {
+#pragma unroll
+    for (int j = 0; j < C::kFN; ++j)
+#pragma unroll
+      for (int i = 0; i < C::kFM; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[j], xf[i], acc[j][i], 0, 0, 0);
+  };
+  auto stage_ptr = [&](int kt) { return smem + (kt & 1) * C::kStage; };
+
+  // Software pipeline over the 4 substeps of a stage: the fragments of the
+  // next substep are read from LDS while the MFMAs of the current one run.
+  // The stage hand-over sits in front of the last substep's MFMAs: wait for
+  // the next stage's transfers, retire this wave's LDS reads, barrier (now no
+  // wave reads the current buffer any more), start the transfers of the
+  // stage after next into it, read the next stage's first fragments.
+  v4i fx[2][C::kFM], fw[2][C::kFN];
+  if (nk > 1)
+    wait_vmcnt<C::kDma>();
+  else
+    wait_vmcnt<0>();
+  lds_barrier();
+  read_frags(stage_ptr(0), 0, fx[0], fw[0]);
+  wait_lgkmcnt0();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int8_t* cur = stage_ptr(kt);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int p = ks & 1;
+      if (ks < 3) {
+        read_frags(cur, ks + 1, fx[p ^ 1], fw[p ^ 1]);
+      } else if (kt + 1 < nk) {
+        wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        lds_barrier();
+        if (kt + 2 < nk) issue(kt + 2);
+        read_frags(stage_ptr(kt + 1), 0, fx[p ^ 1], fw[p ^ 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(fx[p], fw[p]);
+      __builtin_amdgcn_sched_barrier(0);
+      // retire the prefetch issued a substep ago (long complete) so that at
+      // most one substep's reads are ever outstanding
+      if (ks != 3) wait_lgkmcnt0();
+    }
+    wait_lgkmcnt0();
+  }
+
+  // ---- epilogue: lane holds D[n][m] with m = l%32 and n = 8*(r/4) + 4*(l/32) + r%4 of each 32x32 block
+  const int mw = m0 + wm * 128;
+  const int nw = n0 + wn * C::kWN;
+  int mrow[C::kFM];
+  float xs[C::kFM];
+#pragma unroll
+  for (int i = 0; i < C::kFM; ++i) {
+    mrow[i] = mw + 32 * i + frow;
+    xs[i] = (kOut != kBigI32 && mrow[i] < M) ? ep.x_scale[mrow[i]] : 0.f;
+  }
+  const int cnt = kOut == kBigDecomp ? *ep.dec.count : 0;
+#pragma unroll
+  for (int j = 0; j < C::kFN; ++j) {
+    float yo[C::kFM][16];
+    if (kOut == kBigDecomp) {
+#pragma unroll
+      for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) yo[i][r] = 0.f;
+      for (int c = 0; c < cnt; ++c) {
+        const int64_t jc = ep.dec.idx[c];
+        float xv[C::kFM];
+#pragma unroll
+        for (int i = 0; i < C::kFM; ++i)
+          xv[i] = mrow[i] < M ? f16_to_f32(ep.dec.x[(int64_t)mrow[i] * ep.dec.ldx + jc]) : 0.f;
+        const uint16_t* wrow = ep.dec.w16 + jc * ep.dec.ldw;
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int n = nw + 32 * j + 8 * rg + 4 * fhalf;
+          float wv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wv[e] = n + e < N ? f16_to_f32(wrow[n + e]) : 0.f;
+#pragma unroll
+          for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yo[i][4 * rg + e] = __fadd_rn(yo[i][4 * rg + e], __fmul_rn(xv[i], wv[e]));
+        }
+      }
+    }
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int n = nw + 32 * j + 8 * rg + 4 * fhalf;
+      if (n >= N) continue;
+      const int nvalid = min(4, N - n);
+      float ws[4] = {0.f, 0.f, 0.f, 0.f};
+      if (kOut != kBigI32) {
+        if (kVec && nvalid == 4) {
+          const float4 w4 = *reinterpret_cast<const float4*>(ep.w_scale + n);
+          ws[0] = w4.x; ws[1] = w4.y; ws[2] = w4.z; ws[3] = w4.w;
+        } else {
+          for (int e = 0; e < nvalid; ++e) ws[e] = ep.w_scale[n + e];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < C::kFM; ++i) {
+        const int m = mrow[i];
+        if (m >= M) continue;
+        int a[4];
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = acc[j][i][4 * rg + e];
+          v[e] = __fmul_rn(__fmul_rn((float)a[e], xs[i]), ws[e]);
+          if (kOut == kBigDecomp) {
+            const float yi = f16_to_f32(f32_to_f16(v[e]));
+            v[e] = __fadd_rn(yi, f16_to_f32(f32_to_f16(yo[i][4 * rg + e])));
+          }
+        }
+        const int64_t off = (int64_t)m * ep.ldy + n;
+        store4<kOut == kBigDecomp ? kBigF16 : kOut>(ep.y, off, v, a, kVec && nvalid == 4, nvalid);
+      }
+    }
+  }
+}
+
+template <int BN, int kOut, bool kVec>
+static void launch_big(const int8_t* xq, const int8_t* wq, int M, int N, int K, const BigEpi& ep, hipStream_t s) {
+  const int tiles = ((M + kBigBM - 1) / kBigBM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_big_kernel<BN, kOut, kVec>), dim3(tiles), dim3(256), 0, s, xq, wq, M, N, K, ep);
+}
+
+template <int BN, int kOut>
+static void launch_big_v(const int8_t* xq, const int8_t* wq, int M, int N, int K, const BigEpi& ep, bool vec,
+                         hipStream_t s) {
+  if (vec)
+    launch_big<BN, kOut, true>(xq, wq, M, N, K, ep, s);
+  else
+    launch_big<BN, kOut, false>(xq, wq, M, N, K, ep, s);
+}
+
+template <int BN>
+static void launch_big_o(const int8_t* xq, const int8_t* wq, int M, int N, int K, const BigEpi& ep, int out, bool vec,
+                         hipStream_t s) {
+  switch (out) {
+    case kBigF32: launch_big_v<BN, kBigF32>(xq, wq, M, N, K, ep, vec, s); break;
+    case kBigBF16: launch_big_v<BN, kBigBF16>(xq, wq, M, N, K, ep, vec, s); break;
+    case kBigF16: launch_big_v<BN, kBigF16>(xq, wq, M, N, K, ep, vec, s); break;
+    case kBigI32: launch_big_v<BN, kBigI32>(xq, wq, M, N, K, ep, vec, s); break;
+    default: launch_big_v<BN, kBigDecomp>(xq, wq, M, N, K, ep, vec, s); break;
+  }
+}
+
+}  // namespace sqk
+
+namespace sqh {
+
+// Output tile width that fills the 256 CUs best: useful outputs over the
+// outputs that the scheduled waves of workgroups could compute.
+static int pick_bn(int64_t m, int64_t n) {
+  const int cands[2] = {256, 192};
+  int best = 256;
+  double best_eff = -1.0;
+  for (int bn : cands) {
+    const int64_t tiles = ((m + sqk::kBigBM - 1) / sqk::kBigBM) * ((n + bn - 1) / bn);
+    const int64_t waves = (tiles + 255) / 256;
+    const double eff = (double)m * (double)n / ((double)waves * 256.0 * sqk::kBigBM * bn);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = bn;
+    }
+  }
+  return best;
+}
+
+bool gemm_big_suits(int64_t m, int64_t n, int64_t k) {
+  return m >= 256 && n >= 192 && k % sqk::kBigBK == 0 && m * n >= ((int64_t)1 << 20);
+}
+
+hipError_t gemm_i8_big(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
+                       int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec,
+                       hipStream_t s) {
+  sqk::BigEpi ep{x_scale, w_scale, y, ldy, dec ? *dec : DecompArgs{}};
+  int out;
+  int eb;
+  if (dec) {
+    out = sqk::kBigDecomp; eb = 2;
+  } else {
+    switch (yt) {
+      case SQ_F32: out = sqk::kBigF32; eb = 4; break;
+      case SQ_BF16: out = sqk::kBigBF16; eb = 2; break;
+      case SQ_F16: out = sqk::kBigF16; eb = 2; break;
+      default: out = sqk::kBigI32; eb = 4; break;
+    }
+  }
+  const bool vec = (ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % (uintptr_t)(4 * eb) == 0) &&
+                   (out == sqk::kBigI32 || reinterpret_cast<uintptr_t>(w_scale) % 16 == 0);
+  const int M = (int)m, N = (int)n, K = (int)k;
+  if (pick_bn(m, n) == 192)
+    sqk::launch_big_o<192>(xq, wq, M, N, K, ep, out, vec, s);
+  else
+    sqk::launch_big_o<256>(xq, wq, M, N, K, ep, out, vec, s);
+  return hipGetLastError();
+}
+
+}  // namespace sqh

@@ -11,13 +11,13 @@
 // taken over the regular (non-outlier) columns only; the outlier columns of
 // Xq are zero.
 //
-// One 256-thread workgroup owns a row at a time (grid-stride over rows). Each
-// thread loads kCh 16-byte vectors of the row (coalesced: consecutive threads
-// read consecutive 16 bytes), keeps the smoothed values in registers, the
-// workgroup reduces the row maximum through LDS, then each thread writes its
-// int8 values with one 4- or 8-byte store per vector. X is read from HBM once
-// and Xq written once. Rows longer than 8 vectors per thread use a two-pass
-// variant that reads the row a second time.
+// Two kernels. quant_wave_kernel (below) serves prefill-sized inputs. For few
+// rows (decode) or very long rows, one 256-thread workgroup owns a row at a
+// time (grid-stride over rows): each thread loads kCh 16-byte vectors of the
+// row (coalesced), keeps the smoothed values in registers, the workgroup
+// reduces the row maximum through LDS, then each thread writes its int8 values
+// with one 4- or 8-byte store per vector; rows longer than 8 vectors per
+// thread use a two-pass variant that reads the row a second time.
 #include "sq_common.hpp"
 #include "sq_launch.hpp"
 
@@ -67,39 +67,6 @@ __device__ __forceinline__ void store_q(int8_t* __restrict__ dst, const float* f
   }
 }
 
-template <class In, int kCh, bool kSmooth, bool kMask>
-__global__ __launch_bounds__(256) void quant_rows_kernel(const uint8_t* __restrict__ x, int64_t m, int64_t nvec,
-                                                         int64_t ldx_bytes, const float* __restrict__ smooth,
-                                                         const uint8_t* __restrict__ mask, int8_t* __restrict__ xq,
-                                                         float* __restrict__ x_scale) {
-  constexpr int V = In::kVec;
-  __shared__ float red[4];
-  const int64_t k = nvec * V;
-  for (int64_t row = blockIdx.x; row < m; row += gridDim.x) {
-    const uint8_t* xr = x + row * ldx_bytes;
-    float f[kCh][V];
-    float amax = 0.f;
-#pragma unroll
-    for (int c = 0; c < kCh; ++c) {
-      const int64_t vi = threadIdx.x + c * 256;
-      if (vi < nvec) {
-        load_smoothed<In, kSmooth, kMask>(xr, smooth, mask, vi, f[c]);
-#pragma unroll
-        for (int e = 0; e < V; ++e) amax = fmaxf(amax, fabsf(f[c][e]));
-      }
-    }
-    amax = block_max<256>(amax, red);
-    const float d = amax / (float)kQMax;
-    if (threadIdx.x == 0) x_scale[row] = d;
-    int8_t* qr = xq + row * k;
-#pragma unroll
-    for (int c = 0; c < kCh; ++c) {
-      const int64_t vi = threadIdx.x + c * 256;
-      if (vi < nvec) store_q<V>(qr + vi * V, f[c], d);
-    }
-  }
-}
-
 // Rows of any length: pass 1 finds the maximum, pass 2 re-reads and quantises.
 template <class In, bool kSmooth, bool kMask>
 __global__ __launch_bounds__(256) void quant_rows_long_kernel(const uint8_t* __restrict__ x, int64_t m, int64_t nvec,
@@ -130,9 +97,281 @@ __global__ __launch_bounds__(256) void quant_rows_long_kernel(const uint8_t* __r
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Fast row kernel. Correctly rounded binary32 division costs about eleven VALU
+// instructions on gfx950 (v_div_scale / v_rcp / FMA refinement / v_div_fmas /
+// v_div_fixup), which made a straightforward kernel ALU-bound at ~20% of HBM
+// bandwidth. Every quotient here uses Markstein's FMA correction instead:
+// with r = RN(1/b),
+//     q0 = a*r,  e = fma(-q0, b, a) (exact),  q = fma(e, r, q0),
+// gives q = RN(a/b) whenever no step leaves the normal range. The divisors are
+// the s_j (each thread forms RN(1/s_j) for its own columns once, with IEEE
+// division, and keeps s_j and 1/s_j in registers for all the rows it visits)
+// and the row scale d (one IEEE division per row).
+// Range argument for the fast path of a whole row: all s_j in [2^-20, 2^20],
+// d >= 2^-30 and max|x/s| <= 2^50. Then any |x| < 2^-60 (where the remainder
+// could underflow) gives |x/s| < 2^-40 and a quantised value of 0 under either
+// division; every other operand stays well inside the normal range. A row
+// outside these bounds is redone with IEEE division, and a launch whose s_j
+// leave the bounds uses IEEE division throughout.
+// kMk = false is the plain IEEE version, used when there are too few rows per
+// workgroup to amortise the reciprocals.
+// Layout: a 256-thread workgroup walks a grid-stride list of rows; thread t
+// owns the 16-byte vectors t, t+256, ... of every row (coalesced loads,
+// 8- or 4-byte coalesced stores), prefetches its vectors of the next row
+// while working on the current one (short rows), and the row maximum is a
+// wave reduction plus one barrier on double-buffered LDS partials.
+constexpr float kFastSMin = 0x1p-20f, kFastSMax = 0x1p20f;
+constexpr float kFastDMin = 0x1p-30f, kFastAMax = 0x1p50f;
+
+__device__ __forceinline__ float div_mk(float a, float b, float rb) {
+  const float q0 = a * rb;
+  const float e = __builtin_fmaf(-q0, b, a);
+  return __builtin_fmaf(e, rb, q0);
+}
+
+// int8 code of one quotient: clamp to [-127, 127], then adding 1.5 * 2^23
+// rounds to the nearest integer with ties to even (the sum lies in
+// [2^23, 2^24), where the binary32 spacing is 1) and leaves the two's-
+// complement code in the low byte of the sum's bit pattern.
+__device__ __forceinline__ uint32_t q_code(float v) {
+  v = __builtin_amdgcn_fmed3f(v, -(float)kQMax, (float)kQMax);
+  return __float_as_uint(v + 12582912.0f);
+}
+
+// Low bytes of four codes -> one little-endian word (v_perm_b32 picks bytes).
+__device__ __forceinline__ uint32_t pack4(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3) {
+  const uint32_t lo = __builtin_amdgcn_perm(c1, c0, 0x0C0C0400u);  // c0.b0, c1.b0
+  const uint32_t hi = __builtin_amdgcn_perm(c3, c2, 0x0C0C0400u);  // c2.b0, c3.b0
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+template <class In, int kCh, int kR, bool kSmooth, bool kMask, bool kMk>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint8_t* __restrict__ x, int64_t m, int nvec,
+                                                         int64_t ldx_bytes, const float* __restrict__ smooth,
+                                                         const uint8_t* __restrict__ mask, int8_t* __restrict__ xq,
+                                                         float* __restrict__ x_scale) {
+  constexpr int V = In::kVec;
+  constexpr bool kSmall = kCh * kR <= 8 && kCh <= 4;  // keep x/s between passes and prefetch the next rows
+  __shared__ float red[2][kR][4];
+  __shared__ int any_bad[4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int64_t k = (int64_t)nvec * V;
+  const int64_t ngroups = (m + kR - 1) / kR;
+
+  auto load_rows = [&](int64_t g, u32x4 (*raw)[kCh]) {
+#pragma unroll
+    for (int j = 0; j < kR; ++j) {
+      const int64_t row = g * kR + j;
+      if (row >= m) continue;
+      const uint8_t* xr = x + row * ldx_bytes;
+#pragma unroll
+      for (int c = 0; c < kCh; ++c) {
+        const int vi = tid + 256 * c;
+        if (vi < nvec) raw[j][c] = load16(xr + (int64_t)vi * 16);
+      }
+    }
+  };
+  // the first rows' loads go out before the reciprocals are formed
+  u32x4 raw[kR][kCh];
+  u32x4 nxt[kSmall ? kR : 1][kCh];
+  int64_t g = blockIdx.x;
+  if (kSmall && g < ngroups) load_rows(g, nxt);
+
+  float sreg[kSmooth ? kCh : 1][V];
+  float rreg[(kSmooth && kMk) ? kCh : 1][V];
+  uint32_t mreg[kMask ? kCh : 1][2];
+  int bad = 0;
+#pragma unroll
+  for (int c = 0; c < kCh; ++c) {
+    const int vi = tid + 256 * c;
+    if (vi >= nvec) continue;
+    if (kSmooth) {
+#pragma unroll
+      for (int e = 0; e < V; e += 4) {
+        const u32x4 sv = load16(smooth + (int64_t)vi * V + e);
+        sreg[c][e] = __uint_as_float(sv.x); sreg[c][e + 1] = __uint_as_float(sv.y);
+        sreg[c][e + 2] = __uint_as_float(sv.z); sreg[c][e + 3] = __uint_as_float(sv.w);
+      }
+      if (kMk) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          rreg[c][e] = 1.0f / sreg[c][e];
+          bad |= !(sreg[c][e] >= kFastSMin && sreg[c][e] <= kFastSMax);
+        }
+      }
+    }
+    if (kMask) {
+      const uint8_t* mp = mask + (int64_t)vi * V;
+      uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w0 |= (uint32_t)(mp[e] != 0) << (8 * e);
+#pragma unroll
+      for (int e = 4; e < V; ++e) w1 |= (uint32_t)(mp[e] != 0) << (8 * (e - 4));
+      mreg[c][0] = w0; mreg[c][1] = w1;
+    }
+  }
+  bool s_ok = kMk;
+  if (kMk && kSmooth) {
+    // workgroup-wide "some s_j outside the fast range", without draining the prefetch
+    const int wbad = __any(bad);
+    if (lane == 0) any_bad[wid] = wbad;
+    lds_barrier();
+    s_ok = !(any_bad[0] | any_bad[1] | any_bad[2] | any_bad[3]);
+  }
+
+  auto smoothed = [&](const u32x4& rv, int c, float* f, bool fast) {
+    In::unpack(rv, f);
+    if (kSmooth) {
+      if (kMk && fast) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) f[e] = div_mk(f[e], sreg[c][e], rreg[kMk ? c : 0][e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) f[e] = f[e] / sreg[c][e];
+      }
+    }
+    if (kMask) {
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        if ((mreg[c][e >> 2] >> (8 * (e & 3))) & 0xFFu) f[e] = 0.f;
+    }
+  };
+  int parity = 0;
+  // maximum over the workgroup of each of the kR per-row values
+  auto block_amax = [&](float* v) {
+#pragma unroll
+    for (int j = 0; j < kR; ++j) {
+      v[j] = wave_max(v[j]);
+      if (lane == 0) red[parity][j][wid] = v[j];
+    }
+    lds_barrier();  // keeps the next rows' prefetched loads in flight
+#pragma unroll
+    for (int j = 0; j < kR; ++j)
+      v[j] = fmaxf(fmaxf(red[parity][j][0], red[parity][j][1]), fmaxf(red[parity][j][2], red[parity][j][3]));
+    parity ^= 1;
+  };
+  auto pass1 = [&](float* amax, float (*keep)[kCh][V], bool fast) {
+#pragma unroll
+    for (int j = 0; j < kR; ++j) {
+      amax[j] = 0.f;
+#pragma unroll
+      for (int c = 0; c < kCh; ++c) {
+        if (tid + 256 * c < nvec) {
+          float f[V];
+          smoothed(raw[j][c], c, f, fast);
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            amax[j] = fmaxf(amax[j], fabsf(f[e]));
+            if (kSmall) keep[kSmall ? j : 0][c][e] = f[e];
+          }
+        }
+      }
+    }
+    block_amax(amax);
+  };
+
+  for (; g < ngroups; g += gridDim.x) {
+    if (kSmall) {
+#pragma unroll
+      for (int j = 0; j < kR; ++j)
+#pragma unroll
+        for (int c = 0; c < kCh; ++c) raw[j][c] = nxt[kSmall ? j : 0][c];
+      if (g + gridDim.x < ngroups) load_rows(g + gridDim.x, nxt);
+    } else {
+      load_rows(g, raw);
+    }
+    float keep[kSmall ? kR : 1][kCh][V];
+    float amax[kR];
+    if (s_ok)
+      pass1(amax, keep, true);
+    else
+      pass1(amax, keep, false);
+    float d[kR];
+    bool all_fast = s_ok;
+#pragma unroll
+    for (int j = 0; j < kR; ++j) {
+      d[j] = amax[j] / (float)kQMax;
+      all_fast = all_fast && d[j] >= kFastDMin && amax[j] <= kFastAMax;
+    }
+    // a row outside the fast bounds (g*kR+j >= m rows are zero, also "slow"
+    // only through d == 0, which needs no quotient) sends the group to IEEE division
+    bool fast = all_fast;
+    if (s_ok && !all_fast) {
+      fast = true;
+#pragma unroll
+      for (int j = 0; j < kR; ++j)
+        if (g * kR + j < m && !(d[j] >= kFastDMin && amax[j] <= kFastAMax)) fast = false;
+      if (!fast && kSmooth) {
+        pass1(amax, keep, false);
+#pragma unroll
+        for (int j = 0; j < kR; ++j) d[j] = amax[j] / (float)kQMax;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kR; ++j) {
+      const int64_t row = g * kR + j;
+      if (row >= m) continue;
+      if (tid == 0) x_scale[row] = d[j];
+      const float rd = (kMk && d[j] > 0.f) ? 1.0f / d[j] : 0.f;
+      int8_t* qr = xq + row * k;
+#pragma unroll
+      for (int c = 0; c < kCh; ++c) {
+        const int vi = tid + 256 * c;
+        if (vi >= nvec) continue;
+        float f[V];
+        if (kSmall) {
+#pragma unroll
+          for (int e = 0; e < V; ++e) f[e] = keep[kSmall ? j : 0][c][e];
+        } else {
+          smoothed(raw[j][c], c, f, fast);
+        }
+        uint32_t code[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          float qv = 0.f;
+          if (d[j] > 0.f) qv = (kMk && fast) ? div_mk(f[e], d[j], rd) : f[e] / d[j];
+          code[e] = q_code(qv);
+        }
+        if constexpr (V == 8) {
+          *reinterpret_cast<uint2*>(qr + (int64_t)vi * V) =
+              make_uint2(pack4(code[0], code[1], code[2], code[3]), pack4(code[4], code[5], code[6], code[7]));
+        } else {
+          *reinterpret_cast<uint32_t*>(qr + (int64_t)vi * V) = pack4(code[0], code[1], code[2], code[3]);
+        }
+      }
+    }
+  }
+}
+
 }  // namespace sqk
 
 namespace sqh {
+
+template <class In, int kCh, bool kSmooth, bool kMask>
+static void launch_rows(const uint8_t* xb, int64_t m, int64_t nvec, int64_t ldb, const float* smooth,
+                        const uint8_t* mask, int8_t* xq, float* x_scale, hipStream_t s) {
+  // Markstein quotients pay off once each workgroup sees several rows
+  // (prefill-sized M); small M (decode) gets one workgroup per row and plain
+  // IEEE division.
+  // Measured on MI355X: one row per iteration with ~4 resident workgroups per
+  // CU beats fewer workgroups with more rows each for short rows (the work is
+  // about one wave per SIMD, so latency hiding wins); long rows prefer 2.
+  constexpr int kR = 1;
+  if (m >= 1024) {
+    const int64_t cap = kCh <= 4 ? 1024 : 512;
+    const int64_t grid = m < cap ? m : cap;
+    hipLaunchKernelGGL((sqk::quant_rows_kernel<In, kCh, kR, kSmooth, kMask, true>), dim3((unsigned)grid), dim3(256),
+                       0, s, xb, m, (int)nvec, ldb, smooth, mask, xq, x_scale);
+  } else {
+    const unsigned grid = (unsigned)m;
+    hipLaunchKernelGGL((sqk::quant_rows_kernel<In, kCh, 1, kSmooth, kMask, false>), dim3(grid), dim3(256), 0, s, xb,
+                       m, (int)nvec, ldb, smooth, mask, xq, x_scale);
+  }
+}
 
 template <class In, bool kSmooth, bool kMask>
 static void launch_quant(const void* x, int64_t m, int64_t k, int64_t ldx, const float* smooth, const uint8_t* mask,
@@ -140,23 +379,18 @@ static void launch_quant(const void* x, int64_t m, int64_t k, int64_t ldx, const
   const int64_t nvec = k / In::kVec;
   const int64_t ldb = ldx * In::kBytes;
   const int64_t per_thread = (nvec + 255) / 256;
-  unsigned grid = (unsigned)(m < 4096 ? m : 4096);
   const uint8_t* xb = (const uint8_t*)x;
   if (per_thread <= 1)
-    hipLaunchKernelGGL((sqk::quant_rows_kernel<In, 1, kSmooth, kMask>), dim3(grid), dim3(256), 0, s, xb, m, nvec, ldb,
-                       smooth, mask, xq, x_scale);
+    launch_rows<In, 1, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s);
   else if (per_thread <= 2)
-    hipLaunchKernelGGL((sqk::quant_rows_kernel<In, 2, kSmooth, kMask>), dim3(grid), dim3(256), 0, s, xb, m, nvec, ldb,
-                       smooth, mask, xq, x_scale);
+    launch_rows<In, 2, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s);
   else if (per_thread <= 4)
-    hipLaunchKernelGGL((sqk::quant_rows_kernel<In, 4, kSmooth, kMask>), dim3(grid), dim3(256), 0, s, xb, m, nvec, ldb,
-                       smooth, mask, xq, x_scale);
+    launch_rows<In, 4, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s);
   else if (per_thread <= 8)
-    hipLaunchKernelGGL((sqk::quant_rows_kernel<In, 8, kSmooth, kMask>), dim3(grid), dim3(256), 0, s, xb, m, nvec, ldb,
-                       smooth, mask, xq, x_scale);
+    launch_rows<In, 8, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s);
   else
-    hipLaunchKernelGGL((sqk::quant_rows_long_kernel<In, kSmooth, kMask>), dim3(grid), dim3(256), 0, s, xb, m, nvec,
-                       ldb, smooth, mask, xq, x_scale);
+    hipLaunchKernelGGL((sqk::quant_rows_long_kernel<In, kSmooth, kMask>), dim3((unsigned)(m < 4096 ? m : 4096)),
+                       dim3(256), 0, s, xb, m, nvec, ldb, smooth, mask, xq, x_scale);
 }
 
 template <class In>

@@ -108,6 +108,21 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return r;
 }
 
+// s_waitcnt lgkmcnt(0) (LDS and scalar loads) with vmcnt and expcnt left alone (gfx9 encoding).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
+
+// Workgroup barrier for LDS traffic only. __syncthreads() also waits for every
+// outstanding global load (vmcnt(0)), which would drain prefetches issued
+// before the barrier; here only this wave's LDS accesses are retired first.
+// The empty asm statements stop the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  wait_lgkmcnt0();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Running maximum of non-negative binary32 values: their bit patterns order like the values.
 __device__ __forceinline__ void atomic_max_nonneg(float* addr, float v) {
   atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));

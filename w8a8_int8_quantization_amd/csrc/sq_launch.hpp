@@ -39,4 +39,10 @@ hipError_t gemm_i8(const int8_t* xq, const float* x_scale, const int8_t* wq, con
                    int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec,
                    hipStream_t s);
 
+// Large-tile prefill GEMM (256-row tiles); gemm_i8 routes to it when it suits.
+bool gemm_big_suits(int64_t m, int64_t n, int64_t k);
+hipError_t gemm_i8_big(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
+                       int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec,
+                       hipStream_t s);
+
 }  // namespace sqh
