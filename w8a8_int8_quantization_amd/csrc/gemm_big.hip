@@ -199,11 +199,28 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restri
   auto stage_ptr = [&](int kt) { return smem + (kt & 1) * C::kStage; };
 
   // Software pipeline over the 4 substeps of a stage: the fragments of the
-  // next substep are read from LDS while the MFMAs of the current one run.
-  // The stage hand-over sits in front of the last substep's MFMAs: wait for
-  // the next stage's transfers, retire this wave's LDS reads, barrier (now no
-  // wave reads the current buffer any more), start the transfers of the
-  // stage after next into it, read the next stage's first fragments.
+  // next substep are read from LDS while the MFMAs of the current one run,
+  // one read after each of the first MFMAs (so they have landed well before
+  // the substep ends). The stage hand-over sits in front of
+  // the last substep: wait for the next stage's transfers, retire this wave's
+  // LDS reads, barrier (now no wave reads the current buffer any more); the
+  // transfers of the stage after next into that buffer are then issued one
+  // per MFMA of the last substep, so the address unit works while the matrix
+  // cores do (issued in one burst they stall the wave for hundreds of cycles).
+  constexpr int kQ = C::kFN * C::kFM > C::kDma ? C::kFN * C::kFM : C::kDma;
+  auto dma_one = [&](int kt, int i) {
+    int8_t* stage = smem + (kt & 1) * C::kStage;
+    __builtin_amdgcn_global_load_lds((const void*)(src[i] + (int64_t)kt * kBigBK), (lds_void*)(stage + dst[i]), 16, 0,
+                                     0);
+  };
+  auto frag_one = [&](const int8_t* stage, int ks, int q, v4i* xf, v4i* wf) {
+    const int c = 2 * ks + fhalf;
+    if (q < C::kFM)
+      xf[q] = *reinterpret_cast<const v4i*>(stage + big_lds_off(wm * 128 + 32 * q + frow, c));
+    else
+      wf[q - C::kFM] = *reinterpret_cast<const v4i*>(
+          stage + C::kStageA + big_lds_off(wn * C::kWN + 32 * (q - C::kFM) + frow, c));
+  };
   v4i fx[2][C::kFM], fw[2][C::kFN];
   if (nk > 1)
     wait_vmcnt<C::kDma>();
@@ -217,23 +234,29 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restri
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int p = ks & 1;
-      if (ks < 3) {
-        read_frags(cur, ks + 1, fx[p ^ 1], fw[p ^ 1]);
-      } else if (kt + 1 < nk) {
+      const bool trans = ks == 3 && kt + 1 < nk;
+      const bool more_dma = trans && kt + 2 < nk;
+      if (trans) {
         wait_vmcnt<0>();
-        wait_lgkmcnt0();
         lds_barrier();
-        if (kt + 2 < nk) issue(kt + 2);
-        read_frags(stage_ptr(kt + 1), 0, fx[p ^ 1], fw[p ^ 1]);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(fx[p], fw[p]);
-      __builtin_amdgcn_sched_barrier(0);
-      // retire the prefetch issued a substep ago (long complete) so that at
-      // most one substep's reads are ever outstanding
-      if (ks != 3) wait_lgkmcnt0();
+      const int8_t* nstage = ks < 3 ? cur : stage_ptr(kt + 1);
+      const int nks = ks < 3 ? ks + 1 : 0;
+      const bool do_frag = ks < 3 || trans;
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        if (q < C::kFN * C::kFM) {
+          const int j = q / C::kFM, i = q % C::kFM;
+          acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[p][j], fx[p][i], acc[j][i], 0, 0, 0);
+        }
+        if (do_frag && q < C::kFM + C::kFN) frag_one(nstage, nks, q, fx[p ^ 1], fw[p ^ 1]);
+        if (more_dma && q < C::kDma) dma_one(kt + 2, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // retire the fragment reads (issued during the MFMAs above) before
+      // the next substep uses them
+      wait_lgkmcnt0();
     }
-    wait_lgkmcnt0();
   }
 
   // ---- epilogue: lane holds D[n][m] with m = l%32 and n = 8*(r/4) + 4*(l/32) + r%4 of each 32x32 block
