@@ -81,6 +81,45 @@ def pmc_traffic(workload: str, kernel_file: str):
     return e.get("hbm_bytes_per_launch")
 
 
+class HipEvents:
+    """hipEvent_t timing on one stream through the HIP runtime the library is linked to."""
+
+    def __init__(self, lib, stream: int):
+        import ctypes
+        self.ct = ctypes
+        self.stream = ctypes.c_void_p(stream)
+        self._create, self._record = lib.hipEventCreate, lib.hipEventRecord
+        self._elapsed, self._destroy = lib.hipEventElapsedTime, lib.hipEventDestroy
+        self._create.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._record.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self._elapsed.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self._destroy.argtypes = [ctypes.c_void_p]
+        for f in (self._create, self._record, self._elapsed, self._destroy):
+            f.restype = ctypes.c_int
+        self.events = []
+
+    def create(self):
+        e = self.ct.c_void_p()
+        if self._create(self.ct.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.events.append(e)
+        return e
+
+    def record(self, e):
+        self._record(e, self.stream)
+
+    def elapsed(self, a, b) -> float:
+        ms = self.ct.c_float()
+        if self._elapsed(self.ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy_all(self):
+        for e in self.events:
+            self._destroy(e)
+        self.events = []
+
+
 def cpu_baseline(c, s_ref, budget_s: float):
     """The CPU oracle's run-time path (quantise, int8 GEMM, dequantise) on row chunks of X."""
     import numpy as np
@@ -135,7 +174,7 @@ def main():
     out_dt = tdt[c.y_dtype]
     print(f"[bench] workload {c.name} M={c.m} K={c.k} N={c.n} alpha={c.alpha}", file=sys.stderr, flush=True)
 
-    # ---- load-time steps (once, timed separately)
+    # ---- load-time steps (once, timed separately; torch's events on its current stream)
     ev = lambda: torch.cuda.Event(enable_timing=True)
     e0, e1, e2 = ev(), ev(), ev()
     absmax = torch.zeros(c.k, dtype=torch.float32, device=dev)
@@ -151,33 +190,58 @@ def main():
     xq = torch.empty((c.m, c.k), dtype=torch.int8, device=dev)
     dx = torch.empty(c.m, dtype=torch.float32, device=dev)
     y = torch.empty((c.m, c.n), dtype=out_dt, device=dev)
+    ws = sq.linear_workspace(c.m, c.n, c.k, dev)
+    decode = c.m <= 64
+    # Decode steps stream the whole weight matrix once; with one copy it would
+    # stay in the 256 MiB last-level cache between steps. Rotating through
+    # copies totalling >= 768 MiB makes every step read its weights from HBM.
+    n_w = -(-(768 << 20) // wq.numel()) if decode else 1
+    wqs = [wq] + [wq.clone() for _ in range(n_w - 1)]
 
-    def step(evs=None):
-        if evs:
-            evs[0].record()
-        sq.sq_quant_act_per_token(x, s, xq=xq, x_scale=dx)
-        if evs:
-            evs[1].record()
-        sq.sq_w8a8_linear(xq, dx, wq, sw, y=y, out_dtype=out_dt)
-        if evs:
-            evs[2].record()
+    # The timed loop calls the C ABI directly with pre-marshalled arguments and
+    # records HIP events on the launch stream, so that the host enqueues work
+    # faster than the GPU drains it even for microsecond decode kernels (the
+    # checked Python wrappers cost more per call than such a kernel runs).
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    q_fn, g_fn = sq.raw["sq_quant_act_per_token"], sq.raw["sq_w8a8_linear"]
+    _, _, ldx = sq._rows(x)
+    q_args = (x.data_ptr(), sq._dt(x), c.m, c.k, ldx, s.data_ptr(), xq.data_ptr(), dx.data_ptr(), stream)
+    nb = ws.numel() if ws is not None else 0
+    g_args = [(xq.data_ptr(), dx.data_ptr(), w_i.data_ptr(), sw.data_ptr(), c.m, c.n, c.k, y.data_ptr(),
+               sq._dt(y), c.n, ws.data_ptr() if ws is not None else None, nb, stream) for w_i in wqs]
+    hip = HipEvents(sq._lib, stream)
 
-    for _ in range(args.warmup):
-        step()
+    def run(steps, evs=None):
+        bad = 0
+        for i in range(steps):
+            if evs:
+                hip.record(evs[i][0])
+            bad |= q_fn(*q_args)
+            if evs:
+                hip.record(evs[i][1])
+            bad |= g_fn(*g_args[i % n_w])
+            if evs:
+                hip.record(evs[i][2])
+        if bad:
+            raise RuntimeError(f"a C-ABI call failed (status bits {bad})")
+
+    run(args.warmup)
     torch.cuda.synchronize()
 
     # ---- timed region: exactly `steps` steps, events around each kernel
-    evs = [[ev(), ev(), ev()] for _ in range(args.steps)]
-    t_start, t_end = ev(), ev()
+    evs = [[hip.create(), hip.create(), hip.create()] for _ in range(args.steps)]
+    t_start, t_end = hip.create(), hip.create()
     torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        step(evs[i])
-    t_end.record()
+    hip.record(t_start)
+    h0 = time.perf_counter()
+    run(args.steps, evs)
+    host_us = (time.perf_counter() - h0) * 1e6 / args.steps
+    hip.record(t_end)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    total_ms = hip.elapsed(t_start, t_end)
+    quant_ms = float(np.mean([hip.elapsed(e[0], e[1]) for e in evs]))
+    gemm_ms = float(np.mean([hip.elapsed(e[1], e[2]) for e in evs]))
+    hip.destroy_all()
 
     ops = 2.0 * c.m * c.n * c.k
     ms_per_step = total_ms / args.steps
@@ -186,14 +250,16 @@ def main():
     in_bytes = {"f32": 4, "bf16": 2}[c.x_dtype]
     quant_bytes = c.m * c.k * in_bytes + 4 * c.k + c.m * c.k + 4 * c.m
     gemm_bytes = c.m * c.k + c.n * c.k + 4 * c.m + 4 * c.n + c.m * c.n * {"f32": 4, "bf16": 2}[c.y_dtype]
-    decode = c.m <= 64
-    traffic = pmc_traffic(c.name if args.m is None else f"{c.name}_m{c.m}", "gemm.hip")
+    big = c.m >= 256 and c.n >= 192 and c.k % 128 == 0 and c.m * c.n >= (1 << 20)
+    kfile, kname = (("gemm_decode.hip", "gemm_decode_kernel") if decode else
+                    ("gemm_big.hip", "gemm_big_kernel") if big else ("gemm.hip", "gemm_i8_kernel"))
+    traffic = pmc_traffic(c.name if args.m is None else f"{c.name}_m{c.m}", kfile)
     if decode:
         roof = {"bound": "hbm", "achieved": gemm_bytes / (gemm_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "kernel": "gemm_i8", "bytes_per_launch": gemm_bytes}
+                "unit": "GB/s", "kernel": kname, "bytes_per_launch": gemm_bytes}
     else:
         roof = {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
-                "kernel": "gemm_i8", "ops_per_launch": ops}
+                "kernel": kname, "ops_per_launch": ops}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic
     roof["launch_us"] = gemm_ms * 1e3
@@ -212,6 +278,8 @@ def main():
         "quant_gbs": quant_bytes / (quant_ms * 1e-3) / 1e9,
         "quant_frac_hbm": quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "step_gbs_algorithmic": (quant_bytes + gemm_bytes) / (ms_per_step * 1e-3) / 1e9,
+        "weight_copies": n_w,
+        "host_enqueue_us_per_step": host_us,
         "load_time": prep,
         "roofline": roof,
     }

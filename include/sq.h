@@ -167,7 +167,16 @@ sq_status sq_quant_act_per_token(const void* x, sq_dtype xt, int64_t m, int64_t 
  * SQ_I32 writes acc itself (scales unused, may be NULL).
  * xq: [M x K], wq: [N x K] (K-contiguous, rows 16-byte aligned), y: [M x ldy].
  * K must not exceed SQ_MAX_K_INT32.
- * ws: workspace of sq_w8a8_linear_workspace_size(m, n, k) bytes.
+ * ws: workspace of sq_w8a8_linear_workspace_size(m, n, k) bytes, 16-byte
+ *     aligned; NULL when that size is 0. The size is non-zero for decode
+ *     shapes (M <= 64, K % 128 == 0) whose K is split over several
+ *     workgroups: the workspace then holds int32 partial tiles and one ticket
+ *     counter per 64 output columns. The caller zero-fills the workspace once,
+ *     before its first use; every call leaves the counters at zero again, so
+ *     later calls need no clearing. One workspace serves one call at a time
+ *     (calls in flight together on different streams need their own).
+ *     The split changes only how the exact int32 sum is formed, never its
+ *     value.
  */
 size_t sq_w8a8_linear_workspace_size(int64_t m, int64_t n, int64_t k);
 sq_status sq_w8a8_linear(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
@@ -176,9 +185,12 @@ sq_status sq_w8a8_linear(const int8_t* xq, const float* x_scale, const int8_t* w
 
 /*
  * The whole run-time path in one call: sq_quant_act_per_token followed by
- * sq_w8a8_linear on the same stream, with Xq and the row scales held in the
- * workspace. The results equal those of the two calls made separately.
- * ws: workspace of sq_w8a8_linear_dyn_workspace_size(m, n, k) bytes.
+ * sq_w8a8_linear on the same stream, with Xq, the row scales and the GEMM's
+ * workspace held in the workspace. The results equal those of the two calls
+ * made separately.
+ * ws: workspace of sq_w8a8_linear_dyn_workspace_size(m, n, k) bytes, 16-byte
+ *     aligned. Its contents need no initialisation: the quantisation launch
+ *     clears the GEMM's split-K counters.
  */
 size_t sq_w8a8_linear_dyn_workspace_size(int64_t m, int64_t n, int64_t k);
 sq_status sq_w8a8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const float* smooth,

@@ -1,0 +1,100 @@
+"""Parity of the decode-shaped GEMM (M <= 64 tokens, K a multiple of 128).
+
+These shapes run the split-K decode kernel: per-slice int32 partial tiles in
+the workspace, ticket counters, the last workgroup of a tile reducing. The
+int32 accumulators must equal the oracle's exact integer product; dequantised
+outputs must be within 1 ulp of the oracle. Every call goes through the C ABI.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import assert_out_close, bits16, dev, host, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+sq = pytest.importorskip("w8a8_int8_quantization_amd")
+
+# (n, k): one step; ragged N (N % 4 != 0 and N % 64 != 0); slices whose step
+# count does not divide among the 4 waves; both 8B decode projections; K near
+# the int32 limit (hundreds of slices).
+NK = [(64, 128), (99, 256), (301, 1152), (130, 8192), (4096, 14336), (14336, 4096), (64, 133120)]
+MS = [1, 5, 16, 17, 33, 64]
+
+
+def _dev_i8(a):
+    return torch.from_numpy(a).to(dev())
+
+
+@pytest.mark.parametrize("n,k", NK)
+@pytest.mark.parametrize("m", MS)
+def test_decode_int32_exact(m, n, k):
+    if k > 20000 and m not in (1, 64):
+        pytest.skip("the longest K runs at the smallest and largest M only")
+    log("decode i32", m, n, k, "ws", sq.raw["sq_w8a8_linear_workspace_size"](m, n, k))
+    xq = workloads.uniform_int8((m, k), seed=m * 7 + n + k, stream=10)
+    wq = workloads.uniform_int8((n, k), seed=m * 7 + n + k, stream=11)
+    acc = sq.sq_w8a8_linear(_dev_i8(xq), None, _dev_i8(wq), None, out_dtype=torch.int32)
+    assert np.array_equal(host(acc), oracle.int8_matmul(xq, wq))
+
+
+@pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("m,n,k", [(1, 4096, 14336), (8, 301, 1152), (32, 14336, 4096), (64, 99, 256)])
+def test_decode_dequant(out, m, n, k):
+    log("decode dequant", out, m, n, k)
+    xq = workloads.uniform_int8((m, k), seed=m + n, stream=12)
+    wq = workloads.uniform_int8((n, k), seed=m + n, stream=13)
+    dx = workloads.positive_scales(m, seed=m, stream=2)
+    dw = workloads.positive_scales(n, seed=n, stream=3) * np.float32(1e-3)
+    y = sq.sq_w8a8_linear(_dev_i8(xq), torch.from_numpy(dx).to(dev()), _dev_i8(wq), torch.from_numpy(dw).to(dev()),
+                          out_dtype={"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[out])
+    frac = assert_out_close(y, oracle.w8a8_linear(xq, dx, wq, dw, out), out)
+    log("  exact fraction", frac)
+
+
+def test_decode_workspace_reuse():
+    """sq_w8a8_linear: a workspace zero-filled once stays usable (the kernel
+    restores its ticket counters). sq_w8a8_linear_dyn: a workspace full of
+    garbage works (the quantisation launch clears the counters)."""
+    m, n, k = 24, 4096, 14336
+    nb = sq.raw["sq_w8a8_linear_workspace_size"](m, n, k)
+    assert nb > 0
+    xq = workloads.uniform_int8((m, k), seed=5, stream=14)
+    wq = workloads.uniform_int8((n, k), seed=5, stream=15)
+    ref = oracle.int8_matmul(xq, wq)
+    ws = sq.linear_workspace(m, n, k, dev())
+    x_d, w_d = _dev_i8(xq), _dev_i8(wq)
+    for _ in range(3):
+        acc = sq.sq_w8a8_linear(x_d, None, w_d, None, out_dtype=torch.int32, ws=ws)
+        assert np.array_equal(host(acc), ref)
+        assert not host(ws[:4 * ((n + 63) // 64)]).any(), "ticket counters not restored"
+    c = workloads.random_linear_case(m=m, k=k, n=n, seed=3, dtype="bf16", calib_rows=64)
+    s_ref = oracle.smoothing_factors(oracle.calibrate_absmax(c.x_calib), oracle.weight_row_absmax(c.w), 0.5)
+    s = torch.from_numpy(s_ref).to(dev())
+    _, wq2, sw2 = sq.sq_smooth_fold_weights(to_dev(c.w, "bf16"), smooth=s, flags=sq.SMOOTH_GIVEN)
+    x = to_dev(c.x, "bf16")
+    nbd = sq.raw["sq_w8a8_linear_dyn_workspace_size"](m, n, k)
+    wsd = torch.full((nbd,), 0x5A, dtype=torch.uint8, device=dev())
+    first = bits16(sq.sq_w8a8_linear_dyn(x, s, wq2, sw2, ws=wsd))
+    for _ in range(2):
+        assert np.array_equal(bits16(sq.sq_w8a8_linear_dyn(x, s, wq2, sw2, ws=wsd)), first)
+    wq_ref, sw_ref = oracle.quantize_weights_per_channel(oracle.fold_weights(c.w, s_ref))
+    y_ref, _, _, _ = oracle.smoothquant_linear(c.x, s_ref, wq_ref, sw_ref, "bf16")
+    assert_out_close(torch.from_numpy(first.view(np.int16)).view(torch.bfloat16), y_ref, "bf16")
+
+
+def test_decode_workspace_validation():
+    m, n, k = 4, 4096, 14336
+    nb = sq.raw["sq_w8a8_linear_workspace_size"](m, n, k)
+    xq = torch.zeros((m, k), dtype=torch.int8, device=dev())
+    wq = torch.zeros((n, k), dtype=torch.int8, device=dev())
+    y = torch.empty((m, n), dtype=torch.int32, device=dev())
+    small = torch.empty(nb - 1, dtype=torch.uint8, device=dev())
+    st = sq.raw["sq_w8a8_linear"](xq.data_ptr(), None, wq.data_ptr(), None, m, n, k, y.data_ptr(), 3, n,
+                                  small.data_ptr(), nb - 1, None)
+    assert st == 6  # SQ_ERR_WORKSPACE
+    st = sq.raw["sq_w8a8_linear"](xq.data_ptr(), None, wq.data_ptr(), None, m, n, k, y.data_ptr(), 3, n,
+                                  None, 0, None)
+    assert st == 6

@@ -116,6 +116,14 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
     return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
 
 
+def linear_workspace(m: int, n: int, k: int, device) -> Optional[torch.Tensor]:
+    """A zero-filled workspace for ``sq_w8a8_linear`` at this shape (None if it needs none).
+
+    Reusable across calls at the same shape: each call leaves it zero-filled."""
+    nb = raw["sq_w8a8_linear_workspace_size"](m, n, k)
+    return torch.zeros(nb, dtype=torch.uint8, device=device) if nb else None
+
+
 def sq_version() -> int:
     return raw["sq_version"]()
 
@@ -160,19 +168,23 @@ def sq_quant_act_per_token(x: torch.Tensor, smooth: Optional[torch.Tensor] = Non
 
 
 def sq_w8a8_linear(xq: torch.Tensor, x_scale: Optional[torch.Tensor], wq: torch.Tensor,
-                   w_scale: Optional[torch.Tensor], out_dtype=torch.bfloat16, y: Optional[torch.Tensor] = None):
-    """int8 GEMM with the fused dequantisation; out_dtype torch.int32 returns the raw accumulator."""
+                   w_scale: Optional[torch.Tensor], out_dtype=torch.bfloat16, y: Optional[torch.Tensor] = None,
+                   ws: Optional[torch.Tensor] = None):
+    """int8 GEMM with the fused dequantisation; out_dtype torch.int32 returns the raw accumulator.
+
+    ``ws``: a workspace from :func:`linear_workspace` (zero-filled, reusable at
+    this shape); a fresh one is allocated when None."""
     m, k, _ = _rows(xq)
     n = wq.shape[0]
     if wq.shape[1] != k:
         raise ValueError("xq and wq disagree on K")
     y = torch.empty((m, n), dtype=out_dtype, device=xq.device) if y is None else y
     _, _, ldy = _rows(y)
-    nb = raw["sq_w8a8_linear_workspace_size"](m, n, k)
-    ws = _workspace(nb, xq.device)
+    if ws is None:
+        ws = linear_workspace(m, n, k, xq.device)
     _check("sq_w8a8_linear", raw["sq_w8a8_linear"](
-        _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), m, n, k, _ptr(y), _dt(y), ldy, _ptr(ws), nb,
-        _stream(xq.device)))
+        _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), m, n, k, _ptr(y), _dt(y), ldy, _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(xq.device)))
     return y
 
 

@@ -127,8 +127,8 @@ sq_status sq_quant_act_per_token(const void* x, sq_dtype xt, int64_t m, int64_t 
 }
 
 size_t sq_w8a8_linear_workspace_size(int64_t m, int64_t n, int64_t k) {
-  (void)m; (void)n; (void)k;
-  return 0;
+  if (m <= 0 || n <= 0 || k <= 0 || k % 64 != 0) return 0;
+  return sqh::gemm_decode_workspace(m, n, k);
 }
 
 // Shapes, output type and the weight-side pointers of the GEMM.
@@ -163,9 +163,15 @@ sq_status sq_w8a8_linear(const int8_t* xq, const float* x_scale, const int8_t* w
                          sq_stream_t stream) {
   SQ_TRY(check_linear(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy));
   if (m == 0 || n == 0) return SQ_OK;
-  if (ws_bytes < sq_w8a8_linear_workspace_size(m, n, k)) return SQ_ERR_WORKSPACE;
-  (void)ws;
-  return hip_status(sqh::gemm_i8(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, nullptr, (hipStream_t)stream));
+  const size_t need = sq_w8a8_linear_workspace_size(m, n, k);
+  if (need > 0 && (!ws || ws_bytes < need)) return SQ_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return SQ_ERR_ALIGN;
+  const hipStream_t s = (hipStream_t)stream;
+  // decode shapes: the workspace's split-K counters are zero on entry (the
+  // caller's contract) and restored to zero by the kernel
+  if (sqh::gemm_decode_suits(m, n, k))
+    return hip_status(sqh::gemm_i8_decode(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, ws, s));
+  return hip_status(sqh::gemm_i8(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, nullptr, s));
 }
 
 size_t sq_w8a8_linear_dyn_workspace_size(int64_t m, int64_t n, int64_t k) {
@@ -186,7 +192,17 @@ sq_status sq_w8a8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const floa
   if (!aligned16(ws)) return SQ_ERR_ALIGN;
   int8_t* xq = reinterpret_cast<int8_t*>(ws);
   float* dx = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + round_up((size_t)m * (size_t)k));
+  void* gws = reinterpret_cast<char*>(ws) + round_up((size_t)m * (size_t)k) + round_up((size_t)m * 4);
   const hipStream_t s = (hipStream_t)stream;
+  if (sqh::gemm_decode_suits(m, n, k)) {
+    // the quantisation launch also clears the GEMM's split-K counters
+    uint32_t* counters;
+    int64_t ncount;
+    sqh::gemm_decode_counters(m, n, k, gws, &counters, &ncount);
+    hipError_t e = sqh::quant_rows(x, xt, m, k, ldx, smooth, nullptr, xq, dx, s, counters, ncount);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(sqh::gemm_i8_decode(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, gws, s));
+  }
   hipError_t e = sqh::quant_rows(x, xt, m, k, ldx, smooth, nullptr, xq, dx, s);
   if (e != hipSuccess) return hip_status(e);
   return hip_status(sqh::gemm_i8(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, nullptr, s));

@@ -1,0 +1,386 @@
+// Decode-shaped int8 GEMM (M <= 64 tokens): Y = dequant(Xq . Wq^T), where the
+// cost is streaming the weight matrix Wq [N x K] from HBM once.
+//
+// The LLM.int8() page, "The architecture: every piece explained" (int8
+// operands, int32 accumulation, dequantisation by the outer product of the row
+// and column scales); "Half the Size, Better Performance, Same Accuracy:
+// Understanding W8A8 INT8 LLM Quantization", "Performance After Quantization"
+// (per decoded token the weights are read once; the layer is memory-bound).
+//
+// Layout of the work on gfx950:
+//  * A 256-thread workgroup owns 64 rows of Wq (output columns n) and one
+//    slice of K. The grid is (ceil(N/64), S): S slices of K, chosen so that a
+//    few hundred workgroups keep every CU streaming.
+//  * Inside the workgroup the 4 waves split the slice's 128-byte k-steps
+//    round-robin (wave w takes steps w, w+4, ...), so the 4 waves read
+//    adjacent 128-byte pieces of the same rows, and every wave covers all 64
+//    rows: one Xq fragment feeds 4 row groups, so Xq (L2-resident) costs no
+//    more load bandwidth than Wq.
+//  * Operands go straight from global memory into registers in the
+//    v_mfma_i32_16x16x64_i8 layout: A = Wq (lane l: row l%16, 16 bytes at
+//    k-offset 16*(l/16) of each 64-byte half step), B = Xq (token l%16, same
+//    k bytes). The step count per wave is a template constant, so the whole
+//    pipeline is unrolled: kDepth steps of loads stay in flight ahead of the
+//    MFMAs. Rows of Wq beyond N and tokens beyond M read a clamped (valid)
+//    row whose results are never stored.
+//  * The 4 waves' int32 tiles are summed through LDS; one thread then owns 4
+//    consecutive outputs of one token (16 threads = 64 contiguous outputs).
+//  * With S > 1 each workgroup writes its int32 partial tile to a workspace,
+//    then takes a ticket from the tile's counter; the workgroup drawing the
+//    last ticket sums the S partials in slice order and runs the epilogue.
+//    All partial sums are int32 additions, so the result equals the unsplit
+//    product bit for bit. The counters must be zero at launch; the last
+//    workgroup of a tile sets its counter back to zero, so a zeroed workspace
+//    stays zeroed from call to call.
+#include "sq_common.hpp"
+#include "sq_launch.hpp"
+
+#include <stdlib.h>
+
+namespace sqk {
+
+constexpr int kDecRows = 64;    // Wq rows per workgroup
+constexpr int kDecStep = 128;   // k bytes per pipeline step
+constexpr int kDecWaves = 4;
+constexpr int kDecMaxNS = 8;    // most steps per wave (template range)
+// Buffer descriptor word 3 of a raw byte buffer on gfx9 (32-bit data format),
+// and the cache-policy operand of device-coherent (sc1) buffer accesses.
+constexpr int kBufDword3 = 0x00020000;
+constexpr int kCoherent = 16;
+
+struct DecodeArgs {
+  const int8_t* xq;
+  const int8_t* wq;
+  const float* x_scale;
+  const float* w_scale;
+  void* y;
+  int64_t ldy;
+  int32_t* partial;    // [S][M][N] int32 (S > 1)
+  uint32_t* counter;   // [ceil(N/64)], zero at launch and at exit (S > 1)
+  int M, N, K;
+  int S;               // number of K slices
+  int slice_steps;     // 128-byte steps per slice
+  int out;             // 0 f32, 1 bf16, 2 f16, 3 i32
+};
+
+__device__ __forceinline__ void dec_epilogue(const DecodeArgs& a, int m, int n, const int32_t* acc) {
+  if (m >= a.M || n >= a.N) return;
+  const int nv = min(4, a.N - n);
+  const int64_t off = (int64_t)m * a.ldy + n;
+  if (a.out == 3) {
+    int32_t* p = reinterpret_cast<int32_t*>(a.y) + off;
+    if (nv == 4 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+      *reinterpret_cast<int4*>(p) = make_int4(acc[0], acc[1], acc[2], acc[3]);
+    } else {
+      for (int e = 0; e < nv; ++e) p[e] = acc[e];
+    }
+    return;
+  }
+  const float xs = a.x_scale[m];
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = e < nv ? __fmul_rn(__fmul_rn((float)acc[e], xs), a.w_scale[n + e]) : 0.f;
+  if (a.out == 0) {
+    float* p = reinterpret_cast<float*>(a.y) + off;
+    if (nv == 4 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+      *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+      for (int e = 0; e < nv; ++e) p[e] = v[e];
+    }
+    return;
+  }
+  uint16_t h[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) h[e] = a.out == 1 ? f32_to_bf16(v[e]) : f32_to_f16(v[e]);
+  uint16_t* p = reinterpret_cast<uint16_t*>(a.y) + off;
+  if (nv == 4 && (reinterpret_cast<uintptr_t>(p) & 7) == 0) {
+    *reinterpret_cast<uint2*>(p) = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                              (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+  } else {
+    for (int e = 0; e < nv; ++e) p[e] = h[e];
+  }
+}
+
+template <int kMB, int kNS>
+__global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
+  constexpr int kTok = 16 * kMB;
+  // steps of loads in flight: all of them when the registers allow (the
+  // workgroup's whole share of Wq is requested at once); the caps are the
+  // deepest pipelines the compiler allocates without spilling
+  constexpr int kMaxDepth = kMB == 4 ? 6 : 8;
+  constexpr int kDepth = kNS < kMaxDepth ? kNS : kMaxDepth;
+  __shared__ int32_t red[kDecWaves][kTok][kDecRows];
+  __shared__ uint32_t last_ticket;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int tile = blockIdx.x;
+  const int slice = blockIdx.y;
+  const int n0 = tile * kDecRows;
+  const int step0 = slice * a.slice_steps;
+  const int nsl = min(a.slice_steps, a.K / kDecStep - step0);  // >= 1 by construction of S
+
+  const int kb = 16 * (lane >> 4);
+  const int8_t* wp[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) wp[g] = a.wq + (int64_t)min(n0 + 16 * g + (lane & 15), a.N - 1) * a.K + kb;
+  const int8_t* xp[kMB];
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb) xp[mb] = a.xq + (int64_t)min(16 * mb + (lane & 15), a.M - 1) * a.K + kb;
+
+  v4i acc[4][kMB];
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) acc[g][mb] = v4i{0, 0, 0, 0};
+
+  u32x4 wb[kDepth][4][2];
+  u32x4 xb[kDepth][kMB][2];
+  // step i of this wave is slice step wid + 4 i; past the slice end it reloads
+  // the last step (valid memory) and its product is skipped
+  auto load = [&](int i, int slot) {
+    const int64_t off = (int64_t)(step0 + min(wid + kDecWaves * i, nsl - 1)) * kDecStep;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      wb[slot][g][0] = load16(wp[g] + off);
+      wb[slot][g][1] = load16(wp[g] + off + 64);
+    }
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      xb[slot][mb][0] = load16(xp[mb] + off);
+      xb[slot][mb][1] = load16(xp[mb] + off + 64);
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kDepth; ++i) load(i, i);
+  // keep the scheduler from trading the loads in flight for registers
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kNS; ++i) {
+    const int slot = i % kDepth;
+    u32x4 w[4][2], x[kMB][2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      w[g][0] = wb[slot][g][0];
+      w[g][1] = wb[slot][g][1];
+    }
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      x[mb][0] = xb[slot][mb][0];
+      x[mb][1] = xb[slot][mb][1];
+    }
+    if (i + kDepth < kNS) load(i + kDepth, slot);
+    // a step past the slice end contributes zero (a select, not a branch, so
+    // that the compiler keeps every load at its place in the pipeline)
+    const bool valid = wid + kDecWaves * i < nsl;
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      x[mb][0] = valid ? x[mb][0] : u32x4{0u, 0u, 0u, 0u};
+      x[mb][1] = valid ? x[mb][1] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+          acc[g][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, w[g][h]),
+                                                             __builtin_bit_cast(v4i, x[mb][h]), acc[g][mb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // 16x16 result layout: lane l holds token 16 mb + l%16 and rows
+  // 16 g + 4 (l/16) + r, r = 0..3. Quads of rows are XOR-swizzled by the
+  // token so that both this store and the row-wise reads below are free of
+  // bank conflicts.
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      const int tok = 16 * mb + (lane & 15);
+      const int quad = (4 * g + (lane >> 4)) ^ (tok & 15);
+      *reinterpret_cast<v4i*>(&red[wid][tok][4 * quad]) = acc[g][mb];
+    }
+  __syncthreads();
+
+  const int q = tid & 15;
+  int32_t sum[kMB][4];
+#pragma unroll
+  for (int j = 0; j < kMB; ++j) {
+    const int tok = (tid >> 4) + 16 * j;
+    const int sq = q ^ (tok & 15);
+    v4i s = *reinterpret_cast<const v4i*>(&red[0][tok][4 * sq]);
+#pragma unroll
+    for (int w = 1; w < kDecWaves; ++w) s += *reinterpret_cast<const v4i*>(&red[w][tok][4 * sq]);
+    sum[j][0] = s[0]; sum[j][1] = s[1]; sum[j][2] = s[2]; sum[j][3] = s[3];
+  }
+  const int n = n0 + 4 * q;
+  if (a.S == 1) {
+#pragma unroll
+    for (int j = 0; j < kMB; ++j) dec_epilogue(a, (tid >> 4) + 16 * j, n, sum[j]);
+    return;
+  }
+
+  // Split K: publish this slice's tile; the last workgroup of the tile
+  // reduces. The partial tiles cross XCDs, whose L2 caches are not coherent
+  // with each other, so they are written and read with device-coherent (sc1)
+  // buffer accesses; a device-scope fence would instead write back and
+  // invalidate the whole L2 of the XCD in every workgroup. Order: coherent
+  // stores, wait until every store of the workgroup has completed, then the
+  // ticket (an agent-scope atomic); the holder of the last ticket then reads
+  // the partials coherently.
+  const uint32_t pbytes = (uint32_t)((size_t)a.S * a.M * a.N * 4);
+  const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(a.partial, (short)0, pbytes, kBufDword3);
+  const bool vec = (a.N & 3) == 0;
+#pragma unroll
+  for (int j = 0; j < kMB; ++j) {
+    const int m = (tid >> 4) + 16 * j;
+    if (m < a.M && n < a.N) {
+      const uint32_t off = (uint32_t)((((size_t)slice * a.M + m) * a.N + n) * 4);
+      if (vec) {
+        const v4i v = {sum[j][0], sum[j][1], sum[j][2], sum[j][3]};
+        __builtin_amdgcn_raw_buffer_store_b128(v, pr, off, 0, kCoherent);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < a.N) __builtin_amdgcn_raw_buffer_store_b32(sum[j][e], pr, off + 4 * e, 0, kCoherent);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    last_ticket = __hip_atomic_fetch_add(a.counter + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (last_ticket != (uint32_t)(a.S - 1)) return;
+#pragma unroll
+  for (int j = 0; j < kMB; ++j) {
+    const int m = (tid >> 4) + 16 * j;
+    if (m >= a.M || n >= a.N) continue;
+    v4i t = {0, 0, 0, 0};
+    const uint32_t off0 = (uint32_t)(((size_t)m * a.N + n) * 4);
+    const uint32_t sstride = (uint32_t)((size_t)a.M * a.N * 4);
+    if (vec) {
+      // eight slices per round trip; slices past S read beyond the buffer's
+      // range, which a raw buffer load returns as zero
+      for (int s = 0; s < a.S; s += 8) {
+        v4i part[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          part[u] = __builtin_amdgcn_raw_buffer_load_b128(pr, off0 + (uint32_t)(s + u) * sstride, 0, kCoherent);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t += part[u];
+      }
+    } else {
+      for (int s = 0; s < a.S; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < a.N) t[e] += __builtin_amdgcn_raw_buffer_load_b32(pr, off0 + s * sstride + 4 * e, 0, kCoherent);
+    }
+    const int32_t tt[4] = {t[0], t[1], t[2], t[3]};
+    dec_epilogue(a, m, n, tt);
+  }
+  // every ticket of this tile has been drawn: restore the counter for the next call
+  if (tid == 0) __hip_atomic_store(a.counter + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace sqk
+
+namespace sqh {
+
+namespace {
+
+struct DecodePlan {
+  int S = 1;
+  int slice_steps = 0;
+  int ns = 0;      // steps per wave
+  int tiles = 0;
+};
+
+DecodePlan decode_plan(int64_t n, int64_t k) {
+  DecodePlan p;
+  const int steps = (int)(k / sqk::kDecStep);
+  p.tiles = (int)((n + sqk::kDecRows - 1) / sqk::kDecRows);
+  // at least one workgroup per CU (256 CUs), with at most kDecMaxNS steps
+  // per wave; measured on MI355X, more slices than that only add partial-tile
+  // traffic and reduction latency
+  int want = (256 + p.tiles - 1) / p.tiles;
+#ifdef SQ_TUNE
+  if (const char* e = getenv("SQ_DECODE_SPLIT")) want = atoi(e);
+#endif
+  if (want < 1) want = 1;
+  if (want > steps) want = steps;
+  int per = (steps + want - 1) / want;
+  const int cap = sqk::kDecWaves * sqk::kDecMaxNS;
+  if (per > cap) per = cap;
+  p.slice_steps = per;
+  p.S = (steps + per - 1) / per;
+  p.ns = (per + sqk::kDecWaves - 1) / sqk::kDecWaves;
+  return p;
+}
+
+size_t counter_bytes(int tiles) { return ((size_t)tiles * 4 + 255) / 256 * 256; }
+
+template <int kMB>
+hipError_t launch_decode(const sqk::DecodeArgs& a, int ns, dim3 grid, hipStream_t s) {
+  switch (ns) {
+    case 1: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 2>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 3>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 4>), grid, dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 5>), grid, dim3(256), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 6>), grid, dim3(256), 0, s, a); break;
+    case 7: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 7>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 8>), grid, dim3(256), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_decode_suits(int64_t m, int64_t n, int64_t k) {
+  return m >= 1 && m <= 64 && n >= 1 && k % sqk::kDecStep == 0;
+}
+
+size_t gemm_decode_workspace(int64_t m, int64_t n, int64_t k) {
+  if (!gemm_decode_suits(m, n, k)) return 0;
+  const DecodePlan p = decode_plan(n, k);
+  if (p.S == 1) return 0;
+  return counter_bytes(p.tiles) + (size_t)p.S * (size_t)m * (size_t)n * 4;
+}
+
+void gemm_decode_counters(int64_t m, int64_t n, int64_t k, void* ws, uint32_t** counters, int64_t* count) {
+  *counters = nullptr;
+  *count = 0;
+  if (!gemm_decode_suits(m, n, k)) return;
+  const DecodePlan p = decode_plan(n, k);
+  if (p.S == 1) return;
+  *counters = reinterpret_cast<uint32_t*>(ws);
+  *count = p.tiles;
+}
+
+hipError_t gemm_i8_decode(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
+                          int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, hipStream_t s) {
+  const DecodePlan p = decode_plan(n, k);
+  sqk::DecodeArgs a{};
+  a.xq = xq; a.wq = wq; a.x_scale = x_scale; a.w_scale = w_scale; a.y = y; a.ldy = ldy;
+  a.M = (int)m; a.N = (int)n; a.K = (int)k;
+  a.S = p.S;
+  a.slice_steps = p.slice_steps;
+  a.out = yt == SQ_F32 ? 0 : yt == SQ_BF16 ? 1 : yt == SQ_F16 ? 2 : 3;
+  if (p.S > 1) {
+    a.counter = reinterpret_cast<uint32_t*>(ws);
+    a.partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + counter_bytes(p.tiles));
+  }
+  const dim3 grid((unsigned)p.tiles, (unsigned)p.S);
+  bool mb1 = m <= 16;
+#ifdef SQ_TUNE
+  if (getenv("SQ_DECODE_MB2")) mb1 = false;
+#endif
+  if (mb1) return launch_decode<1>(a, p.ns, grid, s);
+  if (m <= 32) return launch_decode<2>(a, p.ns, grid, s);
+  return launch_decode<4>(a, p.ns, grid, s);
+}
+
+}  // namespace sqh

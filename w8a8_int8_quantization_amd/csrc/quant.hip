@@ -11,13 +11,15 @@
 // taken over the regular (non-outlier) columns only; the outlier columns of
 // Xq are zero.
 //
-// Two kernels. quant_wave_kernel (below) serves prefill-sized inputs. For few
-// rows (decode) or very long rows, one 256-thread workgroup owns a row at a
-// time (grid-stride over rows): each thread loads kCh 16-byte vectors of the
-// row (coalesced), keeps the smoothed values in registers, the workgroup
-// reduces the row maximum through LDS, then each thread writes its int8 values
-// with one 4- or 8-byte store per vector; rows longer than 8 vectors per
-// thread use a two-pass variant that reads the row a second time.
+// Two kernels. quant_rows_kernel (the fast one, below) keeps up to eight
+// 16-byte vectors of a row per thread in registers: one 256-thread workgroup
+// owns a row at a time (grid-stride over rows), loads it coalesced, reduces
+// the row maximum through LDS and writes its int8 values with one 4- or
+// 8-byte store per vector. Longer rows use quant_rows_long_kernel, which
+// reads the row a second time instead of keeping it.
+// Either kernel can also clear a few words of device memory in its first
+// workgroup (the split-K ticket counters of a decode GEMM launched next on
+// the same stream), which saves that GEMM a launch.
 #include "sq_common.hpp"
 #include "sq_launch.hpp"
 
@@ -72,9 +74,12 @@ template <class In, bool kSmooth, bool kMask>
 __global__ __launch_bounds__(256) void quant_rows_long_kernel(const uint8_t* __restrict__ x, int64_t m, int64_t nvec,
                                                               int64_t ldx_bytes, const float* __restrict__ smooth,
                                                               const uint8_t* __restrict__ mask,
-                                                              int8_t* __restrict__ xq, float* __restrict__ x_scale) {
+                                                              int8_t* __restrict__ xq, float* __restrict__ x_scale,
+                                                              uint32_t* __restrict__ zero, int nzero) {
   constexpr int V = In::kVec;
   __shared__ float red[4];
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nzero; i += 256) zero[i] = 0u;
   const int64_t k = nvec * V;
   for (int64_t row = blockIdx.x; row < m; row += gridDim.x) {
     const uint8_t* xr = x + row * ldx_bytes;
@@ -151,7 +156,8 @@ template <class In, int kCh, int kR, bool kSmooth, bool kMask, bool kMk>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint8_t* __restrict__ x, int64_t m, int nvec,
                                                          int64_t ldx_bytes, const float* __restrict__ smooth,
                                                          const uint8_t* __restrict__ mask, int8_t* __restrict__ xq,
-                                                         float* __restrict__ x_scale) {
+                                                         float* __restrict__ x_scale, uint32_t* __restrict__ zero,
+                                                         int nzero) {
   constexpr int V = In::kVec;
   constexpr bool kSmall = kCh * kR <= 8 && kCh <= 4;  // keep x/s between passes and prefetch the next rows
   __shared__ float red[2][kR][4];
@@ -180,6 +186,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint8_t* __restri
   u32x4 nxt[kSmall ? kR : 1][kCh];
   int64_t g = blockIdx.x;
   if (kSmall && g < ngroups) load_rows(g, nxt);
+  if (blockIdx.x == 0)
+    for (int i = tid; i < nzero; i += 256) zero[i] = 0u;
 
   float sreg[kSmooth ? kCh : 1][V];
   float rreg[(kSmooth && kMk) ? kCh : 1][V];
@@ -353,7 +361,7 @@ namespace sqh {
 
 template <class In, int kCh, bool kSmooth, bool kMask>
 static void launch_rows(const uint8_t* xb, int64_t m, int64_t nvec, int64_t ldb, const float* smooth,
-                        const uint8_t* mask, int8_t* xq, float* x_scale, hipStream_t s) {
+                        const uint8_t* mask, int8_t* xq, float* x_scale, hipStream_t s, uint32_t* zero, int nzero) {
   // Markstein quotients pay off once each workgroup sees several rows
   // (prefill-sized M); small M (decode) gets one workgroup per row and plain
   // IEEE division.
@@ -365,52 +373,54 @@ static void launch_rows(const uint8_t* xb, int64_t m, int64_t nvec, int64_t ldb,
     const int64_t cap = kCh <= 4 ? 1024 : 512;
     const int64_t grid = m < cap ? m : cap;
     hipLaunchKernelGGL((sqk::quant_rows_kernel<In, kCh, kR, kSmooth, kMask, true>), dim3((unsigned)grid), dim3(256),
-                       0, s, xb, m, (int)nvec, ldb, smooth, mask, xq, x_scale);
+                       0, s, xb, m, (int)nvec, ldb, smooth, mask, xq, x_scale, zero, nzero);
   } else {
     const unsigned grid = (unsigned)m;
     hipLaunchKernelGGL((sqk::quant_rows_kernel<In, kCh, 1, kSmooth, kMask, false>), dim3(grid), dim3(256), 0, s, xb,
-                       m, (int)nvec, ldb, smooth, mask, xq, x_scale);
+                       m, (int)nvec, ldb, smooth, mask, xq, x_scale, zero, nzero);
   }
 }
 
 template <class In, bool kSmooth, bool kMask>
 static void launch_quant(const void* x, int64_t m, int64_t k, int64_t ldx, const float* smooth, const uint8_t* mask,
-                         int8_t* xq, float* x_scale, hipStream_t s) {
+                         int8_t* xq, float* x_scale, hipStream_t s, uint32_t* zero, int nzero) {
   const int64_t nvec = k / In::kVec;
   const int64_t ldb = ldx * In::kBytes;
   const int64_t per_thread = (nvec + 255) / 256;
   const uint8_t* xb = (const uint8_t*)x;
   if (per_thread <= 1)
-    launch_rows<In, 1, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s);
+    launch_rows<In, 1, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s, zero, nzero);
   else if (per_thread <= 2)
-    launch_rows<In, 2, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s);
+    launch_rows<In, 2, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s, zero, nzero);
   else if (per_thread <= 4)
-    launch_rows<In, 4, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s);
+    launch_rows<In, 4, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s, zero, nzero);
   else if (per_thread <= 8)
-    launch_rows<In, 8, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s);
+    launch_rows<In, 8, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s, zero, nzero);
   else
     hipLaunchKernelGGL((sqk::quant_rows_long_kernel<In, kSmooth, kMask>), dim3((unsigned)(m < 4096 ? m : 4096)),
-                       dim3(256), 0, s, xb, m, nvec, ldb, smooth, mask, xq, x_scale);
+                       dim3(256), 0, s, xb, m, nvec, ldb, smooth, mask, xq, x_scale, zero, nzero);
 }
 
 template <class In>
 static void launch_quant_t(const void* x, int64_t m, int64_t k, int64_t ldx, const float* smooth, const uint8_t* mask,
-                           int8_t* xq, float* x_scale, hipStream_t s) {
+                           int8_t* xq, float* x_scale, hipStream_t s, uint32_t* zero, int nzero) {
   if (mask)
-    launch_quant<In, false, true>(x, m, k, ldx, nullptr, mask, xq, x_scale, s);
+    launch_quant<In, false, true>(x, m, k, ldx, nullptr, mask, xq, x_scale, s, zero, nzero);
   else if (smooth)
-    launch_quant<In, true, false>(x, m, k, ldx, smooth, nullptr, xq, x_scale, s);
+    launch_quant<In, true, false>(x, m, k, ldx, smooth, nullptr, xq, x_scale, s, zero, nzero);
   else
-    launch_quant<In, false, false>(x, m, k, ldx, nullptr, nullptr, xq, x_scale, s);
+    launch_quant<In, false, false>(x, m, k, ldx, nullptr, nullptr, xq, x_scale, s, zero, nzero);
 }
 
 hipError_t quant_rows(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, const float* smooth,
-                      const uint8_t* mask, int8_t* xq, float* x_scale, hipStream_t s) {
-  if (m <= 0) return hipSuccess;
+                      const uint8_t* mask, int8_t* xq, float* x_scale, hipStream_t s, uint32_t* zero,
+                      int64_t nzero) {
+  if (m <= 0) return nzero > 0 ? fill_u32(zero, 0u, nzero, s) : hipSuccess;
+  if (!zero) nzero = 0;
   switch (xt) {
-    case SQ_F32: launch_quant_t<sqk::F32In>(x, m, k, ldx, smooth, mask, xq, x_scale, s); break;
-    case SQ_BF16: launch_quant_t<sqk::BF16In>(x, m, k, ldx, smooth, mask, xq, x_scale, s); break;
-    default: launch_quant_t<sqk::F16In>(x, m, k, ldx, smooth, mask, xq, x_scale, s); break;
+    case SQ_F32: launch_quant_t<sqk::F32In>(x, m, k, ldx, smooth, mask, xq, x_scale, s, zero, (int)nzero); break;
+    case SQ_BF16: launch_quant_t<sqk::BF16In>(x, m, k, ldx, smooth, mask, xq, x_scale, s, zero, (int)nzero); break;
+    default: launch_quant_t<sqk::F16In>(x, m, k, ldx, smooth, mask, xq, x_scale, s, zero, (int)nzero); break;
   }
   return hipGetLastError();
 }

@@ -32,8 +32,11 @@ hipError_t fold_weights(const float* absmax, const void* w, sq_dtype wt, int64_t
                         double alpha, uint32_t flags, float* smooth, int8_t* wq, float* w_scale,
                         float* colmax_ws, hipStream_t s);
 
+// zero / nzero: optional words the launch also clears (the split-K counters of
+// a decode GEMM that follows on the same stream).
 hipError_t quant_rows(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, const float* smooth,
-                      const uint8_t* mask, int8_t* xq, float* x_scale, hipStream_t s);
+                      const uint8_t* mask, int8_t* xq, float* x_scale, hipStream_t s, uint32_t* zero = nullptr,
+                      int64_t nzero = 0);
 
 hipError_t gemm_i8(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
                    int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec,
@@ -44,5 +47,13 @@ bool gemm_big_suits(int64_t m, int64_t n, int64_t k);
 hipError_t gemm_i8_big(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
                        int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec,
                        hipStream_t s);
+
+// Decode GEMM (M <= 64): split-K over workgroups, partial tiles and ticket
+// counters in the workspace. The counters must be zero at launch.
+bool gemm_decode_suits(int64_t m, int64_t n, int64_t k);
+size_t gemm_decode_workspace(int64_t m, int64_t n, int64_t k);
+void gemm_decode_counters(int64_t m, int64_t n, int64_t k, void* ws, uint32_t** counters, int64_t* count);
+hipError_t gemm_i8_decode(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
+                          int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, hipStream_t s);
 
 }  // namespace sqh
