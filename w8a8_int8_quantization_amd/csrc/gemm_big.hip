@@ -72,6 +72,7 @@ struct BigEpi {
   void* y;
   int64_t ldy;
   sqh::DecompArgs dec;
+  bool rows16;  // y and every output row start 16-byte aligned: staged full-row stores
 };
 
 // s_waitcnt vmcnt(n) with the lgkm and exp counters left alone (gfx9 encoding).
@@ -270,63 +271,144 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restri
     xs[i] = (kOut != kBigI32 && mrow[i] < M) ? ep.x_scale[mrow[i]] : 0.f;
   }
   const int cnt = kOut == kBigDecomp ? *ep.dec.count : 0;
+  // fp16 outlier-slice products of fragments i in [i0, i1) for column block j
+  auto outlier_slice = [&](int j, int i0, int i1, float (*yo)[16]) {
 #pragma unroll
-  for (int j = 0; j < C::kFN; ++j) {
-    float yo[C::kFM][16];
-    if (kOut == kBigDecomp) {
+    for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) yo[i][r] = 0.f;
+    for (int c = 0; c < cnt; ++c) {
+      const int64_t jc = ep.dec.idx[c];
+      float xv[C::kFM];
 #pragma unroll
       for (int i = 0; i < C::kFM; ++i)
+        xv[i] = (i >= i0 && i < i1 && mrow[i] < M) ? f16_to_f32(ep.dec.x[(int64_t)mrow[i] * ep.dec.ldx + jc]) : 0.f;
+      const uint16_t* wrow = ep.dec.w16 + jc * ep.dec.ldw;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) yo[i][r] = 0.f;
-      for (int c = 0; c < cnt; ++c) {
-        const int64_t jc = ep.dec.idx[c];
-        float xv[C::kFM];
+      for (int rg = 0; rg < 4; ++rg) {
+        const int n = nw + 32 * j + 8 * rg + 4 * fhalf;
+        float wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wv[e] = n + e < N ? f16_to_f32(wrow[n + e]) : 0.f;
 #pragma unroll
         for (int i = 0; i < C::kFM; ++i)
-          xv[i] = mrow[i] < M ? f16_to_f32(ep.dec.x[(int64_t)mrow[i] * ep.dec.ldx + jc]) : 0.f;
-        const uint16_t* wrow = ep.dec.w16 + jc * ep.dec.ldw;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) yo[i][4 * rg + e] = __fadd_rn(yo[i][4 * rg + e], __fmul_rn(xv[i], wv[e]));
+      }
+    }
+  };
+  // column scales of the 4 outputs a lane holds in row group rg of block j
+  auto col_scales = [&](int n, int nvalid, float* ws) {
+    ws[0] = ws[1] = ws[2] = ws[3] = 0.f;
+    if (kOut == kBigI32 || n >= N) return;
+    if (kVec && nvalid == 4) {
+      const float4 w4 = *reinterpret_cast<const float4*>(ep.w_scale + n);
+      ws[0] = w4.x; ws[1] = w4.y; ws[2] = w4.z; ws[3] = w4.w;
+    } else {
+      for (int e = 0; e < nvalid; ++e) ws[e] = ep.w_scale[n + e];
+    }
+  };
+  // output values of fragment (j, i), row group rg: dequantised, plus the
+  // outlier slice for LLM.int8()
+  auto out_values = [&](int j, int i, int rg, const float* ws, const float (*yo)[16], float* v, int* a) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = acc[j][i][4 * rg + e];
+      v[e] = __fmul_rn(__fmul_rn((float)a[e], xs[i]), ws[e]);
+      if (kOut == kBigDecomp) {
+        const float yi = f16_to_f32(f32_to_f16(v[e]));
+        v[e] = __fadd_rn(yi, f16_to_f32(f32_to_f16(yo[i][4 * rg + e])));
+      }
+    }
+  };
+
+  if (ep.rows16) {
+    // Staged through LDS, one band of tile rows at a time: the lanes' 4-column
+    // pieces are assembled into whole tile rows, which then leave as 16-byte
+    // chunks, consecutive threads writing consecutive chunks of a row (whole
+    // 128-byte lines; written straight from the fragments, 32 rows x 16 bytes
+    // per instruction, the partial lines cost about three times the output
+    // size in HBM writes).
+    constexpr int kEl = (kOut == kBigF32 || kOut == kBigI32) ? 4 : 2;
+    constexpr int kRowB = BN * kEl + 16;  // staged row pitch; the pad spreads the row-strided writes over the banks
+    constexpr int kBand = 128 * kRowB <= kBigStages * C::kStage ? 128 : 64;
+    constexpr int kChunks = BN * kEl / 16;
+    constexpr int kPer = 16 / kEl;  // outputs per chunk
+#pragma unroll 1
+    for (int band = 0; band < kBigBM / kBand; ++band) {
+      __syncthreads();  // every wave is done with the LDS contents
+#pragma unroll
+      for (int j = 0; j < C::kFN; ++j) {
+        // fragments of this wave inside the band (the test is uniform per wave)
+        const int i0 = (band * kBand - wm * 128) / 32;
+        const int lo = i0 < 0 ? 0 : i0, hi = min(C::kFM, i0 + kBand / 32);
+        if (lo >= hi) continue;
+        float yo[kOut == kBigDecomp ? C::kFM : 1][16];
+        if (kOut == kBigDecomp) outlier_slice(j, lo, hi, yo);
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-          const int n = nw + 32 * j + 8 * rg + 4 * fhalf;
-          float wv[4];
+          const int nl = wn * C::kWN + 32 * j + 8 * rg + 4 * fhalf;
+          const int n = n0 + nl;
+          float ws[4];
+          col_scales(n, min(4, N - n), ws);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) wv[e] = n + e < N ? f16_to_f32(wrow[n + e]) : 0.f;
+          for (int i = 0; i < C::kFM; ++i) {
+            if (i < lo || i >= hi) continue;
+            int a[4];
+            float v[4];
+            out_values(j, i, rg, ws, yo, v, a);
+            int8_t* dst = smem + (wm * 128 + 32 * i + frow - band * kBand) * kRowB + nl * kEl;
+            if (kOut == kBigI32) {
+              *reinterpret_cast<int4*>(dst) = make_int4(a[0], a[1], a[2], a[3]);
+            } else if (kOut == kBigF32) {
+              *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+              uint32_t h[4];
 #pragma unroll
-          for (int i = 0; i < C::kFM; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) yo[i][4 * rg + e] = __fadd_rn(yo[i][4 * rg + e], __fmul_rn(xv[i], wv[e]));
+              for (int e = 0; e < 4; ++e)
+                h[e] = (kOut == kBigBF16) ? f32_to_bf16(v[e]) : f32_to_f16(v[e]);
+              *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            }
+          }
+        }
+      }
+      __syncthreads();
+      for (int c = tid; c < kBand * kChunks; c += 256) {
+        const int r = c / kChunks, ch = c - r * kChunks;
+        const int m = m0 + band * kBand + r;
+        const int n = n0 + ch * kPer;
+        if (m >= M || n >= N) continue;
+        const int8_t* srcp = smem + r * kRowB + ch * 16;
+        int8_t* dst = reinterpret_cast<int8_t*>(ep.y) + ((int64_t)m * ep.ldy + n) * kEl;
+        if (n + kPer <= N) {
+          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(srcp);
+        } else {
+          for (int e = 0; e < (N - n) * kEl; ++e) dst[e] = srcp[e];
         }
       }
     }
+    return;
+  }
+
+  // Direct stores (output rows not 16-byte aligned): 4 outputs per lane.
+#pragma unroll
+  for (int j = 0; j < C::kFN; ++j) {
+    float yo[kOut == kBigDecomp ? C::kFM : 1][16];
+    if (kOut == kBigDecomp) outlier_slice(j, 0, C::kFM, yo);
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const int n = nw + 32 * j + 8 * rg + 4 * fhalf;
       if (n >= N) continue;
       const int nvalid = min(4, N - n);
-      float ws[4] = {0.f, 0.f, 0.f, 0.f};
-      if (kOut != kBigI32) {
-        if (kVec && nvalid == 4) {
-          const float4 w4 = *reinterpret_cast<const float4*>(ep.w_scale + n);
-          ws[0] = w4.x; ws[1] = w4.y; ws[2] = w4.z; ws[3] = w4.w;
-        } else {
-          for (int e = 0; e < nvalid; ++e) ws[e] = ep.w_scale[n + e];
-        }
-      }
+      float ws[4];
+      col_scales(n, nvalid, ws);
 #pragma unroll
       for (int i = 0; i < C::kFM; ++i) {
         const int m = mrow[i];
         if (m >= M) continue;
         int a[4];
         float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = acc[j][i][4 * rg + e];
-          v[e] = __fmul_rn(__fmul_rn((float)a[e], xs[i]), ws[e]);
-          if (kOut == kBigDecomp) {
-            const float yi = f16_to_f32(f32_to_f16(v[e]));
-            v[e] = __fadd_rn(yi, f16_to_f32(f32_to_f16(yo[i][4 * rg + e])));
-          }
-        }
+        out_values(j, i, rg, ws, yo, v, a);
         const int64_t off = (int64_t)m * ep.ldy + n;
         store4<kOut == kBigDecomp ? kBigF16 : kOut>(ep.y, off, v, a, kVec && nvalid == 4, nvalid);
       }
@@ -390,7 +472,7 @@ bool gemm_big_suits(int64_t m, int64_t n, int64_t k) {
 hipError_t gemm_i8_big(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
                        int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec,
                        hipStream_t s) {
-  sqk::BigEpi ep{x_scale, w_scale, y, ldy, dec ? *dec : DecompArgs{}};
+  sqk::BigEpi ep{x_scale, w_scale, y, ldy, dec ? *dec : DecompArgs{}, false};
   int out;
   int eb;
   if (dec) {
@@ -405,6 +487,7 @@ hipError_t gemm_i8_big(const int8_t* xq, const float* x_scale, const int8_t* wq,
   }
   const bool vec = (ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % (uintptr_t)(4 * eb) == 0) &&
                    (out == sqk::kBigI32 || reinterpret_cast<uintptr_t>(w_scale) % 16 == 0);
+  ep.rows16 = (ldy * eb) % 16 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0;
   const int M = (int)m, N = (int)n, K = (int)k;
   if (pick_bn(m, n) == 192)
     sqk::launch_big_o<192>(xq, wq, M, N, K, ep, out, vec, s);
