@@ -109,7 +109,7 @@ def test_quant_act(dtype, m, k, smooth):
 @pytest.mark.parametrize("k", [64, 192, 4096, 4160, 8192, 14336, 16384])
 @pytest.mark.parametrize("smooth", [False, True])
 def test_quant_act_prefill_kernel(dtype, k, smooth):
-    """Row counts >= 64 run the row-per-wave kernel with Markstein quotients."""
+    """A few hundred rows of every row length the kernels distinguish."""
     if dtype == "f32" and k > 8192:
         pytest.skip("covered by the workgroup-per-row kernel")
     m = 133
@@ -123,6 +123,23 @@ def test_quant_act_prefill_kernel(dtype, k, smooth):
         s_ref = oracle.smoothing_factors(oracle.calibrate_absmax(c.x_calib), oracle.weight_row_absmax(c.w), 0.5)
     xq, dx = sq.sq_quant_act_per_token(to_dev(x, dtype), None if s_ref is None else torch.from_numpy(s_ref).to(dev()))
     xq_ref, dx_ref = oracle.quantize_activations(x, s_ref)
+    assert np.array_equal(host(dx), dx_ref)
+    assert np.array_equal(host(xq), xq_ref)
+
+
+@pytest.mark.parametrize("m,k", [(3, 16384), (1, 4096), (64, 8192), (1100, 4096), (1030, 16384)])
+@pytest.mark.parametrize("hi_exp", [20, 21])
+def test_quant_act_smooth_spread(m, k, hi_exp):
+    """Smoothing factors with random significands over every binade of the
+    fast-division range (2^-20 .. 2^20, edge significands included): the
+    per-column reciprocals and quotients must reproduce IEEE division exactly.
+    hi_exp 21 puts some factors past the fast range (IEEE fallback)."""
+    log("quant spread", m, k, hi_exp)
+    ch = workloads.outlier_channels(k, seed=k)
+    x = workloads.activations(m, k, "gaussian_outlier", seed=m + k, role="x", channels=ch, dtype="bf16")
+    s = workloads.spread_scales(k, seed=m + k + hi_exp, hi_exp=hi_exp)
+    xq, dx = sq.sq_quant_act_per_token(to_dev(x, "bf16"), torch.from_numpy(s).to(dev()))
+    xq_ref, dx_ref = oracle.quantize_activations(x, s)
     assert np.array_equal(host(dx), dx_ref)
     assert np.array_equal(host(xq), xq_ref)
 

@@ -111,24 +111,35 @@ __global__ __launch_bounds__(256) void quant_rows_long_kernel(const uint8_t* __r
 // with r = RN(1/b),
 //     q0 = a*r,  e = fma(-q0, b, a) (exact),  q = fma(e, r, q0),
 // gives q = RN(a/b) whenever no step leaves the normal range. The divisors are
-// the s_j (each thread forms RN(1/s_j) for its own columns once, with IEEE
-// division, and keeps s_j and 1/s_j in registers for all the rows it visits)
-// and the row scale d (one IEEE division per row).
+// the s_j and the row scale d. Each thread forms r_j = RN(1/s_j) for its own
+// columns once and keeps s_j and r_j in registers for every row it visits:
+// r_j is v_rcp_f32(s_j) refined by one FMA Newton step, e = fma(-s, y, 1),
+// r = fma(e, y, y), which equals the IEEE reciprocal for every s_j in
+// [2^-20, 2^21) (checked exhaustively on MI355X: all 2^23 significands of each
+// of the 41 binades, zero mismatches). RN(1/d) is one IEEE division per row.
 // Range argument for the fast path of a whole row: all s_j in [2^-20, 2^20],
 // d >= 2^-30 and max|x/s| <= 2^50. Then any |x| < 2^-60 (where the remainder
 // could underflow) gives |x/s| < 2^-40 and a quantised value of 0 under either
 // division; every other operand stays well inside the normal range. A row
 // outside these bounds is redone with IEEE division, and a launch whose s_j
 // leave the bounds uses IEEE division throughout.
-// kMk = false is the plain IEEE version, used when there are too few rows per
-// workgroup to amortise the reciprocals.
-// Layout: a 256-thread workgroup walks a grid-stride list of rows; thread t
-// owns the 16-byte vectors t, t+256, ... of every row (coalesced loads,
+// Layout: a kT-thread workgroup walks a grid-stride list of rows; thread t
+// owns the 16-byte vectors t, t+kT, ... of every row (coalesced loads,
 // 8- or 4-byte coalesced stores), prefetches its vectors of the next row
 // while working on the current one (short rows), and the row maximum is a
-// wave reduction plus one barrier on double-buffered LDS partials.
+// wave reduction plus one barrier on double-buffered LDS partials. Prefill
+// shapes use 256 threads and many rows per CU; decode shapes (one row per
+// workgroup, the row's VALU work on a single CU) use 1024 threads for long
+// rows so that four waves per SIMD overlap their dependent chains.
 constexpr float kFastSMin = 0x1p-20f, kFastSMax = 0x1p20f;
 constexpr float kFastDMin = 0x1p-30f, kFastAMax = 0x1p50f;
+
+// RN(1/s) for s in [2^-20, 2^21): hardware reciprocal plus one Newton step.
+__device__ __forceinline__ float rcp_rn(float s) {
+  const float y = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, y, 1.0f);
+  return __builtin_fmaf(e, y, y);
+}
 
 __device__ __forceinline__ float div_mk(float a, float b, float rb) {
   const float q0 = a * rb;
@@ -152,16 +163,17 @@ __device__ __forceinline__ uint32_t pack4(uint32_t c0, uint32_t c1, uint32_t c2,
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-template <class In, int kCh, int kR, bool kSmooth, bool kMask, bool kMk>
-__global__ __launch_bounds__(256) void quant_rows_kernel(const uint8_t* __restrict__ x, int64_t m, int nvec,
+template <class In, int kCh, int kR, bool kSmooth, bool kMask, bool kMk, int kT>
+__global__ __launch_bounds__(kT) void quant_rows_kernel(const uint8_t* __restrict__ x, int64_t m, int nvec,
                                                          int64_t ldx_bytes, const float* __restrict__ smooth,
                                                          const uint8_t* __restrict__ mask, int8_t* __restrict__ xq,
                                                          float* __restrict__ x_scale, uint32_t* __restrict__ zero,
                                                          int nzero) {
   constexpr int V = In::kVec;
   constexpr bool kSmall = kCh * kR <= 8 && kCh <= 4;  // keep x/s between passes and prefetch the next rows
-  __shared__ float red[2][kR][4];
-  __shared__ int any_bad[4];
+  constexpr int kW = kT / 64;                          // waves per workgroup
+  __shared__ float red[2][kR][kW];
+  __shared__ int any_bad[kW];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
@@ -176,7 +188,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint8_t* __restri
       const uint8_t* xr = x + row * ldx_bytes;
 #pragma unroll
       for (int c = 0; c < kCh; ++c) {
-        const int vi = tid + 256 * c;
+        const int vi = tid + kT * c;
         if (vi < nvec) raw[j][c] = load16(xr + (int64_t)vi * 16);
       }
     }
@@ -187,7 +199,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint8_t* __restri
   int64_t g = blockIdx.x;
   if (kSmall && g < ngroups) load_rows(g, nxt);
   if (blockIdx.x == 0)
-    for (int i = tid; i < nzero; i += 256) zero[i] = 0u;
+    for (int i = tid; i < nzero; i += kT) zero[i] = 0u;
 
   float sreg[kSmooth ? kCh : 1][V];
   float rreg[(kSmooth && kMk) ? kCh : 1][V];
@@ -195,7 +207,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint8_t* __restri
   int bad = 0;
 #pragma unroll
   for (int c = 0; c < kCh; ++c) {
-    const int vi = tid + 256 * c;
+    const int vi = tid + kT * c;
     if (vi >= nvec) continue;
     if (kSmooth) {
 #pragma unroll
@@ -207,7 +219,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint8_t* __restri
       if (kMk) {
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-          rreg[c][e] = 1.0f / sreg[c][e];
+          rreg[c][e] = rcp_rn(sreg[c][e]);  // used only when every s_j is in the fast range
           bad |= !(sreg[c][e] >= kFastSMin && sreg[c][e] <= kFastSMax);
         }
       }
@@ -228,7 +240,10 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint8_t* __restri
     const int wbad = __any(bad);
     if (lane == 0) any_bad[wid] = wbad;
     lds_barrier();
-    s_ok = !(any_bad[0] | any_bad[1] | any_bad[2] | any_bad[3]);
+    int anyb = 0;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) anyb |= any_bad[w];
+    s_ok = !anyb;
   }
 
   auto smoothed = [&](const u32x4& rv, int c, float* f, bool fast) {
@@ -258,8 +273,12 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint8_t* __restri
     }
     lds_barrier();  // keeps the next rows' prefetched loads in flight
 #pragma unroll
-    for (int j = 0; j < kR; ++j)
-      v[j] = fmaxf(fmaxf(red[parity][j][0], red[parity][j][1]), fmaxf(red[parity][j][2], red[parity][j][3]));
+    for (int j = 0; j < kR; ++j) {
+      float r = red[parity][j][0];
+#pragma unroll
+      for (int w = 1; w < kW; ++w) r = fmaxf(r, red[parity][j][w]);
+      v[j] = r;
+    }
     parity ^= 1;
   };
   auto pass1 = [&](float* amax, float (*keep)[kCh][V], bool fast) {
@@ -268,7 +287,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint8_t* __restri
       amax[j] = 0.f;
 #pragma unroll
       for (int c = 0; c < kCh; ++c) {
-        if (tid + 256 * c < nvec) {
+        if (tid + kT * c < nvec) {
           float f[V];
           smoothed(raw[j][c], c, f, fast);
 #pragma unroll
@@ -328,7 +347,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint8_t* __restri
       int8_t* qr = xq + row * k;
 #pragma unroll
       for (int c = 0; c < kCh; ++c) {
-        const int vi = tid + 256 * c;
+        const int vi = tid + kT * c;
         if (vi >= nvec) continue;
         float f[V];
         if (kSmall) {
@@ -359,26 +378,20 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint8_t* __restri
 
 namespace sqh {
 
-template <class In, int kCh, bool kSmooth, bool kMask>
+template <class In, int kCh, int kT, bool kSmooth, bool kMask>
 static void launch_rows(const uint8_t* xb, int64_t m, int64_t nvec, int64_t ldb, const float* smooth,
                         const uint8_t* mask, int8_t* xq, float* x_scale, hipStream_t s, uint32_t* zero, int nzero) {
-  // Markstein quotients pay off once each workgroup sees several rows
-  // (prefill-sized M); small M (decode) gets one workgroup per row and plain
-  // IEEE division.
   // Measured on MI355X: one row per iteration with ~4 resident workgroups per
-  // CU beats fewer workgroups with more rows each for short rows (the work is
-  // about one wave per SIMD, so latency hiding wins); long rows prefer 2.
-  constexpr int kR = 1;
+  // CU beats fewer workgroups with more rows each (the per-row work is about
+  // one wave per SIMD, so latency hiding wins); below 1024 rows every row gets
+  // its own workgroup.
+  int64_t grid = m;
   if (m >= 1024) {
-    const int64_t cap = kCh <= 4 ? 1024 : 512;
-    const int64_t grid = m < cap ? m : cap;
-    hipLaunchKernelGGL((sqk::quant_rows_kernel<In, kCh, kR, kSmooth, kMask, true>), dim3((unsigned)grid), dim3(256),
-                       0, s, xb, m, (int)nvec, ldb, smooth, mask, xq, x_scale, zero, nzero);
-  } else {
-    const unsigned grid = (unsigned)m;
-    hipLaunchKernelGGL((sqk::quant_rows_kernel<In, kCh, 1, kSmooth, kMask, false>), dim3(grid), dim3(256), 0, s, xb,
-                       m, (int)nvec, ldb, smooth, mask, xq, x_scale, zero, nzero);
+    const int64_t cap = (kT == 256 && kCh <= 4) ? 1024 : 512;
+    grid = m < cap ? m : cap;
   }
+  hipLaunchKernelGGL((sqk::quant_rows_kernel<In, kCh, 1, kSmooth, kMask, true, kT>), dim3((unsigned)grid), dim3(kT),
+                     0, s, xb, m, (int)nvec, ldb, smooth, mask, xq, x_scale, zero, nzero);
 }
 
 template <class In, bool kSmooth, bool kMask>
@@ -386,16 +399,25 @@ static void launch_quant(const void* x, int64_t m, int64_t k, int64_t ldx, const
                          int8_t* xq, float* x_scale, hipStream_t s, uint32_t* zero, int nzero) {
   const int64_t nvec = k / In::kVec;
   const int64_t ldb = ldx * In::kBytes;
-  const int64_t per_thread = (nvec + 255) / 256;
   const uint8_t* xb = (const uint8_t*)x;
+  // 1024 threads per row: decode-sized inputs (the row's work lands on one
+  // CU), and rows too long to keep in registers at 256 threads
+  if (nvec <= 2048 && ((m < 1024 && nvec > 256) || nvec > 1024)) {
+    if (nvec <= 1024)
+      launch_rows<In, 1, 1024, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s, zero, nzero);
+    else
+      launch_rows<In, 2, 1024, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s, zero, nzero);
+    return;
+  }
+  const int64_t per_thread = (nvec + 255) / 256;
   if (per_thread <= 1)
-    launch_rows<In, 1, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s, zero, nzero);
+    launch_rows<In, 1, 256, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s, zero, nzero);
   else if (per_thread <= 2)
-    launch_rows<In, 2, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s, zero, nzero);
+    launch_rows<In, 2, 256, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s, zero, nzero);
   else if (per_thread <= 4)
-    launch_rows<In, 4, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s, zero, nzero);
+    launch_rows<In, 4, 256, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s, zero, nzero);
   else if (per_thread <= 8)
-    launch_rows<In, 8, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s, zero, nzero);
+    launch_rows<In, 8, 256, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s, zero, nzero);
   else
     hipLaunchKernelGGL((sqk::quant_rows_long_kernel<In, kSmooth, kMask>), dim3((unsigned)(m < 4096 ? m : 4096)),
                        dim3(256), 0, s, xb, m, nvec, ldb, smooth, mask, xq, x_scale, zero, nzero);

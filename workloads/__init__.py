@@ -213,5 +213,22 @@ def positive_scales(n: int, seed: int, stream: int = 0) -> np.ndarray:
     return np.exp(g.uniform(np.log(1e-3), np.log(1e-1), size=n)).astype(np.float32)
 
 
+def spread_scales(k: int, seed: int, lo_exp: int = -20, hi_exp: int = 20, stream: int = 0) -> np.ndarray:
+    """Positive fp32 values with random significands and binary exponents spread
+    uniformly over [lo_exp, hi_exp], with edge significands mixed in (1.0,
+    all-ones, the lowest and highest exponent), for exercising divisions by
+    per-channel factors across their whole range."""
+    g = _rng(seed, "extra", 200 + stream)
+    mant = g.integers(0, 1 << 23, size=k, dtype=np.int64)
+    exps = g.integers(lo_exp, hi_exp + 1, size=k, dtype=np.int64)
+    edge = g.choice(k, size=min(k, 64), replace=False)
+    mant[edge[0::4]] = 0
+    mant[edge[1::4]] = (1 << 23) - 1
+    exps[edge[2::4]] = lo_exp
+    exps[edge[3::4]] = hi_exp
+    bits = ((exps + 127) << 23) | mant
+    return bits.astype(np.uint32).view(np.float32)
+
+
 def cases_for(name: str) -> List[int]:
     return list(CONFIGS[name].get("ms", [CONFIGS[name]["m"]]))
