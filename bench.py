@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="qkv_prefill",
-                   help="qkv_prefill (default), gateup_prefill, down_prefill, decode_up, decode_down, tiny")
+                   help="qkv_prefill (default), gateup_prefill, down_prefill, decode_up, decode_down, tiny, llm_int8")
     p.add_argument("--m", type=int, default=None, help="override the token count (decode workloads)")
     p.add_argument("--alpha", type=float, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -120,16 +120,20 @@ class HipEvents:
         self.events = []
 
 
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(c, s_ref, budget_s: float):
     """The CPU oracle's run-time path (quantise, int8 GEMM, dequantise) on row chunks of X."""
     import numpy as np
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    threads = _blas_threads()
     _, wq, sw = oracle.smooth_fold_quantize(None, c.w, c.alpha, s=s_ref)
     # row chunks of X, cycling over the workload until the time budget is spent
     rows, t_total = 0, 0.0
@@ -144,6 +148,110 @@ def cpu_baseline(c, s_ref, budget_s: float):
         chunk = min(chunk * 2, 512)
     tops = 2.0 * rows * c.n * c.k / t_total / 1e12
     return {"value": tops, "unit": "TOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} rows of X ({rows / c.m:.2f} passes over the {c.m}-row workload, all N={c.n} "
+                      f"outputs, K={c.k}), {t_total:.1f} s of numpy/BLAS work"}
+
+
+def bench_llm_int8(args, dev):
+    """LLM.int8() decomposition, fp16 in and out: a step is outlier detection
+    (column max + selection), the masked row-wise quantisation, and the int8
+    GEMM whose epilogue adds the fp16 outlier slice, each a C-ABI call timed
+    with HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    import workloads
+    import w8a8_int8_quantization_amd as sq
+
+    c = workloads.decomp_case(m=args.m)
+    print(f"[bench] workload llm_int8 M={c.m} K={c.k} N={c.n} threshold={c.threshold}", file=sys.stderr, flush=True)
+    h = lambda a: torch.from_numpy(a).to(torch.float16).to(dev)
+    x, w16 = h(c.x), h(c.w)
+    _, wq, sw = sq.sq_smooth_fold_weights(w16, flags=sq.SMOOTH_NONE)
+    mask = torch.empty(c.k, dtype=torch.uint8, device=dev)
+    idx = torch.empty(c.k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, dtype=torch.int32, device=dev)
+    xq = torch.empty((c.m, c.k), dtype=torch.int8, device=dev)
+    dx = torch.empty(c.m, dtype=torch.float32, device=dev)
+    y = torch.empty((c.m, c.n), dtype=torch.float16, device=dev)
+    nb = sq.raw["sq_outlier_detect_workspace_size"](c.k)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    det, qm, gm = sq.raw["sq_outlier_detect"], sq.raw["sq_quant_act_rows_masked"], sq.raw["sq_int8_decomp_gemm"]
+    det_a = (x.data_ptr(), sq.SQ_F16, c.m, c.k, c.k, float(c.threshold), mask.data_ptr(), idx.data_ptr(),
+             cnt.data_ptr(), ws.data_ptr(), nb, stream)
+    qm_a = (x.data_ptr(), sq.SQ_F16, c.m, c.k, c.k, mask.data_ptr(), xq.data_ptr(), dx.data_ptr(), stream)
+    gm_a = (xq.data_ptr(), dx.data_ptr(), x.data_ptr(), c.k, wq.data_ptr(), sw.data_ptr(), w16.data_ptr(), c.n,
+            idx.data_ptr(), cnt.data_ptr(), c.m, c.n, c.k, y.data_ptr(), c.n, stream)
+    hip = HipEvents(sq._lib, stream)
+
+    def run(steps, evs=None):
+        bad = 0
+        for i in range(steps):
+            if evs:
+                hip.record(evs[i][0])
+            bad |= det(*det_a)
+            if evs:
+                hip.record(evs[i][1])
+            bad |= qm(*qm_a)
+            if evs:
+                hip.record(evs[i][2])
+            bad |= gm(*gm_a)
+            if evs:
+                hip.record(evs[i][3])
+        if bad:
+            raise RuntimeError(f"a C-ABI call failed (status bits {bad})")
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    evs = [[hip.create() for _ in range(4)] for _ in range(args.steps)]
+    t0, t1 = hip.create(), hip.create()
+    hip.record(t0)
+    run(args.steps, evs)
+    hip.record(t1)
+    torch.cuda.synchronize()
+    total_ms = hip.elapsed(t0, t1)
+    part = [float(np.mean([hip.elapsed(e[j], e[j + 1]) for e in evs])) for j in range(3)]
+    hip.destroy_all()
+    n_out = int(cnt.cpu()[0])
+    ops = 2.0 * c.m * c.n * c.k
+    ms = total_ms / args.steps
+    gemm_tops = ops / (part[2] * 1e-3) / 1e12
+    traffic = pmc_traffic("llm_int8" if args.m is None else f"llm_int8_m{c.m}", "gemm_big.hip")
+    result = {
+        "metric": METRIC, "value": ops / (ms * 1e-3) / 1e12, "unit": "TOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8", "data": "synthetic",
+        "config": {"workload": f"llm_int8: X f16 [{c.m} x {c.k}] -> W [{c.k} x {c.n}], f16 out, threshold "
+                               f"{c.threshold}, {n_out} outlier columns detected", "M": c.m, "K": c.k, "N": c.n},
+        "detect_us": part[0] * 1e3, "quant_us": part[1] * 1e3, "gemm_us": part[2] * 1e3, "gemm_only_tops": gemm_tops,
+        "outlier_columns": n_out,
+        "roofline": {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                     "frac": gemm_tops / PEAK_INT8_TOPS, "traffic": traffic, "kernel": "gemm_big_kernel",
+                     "ops_per_launch": ops, "launch_us": part[2] * 1e3},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_decomp(c, args.cpu_seconds),
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_decomp(c, budget_s: float):
+    """The CPU oracle's LLM.int8() layer on row chunks of X (the column mask from all rows, as on the GPU)."""
+    import numpy as np
+    import oracle
+
+    threads = _blas_threads()
+    mask = oracle.detect_outliers(c.x, c.threshold)
+    wq, sw = oracle.quantize_weights_per_channel(c.w)
+    rows, t_total, start, chunk = 0, 0.0, 0, 64
+    while t_total < budget_s:
+        r1 = min(c.m, start + chunk)
+        t0 = time.perf_counter()
+        oracle.int8_decomp_linear(c.x[start:r1], wq, sw, c.w, c.threshold, mask=mask)
+        t_total += time.perf_counter() - t0
+        rows += r1 - start
+        start = 0 if r1 == c.m else r1
+        chunk = min(chunk * 2, 512)
+    return {"value": 2.0 * rows * c.n * c.k / t_total / 1e12, "unit": "TOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows} rows of X ({rows / c.m:.2f} passes over the {c.m}-row workload, all N={c.n} "
                       f"outputs, K={c.k}), {t_total:.1f} s of numpy/BLAS work"}
 
@@ -169,6 +277,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.workload == "llm_int8":
+        bench_llm_int8(args, dev)
+        return
     c = workloads.linear_case(args.workload, m=args.m, alpha=args.alpha)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
     to = lambda a, dt: torch.from_numpy(a).to(tdt[dt]).to(dev)

@@ -253,6 +253,32 @@ sq_status sq_int8_decomp_linear(const void* x, int64_t ldx, const int8_t* wq, co
                                 float threshold, void* y, int64_t ldy, int32_t* n_outliers,
                                 void* ws, size_t ws_bytes, sq_stream_t stream);
 
+/*
+ * The second half of sq_int8_decomp_linear on its own, for callers that run
+ * detection (sq_outlier_detect) and the masked quantisation
+ * (sq_quant_act_rows_masked) themselves, e.g. to reuse one detection:
+ * the int8 GEMM of the masked, row-quantised X with the fp16 outlier slice
+ * added in the epilogue.
+ * [INT8] "The architecture: every piece explained" (int8 path with the outer
+ * product of row and column scales, fp16 path over the outlier slice, sum in
+ * fp16); "End-to-end flow".
+ *
+ *   y[i][n] = fp16( y_int + y_out ) with y_int and y_out as defined for
+ *   sq_int8_decomp_linear, the outlier columns being idx[0 .. *n_outliers-1]
+ *
+ * xq: [M x K] int8 with the outlier columns zero, x_scale: [M] (both from
+ * sq_quant_act_rows_masked). x: [M x ldx] fp16 activations (only the outlier
+ * columns are read). wq: [N x K] int8, w_scale: [N]. w16: [K x ldw16] fp16
+ * (only the outlier rows are read). idx, n_outliers: from sq_outlier_detect
+ * (device memory). y: [M x ldy] fp16 output. Pointers to fp16 data need
+ * 2-byte alignment, xq and wq 16-byte alignment. Results equal those of
+ * sq_int8_decomp_linear bit for bit.
+ */
+sq_status sq_int8_decomp_gemm(const int8_t* xq, const float* x_scale, const void* x, int64_t ldx, const int8_t* wq,
+                              const float* w_scale, const void* w16, int64_t ldw16, const int32_t* idx,
+                              const int32_t* n_outliers, int64_t m, int64_t n, int64_t k, void* y, int64_t ldy,
+                              sq_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

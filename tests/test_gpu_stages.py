@@ -326,3 +326,19 @@ def test_int8_decomp_infinite_threshold_is_plain_int8():
     y2 = sq.sq_w8a8_linear(xq, dx, wq, sw, out_dtype=torch.float16)
     assert int(host(n_out)[0]) == 0
     assert np.array_equal(bits16(y), bits16(y2))
+
+
+@pytest.mark.parametrize("m,k,n,nout", [(300, 1024, 520, 6), (2048, 4096, 1024, 8), (17, 512, 64, 0)])
+def test_int8_decomp_gemm_equals_linear(m, k, n, nout):
+    """The GEMM half on its own, after detection and masked quantisation made by
+    their own entry points, reproduces the one-call decomposition bit for bit."""
+    log("decomp gemm", m, k, n, nout)
+    cfg = workloads.decomp_case(seed=m + k, m=m, k=k, n=n, n_outlier_cols=nout)
+    xh, wh = to_dev(cfg.x, "f16"), to_dev(cfg.w, "f16")
+    _, wq, sw = sq.sq_smooth_fold_weights(wh, flags=sq.SMOOTH_NONE)
+    y1, n1 = sq.sq_int8_decomp_linear(xh, wq, sw, wh, cfg.threshold)
+    mask, idx, count = sq.sq_outlier_detect(xh, cfg.threshold)
+    xq, dx = sq.sq_quant_act_rows_masked(xh, mask)
+    y2 = sq.sq_int8_decomp_gemm(xq, dx, xh, wq, sw, wh, idx, count)
+    assert int(host(n1)[0]) == int(host(count)[0])
+    assert np.array_equal(bits16(y1), bits16(y2))

@@ -20,6 +20,7 @@ __all__ = [
     "SQError", "lib_path", "sq_version",
     "sq_calibrate_absmax", "sq_smooth_fold_weights", "sq_quant_act_per_token", "sq_w8a8_linear",
     "sq_w8a8_linear_dyn", "sq_outlier_detect", "sq_quant_act_rows_masked", "sq_int8_decomp_linear",
+    "sq_int8_decomp_gemm", "linear_workspace",
     "SMOOTH_COMPUTE", "SMOOTH_GIVEN", "SMOOTH_NONE", "MAX_K_INT32", "EXPORTED_SYMBOLS",
 ]
 
@@ -29,7 +30,7 @@ lib_path = os.path.join(_PKG, "libsq.so")
 if not os.path.exists(lib_path):
     raise ImportError(
         f"{lib_path} is missing: the HIP library has not been built. "
-        "Run `python -m w8a8_int8_quantization_amd.build` (or __graft_entry__.build()).")
+        "Run `python w8a8_int8_quantization_amd/build.py` (or __graft_entry__.build()).")
 
 _lib = ctypes.CDLL(lib_path)
 
@@ -58,6 +59,7 @@ _SIGS = {
     "sq_outlier_detect": (_st, [_p, _st, _i64, _i64, _i64, _f, _p, _p, _p, _p, _sz, _p]),
     "sq_quant_act_rows_masked": (_st, [_p, _st, _i64, _i64, _i64, _p, _p, _p, _p]),
     "sq_int8_decomp_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "sq_int8_decomp_gemm": (_st, [_p, _p, _p, _i64, _p, _p, _p, _i64, _p, _p, _i64, _i64, _i64, _p, _i64, _p]),
     "sq_int8_decomp_linear": (_st, [_p, _i64, _p, _p, _p, _i64, _i64, _i64, _i64, _f, _p, _i64, _p, _p, _sz, _p]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
@@ -247,3 +249,19 @@ def sq_int8_decomp_linear(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tens
         _ptr(x), ldx, _ptr(wq), _ptr(w_scale), _ptr(w16), ldw, m, n, k, float(threshold), _ptr(y), ldy,
         _ptr(cnt), _ptr(ws), ws.numel() if ws is not None else 0, _stream(x.device)))
     return y, cnt
+
+
+def sq_int8_decomp_gemm(xq: torch.Tensor, x_scale: torch.Tensor, x: torch.Tensor, wq: torch.Tensor,
+                        w_scale: torch.Tensor, w16: torch.Tensor, idx: torch.Tensor, count: torch.Tensor,
+                        y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int8 GEMM of the masked quantised X plus the fp16 outlier slice (LLM.int8() second half)."""
+    m, k, _ = _rows(xq)
+    _, _, ldx = _rows(x)
+    n = wq.shape[0]
+    _, _, ldw = _rows(w16)
+    y = torch.empty((m, n), dtype=torch.float16, device=xq.device) if y is None else y
+    _, _, ldy = _rows(y)
+    _check("sq_int8_decomp_gemm", raw["sq_int8_decomp_gemm"](
+        _ptr(xq), _ptr(x_scale), _ptr(x), ldx, _ptr(wq), _ptr(w_scale), _ptr(w16), ldw, _ptr(idx), _ptr(count),
+        m, n, k, _ptr(y), ldy, _stream(xq.device)))
+    return y

@@ -1,6 +1,7 @@
 """Build the HIP library ``libsq.so`` in-tree for gfx950.
 
-Run ``python -m w8a8_int8_quantization_amd.build`` (or ``__graft_entry__.build()``).
+Run ``python w8a8_int8_quantization_amd/build.py`` (or ``__graft_entry__.build()``); this
+file imports nothing from the package, whose import needs the built library.
 Every build compiles from source; nothing is cached outside this directory.
 """
 from __future__ import annotations

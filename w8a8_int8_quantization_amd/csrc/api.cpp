@@ -284,4 +284,23 @@ sq_status sq_int8_decomp_linear(const void* x, int64_t ldx, const int8_t* wq, co
   return hip_status(sqh::gemm_i8(xq, dx, wq, w_scale, m, n, k, y, SQ_F16, ldy, &d, s));
 }
 
+sq_status sq_int8_decomp_gemm(const int8_t* xq, const float* x_scale, const void* x, int64_t ldx, const int8_t* wq,
+                              const float* w_scale, const void* w16, int64_t ldw16, const int32_t* idx,
+                              const int32_t* n_outliers, int64_t m, int64_t n, int64_t k, void* y, int64_t ldy,
+                              sq_stream_t stream) {
+  SQ_TRY(check_k(k));
+  if (k > SQ_MAX_K_INT32) return SQ_ERR_RANGE;
+  if (m < 0 || n < 0) return SQ_ERR_SHAPE;
+  if (ldx < k || ldw16 < n || ldy < n) return SQ_ERR_SHAPE;
+  if (m > INT32_MAX || n > INT32_MAX) return SQ_ERR_SHAPE;
+  if (m == 0 || n == 0) return SQ_OK;
+  if (!xq || !x_scale || !x || !wq || !w_scale || !w16 || !idx || !n_outliers || !y) return SQ_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(wq)) return SQ_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(x) & 1u) || (reinterpret_cast<uintptr_t>(w16) & 1u) ||
+      (reinterpret_cast<uintptr_t>(y) & 1u))
+    return SQ_ERR_ALIGN;
+  sqh::DecompArgs d{(const uint16_t*)x, ldx, (const uint16_t*)w16, ldw16, idx, n_outliers};
+  return hip_status(sqh::gemm_i8(xq, x_scale, wq, w_scale, m, n, k, y, SQ_F16, ldy, &d, (hipStream_t)stream));
+}
+
 }  // extern "C"

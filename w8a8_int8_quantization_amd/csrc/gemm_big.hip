@@ -43,6 +43,7 @@ constexpr int kBigBM = 256;
 constexpr int kBigBK = 128;    // k bytes per pipeline stage: one 128-byte line per tile row
 constexpr int kBigStages = 2;  // LDS double buffer
 constexpr int kGroupM = 4;
+constexpr int kSliceCols = 16;  // outlier columns staged in LDS by the LLM.int8() epilogue
 
 enum BigOut { kBigF32 = 0, kBigBF16 = 1, kBigF16 = 2, kBigI32 = 3, kBigDecomp = 4 };
 
@@ -117,6 +118,9 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restri
                                                           int M, int N, int K, BigEpi ep) {
   using C = BigCfg<BN>;
   __shared__ __attribute__((aligned(1024))) int8_t smem[kBigStages * C::kStage];
+  // LLM.int8(): the tile's fp16 outlier slices of X and W, gathered once
+  __shared__ uint16_t slice_x[kOut == kBigDecomp ? kBigBM * kSliceCols : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t slice_w[kOut == kBigDecomp ? kSliceCols * BN : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -271,12 +275,50 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restri
     xs[i] = (kOut != kBigI32 && mrow[i] < M) ? ep.x_scale[mrow[i]] : 0.f;
   }
   const int cnt = kOut == kBigDecomp ? *ep.dec.count : 0;
+  // Up to kSliceCols outlier columns: gather X[tile rows][idx] and
+  // W16[idx][tile columns] into LDS once (the direct version below gathers
+  // them from global memory for every 32-column block of every wave).
+  const bool staged = kOut == kBigDecomp && cnt <= kSliceCols;
+  if (kOut == kBigDecomp && staged && cnt > 0) {
+    {
+      const int row = tid;  // 256 threads, 256 tile rows
+      const int64_t m = (int64_t)m0 + row;
+      for (int c = 0; c < cnt; ++c)
+        slice_x[row * kSliceCols + c] = m < M ? ep.dec.x[m * ep.dec.ldx + ep.dec.idx[c]] : (uint16_t)0;
+    }
+    for (int e = tid; e < cnt * BN; e += 256) {
+      const int c = e / BN, nl = e - c * BN;
+      const int64_t n = (int64_t)n0 + nl;
+      slice_w[c * BN + nl] = n < N ? ep.dec.w16[(int64_t)ep.dec.idx[c] * ep.dec.ldw + n] : (uint16_t)0;
+    }
+    __syncthreads();
+  }
   // fp16 outlier-slice products of fragments i in [i0, i1) for column block j
   auto outlier_slice = [&](int j, int i0, int i1, float (*yo)[16]) {
 #pragma unroll
     for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) yo[i][r] = 0.f;
+    if (staged) {
+      for (int c = 0; c < cnt; ++c) {
+        float xv[C::kFM];
+#pragma unroll
+        for (int i = 0; i < C::kFM; ++i)
+          xv[i] = (i >= i0 && i < i1) ? f16_to_f32(slice_x[(wm * 128 + 32 * i + frow) * kSliceCols + c]) : 0.f;
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int nl = wn * C::kWN + 32 * j + 8 * rg + 4 * fhalf;
+          const uint2 wp = *reinterpret_cast<const uint2*>(&slice_w[c * BN + nl]);
+          const float wv[4] = {f16_to_f32((uint16_t)(wp.x & 0xFFFFu)), f16_to_f32((uint16_t)(wp.x >> 16)),
+                               f16_to_f32((uint16_t)(wp.y & 0xFFFFu)), f16_to_f32((uint16_t)(wp.y >> 16))};
+#pragma unroll
+          for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yo[i][4 * rg + e] = __fadd_rn(yo[i][4 * rg + e], __fmul_rn(xv[i], wv[e]));
+        }
+      }
+      return;
+    }
     for (int c = 0; c < cnt; ++c) {
       const int64_t jc = ep.dec.idx[c];
       float xv[C::kFM];

@@ -9,11 +9,12 @@
 // explained" -- a feature column whose magnitude exceeds the threshold is an
 // outlier column.
 //
-// Layout: X is row-major [T x ldx]. One thread owns one 16-byte column vector
-// (4 fp32 or 8 bf16/fp16 columns) and walks a slab of rows, so every wave
-// reads 1 KiB of contiguous row memory per step; partial maxima of a slab are
-// merged with one integer atomicMax per column (non-negative binary32 values
-// order like their bit patterns, so the result is exact and order free).
+// Layout: X is row-major [T x ldx]. A lane owns one 16-byte column vector
+// (4 fp32 or 8 bf16/fp16 columns) and walks rows of a slab, so every wave
+// reads 1 KiB of contiguous row memory per step; the slab maxima are merged
+// with one integer atomicMax per column and workgroup (non-negative binary32
+// values order like their bit patterns, so the result is exact and order
+// free).
 #include "sq_common.hpp"
 #include "sq_launch.hpp"
 
@@ -23,72 +24,93 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p,
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
 }
 
+// A 256-thread workgroup covers 64 column vectors (1 KiB of a row) and a slab
+// of rows: wave w reads rows w, w+4, ... of the slab, eight loads in flight
+// per thread; the four waves' maxima meet in LDS and one atomicMax per column
+// leaves the workgroup.
 template <class In>
 __global__ __launch_bounds__(256) void absmax_cols_kernel(const uint8_t* __restrict__ x, int64_t t, int64_t nvec,
                                                           int64_t ldx_bytes, int64_t rows_per_block,
                                                           float* __restrict__ absmax) {
   constexpr int V = In::kVec;
-  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (v >= nvec) return;
+  constexpr int kU = 8;
+  __shared__ float part[4][64][V + 1];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int64_t v = (int64_t)blockIdx.x * 64 + lane;
+  const bool active = v < nvec;
   const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
   const int64_t r1 = r0 + rows_per_block < t ? r0 + rows_per_block : t;
   float m[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) m[e] = 0.f;
-  const uint8_t* p = x + r0 * ldx_bytes + v * 16;
-  int64_t r = r0;
-  for (; r + 4 <= r1; r += 4) {
-    u32x4 q[4];
+  if (active) {
+    const uint8_t* p = x + v * 16;
+    int64_t r = r0 + wid;
+    for (; r + 4 * (kU - 1) < r1; r += 4 * kU) {
+      u32x4 q[kU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) q[u] = load16(p + u * ldx_bytes);
-    p += 4 * ldx_bytes;
+      for (int u = 0; u < kU; ++u) q[u] = load16(p + (r + 4 * u) * ldx_bytes);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kU; ++u) {
+        float f[V];
+        In::unpack(q[u], f);
+#pragma unroll
+        for (int e = 0; e < V; ++e) m[e] = fmaxf(m[e], fabsf(f[e]));
+      }
+    }
+    for (; r < r1; r += 4) {
       float f[V];
-      In::unpack(q[u], f);
+      In::unpack(load16(p + r * ldx_bytes), f);
 #pragma unroll
       for (int e = 0; e < V; ++e) m[e] = fmaxf(m[e], fabsf(f[e]));
     }
   }
-  for (; r < r1; ++r) {
-    float f[V];
-    In::unpack(load16(p), f);
-    p += ldx_bytes;
 #pragma unroll
-    for (int e = 0; e < V; ++e) m[e] = fmaxf(m[e], fabsf(f[e]));
+  for (int e = 0; e < V; ++e) part[wid][lane][e] = m[e];
+  __syncthreads();
+  if (wid == 0 && active) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const float mm = fmaxf(fmaxf(part[0][lane][e], part[1][lane][e]), fmaxf(part[2][lane][e], part[3][lane][e]));
+      if (mm > 0.f) atomic_max_nonneg(absmax + v * V + e, mm);
+    }
   }
-#pragma unroll
-  for (int e = 0; e < V; ++e)
-    if (m[e] > 0.f) atomic_max_nonneg(absmax + v * V + e, m[e]);
 }
 
 // One workgroup: mask, ascending index list and count of the columns whose
-// maximum magnitude is strictly above the threshold.
+// maximum magnitude is strictly above the threshold. Rounds of 1024 columns,
+// one per thread in order: a wave's ballot gives each outlier lane its rank
+// among the wave's outliers, the 16 wave counts in LDS give the wave offsets,
+// and a running total carries across rounds, so the list comes out ascending.
 __global__ __launch_bounds__(1024) void outlier_select_kernel(const float* __restrict__ colmax, int64_t k, float thr,
                                                               uint8_t* __restrict__ mask, int32_t* __restrict__ idx,
                                                               int32_t* __restrict__ count) {
-  __shared__ int sums[1024];
+  __shared__ int wcount[2][16];
   const int tid = threadIdx.x;
-  const int64_t seg = (k + 1023) / 1024;
-  const int64_t b = tid * seg;
-  const int64_t e = b + seg < k ? b + seg : k;
-  int c = 0;
-  for (int64_t j = b; j < e; ++j) c += colmax[j] > thr ? 1 : 0;
-  sums[tid] = c;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int add = tid >= off ? sums[tid - off] : 0;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  int base = 0;
+  int parity = 0;
+  for (int64_t j0 = 0; j0 < k; j0 += 1024) {
+    const int64_t j = j0 + tid;
+    const bool o = j < k && colmax[j] > thr;
+    if (j < k) mask[j] = o ? 1 : 0;
+    const uint64_t bal = __ballot(o);
+    if (lane == 0) wcount[parity][wid] = __popcll(bal);
     __syncthreads();
-    sums[tid] += add;
-    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int c = wcount[parity][w];
+      before += w < wid ? c : 0;
+      total += c;
+    }
+    if (o) idx[base + before + __popcll(bal & ((1ull << lane) - 1ull))] = (int32_t)j;
+    base += total;
+    parity ^= 1;  // the next round writes the other buffer, so one barrier per round suffices
   }
-  int pos = sums[tid] - c;
-  for (int64_t j = b; j < e; ++j) {
-    const bool o = colmax[j] > thr;
-    mask[j] = o ? 1 : 0;
-    if (o) idx[pos++] = (int32_t)j;
-  }
-  if (tid == 1023) *count = sums[1023];
+  if (tid == 0) *count = base;
 }
 
 }  // namespace sqk
@@ -109,10 +131,10 @@ hipError_t absmax_cols(const void* x, sq_dtype xt, int64_t t, int64_t k, int64_t
   const int bytes = xt == SQ_F32 ? 4 : 2;
   const int vec = 16 / bytes;
   const int64_t nvec = k / vec;
-  const int64_t gx = (nvec + 255) / 256;
-  // about 2048 workgroups, each over a slab of at least 8 rows
-  int64_t rpb = (t * gx + 2047) / 2048;
-  if (rpb < 8) rpb = 8;
+  const int64_t gx = (nvec + 63) / 64;
+  // about 1024 workgroups (four per CU), each over a slab of at least 32 rows
+  int64_t rpb = (t * gx + 1023) / 1024;
+  if (rpb < 32) rpb = 32;
   int64_t gy = (t + rpb - 1) / rpb;
   if (gy > 65535) {
     rpb = (t + 65534) / 65535;
