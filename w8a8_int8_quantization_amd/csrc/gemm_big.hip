@@ -311,10 +311,12 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restri
           const uint2 wp = *reinterpret_cast<const uint2*>(&slice_w[c * BN + nl]);
           const float wv[4] = {f16_to_f32((uint16_t)(wp.x & 0xFFFFu)), f16_to_f32((uint16_t)(wp.x >> 16)),
                                f16_to_f32((uint16_t)(wp.y & 0xFFFFu)), f16_to_f32((uint16_t)(wp.y >> 16))};
+          // fp16 x fp16 is exact in binary32 (22 significant bits), so one
+          // fused multiply-add rounds exactly like product-then-sum
 #pragma unroll
           for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) yo[i][4 * rg + e] = __fadd_rn(yo[i][4 * rg + e], __fmul_rn(xv[i], wv[e]));
+            for (int e = 0; e < 4; ++e) yo[i][4 * rg + e] = __builtin_fmaf(xv[i], wv[e], yo[i][4 * rg + e]);
         }
       }
       return;
