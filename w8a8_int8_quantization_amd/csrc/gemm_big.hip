@@ -51,7 +51,7 @@ enum BigOut { kBigF32 = 0, kBigBF16 = 1, kBigF16 = 2, kBigI32 = 3, kBigDecomp = 
 // rows). The chunk index is XOR-ed with r & 7, so the MFMA fragment reads (32
 // consecutive rows x one chunk per half-wave) spread over all banks; without
 // it every lane of a half-wave would hit the same bank group.
-__device__ __forceinline__ int big_swz(int r) { return r & 7; }
+__device__ __forceinline__ int big_swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int big_lds_off(int r, int c) { return r * kBigBK + ((c ^ big_swz(r)) << 4); }
 
 template <int BN>
