@@ -9,28 +9,25 @@
 // Quantization" (Inter-Token Latency): the result goes back to bf16.
 //
 // Design for gfx950 (256 CUs, 160 KiB LDS per CU, 64-wide waves):
-//  * one 256-thread workgroup per CU computes a 256 x BN output tile
-//    (BN = 256, or 192 when that fills the 256 CUs better); 4 waves in a 2 x 2
-//    grid, each owning 128 x BN/2 outputs = 4 x BN/64 blocks of
-//    v_mfma_i32_32x32x32_i8 with int32 accumulators in AGPRs. A 128-row wave
-//    tile needs 64 B of LDS reads per clock per CU at full MFMA rate, half of
-//    what a 64-row tile needs.
+//  * one 512-thread workgroup per CU computes a 256 x BN output tile
+//    (BN = 256, or 192 when that fills the 256 CUs better); 8 waves, two per
+//    SIMD, in a 4 x 2 grid, each owning 64 x BN/2 outputs = 2 x BN/64 blocks
+//    of v_mfma_i32_32x32x32_i8 with int32 accumulators in AGPRs.
 //  * K advances 128 bytes per stage through a double-buffered LDS (2 x 64
 //    KiB) filled by gfx950's direct global-to-LDS transfers (global_load_lds,
 //    16 bytes per lane): no registers stage the tiles, every tile row is one
 //    full 128-byte line per stage (full-line requests: the L1 sustains only
 //    a bounded number of requests in flight, so 64-byte requests halve the
-//    bandwidth), and each stage's transfers start a full stage (~2000 MFMA
-//    cycles) before it is consumed. Completion is tracked with explicit vmcnt
-//    waits and one barrier per stage.
+//    bandwidth), and each stage's transfers start a full stage before it is
+//    consumed. Completion is tracked with explicit vmcnt waits and one
+//    barrier per stage.
 //  * LDS rows are 128 bytes; the eight 16-byte chunks of row r are XOR-
-//    swizzled with r & 7, and each transfer lane fetches the chunk that
-//    belongs at its fixed LDS slot, so the MFMA fragment reads are free of
-//    bank conflicts.
+//    swizzled with (r >> 1) & 7, and each transfer lane fetches the chunk
+//    that belongs at its fixed LDS slot. ds_read_b128 is served 16 lanes at a
+//    time: the 16 rows of such a group then hit 16 distinct bank groups.
 //  * The MFMA A operand is the Wq fragment and B the Xq fragment, so a lane's
 //    four consecutive accumulator registers are four consecutive output
-//    columns of one token: the epilogue writes 8-byte (bf16/fp16) or 16-byte
-//    (fp32/int32) vectors.
+//    columns of one token; the epilogue assembles whole output rows in LDS.
 //  * Workgroups are dispatched round-robin over the 8 XCDs; the tile order
 //    gives each XCD a contiguous range of tiles, grouped 4 tile-rows at a time,
 //    so that tiles sharing Xq and Wq panels run under the same L2.
@@ -40,6 +37,13 @@
 namespace sqk {
 
 constexpr int kBigBM = 256;
+// Eight waves, two per SIMD, in a 4 x 2 grid over the tile: while one wave of
+// a SIMD waits on its fragment reads or the stage barrier, the other keeps the
+// matrix core busy (measured on MI355X against four waves of twice the
+// sub-tile: QKV 62 -> 55 us, gate/up 1010 -> 942 us, down 425 -> 406 us), at
+// the price of ~40% more LDS fragment reads, which the LDS has room for.
+constexpr int kBigWaves = 8;
+constexpr int kBigThreads = 64 * kBigWaves;
 constexpr int kBigBK = 128;    // k bytes per pipeline stage: one 128-byte line per tile row
 constexpr int kBigStages = 2;  // LDS double buffer
 constexpr int kGroupM = 4;
@@ -48,22 +52,26 @@ constexpr int kSliceCols = 16;  // outlier columns staged in LDS by the LLM.int8
 enum BigOut { kBigF32 = 0, kBigBF16 = 1, kBigF16 = 2, kBigI32 = 3, kBigDecomp = 4 };
 
 // Byte offset of 16-byte chunk c (0..7) of tile row r in a stage (128-byte
-// rows). The chunk index is XOR-ed with r & 7, so the MFMA fragment reads (32
-// consecutive rows x one chunk per half-wave) spread over all banks; without
-// it every lane of a half-wave would hit the same bank group.
+// rows). The chunk index is XOR-ed with (r >> 1) & 7: a 128-byte row covers
+// half of the 64 banks, so rows r and r+1 fall in different halves, and the
+// eight even (odd) rows of a 16-lane group get eight distinct chunks. Without
+// it every lane of a half-wave would hit the same bank group; with r & 7,
+// rows r and r + 8 collided (measured: 3.96M bank-conflict cycles per QKV
+// dispatch, 0.29M with this one).
 __device__ __forceinline__ int big_swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int big_lds_off(int r, int c) { return r * kBigBK + ((c ^ big_swz(r)) << 4); }
 
 template <int BN>
 struct BigCfg {
-  static constexpr int kWN = BN / 2;
+  static constexpr int kWN = BN / 2;                  // output columns per wave
   static constexpr int kFN = kWN / 32;
-  static constexpr int kFM = 4;
+  static constexpr int kWM = kBigBM / (kBigWaves / 2);  // tokens per wave
+  static constexpr int kFM = kWM / 32;
   static constexpr int kStageA = kBigBM * kBigBK;
   static constexpr int kStage = (kBigBM + BN) * kBigBK;
   // 1 KiB direct-to-LDS transfers (8 rows each) per wave and stage
-  static constexpr int kDmaA = kBigBM / 8 / 4;
-  static constexpr int kDmaB = BN / 8 / 4;
+  static constexpr int kDmaA = kBigBM / 8 / kBigWaves;
+  static constexpr int kDmaB = BN / 8 / kBigWaves;
   static constexpr int kDma = kDmaA + kDmaB;
 };
 
@@ -114,7 +122,7 @@ __device__ __forceinline__ void store4(void* y, int64_t off, const float* v, con
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int BN, int kOut, bool kVec>
-__global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
+__global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
                                                           int M, int N, int K, BigEpi ep) {
   using C = BigCfg<BN>;
   __shared__ __attribute__((aligned(1024))) int8_t smem[kBigStages * C::kStage];
@@ -150,7 +158,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restri
 #pragma unroll
   for (int i = 0; i < C::kDma; ++i) {
     const bool is_a = i < C::kDmaA;
-    const int blk = (is_a ? i : i - C::kDmaA) * 4 + wid;  // 8-row block within the operand tile
+    const int blk = (is_a ? i : i - C::kDmaA) * kBigWaves + wid;  // 8-row block within the operand tile
     const int r = blk * 8 + (lane >> 3);
     const int c = (lane & 7) ^ big_swz(r);
     if (is_a) {
@@ -189,7 +197,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restri
     const int c = 2 * ks + fhalf;
 #pragma unroll
     for (int i = 0; i < C::kFM; ++i)
-      xf[i] = *reinterpret_cast<const v4i*>(stage + big_lds_off(wm * 128 + 32 * i + frow, c));
+      xf[i] = *reinterpret_cast<const v4i*>(stage + big_lds_off(wm * C::kWM + 32 * i + frow, c));
 #pragma unroll
     for (int j = 0; j < C::kFN; ++j)
       wf[j] = *reinterpret_cast<const v4i*>(stage + C::kStageA + big_lds_off(wn * C::kWN + 32 * j + frow, c));
@@ -221,7 +229,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restri
   auto frag_one = [&](const int8_t* stage, int ks, int q, v4i* xf, v4i* wf) {
     const int c = 2 * ks + fhalf;
     if (q < C::kFM)
-      xf[q] = *reinterpret_cast<const v4i*>(stage + big_lds_off(wm * 128 + 32 * q + frow, c));
+      xf[q] = *reinterpret_cast<const v4i*>(stage + big_lds_off(wm * C::kWM + 32 * q + frow, c));
     else
       wf[q - C::kFM] = *reinterpret_cast<const v4i*>(
           stage + C::kStageA + big_lds_off(wn * C::kWN + 32 * (q - C::kFM) + frow, c));
@@ -265,7 +273,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restri
   }
 
   // ---- epilogue: lane holds D[n][m] with m = l%32 and n = 8*(r/4) + 4*(l/32) + r%4 of each 32x32 block
-  const int mw = m0 + wm * 128;
+  const int mw = m0 + wm * C::kWM;
   const int nw = n0 + wn * C::kWN;
   int mrow[C::kFM];
   float xs[C::kFM];
@@ -280,13 +288,13 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restri
   // them from global memory for every 32-column block of every wave).
   const bool staged = kOut == kBigDecomp && cnt <= kSliceCols;
   if (kOut == kBigDecomp && staged && cnt > 0) {
-    {
-      const int row = tid;  // 256 threads, 256 tile rows
+    if (tid < kBigBM) {
+      const int row = tid;  // one thread per tile row
       const int64_t m = (int64_t)m0 + row;
       for (int c = 0; c < cnt; ++c)
         slice_x[row * kSliceCols + c] = m < M ? ep.dec.x[m * ep.dec.ldx + ep.dec.idx[c]] : (uint16_t)0;
     }
-    for (int e = tid; e < cnt * BN; e += 256) {
+    for (int e = tid; e < cnt * BN; e += kBigThreads) {
       const int c = e / BN, nl = e - c * BN;
       const int64_t n = (int64_t)n0 + nl;
       slice_w[c * BN + nl] = n < N ? ep.dec.w16[(int64_t)ep.dec.idx[c] * ep.dec.ldw + n] : (uint16_t)0;
@@ -304,7 +312,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restri
         float xv[C::kFM];
 #pragma unroll
         for (int i = 0; i < C::kFM; ++i)
-          xv[i] = (i >= i0 && i < i1) ? f16_to_f32(slice_x[(wm * 128 + 32 * i + frow) * kSliceCols + c]) : 0.f;
+          xv[i] = (i >= i0 && i < i1) ? f16_to_f32(slice_x[(wm * C::kWM + 32 * i + frow) * kSliceCols + c]) : 0.f;
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const int nl = wn * C::kWN + 32 * j + 8 * rg + 4 * fhalf;
@@ -384,7 +392,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restri
 #pragma unroll
       for (int j = 0; j < C::kFN; ++j) {
         // fragments of this wave inside the band (the test is uniform per wave)
-        const int i0 = (band * kBand - wm * 128) / 32;
+        const int i0 = (band * kBand - wm * C::kWM) / 32;
         const int lo = i0 < 0 ? 0 : i0, hi = min(C::kFM, i0 + kBand / 32);
         if (lo >= hi) continue;
         float yo[kOut == kBigDecomp ? C::kFM : 1][16];
@@ -401,7 +409,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restri
             int a[4];
             float v[4];
             out_values(j, i, rg, ws, yo, v, a);
-            int8_t* dst = smem + (wm * 128 + 32 * i + frow - band * kBand) * kRowB + nl * kEl;
+            int8_t* dst = smem + (wm * C::kWM + 32 * i + frow - band * kBand) * kRowB + nl * kEl;
             if (kOut == kBigI32) {
               *reinterpret_cast<int4*>(dst) = make_int4(a[0], a[1], a[2], a[3]);
             } else if (kOut == kBigF32) {
@@ -417,7 +425,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restri
         }
       }
       __syncthreads();
-      for (int c = tid; c < kBand * kChunks; c += 256) {
+      for (int c = tid; c < kBand * kChunks; c += kBigThreads) {
         const int r = c / kChunks, ch = c - r * kChunks;
         const int m = m0 + band * kBand + r;
         const int n = n0 + ch * kPer;
@@ -463,7 +471,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const int8_t* __restri
 template <int BN, int kOut, bool kVec>
 static void launch_big(const int8_t* xq, const int8_t* wq, int M, int N, int K, const BigEpi& ep, hipStream_t s) {
   const int tiles = ((M + kBigBM - 1) / kBigBM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_big_kernel<BN, kOut, kVec>), dim3(tiles), dim3(256), 0, s, xq, wq, M, N, K, ep);
+  hipLaunchKernelGGL((gemm_big_kernel<BN, kOut, kVec>), dim3(tiles), dim3(kBigThreads), 0, s, xq, wq, M, N, K, ep);
 }
 
 template <int BN, int kOut>
