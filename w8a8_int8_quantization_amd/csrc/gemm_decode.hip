@@ -298,14 +298,18 @@ struct DecodePlan {
   int tiles = 0;
 };
 
-DecodePlan decode_plan(int64_t n, int64_t k) {
+DecodePlan decode_plan(int64_t m, int64_t n, int64_t k) {
   DecodePlan p;
   const int steps = (int)(k / sqk::kDecStep);
   p.tiles = (int)((n + sqk::kDecRows - 1) / sqk::kDecRows);
   // at least one workgroup per CU (256 CUs), with at most kDecMaxNS steps
   // per wave; measured on MI355X, more slices than that only add partial-tile
-  // traffic and reduction latency
+  // traffic and reduction latency. Above 16 tokens the partial tiles grow
+  // (S x M x N x 4 bytes written and read back), and three workgroups in four
+  // of the CUs streaming unsplit K are faster (14336 columns: M 64 26.8 ->
+  // 22.9 us, M 32 18.3 -> 16.4 us).
   int want = (256 + p.tiles - 1) / p.tiles;
+  if (m > 16 && p.tiles >= 192) want = 1;
 #ifdef SQ_TUNE
   if (const char* e = getenv("SQ_DECODE_SPLIT")) want = atoi(e);
 #endif
@@ -345,7 +349,7 @@ bool gemm_decode_suits(int64_t m, int64_t n, int64_t k) {
 
 size_t gemm_decode_workspace(int64_t m, int64_t n, int64_t k) {
   if (!gemm_decode_suits(m, n, k)) return 0;
-  const DecodePlan p = decode_plan(n, k);
+  const DecodePlan p = decode_plan(m, n, k);
   if (p.S == 1) return 0;
   return counter_bytes(p.tiles) + (size_t)p.S * (size_t)m * (size_t)n * 4;
 }
@@ -354,7 +358,7 @@ void gemm_decode_counters(int64_t m, int64_t n, int64_t k, void* ws, uint32_t** 
   *counters = nullptr;
   *count = 0;
   if (!gemm_decode_suits(m, n, k)) return;
-  const DecodePlan p = decode_plan(n, k);
+  const DecodePlan p = decode_plan(m, n, k);
   if (p.S == 1) return;
   *counters = reinterpret_cast<uint32_t*>(ws);
   *count = p.tiles;
@@ -362,7 +366,7 @@ void gemm_decode_counters(int64_t m, int64_t n, int64_t k, void* ws, uint32_t** 
 
 hipError_t gemm_i8_decode(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
                           int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, hipStream_t s) {
-  const DecodePlan p = decode_plan(n, k);
+  const DecodePlan p = decode_plan(m, n, k);
   sqk::DecodeArgs a{};
   a.xq = xq; a.wq = wq; a.x_scale = x_scale; a.w_scale = w_scale; a.y = y; a.ldy = ldy;
   a.M = (int)m; a.N = (int)n; a.K = (int)k;
