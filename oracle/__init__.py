@@ -1,4 +1,5 @@
-"""CPU oracle for the SmoothQuant W8A8 linear layer and the LLM.int8() variant.
+"""CPU oracle for the SmoothQuant W8A8 linear layer, the RMSNorm that carries its
+smoothing factor, and the LLM.int8() variant.
 
 TEST INFRASTRUCTURE ONLY. This package is the plain, slow, obviously correct
 definition of what the HIP path computes; it exists to check that path. Only
@@ -28,6 +29,7 @@ from .smoothquant import (
     per_tensor_int8_linear,
 )
 from .llm_int8 import detect_outliers, quantize_rows_regular, fp16_outlier_product, int8_decomp_linear
+from .rmsnorm import fold_norm_gain, rms_inverse, apply_gain, rmsnorm, rmsnorm_quantize
 
 __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "round_bf16", "round_f16", "round_to",
@@ -35,5 +37,6 @@ __all__ = [
     "quantize_weights_per_channel", "smooth_fold_quantize", "smooth_activations",
     "quantize_activations", "int8_matmul", "dequantize", "w8a8_linear", "smoothquant_linear",
     "per_tensor_int8_linear", "detect_outliers", "quantize_rows_regular",
-    "fp16_outlier_product", "int8_decomp_linear",
+    "fp16_outlier_product", "int8_decomp_linear", "fold_norm_gain", "rms_inverse", "apply_gain", "rmsnorm",
+    "rmsnorm_quantize",
 ]

@@ -11,6 +11,7 @@ that some pin fails for every one of them.
 from __future__ import annotations
 
 import json
+import math
 import os
 
 import numpy as np
@@ -389,9 +390,135 @@ def pin_llm_int8(o):
                   <= np.abs(r["y"].astype(np.float64)) * 2 ** -11 + 2 ** -24)
 
 
+# ---------------------------------------------------------------------------
+# RMSNorm with the folded gain, then per-token quantisation
+# ---------------------------------------------------------------------------
+def pin_norm_gain_example(o):
+    """The W8A8 post, "Where the outlier actually comes from": the gain gamma
+    makes the outlier; gamma divided by s = (1, 1, 1, 100) removes it."""
+    g = golden("smoothed_act_example.json")
+    n = np.array([g["normalized"]], dtype=F32)
+    gamma = np.array(g["gamma"], dtype=F32)
+    s = np.array(g["smoothing"], dtype=F32)
+    act = o.apply_gain(n, gamma)[0]
+    assert np.array_equal(act, np.array(g["activation_expected"], dtype=F32)), act
+    gf = o.fold_norm_gain(gamma, s)
+    assert np.array_equal(gf, np.ones(4, F32)), gf
+    assert np.array_equal(o.fold_norm_gain(gamma, None), gamma)
+    act_s = o.apply_gain(n, gf)[0]
+    assert np.array_equal(act_s, np.array(g["smoothed_activation_expected"], dtype=F32))
+    xq, _ = o.quantize_activations(act_s[None, :])
+    assert np.array_equal(xq[0].astype(np.int64), g["q_expected"]), xq
+
+
+def pin_rms_closed_forms(o):
+    ones = lambda k: np.ones(k, F32)
+    # a constant row c (power of two) has rms |c|: every normalised value is +-1
+    for k in (4, 64, 4096):
+        for c in (2.0 ** -3, 1.0, 2.0 ** 5):
+            x = np.full((1, k), c, F32)
+            x[0, ::3] *= -1
+            assert float(o.rms_inverse(x)[0]) == 1.0 / c
+            assert np.array_equal(o.rmsnorm(x, ones(k)), np.sign(x).astype(F32))
+    # one unit entry among K zeros: mean = 1/K, so 1/rms = sqrt(K) (the mean,
+    # not the sum, and every entry counted: the unit sits in the last column)
+    for k, root in ((4, 2.0), (64, 8.0), (4096, 64.0)):
+        x = np.zeros((1, k), F32)
+        x[0, -1] = 1.0
+        assert float(o.rms_inverse(x)[0]) == root
+        a = o.rmsnorm(x, np.full(k, 3.0, F32))
+        assert float(a[0, -1]) == 3.0 * root and not a[0, :-1].any()
+    # eps inside the square root: mean 2^-20 plus eps 3*2^-20 gives 1/rms = 2^9
+    x = np.full((2, 64), 2.0 ** -10, F32)
+    assert np.array_equal(o.rms_inverse(x, 3 * 2.0 ** -20), np.full(2, 512.0, F32))
+    assert np.array_equal(o.rmsnorm(x, ones(64), 3 * 2.0 ** -20), np.full((2, 64), 0.5, F32))
+    # (3, 4): mean of squares 12.5
+    inv = float(o.rms_inverse(np.array([[3.0, 4.0]], F32))[0])
+    assert inv == float(np.float32(1.0 / math.sqrt(12.5)))
+    # degenerate rows: all zero, and a row whose 1/rms overflows binary32 with eps = 0
+    z = np.zeros((1, 64), F32)
+    assert float(o.rms_inverse(z)[0]) == 0.0
+    assert float(o.rms_inverse(z, 1e-5)[0]) == float(np.float32(1.0 / math.sqrt(float(np.float32(1e-5)))))
+    tiny = np.full((1, 64), 2.0 ** -130, F32)
+    assert float(o.rms_inverse(tiny)[0]) == 0.0
+    q, d = o.rmsnorm_quantize(tiny, ones(64))
+    assert not q.any() and float(d[0]) == 0.0
+    # power-of-two scaling of x leaves the normalised row unchanged (eps = 0)
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((3, 256)).astype(F32)
+    gam = rng.uniform(0.5, 2.0, 256).astype(F32)
+    for e in (-40, -3, 7, 60):
+        assert np.array_equal(o.rmsnorm(x * F32(2.0 ** e), gam), o.rmsnorm(x, gam))
+
+
+def _rn32_exact(y):
+    """Correctly rounded binary32 of a positive Decimal (ties to even)."""
+    import decimal
+    c = np.float32(float(y))
+    lo, hi = (c, np.nextafter(c, np.float32(np.inf))) if decimal.Decimal(float(c)) <= y else \
+        (np.nextafter(c, np.float32(0)), c)
+    mid = (decimal.Decimal(float(lo)) + decimal.Decimal(float(hi))) / 2
+    if y < mid:
+        return lo, mid
+    if y > mid:
+        return hi, mid
+    return (lo if (lo.view(np.uint32) & 1) == 0 else hi), mid
+
+
+def pin_rms_bruteforce(o):
+    """1/rms against exact rational arithmetic on small rows with a wide range
+    of magnitudes (bf16-representable values from 2^-120 to 2^100)."""
+    import decimal
+    from fractions import Fraction
+    decimal.getcontext().prec = 80
+    rng = np.random.default_rng(12)
+    for t in range(60):
+        k = int(rng.integers(1, 40))
+        mant = rng.integers(128, 256, k)
+        ex = rng.integers(-60, 50, k) * (2 if t % 3 == 0 else 1)
+        x = (mant * np.exp2(ex - 7.0) * rng.choice([-1.0, 1.0], k)).astype(F32)
+        x[rng.random(k) < 0.2] = 0.0
+        eps = [0.0, 1e-5, 2.0 ** -30][t % 3]
+        got = float(o.rms_inverse(x[None, :], eps)[0])
+        v = sum(Fraction(float(a)) ** 2 for a in x) / k + Fraction(float(np.float32(eps)))
+        if v == 0:
+            assert got == 0.0
+            continue
+        y = 1 / (decimal.Decimal(v.numerator) / decimal.Decimal(v.denominator)).sqrt()
+        if y > decimal.Decimal(float(np.finfo(F32).max)):
+            assert got == 0.0
+            continue
+        want, mid = _rn32_exact(y)
+        if abs(y - mid) > y * decimal.Decimal(2) ** -48:  # outside the double-rounding zone
+            assert got == float(want), (t, got, float(want))
+        else:
+            assert abs(decimal.Decimal(got) - y) <= abs(decimal.Decimal(float(want)) - y) * 2 + y * decimal.Decimal(2) ** -48
+        # the normalised row has rms 1 (eps = 0, no degenerate row)
+        if eps == 0.0 and got > 0:
+            n = o.rmsnorm(x[None, :], np.ones(k, F32))[0].astype(np.float64)
+            assert abs(math.sqrt(np.mean(n * n)) - 1.0) < 2.0 ** -21
+
+
+def pin_norm_fold_identity(o):
+    """(gamma/s) inside the norm equals dividing the norm's output by s: bit for
+    bit with power-of-two s, within one binary32 rounding otherwise."""
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((6, 128)) * 3).astype(F32)
+    gam = rng.uniform(0.2, 4.0, 128).astype(F32)
+    s2 = np.exp2(rng.integers(-6, 7, 128)).astype(F32)
+    q1, d1 = o.rmsnorm_quantize(x, o.fold_norm_gain(gam, s2), 1e-5)
+    q2, d2 = o.quantize_activations(o.rmsnorm(x, gam, 1e-5), s2)
+    assert np.array_equal(q1, q2) and np.array_equal(d1, d2)
+    s = rng.uniform(0.3, 30.0, 128).astype(F32)
+    q1, d1 = o.rmsnorm_quantize(x, o.fold_norm_gain(gam, s), 1e-5)
+    q2, d2 = o.quantize_activations(o.rmsnorm(x, gam, 1e-5), s)
+    assert np.all(np.abs(q1.astype(int) - q2.astype(int)) <= 1)
+    assert np.all(np.abs(d1 / d2 - 1) <= 2.0 ** -21)
+
+
 ALL_PINS = [
     pin_weight_example, pin_act_example, pin_smoothed_example, pin_per_tensor_crush, pin_trace_shapes,
     pin_calibration, pin_smoothing_closed_forms, pin_smoothing_identity, pin_quant_invariants,
     pin_gemm_bruteforce, pin_rounding_vs_torch, pin_f16_from_f64, pin_dequant, pin_error_ordering,
-    pin_llm_int8,
+    pin_llm_int8, pin_norm_gain_example, pin_rms_closed_forms, pin_rms_bruteforce, pin_norm_fold_identity,
 ]

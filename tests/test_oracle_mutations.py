@@ -5,6 +5,8 @@ term, a wrong sign or exponent, a transposed operand, a wrong rounding). The
 test passes only if at least one pin in ``oracle_pins.ALL_PINS`` fails on the
 mutant, which shows the pins constrain every part of the oracle.
 """
+import importlib
+
 import numpy as np
 import pytest
 
@@ -13,6 +15,9 @@ from oracle import llm_int8 as o_int8
 from oracle import numerics as o_num
 from oracle import smoothquant as o_sq
 from tests import oracle_pins
+
+# the submodule (the package attribute of the same name is the function rmsnorm)
+o_rms = importlib.import_module("oracle.rmsnorm")
 
 F32 = np.float32
 
@@ -169,6 +174,52 @@ def _outlier_product_wrong_row(x, w16, mask):
     return o_int8.__dict__["_orig_fp16_outlier_product"](x, np.roll(np.asarray(w16), 1, axis=0), mask)
 
 
+def _rms_chain(x, eps, reduce):
+    x = np.asarray(x, F32)
+    out = np.zeros(x.shape[0], F32)
+    for i in range(x.shape[0]):
+        v = reduce(x[i].astype(np.float64), float(F32(eps)))
+        with np.errstate(all="ignore"):
+            inv = F32(1.0 / v) if v > 0 else F32(0)
+        out[i] = inv if np.isfinite(inv) else 0
+    return out
+
+
+def _rms_sum_not_mean(x, eps=0.0):
+    return _rms_chain(x, eps, lambda r, e: np.sqrt(np.sum(r * r) + e))
+
+
+def _rms_eps_outside_root(x, eps=0.0):
+    return _rms_chain(x, eps, lambda r, e: np.sqrt(np.mean(r * r)) + e)
+
+
+def _rms_drops_last(x, eps=0.0):
+    return _rms_chain(x, eps, lambda r, e: np.sqrt(np.sum(r[:-1] ** 2) / len(r) + e))
+
+
+def _rms_mean_abs(x, eps=0.0):
+    return _rms_chain(x, eps, lambda r, e: np.mean(np.abs(r)) + e)
+
+
+def _gain_divides(normalized, gain):
+    return (np.asarray(normalized, F32) / np.asarray(gain, F32)[None, :]).astype(F32)
+
+
+def _fold_gain_multiplies(gamma, s):
+    g = np.asarray(gamma, F32)
+    return g.copy() if s is None else (g * np.asarray(s, F32)).astype(F32)
+
+
+def _rmsnorm_drops_gain(x, gain, eps=0.0):
+    x = np.asarray(x, F32)
+    return (x * o_rms.rms_inverse(x, eps)[:, None]).astype(F32)
+
+
+def _rmsnorm_gain_before_norm(x, gain, eps=0.0):
+    xg = o_rms.apply_gain(x, gain)
+    return (xg * o_rms.rms_inverse(xg, eps)[:, None]).astype(F32)
+
+
 MUTANTS = {
     "s_exponents_swapped": (o_sq, "smoothing_factors", _smooth_swapped),
     "s_product_not_quotient": (o_sq, "smoothing_factors", _smooth_product),
@@ -194,6 +245,14 @@ MUTANTS = {
     "row_scale_includes_outliers": (o_int8, "quantize_rows_regular", _rows_regular_all_cols),
     "fp16_slice_drops_column": (o_int8, "fp16_outlier_product", _outlier_product_drops_last),
     "fp16_slice_wrong_weight_row": (o_int8, "fp16_outlier_product", _outlier_product_wrong_row),
+    "rms_sum_not_mean": (o_rms, "rms_inverse", _rms_sum_not_mean),
+    "rms_eps_outside_root": (o_rms, "rms_inverse", _rms_eps_outside_root),
+    "rms_drops_last_channel": (o_rms, "rms_inverse", _rms_drops_last),
+    "rms_mean_abs_not_root_mean_square": (o_rms, "rms_inverse", _rms_mean_abs),
+    "norm_gain_divides": (o_rms, "apply_gain", _gain_divides),
+    "norm_fold_multiplies": (o_rms, "fold_norm_gain", _fold_gain_multiplies),
+    "rmsnorm_drops_gain": (o_rms, "rmsnorm", _rmsnorm_drops_gain),
+    "rmsnorm_gain_before_norm": (o_rms, "rmsnorm", _rmsnorm_gain_before_norm),
 }
 
 
@@ -203,7 +262,7 @@ def _plant(monkeypatch, module, name, fn):
     if hasattr(oracle, name):
         monkeypatch.setattr(oracle, name, fn)
     # functions re-exported through another submodule's namespace
-    for mod in (o_sq, o_int8, o_num):
+    for mod in (o_sq, o_int8, o_num, o_rms):
         if mod is not module and name in mod.__dict__:
             monkeypatch.setitem(mod.__dict__, name, fn)
 
