@@ -71,6 +71,8 @@ typedef enum sq_dtype {
 /* Largest K for which the int32 accumulator cannot overflow:
  * 127 * 127 * K < 2^31  <=>  K <= 133144. */
 #define SQ_MAX_K_INT32 133144
+/* Longest row sq_rmsnorm_quant accepts (its exact sum of squares is sized for it). */
+#define SQ_MAX_K_NORM 32768
 
 /* Flags of sq_smooth_fold_weights. */
 #define SQ_SMOOTH_COMPUTE 0u /* compute s from absmax and W, write it to `smooth` */
@@ -197,6 +199,58 @@ sq_status sq_w8a8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const floa
                              const int8_t* wq, const float* w_scale, int64_t m, int64_t n, int64_t k,
                              void* y, sq_dtype yt, int64_t ldy, void* ws, size_t ws_bytes,
                              sq_stream_t stream);
+
+/*
+ * The smoothing factor moved into RMSNorm's gain, once at load time.
+ * [W8A8] "How the smoothing factor is computed" (SmoothQuant divides the
+ * norm's gamma by s and multiplies the matching weight rows by s, which
+ * sq_smooth_fold_weights does) and the smoothed example of "Where the outlier
+ * actually comes from".
+ *
+ *   gain_j = fl32(gamma_j / s_j)          (gamma_j itself when smooth == NULL)
+ *
+ * gamma: [K] of type gt (SQ_F32, SQ_BF16 or SQ_F16), element-aligned.
+ * smooth: [K] binary32 or NULL. gain: [K] binary32 output. Any K >= 0.
+ */
+sq_status sq_fold_norm_gain(const void* gamma, sq_dtype gt, const float* smooth, int64_t k, float* gain,
+                            sq_stream_t stream);
+
+/*
+ * RMSNorm with the folded gain, fused with the per-token int8 quantisation of
+ * its output: the activation never goes to memory in floating point.
+ * [W8A8] "Where the outlier actually comes from" (divide by the vector's
+ * root-mean-square, then scale channel j by the gain), "How the smoothing
+ * factor is computed" (the gain carries 1/s, so no division by s is left),
+ * "How the Model Was Compressed" and "Why Activation Quantization Is Hard"
+ * (one scale per token, max|a| / 127).
+ *
+ *   S_i    = sum_j x_ij^2, summed exactly and rounded once to binary64
+ *   inv_i  = RN32(1 / sqrt(S_i / K + eps)), each binary64 operation
+ *            (divide, add, square root, reciprocal) correctly rounded
+ *   a_ij   = fl32(fl32(x_ij * inv_i) * gain_j)
+ *   d_i    = fl32(max_j |a_ij| / 127)
+ *   xq_ij  = clamp(round_half_even(fl32(a_ij / d_i)), -127, 127); 0 when d_i == 0
+ *
+ * A row whose S_i / K + eps is 0, or whose inv_i overflows binary32 (only
+ * possible with eps == 0 and every |x| below about 2^-124), normalises to 0.
+ * x: [M x ldx] of type xt (SQ_F32, SQ_BF16 or SQ_F16). gain: [K] binary32
+ * (from sq_fold_norm_gain), 16-byte aligned. eps: finite, >= 0 (SQ_ERR_RANGE
+ * otherwise). K <= SQ_MAX_K_NORM (SQ_ERR_RANGE otherwise).
+ * xq: [M x K] int8 output. x_scale: [M] binary32 output.
+ */
+sq_status sq_rmsnorm_quant(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, const float* gain,
+                           float eps, int8_t* xq, float* x_scale, sq_stream_t stream);
+
+/*
+ * sq_rmsnorm_quant followed by sq_w8a8_linear on the same stream, with Xq,
+ * the row scales and the GEMM's workspace held in ws (the same layout and
+ * size as sq_w8a8_linear_dyn; its contents need no initialisation). The
+ * results equal those of the two calls made separately.
+ */
+size_t sq_rmsnorm_w8a8_linear_workspace_size(int64_t m, int64_t n, int64_t k);
+sq_status sq_rmsnorm_w8a8_linear(const void* x, sq_dtype xt, int64_t ldx, const float* gain, float eps,
+                                 const int8_t* wq, const float* w_scale, int64_t m, int64_t n, int64_t k, void* y,
+                                 sq_dtype yt, int64_t ldy, void* ws, size_t ws_bytes, sq_stream_t stream);
 
 /*
  * LLM.int8() outlier detection over the feature columns of X.

@@ -159,3 +159,38 @@ def test_validation_decomp_gemm(sq):
     assert f(*a) == ALIGN
     a = list(args); a[10] = 0
     assert f(*a) == OK
+
+
+def test_validation_rmsnorm(sq):
+    f = sq.raw["sq_rmsnorm_quant"]
+    assert f(P, sq.SQ_BF16, 4, 100, 100, P, 1e-5, P, P, None) == SHAPE        # K not a multiple of 64
+    assert f(P, sq.SQ_BF16, 4, 32768 + 64, 32768 + 64, P, 1e-5, P, P, None) == RANGE  # beyond SQ_MAX_K_NORM
+    assert f(P, sq.SQ_I8, 4, 64, 64, P, 1e-5, P, P, None) == DTYPE
+    assert f(P, sq.SQ_BF16, 4, 64, 64, P, -1.0, P, P, None) == RANGE         # eps < 0
+    assert f(P, sq.SQ_BF16, 4, 64, 64, P, float("inf"), P, P, None) == RANGE
+    assert f(P, sq.SQ_BF16, 4, 64, 64, P, float("nan"), P, P, None) == RANGE
+    assert f(P, sq.SQ_BF16, 4, 64, 64, None, 0.0, P, P, None) == NULL        # gain
+    assert f(P, sq.SQ_BF16, 4, 64, 64, P, 0.0, None, P, None) == NULL
+    assert f(P, sq.SQ_BF16, 4, 64, 64, P, 0.0, P, None, None) == NULL
+    assert f(P, sq.SQ_BF16, 4, 64, 64, BAD, 0.0, P, P, None) == ALIGN        # gain alignment
+    assert f(P, sq.SQ_BF16, 4, 64, 64, P, 0.0, BAD, P, None) == ALIGN
+    assert f(P, sq.SQ_BF16, 4, 64, 68, P, 0.0, P, P, None) == ALIGN          # row pitch
+    assert f(None, sq.SQ_BF16, 0, 64, 64, None, 0.0, None, None, None) == OK  # empty batch: no work
+    g = sq.raw["sq_fold_norm_gain"]
+    assert g(P, sq.SQ_I8, P, 64, P, None) == DTYPE
+    assert g(None, sq.SQ_BF16, P, 64, P, None) == NULL
+    assert g(P, sq.SQ_BF16, P, 64, None, None) == NULL
+    assert g(P + 1, sq.SQ_BF16, P, 64, P, None) == ALIGN
+    assert g(P, sq.SQ_F32, P + 2, 64, P, None) == ALIGN
+    assert g(P, sq.SQ_BF16, P, -1, P, None) == SHAPE
+    assert g(None, sq.SQ_BF16, None, 0, None, None) == OK
+    h = sq.raw["sq_rmsnorm_w8a8_linear"]
+    nb = sq.raw["sq_rmsnorm_w8a8_linear_workspace_size"](16, 128, 256)
+    assert nb == sq.raw["sq_w8a8_linear_dyn_workspace_size"](16, 128, 256) > 0
+    assert h(P, sq.SQ_BF16, 256, P, 0.0, P, P, 16, 128, 256, P, sq.SQ_I32, 128, P, nb, None) == DTYPE
+    assert h(P, sq.SQ_BF16, 256, P, 0.0, P, P, 16, 128, 256, P, sq.SQ_BF16, 128, P, nb - 1, None) == WS
+    assert h(P, sq.SQ_BF16, 256, P, 0.0, P, P, 16, 128, 256, P, sq.SQ_BF16, 128, None, 0, None) == WS
+    assert h(P, sq.SQ_BF16, 256, P, -2.0, P, P, 16, 128, 256, P, sq.SQ_BF16, 128, P, nb, None) == RANGE
+    assert h(P, sq.SQ_BF16, 256, None, 0.0, P, P, 16, 128, 256, P, sq.SQ_BF16, 128, P, nb, None) == NULL
+    assert h(P, sq.SQ_BF16, 256, P, 0.0, None, P, 16, 128, 256, P, sq.SQ_BF16, 128, P, nb, None) == NULL
+    assert h(P, sq.SQ_BF16, 256, P, 0.0, P, P, 16, 128, 256, P, sq.SQ_BF16, 100, P, nb, None) == SHAPE

@@ -20,7 +20,7 @@ __all__ = [
     "SQError", "lib_path", "sq_version",
     "sq_calibrate_absmax", "sq_smooth_fold_weights", "sq_quant_act_per_token", "sq_w8a8_linear",
     "sq_w8a8_linear_dyn", "sq_outlier_detect", "sq_quant_act_rows_masked", "sq_int8_decomp_linear",
-    "sq_int8_decomp_gemm", "linear_workspace",
+    "sq_int8_decomp_gemm", "linear_workspace", "sq_fold_norm_gain", "sq_rmsnorm_quant", "sq_rmsnorm_w8a8_linear",
     "SMOOTH_COMPUTE", "SMOOTH_GIVEN", "SMOOTH_NONE", "MAX_K_INT32", "EXPORTED_SYMBOLS",
 ]
 
@@ -55,6 +55,10 @@ _SIGS = {
     "sq_w8a8_linear": (_st, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _st, _i64, _p, _sz, _p]),
     "sq_w8a8_linear_dyn_workspace_size": (_sz, [_i64, _i64, _i64]),
     "sq_w8a8_linear_dyn": (_st, [_p, _st, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _st, _i64, _p, _sz, _p]),
+    "sq_fold_norm_gain": (_st, [_p, _st, _p, _i64, _p, _p]),
+    "sq_rmsnorm_quant": (_st, [_p, _st, _i64, _i64, _i64, _p, _f, _p, _p, _p]),
+    "sq_rmsnorm_w8a8_linear_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "sq_rmsnorm_w8a8_linear": (_st, [_p, _st, _i64, _p, _f, _p, _p, _i64, _i64, _i64, _p, _st, _i64, _p, _sz, _p]),
     "sq_outlier_detect_workspace_size": (_sz, [_i64]),
     "sq_outlier_detect": (_st, [_p, _st, _i64, _i64, _i64, _f, _p, _p, _p, _p, _sz, _p]),
     "sq_quant_act_rows_masked": (_st, [_p, _st, _i64, _i64, _i64, _p, _p, _p, _p]),
@@ -203,6 +207,44 @@ def sq_w8a8_linear_dyn(x: torch.Tensor, smooth: Optional[torch.Tensor], wq: torc
         ws = _workspace(nb, x.device)
     _check("sq_w8a8_linear_dyn", raw["sq_w8a8_linear_dyn"](
         _ptr(x), _dt(x), ldx, _ptr(smooth), _ptr(wq), _ptr(w_scale), m, n, k, _ptr(y), _dt(y), ldy,
+        _ptr(ws), ws.numel() if ws is not None else 0, _stream(x.device)))
+    return y
+
+
+def sq_fold_norm_gain(gamma: torch.Tensor, smooth: Optional[torch.Tensor] = None,
+                      gain: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """RMSNorm gain with the smoothing factor folded in: gamma / s (binary32 [K])."""
+    k = gamma.numel()
+    gain = torch.empty(k, dtype=torch.float32, device=gamma.device) if gain is None else gain
+    _check("sq_fold_norm_gain", raw["sq_fold_norm_gain"](
+        _ptr(gamma), _dt(gamma), _ptr(smooth), k, _ptr(gain), _stream(gamma.device)))
+    return gain
+
+
+def sq_rmsnorm_quant(x: torch.Tensor, gain: torch.Tensor, eps: float = 0.0,
+                     xq: Optional[torch.Tensor] = None, x_scale: Optional[torch.Tensor] = None):
+    """RMSNorm of X [M x K] with the folded gain, then per-token int8 quantisation."""
+    m, k, ldx = _rows(x)
+    xq = torch.empty((m, k), dtype=torch.int8, device=x.device) if xq is None else xq
+    x_scale = torch.empty(m, dtype=torch.float32, device=x.device) if x_scale is None else x_scale
+    _check("sq_rmsnorm_quant", raw["sq_rmsnorm_quant"](
+        _ptr(x), _dt(x), m, k, ldx, _ptr(gain), float(eps), _ptr(xq), _ptr(x_scale), _stream(x.device)))
+    return xq, x_scale
+
+
+def sq_rmsnorm_w8a8_linear(x: torch.Tensor, gain: torch.Tensor, eps: float, wq: torch.Tensor,
+                           w_scale: torch.Tensor, out_dtype=torch.bfloat16, y: Optional[torch.Tensor] = None,
+                           ws: Optional[torch.Tensor] = None):
+    """RMSNorm with the folded gain, per-token quantisation and the W8A8 GEMM in one call."""
+    m, k, ldx = _rows(x)
+    n = wq.shape[0]
+    y = torch.empty((m, n), dtype=out_dtype, device=x.device) if y is None else y
+    _, _, ldy = _rows(y)
+    nb = raw["sq_rmsnorm_w8a8_linear_workspace_size"](m, n, k)
+    if ws is None:
+        ws = _workspace(nb, x.device)
+    _check("sq_rmsnorm_w8a8_linear", raw["sq_rmsnorm_w8a8_linear"](
+        _ptr(x), _dt(x), ldx, _ptr(gain), float(eps), _ptr(wq), _ptr(w_scale), m, n, k, _ptr(y), _dt(y), ldy,
         _ptr(ws), ws.numel() if ws is not None else 0, _stream(x.device)))
     return y
 

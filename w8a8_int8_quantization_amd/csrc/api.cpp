@@ -54,6 +54,29 @@ sq_status hip_status(hipError_t e) {
     if (st_ != SQ_OK) return st_; \
   } while (0)
 
+// Quantisation (by `quant`, which writes Xq and the row scales and clears the
+// given counter words) followed by the GEMM, with Xq, the scales and the
+// GEMM's workspace carved out of ws.
+template <class Quant>
+sq_status quant_then_gemm(Quant quant, const int8_t* wq, const float* w_scale, int64_t m, int64_t n, int64_t k,
+                          void* y, sq_dtype yt, int64_t ldy, void* ws, hipStream_t s) {
+  int8_t* xq = reinterpret_cast<int8_t*>(ws);
+  float* dx = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + round_up((size_t)m * (size_t)k));
+  void* gws = reinterpret_cast<char*>(ws) + round_up((size_t)m * (size_t)k) + round_up((size_t)m * 4);
+  if (sqh::gemm_decode_suits(m, n, k)) {
+    // the quantisation launch also clears the GEMM's split-K counters
+    uint32_t* counters;
+    int64_t ncount;
+    sqh::gemm_decode_counters(m, n, k, gws, &counters, &ncount);
+    hipError_t e = quant(xq, dx, counters, ncount);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(sqh::gemm_i8_decode(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, gws, s));
+  }
+  hipError_t e = quant(xq, dx, nullptr, 0);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(sqh::gemm_i8(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, nullptr, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -190,22 +213,65 @@ sq_status sq_w8a8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const floa
   if (m == 0 || n == 0) return SQ_OK;
   if (!ws || ws_bytes < sq_w8a8_linear_dyn_workspace_size(m, n, k)) return SQ_ERR_WORKSPACE;
   if (!aligned16(ws)) return SQ_ERR_ALIGN;
-  int8_t* xq = reinterpret_cast<int8_t*>(ws);
-  float* dx = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + round_up((size_t)m * (size_t)k));
-  void* gws = reinterpret_cast<char*>(ws) + round_up((size_t)m * (size_t)k) + round_up((size_t)m * 4);
   const hipStream_t s = (hipStream_t)stream;
-  if (sqh::gemm_decode_suits(m, n, k)) {
-    // the quantisation launch also clears the GEMM's split-K counters
-    uint32_t* counters;
-    int64_t ncount;
-    sqh::gemm_decode_counters(m, n, k, gws, &counters, &ncount);
-    hipError_t e = sqh::quant_rows(x, xt, m, k, ldx, smooth, nullptr, xq, dx, s, counters, ncount);
-    if (e != hipSuccess) return hip_status(e);
-    return hip_status(sqh::gemm_i8_decode(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, gws, s));
-  }
-  hipError_t e = sqh::quant_rows(x, xt, m, k, ldx, smooth, nullptr, xq, dx, s);
-  if (e != hipSuccess) return hip_status(e);
-  return hip_status(sqh::gemm_i8(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, nullptr, s));
+  auto quant = [&](int8_t* xq, float* dx, uint32_t* zero, int64_t nzero) {
+    return sqh::quant_rows(x, xt, m, k, ldx, smooth, nullptr, xq, dx, s, zero, nzero);
+  };
+  return quant_then_gemm(quant, wq, w_scale, m, n, k, y, yt, ldy, ws, s);
+}
+
+// ---------------------------------------------------------------- RMSNorm with the folded gain
+static sq_status check_norm(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, const float* gain,
+                            float eps) {
+  SQ_TRY(check_k(k));
+  if (k > SQ_MAX_K_NORM) return SQ_ERR_RANGE;
+  SQ_TRY(check_vec_matrix(x, xt, m, k, ldx));
+  if (!(eps >= 0.f && eps <= 3.4028234663852886e38f)) return SQ_ERR_RANGE;
+  if (m == 0) return SQ_OK;
+  if (!gain) return SQ_ERR_NULL;
+  if (!aligned16(gain)) return SQ_ERR_ALIGN;
+  return SQ_OK;
+}
+
+sq_status sq_fold_norm_gain(const void* gamma, sq_dtype gt, const float* smooth, int64_t k, float* gain,
+                            sq_stream_t stream) {
+  if (k < 0) return SQ_ERR_SHAPE;
+  if (!float_input(gt)) return SQ_ERR_DTYPE;
+  if (k == 0) return SQ_OK;
+  if (!gamma || !gain) return SQ_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(gamma) % (uintptr_t)elem_bytes(gt) != 0) return SQ_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(gain) % 4 != 0 || reinterpret_cast<uintptr_t>(smooth) % 4 != 0)
+    return SQ_ERR_ALIGN;
+  return hip_status(sqh::fold_norm_gain(gamma, gt, smooth, k, gain, (hipStream_t)stream));
+}
+
+sq_status sq_rmsnorm_quant(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, const float* gain,
+                           float eps, int8_t* xq, float* x_scale, sq_stream_t stream) {
+  SQ_TRY(check_norm(x, xt, m, k, ldx, gain, eps));
+  if (m == 0) return SQ_OK;
+  if (!xq || !x_scale) return SQ_ERR_NULL;
+  if (!aligned16(xq)) return SQ_ERR_ALIGN;
+  return hip_status(sqh::rmsnorm_quant(x, xt, m, k, ldx, gain, eps, xq, x_scale, (hipStream_t)stream));
+}
+
+size_t sq_rmsnorm_w8a8_linear_workspace_size(int64_t m, int64_t n, int64_t k) {
+  return sq_w8a8_linear_dyn_workspace_size(m, n, k);
+}
+
+sq_status sq_rmsnorm_w8a8_linear(const void* x, sq_dtype xt, int64_t ldx, const float* gain, float eps,
+                                 const int8_t* wq, const float* w_scale, int64_t m, int64_t n, int64_t k, void* y,
+                                 sq_dtype yt, int64_t ldy, void* ws, size_t ws_bytes, sq_stream_t stream) {
+  SQ_TRY(check_norm(x, xt, m, k, ldx, gain, eps));
+  if (yt == SQ_I32) return SQ_ERR_DTYPE;
+  SQ_TRY(check_gemm_common(wq, w_scale, m, n, k, y, yt, ldy));
+  if (m == 0 || n == 0) return SQ_OK;
+  if (!ws || ws_bytes < sq_rmsnorm_w8a8_linear_workspace_size(m, n, k)) return SQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SQ_ERR_ALIGN;
+  const hipStream_t s = (hipStream_t)stream;
+  auto quant = [&](int8_t* xq, float* dx, uint32_t* zero, int64_t nzero) {
+    return sqh::rmsnorm_quant(x, xt, m, k, ldx, gain, eps, xq, dx, s, zero, nzero);
+  };
+  return quant_then_gemm(quant, wq, w_scale, m, n, k, y, yt, ldy, ws, s);
 }
 
 size_t sq_outlier_detect_workspace_size(int64_t k) { return k > 0 ? round_up((size_t)k * 4) : 0; }

@@ -202,13 +202,6 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
     for (int j = 0; j < C::kFN; ++j)
       wf[j] = *reinterpret_cast<const v4i*>(stage + C::kStageA + big_lds_off(wn * C::kWN + 32 * j + frow, c));
   };
-  auto mfmas = [&](const v4i* xf, const v4i* wf) {
-#pragma unroll
-    for (int j = 0; j < C::kFN; ++j)
-#pragma unroll
-      for (int i = 0; i < C::kFM; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[j], xf[i], acc[j][i], 0, 0, 0);
-  };
   auto stage_ptr = [&](int kt) { return smem + (kt & 1) * C::kStage; };
 
   // Software pipeline over the 4 substeps of a stage: the fragments of the

@@ -136,4 +136,41 @@ __device__ __forceinline__ int quant_rne_clamp(float q) {
   return (int)r;
 }
 
+// ---------------------------------------------------------------- quotients and int8 codes
+// Markstein's FMA-corrected quotient: with r = RN(1/b), q0 = a*r,
+// e = fma(-q0, b, a) (exact), q = fma(e, r, q0) gives q = RN(a/b) whenever no
+// step leaves the normal range; the quantisation kernels check that range per
+// row (below) and fall back to IEEE division outside it.
+constexpr float kFastSMin = 0x1p-20f, kFastSMax = 0x1p20f;
+constexpr float kFastDMin = 0x1p-30f, kFastAMax = 0x1p50f;
+
+// RN(1/s) for s in [2^-20, 2^21): hardware reciprocal plus one Newton step.
+__device__ __forceinline__ float rcp_rn(float s) {
+  const float y = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, y, 1.0f);
+  return __builtin_fmaf(e, y, y);
+}
+
+__device__ __forceinline__ float div_mk(float a, float b, float rb) {
+  const float q0 = a * rb;
+  const float e = __builtin_fmaf(-q0, b, a);
+  return __builtin_fmaf(e, rb, q0);
+}
+
+// int8 code of one quotient: clamp to [-127, 127], then adding 1.5 * 2^23
+// rounds to the nearest integer with ties to even (the sum lies in
+// [2^23, 2^24), where the binary32 spacing is 1) and leaves the two's-
+// complement code in the low byte of the sum's bit pattern.
+__device__ __forceinline__ uint32_t q_code(float v) {
+  v = __builtin_amdgcn_fmed3f(v, -(float)kQMax, (float)kQMax);
+  return __float_as_uint(v + 12582912.0f);
+}
+
+// Low bytes of four codes -> one little-endian word (v_perm_b32 picks bytes).
+__device__ __forceinline__ uint32_t pack4(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3) {
+  const uint32_t lo = __builtin_amdgcn_perm(c1, c0, 0x0C0C0400u);  // c0.b0, c1.b0
+  const uint32_t hi = __builtin_amdgcn_perm(c3, c2, 0x0C0C0400u);  // c2.b0, c3.b0
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
 }  // namespace sqk

@@ -38,6 +38,12 @@ hipError_t quant_rows(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t 
                       const uint8_t* mask, int8_t* xq, float* x_scale, hipStream_t s, uint32_t* zero = nullptr,
                       int64_t nzero = 0);
 
+// RMSNorm with the folded gain, then per-token quantisation (zero / nzero as above).
+hipError_t rmsnorm_quant(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, const float* gain, float eps,
+                         int8_t* xq, float* x_scale, hipStream_t s, uint32_t* zero = nullptr, int64_t nzero = 0);
+hipError_t fold_norm_gain(const void* gamma, sq_dtype gt, const float* smooth, int64_t k, float* out,
+                          hipStream_t s);
+
 hipError_t gemm_i8(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
                    int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec,
                    hipStream_t s);

@@ -22,6 +22,13 @@ not available):
   multiplied by 40.
 * ``llm_int8``: X ~ N(0, 1) fp16 with 8 columns multiplied by magnitudes
   spread evenly over [6, 60], so every one of them crosses the 6.0 threshold.
+* RMSNorm inputs (``norm_case``): the residual stream before the norm, rows
+  x ~ N(0, 1) times a per-row magnitude exp(N(0, 1)) (tokens of different
+  RMS); the gain gamma ~ U(0.5, 1.5) with the outlier channels set to values
+  in [20, 100]. "Where the outlier actually comes from" shows exactly this: a
+  balanced normalised vector and one gain of 100 that makes the outlier.
+  ``wide_range_rows`` gives rows whose binary exponents spread over a chosen
+  range, with zeros, for exercising the exact sum of squares.
 
 Weights are N(0, 0.02) in every configuration.
 """
@@ -42,6 +49,9 @@ __all__ = [
     "linear_case",
     "decomp_case",
     "random_linear_case",
+    "NormCase",
+    "norm_case",
+    "wide_range_rows",
     "CONFIGS",
 ]
 
@@ -183,6 +193,49 @@ def random_linear_case(m: int, k: int, n: int, seed: int, dtype: str = "bf16",
     return LinearCase(name=f"rand_{m}x{k}x{n}_s{seed}", m=m, k=k, n=n, x_dtype=dtype, w_dtype=dtype,
                       y_dtype=y_dtype or dtype, alpha=alpha, channels=ch, x_calib=xc, x=x, w=w,
                       model=model, seed=seed)
+
+
+@dataclasses.dataclass
+class NormCase:
+    """RMSNorm input rows, the norm's gain and calibration rows."""
+
+    m: int
+    k: int
+    dtype: str
+    channels: np.ndarray
+    x: np.ndarray        # [m x k] fp32 holding dtype values (the residual stream)
+    gamma: np.ndarray    # [k] fp32 holding dtype values
+    x_calib: np.ndarray  # [t x k]
+
+
+def _residual_rows(g: np.random.Generator, rows: int, k: int) -> np.ndarray:
+    x = g.standard_normal((rows, k), dtype=np.float32)
+    return x * np.exp(g.standard_normal((rows, 1))).astype(np.float32)
+
+
+def norm_case(m: int, k: int, seed: int, dtype: str = "bf16", calib_rows: int = 256) -> NormCase:
+    ch = outlier_channels(k, seed)
+    gg = _rng(seed, "extra", 300)
+    gamma = gg.uniform(0.5, 1.5, size=k).astype(np.float32)
+    gamma[ch] = gg.uniform(20.0, 100.0, size=len(ch)).astype(np.float32)
+    x = _residual_rows(_rng(seed, "x"), m, k)
+    xc = _residual_rows(_rng(seed, "calib"), calib_rows, k)
+    return NormCase(m=m, k=k, dtype=dtype, channels=ch, x=_as_dtype(x, dtype), gamma=_as_dtype(gamma, dtype),
+                    x_calib=_as_dtype(xc, dtype))
+
+
+def wide_range_rows(m: int, k: int, seed: int, dtype: str, lo_exp: int, hi_exp: int,
+                    zero_frac: float = 0.1) -> np.ndarray:
+    """Rows [m x k] of values m * 2^e, e uniform in [lo_exp, hi_exp] (clipped to
+    what ``dtype`` represents), random signs and significands, some zeros."""
+    g = _rng(seed, "extra", 400)
+    mant = g.uniform(1.0, 2.0, size=(m, k))
+    e = g.integers(lo_exp, hi_exp + 1, size=(m, k))
+    x = mant * np.exp2(e.astype(np.float64)) * g.choice([-1.0, 1.0], size=(m, k))
+    x[g.random((m, k)) < zero_frac] = 0.0
+    lim = {"bf16": 3.0e38, "f32": 3.0e38, "f16": 60000.0}[dtype]
+    x = np.clip(x, -lim, lim).astype(np.float32)
+    return _as_dtype(x, dtype)
 
 
 def decomp_case(seed: int = 0, m: Optional[int] = None, k: Optional[int] = None,
