@@ -14,6 +14,12 @@ rates the GEMM kernel (the dominant one) against the dense int8 MFMA peak (HBM
 bandwidth for decode shapes) with its mean duration from HIP events recorded
 around each launch in a second pass over the same number of steps;
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload.
+
+The ``rmsnorm_*`` workloads start one step earlier, from the residual stream
+before the layer's RMSNorm: the first kernel is the fused RMSNorm (gain
+gamma / s) + per-token quantisation, the second the same GEMM. Their
+smoothing factors come from calibration rows normalised by a plain torch
+RMSNorm (load time, outside the timed region).
 """
 from __future__ import annotations
 
@@ -40,7 +46,11 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="qkv_prefill",
-                   help="qkv_prefill (default), gateup_prefill, down_prefill, decode_up, decode_down, tiny, llm_int8")
+                   help="qkv_prefill (default), gateup_prefill, down_prefill, decode_up, decode_down, tiny, "
+                        "llm_int8; rmsnorm_qkv_prefill, rmsnorm_gateup_prefill, rmsnorm_decode_up (the step "
+                        "starts from the residual stream: fused RMSNorm with the folded gain + quantisation, "
+                        "then the GEMM)")
+    p.add_argument("--eps", type=float, default=1e-5, help="RMSNorm epsilon (rmsnorm_* workloads)")
     p.add_argument("--m", type=int, default=None, help="override the token count (decode workloads)")
     p.add_argument("--alpha", type=float, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -151,6 +161,32 @@ def cpu_baseline(c, s_ref, budget_s: float):
     return {"value": tops, "unit": "TOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows} rows of X ({rows / c.m:.2f} passes over the {c.m}-row workload, all N={c.n} "
                       f"outputs, K={c.k}), {t_total:.1f} s of numpy/BLAS work"}
+
+
+def cpu_baseline_norm(c, nc, eps, budget_s: float):
+    """The CPU oracle's norm path (RMSNorm with the folded gain, quantisation,
+    int8 GEMM, dequantisation) on row chunks of the residual stream; its
+    smoothing factors from the oracle's own calibration (not timed)."""
+    import oracle
+
+    threads = _blas_threads()
+    a = oracle.calibrate_absmax(oracle.rmsnorm(nc.x_calib, nc.gamma, eps))
+    s_ref = oracle.smoothing_factors(a, oracle.weight_row_absmax(c.w), c.alpha)
+    gain = oracle.fold_norm_gain(nc.gamma, s_ref)
+    wq, sw = oracle.quantize_weights_per_channel(oracle.fold_weights(c.w, s_ref))
+    rows, t_total, start, chunk = 0, 0.0, 0, 64
+    while t_total < budget_s:
+        r1 = min(c.m, start + chunk)
+        t0 = time.perf_counter()
+        xq, dx = oracle.rmsnorm_quantize(nc.x[start:r1], gain, eps)
+        oracle.w8a8_linear(xq, dx, wq, sw, c.y_dtype)
+        t_total += time.perf_counter() - t0
+        rows += r1 - start
+        start = 0 if r1 == c.m else r1
+        chunk = min(chunk * 2, 512)
+    return {"value": 2.0 * rows * c.n * c.k / t_total / 1e12, "unit": "TOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} rows of the residual stream ({rows / c.m:.2f} passes over the {c.m}-row workload, "
+                      f"all N={c.n} outputs, K={c.k}), {t_total:.1f} s of numpy/BLAS work"}
 
 
 def bench_llm_int8(args, dev):
@@ -283,12 +319,24 @@ def main():
     if args.workload == "llm_int8":
         bench_llm_int8(args, dev)
         return
-    c = workloads.linear_case(args.workload, m=args.m, alpha=args.alpha)
+    norm = args.workload.startswith("rmsnorm_")
+    base = args.workload[len("rmsnorm_"):] if norm else args.workload
+    c = workloads.linear_case(base, m=args.m, alpha=args.alpha)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
     to = lambda a, dt: torch.from_numpy(a).to(tdt[dt]).to(dev)
-    xc, x, w = to(c.x_calib, c.x_dtype), to(c.x, c.x_dtype), to(c.w, c.w_dtype)
+    w = to(c.w, c.w_dtype)
+    nc = None
+    if norm:
+        nc = workloads.norm_case(c.m, c.k, seed=0, dtype=c.x_dtype, calib_rows=c.x_calib.shape[0])
+        x, gamma = to(nc.x, c.x_dtype), to(nc.gamma, c.x_dtype)
+        # calibration rows of the layer's input: the norm's output, by a plain torch RMSNorm
+        r = to(nc.x_calib, c.x_dtype).float()
+        xc = (r * torch.rsqrt(r.pow(2).mean(dim=1, keepdim=True) + args.eps) * gamma.float()).to(tdt[c.x_dtype])
+        del r
+    else:
+        xc, x = to(c.x_calib, c.x_dtype), to(c.x, c.x_dtype)
     out_dt = tdt[c.y_dtype]
-    print(f"[bench] workload {c.name} M={c.m} K={c.k} N={c.n} alpha={c.alpha}", file=sys.stderr, flush=True)
+    print(f"[bench] workload {args.workload} M={c.m} K={c.k} N={c.n} alpha={c.alpha}", file=sys.stderr, flush=True)
 
     # ---- load-time steps (once, timed separately; torch's events on its current stream)
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -299,6 +347,7 @@ def main():
     e1.record()
     s, wq, sw = sq.sq_smooth_fold_weights(w, c.alpha, absmax=absmax)
     e2.record()
+    gain = sq.sq_fold_norm_gain(gamma, s) if norm else None
     torch.cuda.synchronize()
     prep = {"calibrate_ms": e0.elapsed_time(e1), "smooth_fold_ms": e1.elapsed_time(e2),
             "calib_rows": int(c.x_calib.shape[0])}
@@ -319,9 +368,15 @@ def main():
     # faster than the GPU drains it even for microsecond decode kernels (the
     # checked Python wrappers cost more per call than such a kernel runs).
     stream = torch.cuda.current_stream(dev).cuda_stream
-    q_fn, g_fn = sq.raw["sq_quant_act_per_token"], sq.raw["sq_w8a8_linear"]
+    g_fn = sq.raw["sq_w8a8_linear"]
     _, _, ldx = sq._rows(x)
-    q_args = (x.data_ptr(), sq._dt(x), c.m, c.k, ldx, s.data_ptr(), xq.data_ptr(), dx.data_ptr(), stream)
+    if norm:
+        q_fn = sq.raw["sq_rmsnorm_quant"]
+        q_args = (x.data_ptr(), sq._dt(x), c.m, c.k, ldx, gain.data_ptr(), float(args.eps), xq.data_ptr(),
+                  dx.data_ptr(), stream)
+    else:
+        q_fn = sq.raw["sq_quant_act_per_token"]
+        q_args = (x.data_ptr(), sq._dt(x), c.m, c.k, ldx, s.data_ptr(), xq.data_ptr(), dx.data_ptr(), stream)
     nb = ws.numel() if ws is not None else 0
     g_args = [(xq.data_ptr(), dx.data_ptr(), w_i.data_ptr(), sw.data_ptr(), c.m, c.n, c.k, y.data_ptr(),
                sq._dt(y), c.n, ws.data_ptr() if ws is not None else None, nb, stream) for w_i in wqs]
@@ -377,7 +432,8 @@ def main():
     big = c.m >= 256 and c.n >= 192 and c.k % 128 == 0 and c.m * c.n >= (1 << 20)
     kfile, kname = (("gemm_decode.hip", "gemm_decode_kernel") if decode else
                     ("gemm_big.hip", "gemm_big_kernel") if big else ("gemm.hip", "gemm_i8_kernel"))
-    traffic = pmc_traffic(c.name if args.m is None else f"{c.name}_m{c.m}", kfile)
+    tag = args.workload if args.m is None else f"{args.workload}_m{c.m}"
+    traffic = pmc_traffic(tag, kfile)
     if decode:
         roof = {"bound": "hbm", "achieved": gemm_bytes / (gemm_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "kernel": kname, "bytes_per_launch": gemm_bytes}
@@ -392,15 +448,17 @@ def main():
         "metric": METRIC, "value": value, "unit": "TOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "i8", "data": "synthetic",
-        "config": {"workload": f"{c.name}: X {c.x_dtype} [{c.m} x {c.k}] -> W [{c.k} x {c.n}], "
-                               f"{c.y_dtype} out, alpha {c.alpha}", "M": c.m, "K": c.k, "N": c.n,
+        "config": {"workload": (f"{args.workload}: residual stream {c.x_dtype} [{c.m} x {c.k}] -> RMSNorm "
+                                f"(gain gamma/s, eps {args.eps:g}) -> W [{c.k} x {c.n}]" if norm else
+                                f"{c.name}: X {c.x_dtype} [{c.m} x {c.k}] -> W [{c.k} x {c.n}]") +
+                               f", {c.y_dtype} out, alpha {c.alpha}", "M": c.m, "K": c.k, "N": c.n,
                    "x_dtype": c.x_dtype, "y_dtype": c.y_dtype, "alpha": c.alpha},
         "pct_int8_peak": 100.0 * value / PEAK_INT8_TOPS,
         "gemm_only_tops": gemm_tops,
         "gemm_us": gemm_ms * 1e3,
-        "quant_us": quant_ms * 1e3,
-        "quant_gbs": quant_bytes / (quant_ms * 1e-3) / 1e9,
-        "quant_frac_hbm": quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        ("norm_quant_us" if norm else "quant_us"): quant_ms * 1e3,
+        ("norm_quant_gbs" if norm else "quant_gbs"): quant_bytes / (quant_ms * 1e-3) / 1e9,
+        ("norm_quant_frac_hbm" if norm else "quant_frac_hbm"): quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "step_gbs_algorithmic": (quant_bytes + gemm_bytes) / (ms_per_step * 1e-3) / 1e9,
         "weight_copies": n_w,
         "host_enqueue_us_per_step": host_us,
@@ -408,7 +466,9 @@ def main():
         "load_time": prep,
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and norm:
+        result["cpu_baseline"] = cpu_baseline_norm(c, nc, args.eps, args.cpu_seconds)
+    elif not args.no_cpu_baseline:
         import oracle
         s_ref = oracle.smoothing_factors(oracle.calibrate_absmax(c.x_calib), oracle.weight_row_absmax(c.w),
                                          c.alpha)

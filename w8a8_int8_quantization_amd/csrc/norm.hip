@@ -34,11 +34,23 @@
 // and its round-to-nearest-even binary64 value, scaled by the unit, is S.
 // fp16 squares span 2^58 at most, so fp16 rows never need a second chunk.
 //
+// Fast path (bf16 and fp16). With kDh = 53 - log2(max m^2) - log2(values per
+// thread), rounded down to even, every square within 2^-kDh of the row's
+// largest is a multiple of 2^(2 emax - 2 off - kDh) and below
+// 2^(2 emax - 2 off + log2(max m^2)), so one thread's binary64 FMA sum of such
+// squares is exact whatever its order. A thread converts that exact sum to
+// chunk 0's 128-bit integer once per row; only squares further down (a wave
+// whose smallest non-zero magnitude is below the window: rare) take the
+// integer path one by one. binary32 rows have 48-bit square significands and
+// always take the integer path.
+//
 // Layout: a kT-thread workgroup walks a grid-stride list of rows; thread t
 // owns the 16-byte vectors t, t + kT, ... of every row, keeps them in
 // registers through the three row reductions (largest exponent, sum of
 // squares, largest |a|), and loads the next row's vectors while it works on
 // the current one. The gains of its columns stay in registers for every row.
+// Wave reductions use DPP row shifts and broadcasts (no LDS traffic), the
+// workgroup step one LDS word per wave and one barrier.
 #include <math.h>
 
 #include "sq_common.hpp"
@@ -46,24 +58,28 @@
 
 namespace sqk {
 
-// Integer significand and exponent field of the element formats.
+// Integer significand and exponent field of the element formats. kSqBits
+// bounds the significand of a square (m^2 < 2^kSqBits); kBias is the
+// format's exponent bias.
 template <class In>
 struct NormBits;
 template <>
 struct NormBits<BF16In> {
-  static constexpr int kManBits = 7, kOff = 134, kMaxChunks = 8;
+  static constexpr int kManBits = 7, kOff = 134, kMaxChunks = 8, kSqBits = 16, kBias = 127;
   static constexpr uint32_t kMagMask = 0x7FFFu;
 };
 template <>
 struct NormBits<F16In> {
-  static constexpr int kManBits = 10, kOff = 25, kMaxChunks = 1;
+  static constexpr int kManBits = 10, kOff = 25, kMaxChunks = 1, kSqBits = 22, kBias = 15;
   static constexpr uint32_t kMagMask = 0x7FFFu;
 };
 template <>
 struct NormBits<F32In> {
-  static constexpr int kManBits = 23, kOff = 150, kMaxChunks = 8;
+  static constexpr int kManBits = 23, kOff = 150, kMaxChunks = 8, kSqBits = 48, kBias = 127;
   static constexpr uint32_t kMagMask = 0x7FFFFFFFu;
 };
+
+constexpr int ceil_log2(int v) { return v <= 1 ? 0 : 1 + ceil_log2((v + 1) / 2); }
 
 // Element e of a 16-byte vector as raw magnitude bits (sign dropped).
 template <class In>
@@ -75,6 +91,8 @@ __device__ __forceinline__ uint32_t mag_bits(const u32x4& v, int e) {
     return w[e] & NormBits<In>::kMagMask;
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 struct U128 {
   uint64_t lo, hi;
 };
@@ -85,46 +103,82 @@ __device__ __forceinline__ void add128(U128& a, uint64_t lo, uint64_t hi) {
   a.lo = s;
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-  return ((uint64_t)hi << 32) | lo;
+// ---------------------------------------------------------------- wave reductions over DPP
+// Inclusive scan within each 16-lane row (row_shr 1, 2, 4, 8), then row_bcast
+// 15 / 31 carry the row totals upwards; lane 63 ends with the wave's total,
+// which readlane makes uniform. Lanes whose DPP source does not exist read 0,
+// the identity of every reduction here (sums, and maxima of non-negative values).
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp0(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xF, false);
+}
+
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, dpp0<0x111>(v));
+  v = op(v, dpp0<0x112>(v));
+  v = op(v, dpp0<0x114>(v));
+  v = op(v, dpp0<0x118>(v));
+  v = op(v, dpp0<0x142, 0xA>(v));
+  v = op(v, dpp0<0x143, 0xC>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
-  return v;
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ void add128_dpp(U128& a) {
+  const uint32_t w0 = dpp0<kCtrl, kRowMask>((uint32_t)a.lo), w1 = dpp0<kCtrl, kRowMask>((uint32_t)(a.lo >> 32));
+  const uint32_t w2 = dpp0<kCtrl, kRowMask>((uint32_t)a.hi), w3 = dpp0<kCtrl, kRowMask>((uint32_t)(a.hi >> 32));
+  add128(a, ((uint64_t)w1 << 32) | w0, ((uint64_t)w3 << 32) | w2);
 }
 
 __device__ __forceinline__ U128 wave_sum128(U128 a) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) add128(a, shfl_xor_u64(a.lo, off), shfl_xor_u64(a.hi, off));
-  return a;
+  add128_dpp<0x111>(a);
+  add128_dpp<0x112>(a);
+  add128_dpp<0x114>(a);
+  add128_dpp<0x118>(a);
+  add128_dpp<0x142, 0xA>(a);
+  add128_dpp<0x143, 0xC>(a);
+  const uint32_t w0 = __builtin_amdgcn_readlane((int)(uint32_t)a.lo, 63);
+  const uint32_t w1 = __builtin_amdgcn_readlane((int)(uint32_t)(a.lo >> 32), 63);
+  const uint32_t w2 = __builtin_amdgcn_readlane((int)(uint32_t)a.hi, 63);
+  const uint32_t w3 = __builtin_amdgcn_readlane((int)(uint32_t)(a.hi >> 32), 63);
+  return U128{((uint64_t)w1 << 32) | w0, ((uint64_t)w3 << 32) | w2};
 }
 
-// Round-to-nearest-even binary64 of the integer W[0] + W[1] 2^64 + ... times 2^unit.
+// Maximum of the kW per-wave values in LDS (and v): unrolled for a few waves,
+// one value per lane and a wave reduction for many.
 template <int kW>
-__device__ __forceinline__ double wide_to_f64(const uint64_t (&w)[kW], int unit) {
-  uint64_t top = 0, nxt = 0;
-  bool found = false, have_nxt = false, sticky = false;
-  int t = 0;
+__device__ __forceinline__ uint32_t block_max_lds(const uint32_t* red, int lane, uint32_t v) {
+  if constexpr (kW <= 4) {
 #pragma unroll
-  for (int j = kW - 1; j >= 0; --j) {
-    if (found) {
-      if (have_nxt) sticky |= w[j] != 0;
-      else nxt = w[j];
-      have_nxt = true;
-    } else if (w[j] != 0) {
-      found = true;
-      top = w[j];
-      t = j;
-    }
+    for (int w = 0; w < kW; ++w) v = red[w] > v ? red[w] : v;
+    return v;
+  } else {
+    const uint32_t r = lane < kW ? red[lane] : 0u;
+    return wave_max_u32(r > v ? r : v);
   }
-  if (!found) return 0.0;
+}
+
+// A non-negative binary64 that is an integer multiple of 2^unit and below
+// 2^(unit + 84), as the 128-bit integer acc / 2^unit (exact).
+__device__ __forceinline__ U128 f64_to_fixed(double acc, int unit) {
+  if (!(acc > 0.0)) return U128{0u, 0u};
+  const uint64_t bits = (uint64_t)__double_as_longlong(acc);
+  const int ex = (int)((bits >> 52) & 0x7FF);
+  const uint64_t mant = (bits & 0xFFFFFFFFFFFFFull) | (1ull << 52);
+  const int sh = ex - 1075 - unit;  // acc = mant * 2^(sh + unit); sh in [-52, 32)
+  if (sh >= 0) return U128{mant << sh, sh > 0 ? mant >> (64 - sh) : 0u};
+  return U128{mant >> (-sh), 0u};
+}
+
+// Round to nearest even: the integer whose most significant non-zero 64-bit
+// word is `top` (word index t), followed by the word `nxt`, with `sticky` set
+// when any lower word is non-zero; the value is scaled by 2^unit.
+__device__ __forceinline__ double round_top(uint64_t top, uint64_t nxt, bool sticky, int t, int unit) {
   const int lz = __builtin_clzll(top);
   const uint64_t mant = lz ? (top << lz) | (nxt >> (64 - lz)) : top;  // most significant bit at bit 63
   sticky |= (lz ? (nxt << lz) : nxt) != 0;
@@ -136,6 +190,28 @@ __device__ __forceinline__ double wide_to_f64(const uint64_t (&w)[kW], int unit)
   return ldexp((double)keep, msb - 52 + unit);
 }
 
+// Round-to-nearest-even binary64 of the integer w[0] + w[1] 2^64 + ... +
+// w[n-1] 2^(64(n-1)) times 2^unit.
+__device__ __forceinline__ double wide_to_f64_lds(const uint64_t* w, int n, int unit) {
+  int t = n - 1;
+#pragma unroll 1
+  while (t >= 0 && w[t] == 0) --t;
+  if (t < 0) return 0.0;
+  const uint64_t top = w[t];
+  const uint64_t nxt = t > 0 ? w[t - 1] : 0u;
+  bool sticky = false;
+#pragma unroll 1
+  for (int j = t - 2; j >= 0; --j) sticky |= w[j] != 0;
+  return round_top(top, nxt, sticky, t, unit);
+}
+
+// The same for two words held in registers.
+__device__ __forceinline__ double u128_to_f64(U128 v, int unit) {
+  if (v.hi != 0) return round_top(v.hi, v.lo, false, 1, unit);
+  if (v.lo != 0) return round_top(v.lo, 0u, false, 0, unit);
+  return 0.0;
+}
+
 template <class In, int kCh, int kT>
 __global__ __launch_bounds__(kT) void rmsnorm_quant_kernel(const uint8_t* __restrict__ x, int64_t m, int nvec,
                                                             int64_t ldx_bytes, const float* __restrict__ gain,
@@ -145,10 +221,18 @@ __global__ __launch_bounds__(kT) void rmsnorm_quant_kernel(const uint8_t* __rest
   using NB = NormBits<In>;
   constexpr int V = In::kVec;
   constexpr int kW = kT / 64;
+  // Fast window of the sum of squares (bf16 and fp16): the squares within 2^-kDh
+  // of the largest one, summed per thread in binary64. Every such square is a
+  // multiple of 2^(2 emax - 2 off - kDh) below 2^(2 emax - 2 off + kSqBits), so
+  // a thread's kCh * V of them sum exactly when kDh + kSqBits + log2(kCh V) <= 53.
+  constexpr bool kF64Win = NB::kSqBits <= 22;
+  constexpr int kDh = kF64Win ? ((53 - NB::kSqBits - ceil_log2(kCh * V)) & ~1) : 0;
+  static_assert(!kF64Win || (kDh >= 8 && kDh <= 64), "fast window");
   __shared__ uint32_t red_e[kW];
   __shared__ uint64_t red_s[kW][2];
   __shared__ uint32_t red_more[kW];
-  __shared__ float red_a[kW];
+  __shared__ uint32_t red_a[kW];
+  __shared__ uint64_t wide_s[NB::kMaxChunks + 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
@@ -188,25 +272,44 @@ __global__ __launch_bounds__(kT) void rmsnorm_quant_kernel(const uint8_t* __rest
     for (int c = 0; c < kCh; ++c) raw[c] = nxt[c];
     if (row + gridDim.x < m) load_row(row + gridDim.x, nxt);
 
-    // 1. largest magnitude (bit patterns of non-negative values order like the values)
-    uint32_t mx = 0;
+    // 1. largest magnitude (bit patterns of non-negative values order like the
+    //    values) and, for the 16-bit formats, the smallest non-zero one; two
+    //    elements per packed 16-bit operation
+    uint32_t mx = 0, mnz = 0xFFFFFFFFu;
+    if constexpr (In::kVec == 8) {
+      u16x2 pmax = {0, 0}, pmin = {0xFFFF, 0xFFFF};
 #pragma unroll
-    for (int c = 0; c < kCh; ++c)
+      for (int c = 0; c < kCh; ++c) {
+        const uint32_t w[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        const uint32_t b = mag_bits<In>(raw[c], e);
-        mx = b > mx ? b : mx;
+        for (int i = 0; i < 4; ++i) {
+          const u16x2 b = __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu);
+          pmax = __builtin_elementwise_max(pmax, b);
+          pmin = __builtin_elementwise_min(pmin, b - u16x2{1, 1});  // zero wraps to 0xFFFF
+        }
       }
+      mx = pmax.x > pmax.y ? pmax.x : pmax.y;
+      mnz = (uint32_t)(pmin.x < pmin.y ? pmin.x : pmin.y) + 1u;  // 0x10000: no non-zero element
+    } else {
+#pragma unroll
+      for (int c = 0; c < kCh; ++c)
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const uint32_t b = mag_bits<In>(raw[c], e);
+          mx = b > mx ? b : mx;
+        }
+    }
     mx = wave_max_u32(mx);
     if (lane == 0) red_e[wid] = mx;
     lds_barrier();
-#pragma unroll
-    for (int w = 0; w < kW; ++w) mx = red_e[w] > mx ? red_e[w] : mx;
+    mx = block_max_lds<kW>(red_e, lane, mx);
     const int emax_f = (int)(mx >> NB::kManBits);
     const int emax = emax_f > 1 ? emax_f : 1;
+    const int unit0 = 2 * (emax - NB::kOff) - 64;  // chunk 0's unit, 2^unit0
 
-    // 2. exact sum of squares: chunk 0 from the registers; the rare further
-    //    chunks re-read the row (uniform across the workgroup)
+    // 2. exact sum of squares. Chunk 0 (squares within 2^-64 of the largest)
+    //    from the registers; the rare further chunks re-read the row.
+    // Integer term of chunk c0 (zero outside it); mr: the square lies below chunk c0.
     auto term = [&](uint32_t b, int c0, U128& acc, bool& mr) {
       const uint32_t ef = b >> NB::kManBits;
       const uint32_t mn = b & ((1u << NB::kManBits) - 1u);
@@ -232,36 +335,87 @@ __global__ __launch_bounds__(kT) void rmsnorm_quant_kernel(const uint8_t* __rest
       lds_barrier();
       U128 tot = {0u, 0u};
       uint32_t anym = 0;
+      if constexpr (kW <= 4) {
 #pragma unroll
-      for (int w = 0; w < kW; ++w) {
-        add128(tot, red_s[w][0], red_s[w][1]);
-        anym |= red_more[w];
+        for (int w = 0; w < kW; ++w) {
+          add128(tot, red_s[w][0], red_s[w][1]);
+          anym |= red_more[w];
+        }
+      } else {
+        // one wave's partial per lane, then the wave reduction again
+        if (lane < kW) {
+          tot = U128{red_s[lane][0], red_s[lane][1]};
+          anym = red_more[lane];
+        }
+        tot = wave_sum128(tot);
+        anym = wave_max_u32(anym);
       }
       more = anym != 0;
       return tot;
     };
     bool more = false;
     U128 b0;
+    float fv[kCh][V];  // the row as binary32, later the activations a
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) In::unpack(raw[c], fv[c]);
     {
       U128 acc = {0u, 0u};
       bool mr = false;
+      if constexpr (kF64Win) {
+        // exponent fields >= t_hi lie in the binary64 window (d < kDh)
+        const int t_hi = emax - kDh / 2 + 1;
+        const uint32_t thr_b = t_hi <= 1 ? 0u : (uint32_t)t_hi << NB::kManBits;
+        if (!__any(mnz < thr_b)) {
+          // every square of the wave is in the window: no selection needed
+          double s64 = 0.0;
 #pragma unroll
-      for (int c = 0; c < kCh; ++c)
+          for (int c = 0; c < kCh; ++c)
 #pragma unroll
-        for (int e = 0; e < V; ++e) term(mag_bits<In>(raw[c], e), 0, acc, mr);
+            for (int e = 0; e < V; ++e) {
+              const double fd = (double)fv[c][e];
+              s64 = __builtin_fma(fd, fd, s64);
+            }
+          acc = f64_to_fixed(s64, unit0);
+        } else {
+          // rare: squares in [2^-64, 2^-kDh) of the largest go to integer
+          // terms; the row is read again (L2) rather than kept in registers
+          const uint8_t* xr = x + row * ldx_bytes;
+          double s64 = 0.0;
+#pragma unroll
+          for (int c = 0; c < kCh; ++c) {
+            const int vi = tid + kT * c;
+            const u32x4 rv = vi < nvec ? load16(xr + (int64_t)vi * 16) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+              const uint32_t b = mag_bits<In>(rv, e);
+              const bool in = b >= thr_b;
+              const double fd = (double)(in ? fv[c][e] : 0.f);
+              s64 = __builtin_fma(fd, fd, s64);
+              if (!in) term(b, 0, acc, mr);
+            }
+          }
+          const U128 hi = f64_to_fixed(s64, unit0);
+          add128(acc, hi.lo, hi.hi);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < kCh; ++c)
+#pragma unroll
+          for (int e = 0; e < V; ++e) term(mag_bits<In>(raw[c], e), 0, acc, mr);
+      }
       b0 = block_sum(acc, mr, more);
     }
     double ss;
     if (NB::kMaxChunks == 1 || !more) {
-      const uint64_t w2[2] = {b0.lo, b0.hi};
-      ss = wide_to_f64<2>(w2, 2 * (emax - NB::kOff) - 64);
+      ss = u128_to_f64(b0, unit0);
     } else {
-      // squares below 2^-64 of the largest: Horner over the chunks, W = W * 2^64 + B_c
-      uint64_t wide[NB::kMaxChunks + 1];
-#pragma unroll
-      for (int j = 0; j <= NB::kMaxChunks; ++j) wide[j] = 0u;
-      wide[0] = b0.lo;
-      wide[1] = b0.hi;
+      // squares below 2^-64 of the largest (rare): Horner over the chunks,
+      // W = W * 2^64 + B_c, kept by thread 0 in LDS
+      if (tid == 0) {
+        wide_s[0] = b0.lo;
+        wide_s[1] = b0.hi;
+        for (int j = 2; j <= NB::kMaxChunks; ++j) wide_s[j] = 0u;
+      }
       int nchunks = 1;
       const uint8_t* xr = x + row * ldx_bytes;
 #pragma unroll 1
@@ -276,19 +430,22 @@ __global__ __launch_bounds__(kT) void rmsnorm_quant_kernel(const uint8_t* __rest
           for (int e = 0; e < V; ++e) term(mag_bits<In>(rv, e), c, acc, mr);
         }
         const U128 bc = block_sum(acc, mr, more);
-#pragma unroll
-        for (int j = NB::kMaxChunks; j > 0; --j) wide[j] = wide[j - 1];
-        wide[0] = bc.lo;
-        uint64_t carry = bc.hi;
-#pragma unroll
-        for (int j = 1; j <= NB::kMaxChunks; ++j) {
-          const uint64_t t = wide[j] + carry;
-          carry = t < carry ? 1u : 0u;
-          wide[j] = t;
+        if (tid == 0) {
+#pragma unroll 1
+          for (int j = NB::kMaxChunks; j > 0; --j) wide_s[j] = wide_s[j - 1];
+          wide_s[0] = bc.lo;
+          uint64_t carry = bc.hi;
+#pragma unroll 1
+          for (int j = 1; j <= NB::kMaxChunks; ++j) {
+            const uint64_t t = wide_s[j] + carry;
+            carry = t < carry ? 1u : 0u;
+            wide_s[j] = t;
+          }
         }
         ++nchunks;
       }
-      ss = wide_to_f64<NB::kMaxChunks + 1>(wide, 2 * (emax - NB::kOff) - 64 * nchunks);
+      lds_barrier();
+      ss = wide_to_f64_lds(wide_s, NB::kMaxChunks + 1, 2 * (emax - NB::kOff) - 64 * nchunks);
     }
 
     // 3. 1/rms, binary64 chain, one IEEE operation at a time
@@ -300,52 +457,51 @@ __global__ __launch_bounds__(kT) void rmsnorm_quant_kernel(const uint8_t* __rest
       inv = i32 <= 3.4028234663852886e38f ? i32 : 0.f;
     }
 
-    // 4. a = (x * inv) * g and the row maximum of |a| (a is formed again for the codes)
-    auto act = [&](int c, float* a) {
-      In::unpack(raw[c], a);
-#pragma unroll
-      for (int e = 0; e < V; ++e) a[e] = (a[e] * inv) * g[c][e];
-    };
+    // 4. a = (x * inv) * g and the row maximum of |a|
     float amax = 0.f;
 #pragma unroll
-    for (int c = 0; c < kCh; ++c) {
-      float a[V];
-      act(c, a);
+    for (int c = 0; c < kCh; ++c)
 #pragma unroll
-      for (int e = 0; e < V; ++e) amax = fmaxf(amax, fabsf(a[e]));
-    }
-    amax = wave_max(amax);
-    if (lane == 0) red_a[wid] = amax;
+      for (int e = 0; e < V; ++e) {
+        fv[c][e] = (fv[c][e] * inv) * g[c][e];
+        amax = fmaxf(amax, fabsf(fv[c][e]));
+      }
+    uint32_t abits = wave_max_u32(__float_as_uint(amax));
+    if (lane == 0) red_a[wid] = abits;
     lds_barrier();
-#pragma unroll
-    for (int w = 0; w < kW; ++w) amax = fmaxf(amax, red_a[w]);
+    abits = block_max_lds<kW>(red_a, lane, abits);
+    amax = __uint_as_float(abits);
 
-    // 5. per-token scale and int8 codes (Markstein quotients inside the checked range)
+    // 5. per-token scale and int8 codes (Markstein quotients inside the
+    //    checked range). The row maximum is uniform; one branch per row
+    //    picks the quotient, not one per element.
+    amax = __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(amax)));
     const float dsc = amax / (float)kQMax;
-    const bool fast = dsc >= kFastDMin && amax <= kFastAMax;
     const float rd = dsc > 0.f ? 1.0f / dsc : 0.f;
     if (tid == 0) x_scale[row] = dsc;
     int8_t* qr = xq + row * k;
+    auto emit = [&](auto quot) {
 #pragma unroll
-    for (int c = 0; c < kCh; ++c) {
-      const int vi = tid + kT * c;
-      if (vi >= nvec) continue;
-      float a[V];
-      act(c, a);
-      uint32_t code[V];
+      for (int c = 0; c < kCh; ++c) {
+        const int vi = tid + kT * c;
+        if (vi >= nvec) continue;
+        uint32_t code[V];
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        float qv = 0.f;
-        if (dsc > 0.f) qv = fast ? div_mk(a[e], dsc, rd) : a[e] / dsc;
-        code[e] = q_code(qv);
+        for (int e = 0; e < V; ++e) code[e] = q_code(quot(fv[c][e]));
+        if constexpr (V == 8) {
+          *reinterpret_cast<uint2*>(qr + (int64_t)vi * V) =
+              make_uint2(pack4(code[0], code[1], code[2], code[3]), pack4(code[4], code[5], code[6], code[7]));
+        } else {
+          *reinterpret_cast<uint32_t*>(qr + (int64_t)vi * V) = pack4(code[0], code[1], code[2], code[3]);
+        }
       }
-      if constexpr (V == 8) {
-        *reinterpret_cast<uint2*>(qr + (int64_t)vi * V) =
-            make_uint2(pack4(code[0], code[1], code[2], code[3]), pack4(code[4], code[5], code[6], code[7]));
-      } else {
-        *reinterpret_cast<uint32_t*>(qr + (int64_t)vi * V) = pack4(code[0], code[1], code[2], code[3]);
-      }
-    }
+    };
+    if (dsc >= kFastDMin && amax <= kFastAMax)
+      emit([&](float v) { return div_mk(v, dsc, rd); });
+    else if (dsc > 0.f)
+      emit([&](float v) { return v / dsc; });
+    else
+      emit([](float) { return 0.f; });
   }
 }
 

@@ -20,6 +20,8 @@
 // Either kernel can also clear a few words of device memory in its first
 // workgroup (the split-K ticket counters of a decode GEMM launched next on
 // the same stream), which saves that GEMM a launch.
+#include <type_traits>
+
 #include "sq_common.hpp"
 #include "sq_launch.hpp"
 
@@ -306,38 +308,47 @@ __global__ __launch_bounds__(kT) void quant_rows_kernel(const uint8_t* __restric
         for (int j = 0; j < kR; ++j) d[j] = amax[j] / (float)kQMax;
       }
     }
+    // The row scale and the fast flag are uniform: one branch per row picks
+    // the quotient, instead of one per element.
+    const bool fast_u = __builtin_amdgcn_readfirstlane((int)fast) != 0;
 #pragma unroll
     for (int j = 0; j < kR; ++j) {
       const int64_t row = g * kR + j;
       if (row >= m) continue;
-      if (tid == 0) x_scale[row] = d[j];
-      const float rd = (kMk && d[j] > 0.f) ? 1.0f / d[j] : 0.f;
+      const float dj = __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(d[j])));
+      if (tid == 0) x_scale[row] = dj;
+      const float rd = (kMk && dj > 0.f) ? 1.0f / dj : 0.f;
       int8_t* qr = xq + row * k;
+      auto emit = [&](auto fast_c, auto quot) {
+        constexpr bool kF = decltype(fast_c)::value;
 #pragma unroll
-      for (int c = 0; c < kCh; ++c) {
-        const int vi = tid + kT * c;
-        if (vi >= nvec) continue;
-        float f[V];
-        if (kSmall) {
+        for (int c = 0; c < kCh; ++c) {
+          const int vi = tid + kT * c;
+          if (vi >= nvec) continue;
+          float f[V];
+          if (kSmall) {
 #pragma unroll
-          for (int e = 0; e < V; ++e) f[e] = keep[kSmall ? j : 0][c][e];
-        } else {
-          smoothed(raw[j][c], c, f, fast);
-        }
-        uint32_t code[V];
+            for (int e = 0; e < V; ++e) f[e] = keep[kSmall ? j : 0][c][e];
+          } else {
+            smoothed(raw[j][c], c, f, kF);
+          }
+          uint32_t code[V];
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-          float qv = 0.f;
-          if (d[j] > 0.f) qv = (kMk && fast) ? div_mk(f[e], d[j], rd) : f[e] / d[j];
-          code[e] = q_code(qv);
+          for (int e = 0; e < V; ++e) code[e] = q_code(quot(f[e]));
+          if constexpr (V == 8) {
+            *reinterpret_cast<uint2*>(qr + (int64_t)vi * V) =
+                make_uint2(pack4(code[0], code[1], code[2], code[3]), pack4(code[4], code[5], code[6], code[7]));
+          } else {
+            *reinterpret_cast<uint32_t*>(qr + (int64_t)vi * V) = pack4(code[0], code[1], code[2], code[3]);
+          }
         }
-        if constexpr (V == 8) {
-          *reinterpret_cast<uint2*>(qr + (int64_t)vi * V) =
-              make_uint2(pack4(code[0], code[1], code[2], code[3]), pack4(code[4], code[5], code[6], code[7]));
-        } else {
-          *reinterpret_cast<uint32_t*>(qr + (int64_t)vi * V) = pack4(code[0], code[1], code[2], code[3]);
-        }
-      }
+      };
+      if (kMk && fast_u && dj > 0.f)
+        emit(std::true_type{}, [&](float v) { return div_mk(v, dj, rd); });
+      else if (dj > 0.f)
+        emit(std::false_type{}, [&](float v) { return v / dj; });
+      else
+        emit(std::false_type{}, [](float) { return 0.f; });
     }
   }
 }
