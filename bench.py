@@ -443,6 +443,12 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic
     roof["launch_us"] = gemm_ms * 1e3
+    norm_roof = None
+    if norm:
+        ach = quant_bytes / (quant_ms * 1e-3) / 1e9
+        norm_roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                     "traffic": pmc_traffic(tag + ":norm", "norm.hip"), "kernel": "rmsnorm_quant_kernel",
+                     "bytes_per_launch": quant_bytes, "launch_us": quant_ms * 1e3}
 
     result = {
         "metric": METRIC, "value": value, "unit": "TOP/s", "n_gpus": 1, "steps": args.steps,
@@ -466,6 +472,8 @@ def main():
         "load_time": prep,
         "roofline": roof,
     }
+    if norm:
+        result["norm_roofline"] = norm_roof
     if not args.no_cpu_baseline and norm:
         result["cpu_baseline"] = cpu_baseline_norm(c, nc, args.eps, args.cpu_seconds)
     elif not args.no_cpu_baseline:

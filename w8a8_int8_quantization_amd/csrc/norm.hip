@@ -366,16 +366,18 @@ __global__ __launch_bounds__(kT) void rmsnorm_quant_kernel(const uint8_t* __rest
         const int t_hi = emax - kDh / 2 + 1;
         const uint32_t thr_b = t_hi <= 1 ? 0u : (uint32_t)t_hi << NB::kManBits;
         if (!__any(mnz < thr_b)) {
-          // every square of the wave is in the window: no selection needed
-          double s64 = 0.0;
+          // every square of the wave is in the window: no selection needed;
+          // four independent FMA chains (the sums are exact, so their
+          // grouping cannot change the result)
+          double s4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
           for (int c = 0; c < kCh; ++c)
 #pragma unroll
             for (int e = 0; e < V; ++e) {
               const double fd = (double)fv[c][e];
-              s64 = __builtin_fma(fd, fd, s64);
+              s4[e & 3] = __builtin_fma(fd, fd, s4[e & 3]);
             }
-          acc = f64_to_fixed(s64, unit0);
+          acc = f64_to_fixed((s4[0] + s4[1]) + (s4[2] + s4[3]), unit0);
         } else {
           // rare: squares in [2^-64, 2^-kDh) of the largest go to integer
           // terms; the row is read again (L2) rather than kept in registers
