@@ -103,31 +103,6 @@ __device__ __forceinline__ void add128(U128& a, uint64_t lo, uint64_t hi) {
   a.lo = s;
 }
 
-// ---------------------------------------------------------------- wave reductions over DPP
-// Inclusive scan within each 16-lane row (row_shr 1, 2, 4, 8), then row_bcast
-// 15 / 31 carry the row totals upwards; lane 63 ends with the wave's total,
-// which readlane makes uniform. Lanes whose DPP source does not exist read 0,
-// the identity of every reduction here (sums, and maxima of non-negative values).
-template <int kCtrl, int kRowMask = 0xF>
-__device__ __forceinline__ uint32_t dpp0(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xF, false);
-}
-
-template <class Op>
-__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
-  v = op(v, dpp0<0x111>(v));
-  v = op(v, dpp0<0x112>(v));
-  v = op(v, dpp0<0x114>(v));
-  v = op(v, dpp0<0x118>(v));
-  v = op(v, dpp0<0x142, 0xA>(v));
-  v = op(v, dpp0<0x143, 0xC>(v));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
-}
-
 template <int kCtrl, int kRowMask = 0xF>
 __device__ __forceinline__ void add128_dpp(U128& a) {
   const uint32_t w0 = dpp0<kCtrl, kRowMask>((uint32_t)a.lo), w1 = dpp0<kCtrl, kRowMask>((uint32_t)(a.lo >> 32));
@@ -479,7 +454,7 @@ __global__ __launch_bounds__(kT) void rmsnorm_quant_kernel(const uint8_t* __rest
     //    picks the quotient, not one per element.
     amax = __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(amax)));
     const float dsc = amax / (float)kQMax;
-    const float rd = dsc > 0.f ? 1.0f / dsc : 0.f;
+    const float rd = dsc > 0.f ? rcp_scale(dsc) : 0.f;
     if (tid == 0) x_scale[row] = dsc;
     int8_t* qr = xq + row * k;
     auto emit = [&](auto quot) {

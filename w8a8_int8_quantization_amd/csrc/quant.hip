@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kT) void quant_rows_kernel(const uint8_t* __restric
       if (row >= m) continue;
       const float dj = __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(d[j])));
       if (tid == 0) x_scale[row] = dj;
-      const float rd = (kMk && dj > 0.f) ? 1.0f / dj : 0.f;
+      const float rd = (kMk && dj > 0.f) ? rcp_scale(dj) : 0.f;
       int8_t* qr = xq + row * k;
       auto emit = [&](auto fast_c, auto quot) {
         constexpr bool kF = decltype(fast_c)::value;

@@ -87,12 +87,34 @@ __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cas
 __device__ __forceinline__ void store16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // ---------------------------------------------------------------- reductions
-// Maximum over the 64 lanes of a wavefront (every lane receives it).
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+// ---------------------------------------------------------------- wave reductions over DPP
+// Inclusive scan within each 16-lane row (row_shr 1, 2, 4, 8), then row_bcast
+// 15 / 31 carry the row totals upwards; lane 63 ends with the wave's total,
+// which readlane makes uniform. Lanes whose DPP source does not exist read 0,
+// the identity of every reduction here (sums, and maxima of non-negative values).
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp0(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xF, false);
 }
+
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, dpp0<0x111>(v));
+  v = op(v, dpp0<0x112>(v));
+  v = op(v, dpp0<0x114>(v));
+  v = op(v, dpp0<0x118>(v));
+  v = op(v, dpp0<0x142, 0xA>(v));
+  v = op(v, dpp0<0x143, 0xC>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+
+// Maximum over the 64 lanes of a wavefront of non-negative values (their bit
+// patterns order like the values); every lane receives it.
+__device__ __forceinline__ float wave_max(float v) { return __uint_as_float(wave_max_u32(__float_as_uint(v))); }
 
 // Maximum over a workgroup of kThreads threads; `red` holds kThreads/64 floats of LDS.
 template <int kThreads>
@@ -149,6 +171,12 @@ __device__ __forceinline__ float rcp_rn(float s) {
   const float y = __builtin_amdgcn_rcpf(s);
   const float e = __builtin_fmaf(-s, y, 1.0f);
   return __builtin_fmaf(e, y, y);
+}
+
+// RN(1/d) for a positive row scale: the refined hardware reciprocal inside the
+// range where it equals the IEEE one, IEEE division outside it.
+__device__ __forceinline__ float rcp_scale(float d) {
+  return (d >= 0x1p-20f && d < 0x1p21f) ? rcp_rn(d) : 1.0f / d;
 }
 
 __device__ __forceinline__ float div_mk(float a, float b, float rb) {
