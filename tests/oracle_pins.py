@@ -516,9 +516,76 @@ def pin_norm_fold_identity(o):
     assert np.all(np.abs(d1 / d2 - 1) <= 2.0 ** -21)
 
 
+# ---------------------------------------------------------------------------
+# Gated activation (SiLU(gate) * up) feeding the down projection
+# ---------------------------------------------------------------------------
+def _ulps32(got, ref):
+    ref = np.asarray(ref, np.float64)
+    return np.abs(np.asarray(got, np.float64) - ref) / np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+
+
+def pin_exp32(o):
+    """e^t against the binary64 library exponential over binary32's normal
+    range, and the exact points of the algorithm."""
+    t = np.linspace(-87.0, 88.0, 400001).astype(F32)
+    ref = np.exp(t.astype(np.float64))
+    assert _ulps32(o.exp32(t), ref).max() <= 1.25
+    assert float(o.exp32(np.array([0.0], F32))[0]) == 1.0
+    # beyond the range: overflow to +inf, underflow through the subnormals to 0
+    big = o.exp32(np.array([89.0, 100.5, 1e30], F32))
+    assert np.all(np.isinf(big)) and np.all(big > 0)
+    tiny = o.exp32(np.array([-95.0, -103.0, -105.0, -120.0, -1e30], F32)).astype(np.float64)
+    assert 0 < tiny[0] < 2.0 ** -126 and tiny[3] == 0.0 and tiny[4] == 0.0
+    assert abs(tiny[0] - math.exp(-95.0)) <= 2.0 ** -149
+
+
+def pin_silu(o):
+    """SiLU against z / (1 + e^-z) in binary64, its limits, and the identity
+    SiLU(z) - SiLU(-z) = z."""
+    z = np.linspace(-40.0, 40.0, 200001).astype(F32)
+    ref = z.astype(np.float64) / (1.0 + np.exp(-z.astype(np.float64)))
+    got = o.silu32(z)
+    nz = np.abs(ref) > 1e-30
+    assert _ulps32(got[nz], ref[nz]).max() <= 3.0
+    assert float(o.silu32(np.array([0.0], F32))[0]) == 0.0
+    # sigma(z) rounds to 1 for z >= 17, so SiLU(z) == z; SiLU(z) == -0 for z < -110
+    w = np.array([17.0, 20.0, 100.0, 3.0e38], F32)
+    assert np.array_equal(o.silu32(w), w)
+    assert np.all(o.silu32(np.array([-111.0, -1e30], F32)) == 0.0)
+    zz = np.linspace(0.01, 12.0, 5001).astype(F32)
+    diff = o.silu32(zz).astype(np.float64) - o.silu32(-zz).astype(np.float64)
+    assert np.all(np.abs(diff - zz.astype(np.float64)) <= 4 * np.spacing(zz).astype(np.float64))
+
+
+def pin_gated_activation(o):
+    """h = bf16(SiLU(gate) * up): which operand goes through SiLU, the bf16
+    rounding, and the quantiser it feeds."""
+    g = np.array([[2.0, -1.0, 0.0, 6.0]], F32)
+    u = np.array([[3.0, 2.0, 5.0, -0.5]], F32)
+    h = o.gated_activation(g, u)[0].astype(np.float64)
+    want = [2.0 / (1.0 + math.exp(-2.0)) * 3.0, -1.0 / (1.0 + math.exp(1.0)) * 2.0, 0.0, 6.0 / (1.0 + math.exp(-6.0)) * -0.5]
+    assert np.all(np.abs(h - want) <= np.abs(want) * 2.0 ** -8 + 1e-30), h
+    # every value is a bf16 value
+    rng = np.random.default_rng(21)
+    gg = (rng.standard_normal((8, 256)) * 3).astype(F32)
+    uu = rng.standard_normal((8, 256)).astype(F32)
+    hh = o.gated_activation(gg, uu)
+    assert np.array_equal(hh, o.round_bf16(hh))
+    assert np.array_equal(hh, o.round_bf16((o.silu32(gg) * uu).astype(F32)))
+    s = rng.uniform(0.5, 4.0, 256).astype(F32)
+    q1, d1 = o.silu_mul_quantize(gg, uu, s)
+    q2, d2 = o.quantize_activations(hh, s)
+    assert np.array_equal(q1, q2) and np.array_equal(d1, d2)
+    # against torch's binary32 SiLU: within 1 bf16 ulp, codes within 1
+    ht = torch.nn.functional.silu(torch.from_numpy(gg)) * torch.from_numpy(uu)
+    hb = ht.to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.all(np.abs(hb.astype(np.float64) - hh) <= np.abs(hh) * 2.0 ** -7 + 1e-30)
+
+
 ALL_PINS = [
     pin_weight_example, pin_act_example, pin_smoothed_example, pin_per_tensor_crush, pin_trace_shapes,
     pin_calibration, pin_smoothing_closed_forms, pin_smoothing_identity, pin_quant_invariants,
     pin_gemm_bruteforce, pin_rounding_vs_torch, pin_f16_from_f64, pin_dequant, pin_error_ordering,
     pin_llm_int8, pin_norm_gain_example, pin_rms_closed_forms, pin_rms_bruteforce, pin_norm_fold_identity,
+    pin_exp32, pin_silu, pin_gated_activation,
 ]

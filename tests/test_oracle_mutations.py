@@ -18,6 +18,7 @@ from tests import oracle_pins
 
 # the submodule (the package attribute of the same name is the function rmsnorm)
 o_rms = importlib.import_module("oracle.rmsnorm")
+o_silu = importlib.import_module("oracle.silu")
 
 F32 = np.float32
 
@@ -220,6 +221,38 @@ def _rmsnorm_gain_before_norm(x, gain, eps=0.0):
     return (xg * o_rms.rms_inverse(xg, eps)[:, None]).astype(F32)
 
 
+def _exp_variant(drop_top=False, drop_lo=False):
+    def f(t):
+        t = np.asarray(t, dtype=F32)
+        coefs = o_silu.EXP_COEF[1:] if drop_top else o_silu.EXP_COEF
+        with np.errstate(all="ignore"):
+            k = np.clip(np.rint((t * o_silu.INV_LN2).astype(F32)), -256, 256).astype(F32)
+            r = (t - (k * o_silu.LN2_HI).astype(F32)).astype(F32)
+            if not drop_lo:
+                r = (r - (k * o_silu.LN2_LO).astype(F32)).astype(F32)
+            p = np.full_like(r, coefs[0])
+            for c in coefs[1:]:
+                p = ((p * r).astype(F32) + c).astype(F32)
+            e = np.ldexp(p, k.astype(np.int32)).astype(F32)
+        e = np.where(t > o_silu.T_HI, F32(np.inf), e)
+        return np.where(t < o_silu.T_LO, F32(0.0), e).astype(F32)
+    return f
+
+
+def _silu_wrong_sign(z):
+    z = np.asarray(z, dtype=F32)
+    with np.errstate(all="ignore"):
+        return (z * (F32(1.0) / (F32(1.0) + o_silu.exp32(z)).astype(F32))).astype(F32)
+
+
+def _gated_swapped(gate, up):
+    return o_num.round_bf16((o_silu.silu32(np.asarray(up, F32)) * np.asarray(gate, F32)).astype(F32))
+
+
+def _gated_no_bf16(gate, up):
+    return (o_silu.silu32(np.asarray(gate, F32)) * np.asarray(up, F32)).astype(F32)
+
+
 MUTANTS = {
     "s_exponents_swapped": (o_sq, "smoothing_factors", _smooth_swapped),
     "s_product_not_quotient": (o_sq, "smoothing_factors", _smooth_product),
@@ -253,6 +286,11 @@ MUTANTS = {
     "norm_fold_multiplies": (o_rms, "fold_norm_gain", _fold_gain_multiplies),
     "rmsnorm_drops_gain": (o_rms, "rmsnorm", _rmsnorm_drops_gain),
     "rmsnorm_gain_before_norm": (o_rms, "rmsnorm", _rmsnorm_gain_before_norm),
+    "exp_drops_top_taylor_term": (o_silu, "exp32", _exp_variant(drop_top=True)),
+    "exp_drops_low_ln2_part": (o_silu, "exp32", _exp_variant(drop_lo=True)),
+    "silu_exponent_sign": (o_silu, "silu32", _silu_wrong_sign),
+    "gated_silu_on_up": (o_silu, "gated_activation", _gated_swapped),
+    "gated_no_bf16_rounding": (o_silu, "gated_activation", _gated_no_bf16),
 }
 
 
@@ -262,7 +300,7 @@ def _plant(monkeypatch, module, name, fn):
     if hasattr(oracle, name):
         monkeypatch.setattr(oracle, name, fn)
     # functions re-exported through another submodule's namespace
-    for mod in (o_sq, o_int8, o_num, o_rms):
+    for mod in (o_sq, o_int8, o_num, o_rms, o_silu):
         if mod is not module and name in mod.__dict__:
             monkeypatch.setitem(mod.__dict__, name, fn)
 
