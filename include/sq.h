@@ -73,6 +73,8 @@ typedef enum sq_dtype {
 #define SQ_MAX_K_INT32 133144
 /* Longest row sq_rmsnorm_quant accepts (its exact sum of squares is sized for it). */
 #define SQ_MAX_K_NORM 32768
+/* Longest row sq_silu_mul_quant accepts (its rows stay in registers). */
+#define SQ_MAX_K_SILU 32768
 
 /* Flags of sq_smooth_fold_weights. */
 #define SQ_SMOOTH_COMPUTE 0u /* compute s from absmax and W, write it to `smooth` */
@@ -251,6 +253,44 @@ size_t sq_rmsnorm_w8a8_linear_workspace_size(int64_t m, int64_t n, int64_t k);
 sq_status sq_rmsnorm_w8a8_linear(const void* x, sq_dtype xt, int64_t ldx, const float* gain, float eps,
                                  const int8_t* wq, const float* w_scale, int64_t m, int64_t n, int64_t k, void* y,
                                  sq_dtype yt, int64_t ldy, void* ws, size_t ws_bytes, sq_stream_t stream);
+
+/*
+ * The down projection's input of a gated MLP, h = SiLU(gate) * up, fused with
+ * the smoothing divide and the per-token int8 quantisation of h.
+ * [W8A8] "How the Model Was Compressed" and "Why Activation Quantization Is
+ * Hard" (one scale per token, max / 127), "How the smoothing factor is
+ * computed" (the activation is divided by s), "Performance After
+ * Quantization" (the per-token quantisation steps are memory-bound and cost
+ * inter-token latency: here h never goes to memory in floating point).
+ *
+ *   e      = exp(-gate_ij) by a fixed binary32 algorithm (argument reduction
+ *            k = rint(t * RN32(1/ln2)), r = (t - k*L1) - k*L2, degree-7 Taylor
+ *            polynomial with coefficients RN32(1/n!) in Horner form, ldexp;
+ *            t > 100 -> +inf, t < -110 -> 0), no fused multiply-add
+ *   h_ij   = bf16(fl32(fl32(gate_ij * fl32(1 / fl32(1 + e))) * up_ij))
+ *   xh_ij  = fl32(h_ij / s_j)                (h_ij itself when smooth == NULL)
+ *   d_i    = fl32(max_j |xh_ij| / 127)
+ *   xq_ij  = clamp(round_half_even(fl32(xh_ij / d_i)), -127, 127); 0 when d_i == 0
+ *
+ * gate, up: [M x ldg], [M x ldu] bf16 (t must be SQ_BF16), e.g. the two
+ * halves of one [M x 2K] gate/up output with ldg = ldu = 2K. smooth: [K] or
+ * NULL. K <= SQ_MAX_K_SILU (SQ_ERR_RANGE otherwise). xq: [M x K] int8 output.
+ * x_scale: [M] binary32 output.
+ */
+sq_status sq_silu_mul_quant(const void* gate, const void* up, sq_dtype t, int64_t m, int64_t k, int64_t ldg,
+                            int64_t ldu, const float* smooth, int8_t* xq, float* x_scale, sq_stream_t stream);
+
+/*
+ * sq_silu_mul_quant followed by sq_w8a8_linear (the down projection) on the
+ * same stream; Xq, the row scales and the GEMM's workspace live in ws (the
+ * layout and size of sq_w8a8_linear_dyn; no initialisation needed). The
+ * results equal those of the two calls made separately.
+ */
+size_t sq_silu_mul_w8a8_linear_workspace_size(int64_t m, int64_t n, int64_t k);
+sq_status sq_silu_mul_w8a8_linear(const void* gate, const void* up, sq_dtype t, int64_t ldg, int64_t ldu,
+                                  const float* smooth, const int8_t* wq, const float* w_scale, int64_t m, int64_t n,
+                                  int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, size_t ws_bytes,
+                                  sq_stream_t stream);
 
 /*
  * LLM.int8() outlier detection over the feature columns of X.

@@ -194,3 +194,27 @@ def test_validation_rmsnorm(sq):
     assert h(P, sq.SQ_BF16, 256, None, 0.0, P, P, 16, 128, 256, P, sq.SQ_BF16, 128, P, nb, None) == NULL
     assert h(P, sq.SQ_BF16, 256, P, 0.0, None, P, 16, 128, 256, P, sq.SQ_BF16, 128, P, nb, None) == NULL
     assert h(P, sq.SQ_BF16, 256, P, 0.0, P, P, 16, 128, 256, P, sq.SQ_BF16, 100, P, nb, None) == SHAPE
+
+
+def test_validation_silu(sq):
+    f = sq.raw["sq_silu_mul_quant"]
+    assert f(P, P, sq.SQ_BF16, 4, 100, 100, 100, None, P, P, None) == SHAPE       # K not a multiple of 64
+    assert f(P, P, sq.SQ_BF16, 4, 32768 + 64, 32768 + 64, 32768 + 64, None, P, P, None) == RANGE
+    assert f(P, P, sq.SQ_F16, 4, 64, 64, 64, None, P, P, None) == DTYPE           # bf16 only
+    assert f(P, P, sq.SQ_F32, 4, 64, 64, 64, None, P, P, None) == DTYPE
+    assert f(None, P, sq.SQ_BF16, 4, 64, 64, 64, None, P, P, None) == NULL
+    assert f(P, None, sq.SQ_BF16, 4, 64, 64, 64, None, P, P, None) == NULL
+    assert f(P, P, sq.SQ_BF16, 4, 64, 64, 64, None, None, P, None) == NULL
+    assert f(P, P, sq.SQ_BF16, 4, 64, 64, 64, None, P, None, None) == NULL
+    assert f(BAD, P, sq.SQ_BF16, 4, 64, 64, 64, None, P, P, None) == ALIGN
+    assert f(P, P, sq.SQ_BF16, 4, 64, 64, 68, None, P, P, None) == ALIGN         # up rows not 16-byte aligned
+    assert f(P, P, sq.SQ_BF16, 4, 64, 64, 64, BAD, P, P, None) == ALIGN          # smooth
+    assert f(P, P, sq.SQ_BF16, 4, 64, 64, 32, None, P, P, None) == SHAPE         # ld < K
+    assert f(None, None, sq.SQ_BF16, 0, 64, 64, 64, None, None, None, None) == OK  # empty batch
+    h = sq.raw["sq_silu_mul_w8a8_linear"]
+    nb = sq.raw["sq_silu_mul_w8a8_linear_workspace_size"](16, 128, 256)
+    assert nb == sq.raw["sq_w8a8_linear_dyn_workspace_size"](16, 128, 256) > 0
+    assert h(P, P, sq.SQ_BF16, 256, 256, None, P, P, 16, 128, 256, P, sq.SQ_I32, 128, P, nb, None) == DTYPE
+    assert h(P, P, sq.SQ_BF16, 256, 256, None, P, P, 16, 128, 256, P, sq.SQ_BF16, 128, P, nb - 1, None) == WS
+    assert h(P, P, sq.SQ_F16, 256, 256, None, P, P, 16, 128, 256, P, sq.SQ_BF16, 128, P, nb, None) == DTYPE
+    assert h(P, P, sq.SQ_BF16, 256, 256, None, None, P, 16, 128, 256, P, sq.SQ_BF16, 128, P, nb, None) == NULL

@@ -21,6 +21,7 @@ __all__ = [
     "sq_calibrate_absmax", "sq_smooth_fold_weights", "sq_quant_act_per_token", "sq_w8a8_linear",
     "sq_w8a8_linear_dyn", "sq_outlier_detect", "sq_quant_act_rows_masked", "sq_int8_decomp_linear",
     "sq_int8_decomp_gemm", "linear_workspace", "sq_fold_norm_gain", "sq_rmsnorm_quant", "sq_rmsnorm_w8a8_linear",
+    "sq_silu_mul_quant", "sq_silu_mul_w8a8_linear",
     "SMOOTH_COMPUTE", "SMOOTH_GIVEN", "SMOOTH_NONE", "MAX_K_INT32", "EXPORTED_SYMBOLS",
 ]
 
@@ -59,6 +60,10 @@ _SIGS = {
     "sq_rmsnorm_quant": (_st, [_p, _st, _i64, _i64, _i64, _p, _f, _p, _p, _p]),
     "sq_rmsnorm_w8a8_linear_workspace_size": (_sz, [_i64, _i64, _i64]),
     "sq_rmsnorm_w8a8_linear": (_st, [_p, _st, _i64, _p, _f, _p, _p, _i64, _i64, _i64, _p, _st, _i64, _p, _sz, _p]),
+    "sq_silu_mul_quant": (_st, [_p, _p, _st, _i64, _i64, _i64, _i64, _p, _p, _p, _p]),
+    "sq_silu_mul_w8a8_linear_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "sq_silu_mul_w8a8_linear": (_st, [_p, _p, _st, _i64, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _st, _i64, _p, _sz,
+                                      _p]),
     "sq_outlier_detect_workspace_size": (_sz, [_i64]),
     "sq_outlier_detect": (_st, [_p, _st, _i64, _i64, _i64, _f, _p, _p, _p, _p, _sz, _p]),
     "sq_quant_act_rows_masked": (_st, [_p, _st, _i64, _i64, _i64, _p, _p, _p, _p]),
@@ -246,6 +251,39 @@ def sq_rmsnorm_w8a8_linear(x: torch.Tensor, gain: torch.Tensor, eps: float, wq: 
     _check("sq_rmsnorm_w8a8_linear", raw["sq_rmsnorm_w8a8_linear"](
         _ptr(x), _dt(x), ldx, _ptr(gain), float(eps), _ptr(wq), _ptr(w_scale), m, n, k, _ptr(y), _dt(y), ldy,
         _ptr(ws), ws.numel() if ws is not None else 0, _stream(x.device)))
+    return y
+
+
+def sq_silu_mul_quant(gate: torch.Tensor, up: torch.Tensor, smooth: Optional[torch.Tensor] = None,
+                      xq: Optional[torch.Tensor] = None, x_scale: Optional[torch.Tensor] = None):
+    """h = SiLU(gate) * up (bf16 [M x K] each), divided by ``smooth`` and quantised per token."""
+    m, k, ldg = _rows(gate)
+    mu, ku, ldu = _rows(up)
+    if (mu, ku) != (m, k):
+        raise ValueError("gate and up differ in shape")
+    xq = torch.empty((m, k), dtype=torch.int8, device=gate.device) if xq is None else xq
+    x_scale = torch.empty(m, dtype=torch.float32, device=gate.device) if x_scale is None else x_scale
+    _check("sq_silu_mul_quant", raw["sq_silu_mul_quant"](
+        _ptr(gate), _ptr(up), _dt(gate), m, k, ldg, ldu, _ptr(smooth), _ptr(xq), _ptr(x_scale),
+        _stream(gate.device)))
+    return xq, x_scale
+
+
+def sq_silu_mul_w8a8_linear(gate: torch.Tensor, up: torch.Tensor, smooth: Optional[torch.Tensor], wq: torch.Tensor,
+                            w_scale: torch.Tensor, out_dtype=torch.bfloat16, y: Optional[torch.Tensor] = None,
+                            ws: Optional[torch.Tensor] = None):
+    """SiLU(gate) * up, smoothing, per-token quantisation and the W8A8 GEMM in one call."""
+    m, k, ldg = _rows(gate)
+    _, _, ldu = _rows(up)
+    n = wq.shape[0]
+    y = torch.empty((m, n), dtype=out_dtype, device=gate.device) if y is None else y
+    _, _, ldy = _rows(y)
+    nb = raw["sq_silu_mul_w8a8_linear_workspace_size"](m, n, k)
+    if ws is None:
+        ws = _workspace(nb, gate.device)
+    _check("sq_silu_mul_w8a8_linear", raw["sq_silu_mul_w8a8_linear"](
+        _ptr(gate), _ptr(up), _dt(gate), ldg, ldu, _ptr(smooth), _ptr(wq), _ptr(w_scale), m, n, k, _ptr(y), _dt(y),
+        ldy, _ptr(ws), ws.numel() if ws is not None else 0, _stream(gate.device)))
     return y
 
 

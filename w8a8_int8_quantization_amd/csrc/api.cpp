@@ -274,6 +274,48 @@ sq_status sq_rmsnorm_w8a8_linear(const void* x, sq_dtype xt, int64_t ldx, const 
   return quant_then_gemm(quant, wq, w_scale, m, n, k, y, yt, ldy, ws, s);
 }
 
+// ---------------------------------------------------------------- gated activation -> down projection
+static sq_status check_silu(const void* gate, const void* up, sq_dtype t, int64_t m, int64_t k, int64_t ldg,
+                            int64_t ldu, const float* smooth) {
+  SQ_TRY(check_k(k));
+  if (k > SQ_MAX_K_SILU) return SQ_ERR_RANGE;
+  if (t != SQ_BF16) return SQ_ERR_DTYPE;
+  SQ_TRY(check_vec_matrix(gate, t, m, k, ldg));
+  SQ_TRY(check_vec_matrix(up, t, m, k, ldu));
+  if (smooth && !aligned16(smooth)) return SQ_ERR_ALIGN;
+  return SQ_OK;
+}
+
+sq_status sq_silu_mul_quant(const void* gate, const void* up, sq_dtype t, int64_t m, int64_t k, int64_t ldg,
+                            int64_t ldu, const float* smooth, int8_t* xq, float* x_scale, sq_stream_t stream) {
+  SQ_TRY(check_silu(gate, up, t, m, k, ldg, ldu, smooth));
+  if (m == 0) return SQ_OK;
+  if (!xq || !x_scale) return SQ_ERR_NULL;
+  if (!aligned16(xq)) return SQ_ERR_ALIGN;
+  return hip_status(sqh::silu_quant(gate, up, m, k, ldg, ldu, smooth, xq, x_scale, (hipStream_t)stream));
+}
+
+size_t sq_silu_mul_w8a8_linear_workspace_size(int64_t m, int64_t n, int64_t k) {
+  return sq_w8a8_linear_dyn_workspace_size(m, n, k);
+}
+
+sq_status sq_silu_mul_w8a8_linear(const void* gate, const void* up, sq_dtype t, int64_t ldg, int64_t ldu,
+                                  const float* smooth, const int8_t* wq, const float* w_scale, int64_t m, int64_t n,
+                                  int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, size_t ws_bytes,
+                                  sq_stream_t stream) {
+  SQ_TRY(check_silu(gate, up, t, m, k, ldg, ldu, smooth));
+  if (yt == SQ_I32) return SQ_ERR_DTYPE;
+  SQ_TRY(check_gemm_common(wq, w_scale, m, n, k, y, yt, ldy));
+  if (m == 0 || n == 0) return SQ_OK;
+  if (!ws || ws_bytes < sq_silu_mul_w8a8_linear_workspace_size(m, n, k)) return SQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SQ_ERR_ALIGN;
+  const hipStream_t s = (hipStream_t)stream;
+  auto quant = [&](int8_t* xq, float* dx, uint32_t* zero, int64_t nzero) {
+    return sqh::silu_quant(gate, up, m, k, ldg, ldu, smooth, xq, dx, s, zero, nzero);
+  };
+  return quant_then_gemm(quant, wq, w_scale, m, n, k, y, yt, ldy, ws, s);
+}
+
 size_t sq_outlier_detect_workspace_size(int64_t k) { return k > 0 ? round_up((size_t)k * 4) : 0; }
 
 sq_status sq_outlier_detect(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, float threshold,

@@ -44,6 +44,11 @@ hipError_t rmsnorm_quant(const void* x, sq_dtype xt, int64_t m, int64_t k, int64
 hipError_t fold_norm_gain(const void* gamma, sq_dtype gt, const float* smooth, int64_t k, float* out,
                           hipStream_t s);
 
+// SiLU(gate) * up (bf16), smoothing divide and per-token quantisation (zero / nzero as above).
+hipError_t silu_quant(const void* gate, const void* up, int64_t m, int64_t k, int64_t ldg, int64_t ldu,
+                      const float* smooth, int8_t* xq, float* x_scale, hipStream_t s, uint32_t* zero = nullptr,
+                      int64_t nzero = 0);
+
 hipError_t gemm_i8(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
                    int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec,
                    hipStream_t s);

@@ -29,6 +29,11 @@ not available):
   balanced normalised vector and one gain of 100 that makes the outlier.
   ``wide_range_rows`` gives rows whose binary exponents spread over a chosen
   range, with zeros, for exercising the exact sum of squares.
+* Gate/up projection outputs (``gate_up_case``): gate ~ N(0, 2^2), up ~ N(0, 1)
+  in bf16, with about 1% of the gate values replaced by magnitudes in
+  [15, 120] of either sign (SiLU's saturated regions and the exponential's
+  overflow and underflow), and the persistent outlier channels of the up side
+  scaled by 20.
 
 Weights are N(0, 0.02) in every configuration.
 """
@@ -52,6 +57,8 @@ __all__ = [
     "NormCase",
     "norm_case",
     "wide_range_rows",
+    "GateUpCase",
+    "gate_up_case",
     "CONFIGS",
 ]
 
@@ -236,6 +243,36 @@ def wide_range_rows(m: int, k: int, seed: int, dtype: str, lo_exp: int, hi_exp: 
     lim = {"bf16": 3.0e38, "f32": 3.0e38, "f16": 60000.0}[dtype]
     x = np.clip(x, -lim, lim).astype(np.float32)
     return _as_dtype(x, dtype)
+
+
+@dataclasses.dataclass
+class GateUpCase:
+    """bf16 outputs of a gate/up projection (the down projection's input side)."""
+
+    m: int
+    k: int
+    channels: np.ndarray
+    gate: np.ndarray        # [m x k] fp32 holding bf16 values
+    up: np.ndarray          # [m x k]
+    gate_calib: np.ndarray  # [t x k]
+    up_calib: np.ndarray
+
+
+def _gate_up_rows(g: np.random.Generator, rows: int, k: int, ch: np.ndarray):
+    gate = g.standard_normal((rows, k), dtype=np.float32) * np.float32(2.0)
+    wild = g.random((rows, k)) < 0.01
+    mags = g.uniform(15.0, 120.0, size=(rows, k)).astype(np.float32) * g.choice([-1.0, 1.0], size=(rows, k))
+    gate = np.where(wild, mags.astype(np.float32), gate)
+    up = g.standard_normal((rows, k), dtype=np.float32)
+    up[:, ch] *= np.float32(20.0)
+    return _as_dtype(gate, "bf16"), _as_dtype(up, "bf16")
+
+
+def gate_up_case(m: int, k: int, seed: int, calib_rows: int = 256) -> GateUpCase:
+    ch = outlier_channels(k, seed)
+    gate, up = _gate_up_rows(_rng(seed, "x"), m, k, ch)
+    gc, uc = _gate_up_rows(_rng(seed, "calib"), calib_rows, k, ch)
+    return GateUpCase(m=m, k=k, channels=ch, gate=gate, up=up, gate_calib=gc, up_calib=uc)
 
 
 def decomp_case(seed: int = 0, m: Optional[int] = None, k: Optional[int] = None,
