@@ -20,6 +20,11 @@ before the layer's RMSNorm: the first kernel is the fused RMSNorm (gain
 gamma / s) + per-token quantisation, the second the same GEMM. Their
 smoothing factors come from calibration rows normalised by a plain torch
 RMSNorm (load time, outside the timed region).
+
+The ``silu_*`` workloads start from the gate/up projection's bf16 outputs:
+the first kernel is the fused SiLU(gate) * up + smoothing + per-token
+quantisation, the second the down projection's GEMM. Their smoothing factors
+come from calibration rows of h made by plain torch ops at load time.
 """
 from __future__ import annotations
 
@@ -49,7 +54,9 @@ def parse():
                    help="qkv_prefill (default), gateup_prefill, down_prefill, decode_up, decode_down, tiny, "
                         "llm_int8; rmsnorm_qkv_prefill, rmsnorm_gateup_prefill, rmsnorm_decode_up (the step "
                         "starts from the residual stream: fused RMSNorm with the folded gain + quantisation, "
-                        "then the GEMM)")
+                        "then the GEMM); silu_down_prefill, silu_decode_down (the step starts from the gate/up "
+                        "projection's bf16 outputs: fused SiLU(gate)*up + smoothing + quantisation, then the "
+                        "down projection GEMM)")
     p.add_argument("--eps", type=float, default=1e-5, help="RMSNorm epsilon (rmsnorm_* workloads)")
     p.add_argument("--m", type=int, default=None, help="override the token count (decode workloads)")
     p.add_argument("--alpha", type=float, default=None)
@@ -189,6 +196,31 @@ def cpu_baseline_norm(c, nc, eps, budget_s: float):
                       f"all N={c.n} outputs, K={c.k}), {t_total:.1f} s of numpy/BLAS work"}
 
 
+def cpu_baseline_silu(c, gu, budget_s: float):
+    """The CPU oracle's gated path (SiLU(gate) * up, smoothing, quantisation,
+    int8 GEMM, dequantisation) on row chunks; smoothing factors from the
+    oracle's own calibration (not timed)."""
+    import oracle
+
+    threads = _blas_threads()
+    a = oracle.calibrate_absmax(oracle.gated_activation(gu.gate_calib, gu.up_calib))
+    s_ref = oracle.smoothing_factors(a, oracle.weight_row_absmax(c.w), c.alpha)
+    wq, sw = oracle.quantize_weights_per_channel(oracle.fold_weights(c.w, s_ref))
+    rows, t_total, start, chunk = 0, 0.0, 0, 16
+    while t_total < budget_s:
+        r1 = min(c.m, start + chunk)
+        t0 = time.perf_counter()
+        xq, dx = oracle.silu_mul_quantize(gu.gate[start:r1], gu.up[start:r1], s_ref)
+        oracle.w8a8_linear(xq, dx, wq, sw, c.y_dtype)
+        t_total += time.perf_counter() - t0
+        rows += r1 - start
+        start = 0 if r1 == c.m else r1
+        chunk = min(chunk * 2, 256)
+    return {"value": 2.0 * rows * c.n * c.k / t_total / 1e12, "unit": "TOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} rows of the gate/up outputs ({rows / c.m:.2f} passes over the {c.m}-row workload, "
+                      f"all N={c.n} outputs, K={c.k}), {t_total:.1f} s of numpy/BLAS work"}
+
+
 def bench_llm_int8(args, dev):
     """LLM.int8() decomposition, fp16 in and out: a step is outlier detection
     (column max + selection), the masked row-wise quantisation, and the int8
@@ -320,13 +352,24 @@ def main():
         bench_llm_int8(args, dev)
         return
     norm = args.workload.startswith("rmsnorm_")
-    base = args.workload[len("rmsnorm_"):] if norm else args.workload
+    silu = args.workload.startswith("silu_")
+    base = args.workload[len("rmsnorm_"):] if norm else (
+        {"silu_down_prefill": "down_prefill", "silu_decode_down": "decode_down"}[args.workload] if silu
+        else args.workload)
     c = workloads.linear_case(base, m=args.m, alpha=args.alpha)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
     to = lambda a, dt: torch.from_numpy(a).to(tdt[dt]).to(dev)
     w = to(c.w, c.w_dtype)
-    nc = None
-    if norm:
+    nc = gu = None
+    if silu:
+        gu = workloads.gate_up_case(c.m, c.k, seed=0, calib_rows=c.x_calib.shape[0])
+        gate, up = to(gu.gate, "bf16"), to(gu.up, "bf16")
+        x = gate
+        # calibration rows of the layer's input h = SiLU(gate) * up, by plain torch ops
+        gc, uc = to(gu.gate_calib, "bf16").float(), to(gu.up_calib, "bf16").float()
+        xc = (torch.nn.functional.silu(gc) * uc).to(torch.bfloat16)
+        del gc, uc
+    elif norm:
         nc = workloads.norm_case(c.m, c.k, seed=0, dtype=c.x_dtype, calib_rows=c.x_calib.shape[0])
         x, gamma = to(nc.x, c.x_dtype), to(nc.gamma, c.x_dtype)
         # calibration rows of the layer's input: the norm's output, by a plain torch RMSNorm
@@ -370,7 +413,11 @@ def main():
     stream = torch.cuda.current_stream(dev).cuda_stream
     g_fn = sq.raw["sq_w8a8_linear"]
     _, _, ldx = sq._rows(x)
-    if norm:
+    if silu:
+        q_fn = sq.raw["sq_silu_mul_quant"]
+        q_args = (gate.data_ptr(), up.data_ptr(), sq.SQ_BF16, c.m, c.k, c.k, c.k, s.data_ptr(), xq.data_ptr(),
+                  dx.data_ptr(), stream)
+    elif norm:
         q_fn = sq.raw["sq_rmsnorm_quant"]
         q_args = (x.data_ptr(), sq._dt(x), c.m, c.k, ldx, gain.data_ptr(), float(args.eps), xq.data_ptr(),
                   dx.data_ptr(), stream)
@@ -426,7 +473,7 @@ def main():
     ms_per_step = total_ms / args.steps
     value = ops / (ms_per_step * 1e-3) / 1e12
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
-    in_bytes = {"f32": 4, "bf16": 2}[c.x_dtype]
+    in_bytes = {"f32": 4, "bf16": 2}[c.x_dtype] * (2 if silu else 1)  # gate and up
     quant_bytes = c.m * c.k * in_bytes + 4 * c.k + c.m * c.k + 4 * c.m
     gemm_bytes = c.m * c.k + c.n * c.k + 4 * c.m + 4 * c.n + c.m * c.n * {"f32": 4, "bf16": 2}[c.y_dtype]
     big = c.m >= 256 and c.n >= 192 and c.k % 128 == 0 and c.m * c.n >= (1 << 20)
@@ -443,11 +490,13 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic
     roof["launch_us"] = gemm_ms * 1e3
+    pre = "norm_" if norm else ("silu_" if silu else "")
     norm_roof = None
-    if norm:
+    if norm or silu:
         ach = quant_bytes / (quant_ms * 1e-3) / 1e9
         norm_roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                     "traffic": pmc_traffic(tag + ":norm", "norm.hip"), "kernel": "rmsnorm_quant_kernel",
+                     "traffic": pmc_traffic(tag + (":norm" if norm else ":silu"), "norm.hip" if norm else "silu.hip"),
+                     "kernel": "rmsnorm_quant_kernel" if norm else "silu_quant_kernel",
                      "bytes_per_launch": quant_bytes, "launch_us": quant_ms * 1e3}
 
     result = {
@@ -456,15 +505,17 @@ def main():
         "vs_baseline": None, "dtype": "i8", "data": "synthetic",
         "config": {"workload": (f"{args.workload}: residual stream {c.x_dtype} [{c.m} x {c.k}] -> RMSNorm "
                                 f"(gain gamma/s, eps {args.eps:g}) -> W [{c.k} x {c.n}]" if norm else
+                                f"{args.workload}: gate, up bf16 [{c.m} x {c.k}] -> SiLU(gate)*up -> "
+                                f"W [{c.k} x {c.n}]" if silu else
                                 f"{c.name}: X {c.x_dtype} [{c.m} x {c.k}] -> W [{c.k} x {c.n}]") +
                                f", {c.y_dtype} out, alpha {c.alpha}", "M": c.m, "K": c.k, "N": c.n,
                    "x_dtype": c.x_dtype, "y_dtype": c.y_dtype, "alpha": c.alpha},
         "pct_int8_peak": 100.0 * value / PEAK_INT8_TOPS,
         "gemm_only_tops": gemm_tops,
         "gemm_us": gemm_ms * 1e3,
-        ("norm_quant_us" if norm else "quant_us"): quant_ms * 1e3,
-        ("norm_quant_gbs" if norm else "quant_gbs"): quant_bytes / (quant_ms * 1e-3) / 1e9,
-        ("norm_quant_frac_hbm" if norm else "quant_frac_hbm"): quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        (pre + "quant_us"): quant_ms * 1e3,
+        (pre + "quant_gbs"): quant_bytes / (quant_ms * 1e-3) / 1e9,
+        (pre + "quant_frac_hbm"): quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "step_gbs_algorithmic": (quant_bytes + gemm_bytes) / (ms_per_step * 1e-3) / 1e9,
         "weight_copies": n_w,
         "host_enqueue_us_per_step": host_us,
@@ -474,7 +525,11 @@ def main():
     }
     if norm:
         result["norm_roofline"] = norm_roof
-    if not args.no_cpu_baseline and norm:
+    if silu:
+        result["silu_roofline"] = norm_roof
+    if not args.no_cpu_baseline and silu:
+        result["cpu_baseline"] = cpu_baseline_silu(c, gu, args.cpu_seconds)
+    elif not args.no_cpu_baseline and norm:
         result["cpu_baseline"] = cpu_baseline_norm(c, nc, args.eps, args.cpu_seconds)
     elif not args.no_cpu_baseline:
         import oracle

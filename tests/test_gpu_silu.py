@@ -65,6 +65,12 @@ def test_silu_mul_quant_exp_edges():
     _check(gate, up, workloads.spread_scales(k, seed=7, lo_exp=-6, hi_exp=6))
     z = np.zeros((2, k), np.float32)
     _check(z, z, None)   # all-zero rows: scale 0, codes 0
+    # bf16 values around the tabulated range's ends (|g| near 2^-25 and 128), both signs, and zeros
+    fields = np.concatenate([np.arange(96, 106), np.arange(130, 140)])
+    vals = [((f << 7) | mant) for f in fields for mant in (0, 1, 63, 127)]
+    bits = np.array(vals + [v | 0x8000 for v in vals] + [0, 0x8000], np.uint32)
+    g = (np.resize(bits, (2, k)) << 16).view(np.float32)
+    _check(g, np.full((2, k), 1.5, np.float32), None)
 
 
 def test_silu_mul_quant_padded():

@@ -18,8 +18,10 @@
 //         +inf and t < -110 gives 0
 //   sig = 1 / (1 + e);  h = bf16(RN32(RN32(g * sig) * u))
 //   xh  = RN32(h / s_j);  d = RN32(max |xh| / 127);  q = clamp(rne(RN32(xh / d)))
-// 1 / (1 + e) is the refined hardware reciprocal, which equals the IEEE one on
-// [1, 2^21); a wave with larger values (g < -14.5) takes IEEE division for them.
+// sigma(g) = 1 / (1 + e) of every bf16 g comes from a per-workgroup LDS table
+// built with exactly these steps (IEEE division), or from its exact value
+// where the steps give 0.5, 0 or 1 (see sigma_of): one LDS read per element
+// instead of ~30 instructions.
 //
 // Layout as the other row kernels: a kT-thread workgroup per row (grid-
 // stride), thread t owns the 16-byte vectors t, t + kT, ... of the row in both
@@ -54,6 +56,19 @@ __device__ __forceinline__ float exp_fixed(float t) {
   return e;
 }
 
+// sigma(g) = 1 / (1 + e^-g) over the bf16 inputs, tabulated. A bf16 g with
+// exponent field below 102 (|g| < 2^-25) has e^-g == 1 exactly in the fixed
+// algorithm (k = 0, and the polynomial rounds to 1), so sigma == 0.5; with
+// exponent field 134 or more (|g| >= 128), e^-g is 0 (g > 0: t < -110) or
+// +inf (g < 0: t > 100), so sigma is 1 or 0. The 2 x 32 x 128 = 8192 bf16
+// values in between are tabulated per workgroup in LDS (32 KiB), each entry
+// computed by the same steps as the direct evaluation.
+constexpr int kSigLo = 102, kSigHi = 134;  // tabulated exponent fields [kSigLo, kSigHi)
+constexpr int kSigHalf = (kSigHi - kSigLo) * 128;
+constexpr int kSigEntries = 2 * kSigHalf;
+
+__device__ __forceinline__ float sigma_direct(float g) { return 1.0f / (1.0f + exp_fixed(-g)); }
+
 template <int kCh, int kT>
 __global__ __launch_bounds__(kT) void silu_quant_kernel(const uint8_t* __restrict__ gate,
                                                         const uint8_t* __restrict__ up, int64_t m, int nvec,
@@ -65,10 +80,22 @@ __global__ __launch_bounds__(kT) void silu_quant_kernel(const uint8_t* __restric
   constexpr int kW = kT / 64;
   __shared__ uint32_t red_a[kW];
   __shared__ int any_bad[kW];
+  __shared__ float sig_tab[kSigEntries];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
   const int64_t k = (int64_t)nvec * V;
+
+  // sigma of a bf16 bit pattern: the table, or its exact value outside it
+  auto sigma_of = [&](uint32_t b) {
+    const uint32_t mag = b & 0x7FFFu;
+    const uint32_t off = mag - (uint32_t)(kSigLo << 7);  // wraps for small magnitudes
+    const bool neg = (b & 0x8000u) != 0;
+    const bool in = off < (uint32_t)kSigHalf;
+    // always an in-range read (no per-element branch); the value is used only when in
+    const float tv = sig_tab[(in ? off : 0u) + (neg ? (uint32_t)kSigHalf : 0u)];
+    return in ? tv : (mag < (uint32_t)(kSigLo << 7) ? 0.5f : (neg ? 0.0f : 1.0f));
+  };
 
   auto load_row = [&](int64_t row, u32x4* dg, u32x4* du) {
 #pragma unroll
@@ -84,6 +111,12 @@ __global__ __launch_bounds__(kT) void silu_quant_kernel(const uint8_t* __restric
   if (row < m) load_row(row, ng, nu);
   if (blockIdx.x == 0)
     for (int i = tid; i < nzero; i += kT) zero[i] = 0u;
+  // the sigma table, built while the first row's loads are in flight
+  for (int i = tid; i < kSigEntries; i += kT) {
+    const uint32_t mag = (uint32_t)(kSigLo << 7) + (uint32_t)(i % kSigHalf);
+    const uint32_t b = mag | (i >= kSigHalf ? 0x8000u : 0u);
+    sig_tab[i] = sigma_direct(__uint_as_float(b << 16));
+  }
 
   // the thread's smoothing factors and their reciprocals (1 without smoothing)
   float sreg[kCh][V], rreg[kCh][V];
@@ -123,41 +156,18 @@ __global__ __launch_bounds__(kT) void silu_quant_kernel(const uint8_t* __restric
     }
     if (row + gridDim.x < m) load_row(row + gridDim.x, ng, nu);
 
-    // h = bf16(SiLU(g) * u), as binary32
+    // h = bf16(SiLU(g) * u), as binary32; sigma(g) from the table
     float h[kCh][V];
-    bool big = false;
 #pragma unroll
     for (int c = 0; c < kCh; ++c) {
-      float g[V], u[V];
-      BF16In::unpack(rg[c], g);
+      const uint32_t w[4] = {rg[c].x, rg[c].y, rg[c].z, rg[c].w};
+      float u[V];
       BF16In::unpack(ru[c], u);
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        const float d = 1.0f + exp_fixed(-g[e]);
-        big |= !(d < 0x1p21f);
-        h[c][e] = rcp_rn(d);  // sigma; fixed up below where d >= 2^21
+        const uint32_t b = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
+        h[c][e] = __uint_as_float(f32_to_bf16((__uint_as_float(b << 16) * sigma_of(b)) * u[e]) << 16);
       }
-    }
-    if (__any(big)) {
-      // rare: sigma = 1 / (1 + e) beyond the refined reciprocal's range
-#pragma unroll
-      for (int c = 0; c < kCh; ++c) {
-        float g[V];
-        BF16In::unpack(rg[c], g);
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-          const float d = 1.0f + exp_fixed(-g[e]);
-          if (!(d < 0x1p21f)) h[c][e] = 1.0f / d;
-        }
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < kCh; ++c) {
-      float g[V], u[V];
-      BF16In::unpack(rg[c], g);
-      BF16In::unpack(ru[c], u);
-#pragma unroll
-      for (int e = 0; e < V; ++e) h[c][e] = __uint_as_float(f32_to_bf16((g[e] * h[c][e]) * u[e]) << 16);
     }
 
     // xh = h / s and the row maximum; IEEE division when the row leaves the fast range
