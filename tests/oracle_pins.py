@@ -582,10 +582,87 @@ def pin_gated_activation(o):
     assert np.all(np.abs(hb.astype(np.float64) - hh) <= np.abs(hh) * 2.0 ** -7 + 1e-30)
 
 
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) variant
+# ---------------------------------------------------------------------------
+def _e4m3_nearest(v):
+    """Brute force: the nearest finite E4M3 code, ties to the even mantissa."""
+    vals = np.array([(-1.0 if c & 0x80 else 1.0) * ((c & 7) * 2.0 ** -9 if (c >> 3) & 15 == 0 else
+                     (1 + (c & 7) / 8.0) * 2.0 ** (((c >> 3) & 15) - 7)) for c in range(256)])
+    fin = np.array([not ((c & 0x7F) == 0x7F) for c in range(256)])
+    codes = np.flatnonzero(fin)
+    out = np.empty(len(v), np.uint8)
+    for i, x in enumerate(np.asarray(v, np.float64)):
+        d = np.abs(vals[codes] - x)
+        best = codes[d == d.min()]
+        if len(best) > 1:
+            even = [c for c in best if (c & 1) == 0 and (np.signbit(x) == bool(c & 0x80) or vals[c] == 0)]
+            best = even or list(best)
+        b = int(best[0])
+        if vals[b] == 0:
+            b = 0x80 if np.signbit(x) else 0
+        out[i] = b
+    return out
+
+
+def pin_e4m3(o):
+    """E4M3 codes: the value table's closed forms, brute-force nearest search
+    with ties to even on random values and every midpoint, and torch's
+    float8_e4m3fn conversion."""
+    vals = o.e4m3_values()
+    fin = np.isfinite(vals)
+    assert fin.sum() == 254 and np.nanmax(vals) == 448.0 and vals[1] == 2.0 ** -9 and vals[8] == 2.0 ** -6
+    rng = np.random.default_rng(31)
+    v = (rng.uniform(1, 2, 3000) * np.exp2(rng.integers(-12, 9, 3000)) * rng.choice([-1, 1], 3000)).astype(F32)
+    v = np.clip(v, -448, 448).astype(F32)
+    pos = np.sort(vals[fin & (vals >= 0)])
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(F32)
+    v = np.concatenate([v, mids, -mids, np.nextafter(mids, F32(0)), np.nextafter(mids, F32(1e3)),
+                        pos.astype(F32), np.array([0.0, -0.0], F32)]).astype(F32)
+    got = o.e4m3_encode(v)
+    assert np.array_equal(got, _e4m3_nearest(v))
+    tc = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, tc)
+    assert np.array_equal(o.e4m3_decode(got).astype(np.float64), vals[got])
+
+
+def pin_fp8_quant_and_gemm(o):
+    """Per-token / per-channel E4M3 quantisers reach 448 on every non-zero row
+    or column and stay within half a step; the product against Python ints."""
+    rng = np.random.default_rng(32)
+    x = (rng.standard_normal((9, 96)) * np.exp2(rng.integers(-4, 5, (9, 1)))).astype(F32)
+    x[3] = 0.0
+    q, d = o.quantize_activations_fp8(x)
+    vq = o.e4m3_decode(q).astype(np.float64)
+    for i in range(9):
+        if d[i] == 0:
+            assert not vq[i].any()
+            continue
+        assert np.max(np.abs(vq[i])) == 448.0
+        v = (x[i] / d[i]).astype(F32).astype(np.float64)
+        step = np.exp2(np.clip(np.floor(np.log2(np.maximum(np.abs(v), 1e-30))), -6, 8) - 3)
+        assert np.all(np.abs(vq[i] - v) <= step / 2 + 1e-12)
+    w = (rng.standard_normal((96, 7)) * 0.02).astype(F32)
+    wq, sw = o.quantize_weights_fp8(w)
+    assert wq.shape == (7, 96) and np.all(np.max(np.abs(o.e4m3_decode(wq)), axis=1) == 448.0)
+    assert np.allclose(sw, np.abs(w).max(axis=0) / 448.0, rtol=1e-7)
+    acc = o.fp8_matmul(q, wq)
+    from fractions import Fraction
+    xv = [[Fraction(float(a)) for a in row] for row in o.e4m3_decode(q)]
+    wv = [[Fraction(float(a)) for a in row] for row in o.e4m3_decode(wq)]
+    for i in (0, 4, 8):
+        for n in range(7):
+            assert acc[i, n] == float(sum(a * b for a, b in zip(xv[i], wv[n])))
+    # the dequantised product approximates the float product
+    y = o.fp8_linear(q, d, wq, sw, "f32").astype(np.float64)
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+    assert np.linalg.norm(y - ref) <= 0.05 * np.linalg.norm(ref)
+
+
 ALL_PINS = [
     pin_weight_example, pin_act_example, pin_smoothed_example, pin_per_tensor_crush, pin_trace_shapes,
     pin_calibration, pin_smoothing_closed_forms, pin_smoothing_identity, pin_quant_invariants,
     pin_gemm_bruteforce, pin_rounding_vs_torch, pin_f16_from_f64, pin_dequant, pin_error_ordering,
     pin_llm_int8, pin_norm_gain_example, pin_rms_closed_forms, pin_rms_bruteforce, pin_norm_fold_identity,
-    pin_exp32, pin_silu, pin_gated_activation,
+    pin_exp32, pin_silu, pin_gated_activation, pin_e4m3, pin_fp8_quant_and_gemm,
 ]

@@ -19,6 +19,7 @@ from tests import oracle_pins
 # the submodule (the package attribute of the same name is the function rmsnorm)
 o_rms = importlib.import_module("oracle.rmsnorm")
 o_silu = importlib.import_module("oracle.silu")
+o_fp8 = importlib.import_module("oracle.fp8")
 
 F32 = np.float32
 
@@ -253,6 +254,48 @@ def _gated_no_bf16(gate, up):
     return (o_silu.silu32(np.asarray(gate, F32)) * np.asarray(up, F32)).astype(F32)
 
 
+def _e4m3_round_half_up(v):
+    v = np.asarray(v, dtype=np.float64)
+    vals = o_fp8.e4m3_values()
+    pos = np.sort(vals[np.isfinite(vals) & (vals >= 0)])
+    a = np.minimum(np.abs(v), 448.0)
+    idx = np.searchsorted(pos, a, side="right") - 1
+    idx = np.clip(idx, 0, len(pos) - 2)
+    lo, hi = pos[idx], pos[idx + 1]
+    r = np.where(a - lo >= hi - a, hi, lo)
+    r = np.where(a >= pos[-1], pos[-1], r)
+    out = np.array([int(np.flatnonzero(vals == x)[0]) for x in r], np.uint8)
+    return np.where(np.signbit(v) & (r > 0), out | 0x80, out).astype(np.uint8)
+
+
+def _e4m3_truncate(v):
+    v = np.asarray(v, dtype=np.float64)
+    vals = o_fp8.e4m3_values()
+    pos = np.sort(vals[np.isfinite(vals) & (vals >= 0)])
+    a = np.minimum(np.abs(v), 448.0)
+    r = pos[np.clip(np.searchsorted(pos, a, side="right") - 1, 0, len(pos) - 1)]
+    out = np.array([int(np.flatnonzero(vals == x)[0]) for x in r], np.uint8)
+    return np.where(np.signbit(v) & (r > 0), out | 0x80, out).astype(np.uint8)
+
+
+def _fp8_act_scale_127(x):
+    x = np.asarray(x, F32)
+    d = (np.abs(x).max(axis=1).astype(F32) / F32(127)).astype(F32)
+    with np.errstate(all="ignore"):
+        v = (x / d[:, None]).astype(F32)
+    return o_fp8.e4m3_encode(np.where(d[:, None] > 0, v, F32(0))), d
+
+
+def _fp8_w_scale_per_row(w):
+    w = np.asarray(w, F32)
+    rowmax = np.abs(w).max(axis=1).astype(F32)
+    s = (rowmax / F32(448)).astype(F32)
+    with np.errstate(all="ignore"):
+        v = (w / s[:, None]).astype(F32)
+    codes = o_fp8.e4m3_encode(np.where(s[:, None] > 0, v, F32(0)))
+    return np.ascontiguousarray(codes.T), np.resize(s, w.shape[1]).astype(F32)
+
+
 MUTANTS = {
     "s_exponents_swapped": (o_sq, "smoothing_factors", _smooth_swapped),
     "s_product_not_quotient": (o_sq, "smoothing_factors", _smooth_product),
@@ -291,6 +334,10 @@ MUTANTS = {
     "silu_exponent_sign": (o_silu, "silu32", _silu_wrong_sign),
     "gated_silu_on_up": (o_silu, "gated_activation", _gated_swapped),
     "gated_no_bf16_rounding": (o_silu, "gated_activation", _gated_no_bf16),
+    "e4m3_round_half_up": (o_fp8, "e4m3_encode", _e4m3_round_half_up),
+    "e4m3_truncates": (o_fp8, "e4m3_encode", _e4m3_truncate),
+    "fp8_act_scale_127": (o_fp8, "quantize_activations_fp8", _fp8_act_scale_127),
+    "fp8_weight_scale_per_row": (o_fp8, "quantize_weights_fp8", _fp8_w_scale_per_row),
 }
 
 
@@ -300,7 +347,7 @@ def _plant(monkeypatch, module, name, fn):
     if hasattr(oracle, name):
         monkeypatch.setattr(oracle, name, fn)
     # functions re-exported through another submodule's namespace
-    for mod in (o_sq, o_int8, o_num, o_rms, o_silu):
+    for mod in (o_sq, o_int8, o_num, o_rms, o_silu, o_fp8):
         if mod is not module and name in mod.__dict__:
             monkeypatch.setitem(mod.__dict__, name, fn)
 
