@@ -75,6 +75,8 @@ typedef enum sq_dtype {
 #define SQ_MAX_K_NORM 32768
 /* Longest row sq_silu_mul_quant accepts (its rows stay in registers). */
 #define SQ_MAX_K_SILU 32768
+/* Longest K of the FP8 entry points (their quantiser keeps rows in registers). */
+#define SQ_MAX_K_FP8 32768
 
 /* Flags of sq_smooth_fold_weights. */
 #define SQ_SMOOTH_COMPUTE 0u /* compute s from absmax and W, write it to `smooth` */
@@ -291,6 +293,46 @@ sq_status sq_silu_mul_w8a8_linear(const void* gate, const void* up, sq_dtype t, 
                                   const float* smooth, const int8_t* wq, const float* w_scale, int64_t m, int64_t n,
                                   int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, size_t ws_bytes,
                                   sq_stream_t stream);
+
+/*
+ * FP8 (E4M3) W8A8 variant.
+ * [W8A8] "Conclusion": FP8 quantisation skips the calibration algorithms
+ * (SmoothQuant, GPTQ) and needs newer hardware; the pages give no format or
+ * scaling details. E4M3 here is the OCP encoding (1 sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits, largest finite 448, no infinities), stored
+ * one code per byte; scales are the int8 path's with 448 for 127; no
+ * smoothing.
+ *
+ * sq_quant_act_fp8 (per token):
+ *   d_i = fl32(max_j |x_ij| / 448);  xq_ij = E4M3(fl32(x_ij / d_i)), nearest
+ *   value, ties to even; 0 when d_i == 0.
+ *   x: [M x ldx] of type xt (SQ_F32, SQ_BF16, SQ_F16). xq: [M x K] codes.
+ *   K <= SQ_MAX_K_FP8.
+ * sq_quant_weights_fp8 (per output channel, load time):
+ *   sw_n = fl32(max_k |W_kn| / 448);  wq[n][k] = E4M3(fl32(W_kn / sw_n))
+ *   w: [K x ldw] of type wt, 16-byte aligned rows, N % 64 == 0. wq: [N x K]
+ *   codes (transposed like the int8 weights). ws: at least
+ *   sq_quant_weights_fp8_workspace_size(k, n) bytes (column maxima).
+ * sq_fp8_linear:
+ *   acc_in = sum_k E4M3(xq_ik) * E4M3(wq_nk) on the matrix cores (binary32
+ *            sums that are not rounded to nearest: within ~2^-12 of the sum
+ *            of |products| per 64-term instruction, measured)
+ *   y[i][n] = out(fl32(fl32(acc_in * x_scale_i) * w_scale_n)), yt = SQ_F32,
+ *   SQ_BF16 or SQ_F16. K % 128 == 0, K <= SQ_MAX_K_FP8.
+ * sq_fp8_linear_dyn: sq_quant_act_fp8 then sq_fp8_linear on the same stream,
+ *   with the codes and row scales in ws (sq_fp8_linear_dyn_workspace_size).
+ */
+sq_status sq_quant_act_fp8(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, uint8_t* xq,
+                           float* x_scale, sq_stream_t stream);
+size_t sq_quant_weights_fp8_workspace_size(int64_t k, int64_t n);
+sq_status sq_quant_weights_fp8(const void* w, sq_dtype wt, int64_t k, int64_t n, int64_t ldw, uint8_t* wq,
+                               float* w_scale, void* ws, size_t ws_bytes, sq_stream_t stream);
+sq_status sq_fp8_linear(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
+                        int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, sq_stream_t stream);
+size_t sq_fp8_linear_dyn_workspace_size(int64_t m, int64_t n, int64_t k);
+sq_status sq_fp8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const uint8_t* wq, const float* w_scale,
+                            int64_t m, int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws,
+                            size_t ws_bytes, sq_stream_t stream);
 
 /*
  * LLM.int8() outlier detection over the feature columns of X.

@@ -218,3 +218,30 @@ def test_validation_silu(sq):
     assert h(P, P, sq.SQ_BF16, 256, 256, None, P, P, 16, 128, 256, P, sq.SQ_BF16, 128, P, nb - 1, None) == WS
     assert h(P, P, sq.SQ_F16, 256, 256, None, P, P, 16, 128, 256, P, sq.SQ_BF16, 128, P, nb, None) == DTYPE
     assert h(P, P, sq.SQ_BF16, 256, 256, None, None, P, 16, 128, 256, P, sq.SQ_BF16, 128, P, nb, None) == NULL
+
+
+def test_validation_fp8(sq):
+    f = sq.raw["sq_quant_act_fp8"]
+    assert f(P, sq.SQ_BF16, 4, 100, 100, P, P, None) == SHAPE
+    assert f(P, sq.SQ_BF16, 4, 32768 + 64, 32768 + 64, P, P, None) == RANGE
+    assert f(P, sq.SQ_I8, 4, 64, 64, P, P, None) == DTYPE
+    assert f(P, sq.SQ_BF16, 4, 64, 64, None, P, None) == NULL
+    assert f(P, sq.SQ_BF16, 4, 64, 64, BAD, P, None) == ALIGN
+    assert f(None, sq.SQ_BF16, 0, 64, 64, None, None, None) == OK
+    g = sq.raw["sq_quant_weights_fp8"]
+    nb = sq.raw["sq_quant_weights_fp8_workspace_size"](128, 192)
+    assert nb >= 192 * 4
+    assert g(P, sq.SQ_BF16, 128, 100, 100, P, P, P, nb, None) == SHAPE      # N % 64
+    assert g(P, sq.SQ_BF16, 128, 192, 192, P, P, P, nb - 1, None) == WS
+    assert g(P, sq.SQ_BF16, 128, 192, 192, None, P, P, nb, None) == NULL
+    assert g(P, sq.SQ_BF16, 128, 192, 196, P, P, P, nb, None) == ALIGN      # row pitch
+    h = sq.raw["sq_fp8_linear"]
+    assert h(P, P, P, P, 4, 64, 192, P, sq.SQ_BF16, 64, None) == SHAPE      # K % 128
+    assert h(P, P, P, P, 4, 64, 32768 + 128, P, sq.SQ_BF16, 64, None) == RANGE
+    assert h(P, P, P, P, 4, 64, 256, P, sq.SQ_I32, 64, None) == DTYPE
+    assert h(None, P, P, P, 4, 64, 256, P, sq.SQ_BF16, 64, None) == NULL
+    assert h(P, P, P, P, 4, 64, 256, P, sq.SQ_BF16, 32, None) == SHAPE      # ldy < N
+    assert h(None, None, None, None, 0, 64, 256, None, sq.SQ_BF16, 64, None) == OK
+    dyn = sq.raw["sq_fp8_linear_dyn"]
+    nbd = sq.raw["sq_fp8_linear_dyn_workspace_size"](4, 64, 256)
+    assert dyn(P, sq.SQ_BF16, 256, P, P, 4, 64, 256, P, sq.SQ_BF16, 64, P, nbd - 1, None) == WS

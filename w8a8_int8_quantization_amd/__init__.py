@@ -21,7 +21,8 @@ __all__ = [
     "sq_calibrate_absmax", "sq_smooth_fold_weights", "sq_quant_act_per_token", "sq_w8a8_linear",
     "sq_w8a8_linear_dyn", "sq_outlier_detect", "sq_quant_act_rows_masked", "sq_int8_decomp_linear",
     "sq_int8_decomp_gemm", "linear_workspace", "sq_fold_norm_gain", "sq_rmsnorm_quant", "sq_rmsnorm_w8a8_linear",
-    "sq_silu_mul_quant", "sq_silu_mul_w8a8_linear",
+    "sq_silu_mul_quant", "sq_silu_mul_w8a8_linear", "sq_quant_act_fp8", "sq_quant_weights_fp8", "sq_fp8_linear",
+    "sq_fp8_linear_dyn",
     "SMOOTH_COMPUTE", "SMOOTH_GIVEN", "SMOOTH_NONE", "MAX_K_INT32", "EXPORTED_SYMBOLS",
 ]
 
@@ -64,6 +65,12 @@ _SIGS = {
     "sq_silu_mul_w8a8_linear_workspace_size": (_sz, [_i64, _i64, _i64]),
     "sq_silu_mul_w8a8_linear": (_st, [_p, _p, _st, _i64, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _st, _i64, _p, _sz,
                                       _p]),
+    "sq_quant_act_fp8": (_st, [_p, _st, _i64, _i64, _i64, _p, _p, _p]),
+    "sq_quant_weights_fp8_workspace_size": (_sz, [_i64, _i64]),
+    "sq_quant_weights_fp8": (_st, [_p, _st, _i64, _i64, _i64, _p, _p, _p, _sz, _p]),
+    "sq_fp8_linear": (_st, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _st, _i64, _p]),
+    "sq_fp8_linear_dyn_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "sq_fp8_linear_dyn": (_st, [_p, _st, _i64, _p, _p, _i64, _i64, _i64, _p, _st, _i64, _p, _sz, _p]),
     "sq_outlier_detect_workspace_size": (_sz, [_i64]),
     "sq_outlier_detect": (_st, [_p, _st, _i64, _i64, _i64, _f, _p, _p, _p, _p, _sz, _p]),
     "sq_quant_act_rows_masked": (_st, [_p, _st, _i64, _i64, _i64, _p, _p, _p, _p]),
@@ -284,6 +291,56 @@ def sq_silu_mul_w8a8_linear(gate: torch.Tensor, up: torch.Tensor, smooth: Option
     _check("sq_silu_mul_w8a8_linear", raw["sq_silu_mul_w8a8_linear"](
         _ptr(gate), _ptr(up), _dt(gate), ldg, ldu, _ptr(smooth), _ptr(wq), _ptr(w_scale), m, n, k, _ptr(y), _dt(y),
         ldy, _ptr(ws), ws.numel() if ws is not None else 0, _stream(gate.device)))
+    return y
+
+
+def sq_quant_act_fp8(x: torch.Tensor, xq: Optional[torch.Tensor] = None, x_scale: Optional[torch.Tensor] = None):
+    """Per-token E4M3 quantisation of X [M x K]: (codes uint8 [M x K], scales [M])."""
+    m, k, ldx = _rows(x)
+    xq = torch.empty((m, k), dtype=torch.uint8, device=x.device) if xq is None else xq
+    x_scale = torch.empty(m, dtype=torch.float32, device=x.device) if x_scale is None else x_scale
+    _check("sq_quant_act_fp8", raw["sq_quant_act_fp8"](
+        _ptr(x), _dt(x), m, k, ldx, _ptr(xq), _ptr(x_scale), _stream(x.device)))
+    return xq, x_scale
+
+
+def sq_quant_weights_fp8(w: torch.Tensor):
+    """Per-output-channel E4M3 quantisation of W [K x N]: (codes uint8 [N x K], scales [N])."""
+    k, n, ldw = _rows(w)
+    wq = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    w_scale = torch.empty(n, dtype=torch.float32, device=w.device)
+    nb = raw["sq_quant_weights_fp8_workspace_size"](k, n)
+    ws = _workspace(nb, w.device)
+    _check("sq_quant_weights_fp8", raw["sq_quant_weights_fp8"](
+        _ptr(w), _dt(w), k, n, ldw, _ptr(wq), _ptr(w_scale), _ptr(ws), nb, _stream(w.device)))
+    return wq, w_scale
+
+
+def sq_fp8_linear(xq: torch.Tensor, x_scale: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+                  out_dtype=torch.bfloat16, y: Optional[torch.Tensor] = None):
+    """E4M3 GEMM on the matrix cores with the per-token x per-channel dequantisation."""
+    m, k, _ = _rows(xq)
+    n = wq.shape[0]
+    y = torch.empty((m, n), dtype=out_dtype, device=xq.device) if y is None else y
+    _, _, ldy = _rows(y)
+    _check("sq_fp8_linear", raw["sq_fp8_linear"](
+        _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), m, n, k, _ptr(y), _dt(y), ldy, _stream(xq.device)))
+    return y
+
+
+def sq_fp8_linear_dyn(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, out_dtype=torch.bfloat16,
+                      y: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """Per-token E4M3 quantisation and the E4M3 GEMM in one call."""
+    m, k, ldx = _rows(x)
+    n = wq.shape[0]
+    y = torch.empty((m, n), dtype=out_dtype, device=x.device) if y is None else y
+    _, _, ldy = _rows(y)
+    nb = raw["sq_fp8_linear_dyn_workspace_size"](m, n, k)
+    if ws is None:
+        ws = _workspace(nb, x.device)
+    _check("sq_fp8_linear_dyn", raw["sq_fp8_linear_dyn"](
+        _ptr(x), _dt(x), ldx, _ptr(wq), _ptr(w_scale), m, n, k, _ptr(y), _dt(y), ldy, _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(x.device)))
     return y
 
 

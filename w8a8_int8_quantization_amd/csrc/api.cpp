@@ -316,6 +316,83 @@ sq_status sq_silu_mul_w8a8_linear(const void* gate, const void* up, sq_dtype t, 
   return quant_then_gemm(quant, wq, w_scale, m, n, k, y, yt, ldy, ws, s);
 }
 
+// ---------------------------------------------------------------- FP8 (E4M3) variant
+sq_status sq_quant_act_fp8(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, uint8_t* xq,
+                           float* x_scale, sq_stream_t stream) {
+  SQ_TRY(check_k(k));
+  if (k > SQ_MAX_K_FP8) return SQ_ERR_RANGE;
+  SQ_TRY(check_vec_matrix(x, xt, m, k, ldx));
+  if (m == 0) return SQ_OK;
+  if (!xq || !x_scale) return SQ_ERR_NULL;
+  if (!aligned16(xq)) return SQ_ERR_ALIGN;
+  return hip_status(sqh::quant_f8_rows(x, xt, m, k, ldx, xq, x_scale, (hipStream_t)stream));
+}
+
+size_t sq_quant_weights_fp8_workspace_size(int64_t k, int64_t n) {
+  (void)k;
+  return n > 0 ? round_up((size_t)n * 4) : 0;
+}
+
+sq_status sq_quant_weights_fp8(const void* w, sq_dtype wt, int64_t k, int64_t n, int64_t ldw, uint8_t* wq,
+                               float* w_scale, void* ws, size_t ws_bytes, sq_stream_t stream) {
+  if (k < 0) return SQ_ERR_SHAPE;
+  // the column maxima read W with 16-byte vectors along N
+  SQ_TRY(check_k(n));
+  SQ_TRY(check_vec_matrix(w, wt, k, n, ldw));
+  if (k == 0) return SQ_OK;
+  if (!wq || !w_scale) return SQ_ERR_NULL;
+  if (!ws || ws_bytes < sq_quant_weights_fp8_workspace_size(k, n)) return SQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SQ_ERR_ALIGN;
+  return hip_status(sqh::quant_f8_weights(w, wt, k, n, ldw, reinterpret_cast<float*>(ws), wq, w_scale,
+                                          (hipStream_t)stream));
+}
+
+static sq_status check_fp8_gemm(const uint8_t* wq, const float* w_scale, int64_t m, int64_t n, int64_t k,
+                                 const void* y, sq_dtype yt, int64_t ldy) {
+  if (k < 128 || k % 128 != 0) return SQ_ERR_SHAPE;
+  if (k > SQ_MAX_K_FP8) return SQ_ERR_RANGE;
+  if (m < 0 || n < 0) return SQ_ERR_SHAPE;
+  if (yt != SQ_F32 && yt != SQ_BF16 && yt != SQ_F16) return SQ_ERR_DTYPE;
+  if (ldy < n) return SQ_ERR_SHAPE;
+  if (m == 0 || n == 0) return SQ_OK;
+  if (m > INT32_MAX || n > INT32_MAX) return SQ_ERR_SHAPE;
+  if (!wq || !w_scale || !y) return SQ_ERR_NULL;
+  if (!aligned16(wq)) return SQ_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(y) % (uintptr_t)elem_bytes(yt)) != 0) return SQ_ERR_ALIGN;
+  return SQ_OK;
+}
+
+sq_status sq_fp8_linear(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
+                        int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, sq_stream_t stream) {
+  SQ_TRY(check_fp8_gemm(wq, w_scale, m, n, k, y, yt, ldy));
+  if (m == 0 || n == 0) return SQ_OK;
+  if (!xq || !x_scale) return SQ_ERR_NULL;
+  if (!aligned16(xq)) return SQ_ERR_ALIGN;
+  return hip_status(sqh::gemm_f8(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, (hipStream_t)stream));
+}
+
+size_t sq_fp8_linear_dyn_workspace_size(int64_t m, int64_t n, int64_t k) {
+  (void)n;
+  if (m <= 0 || k <= 0) return 0;
+  return round_up((size_t)m * (size_t)k) + round_up((size_t)m * 4);
+}
+
+sq_status sq_fp8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const uint8_t* wq, const float* w_scale,
+                            int64_t m, int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws,
+                            size_t ws_bytes, sq_stream_t stream) {
+  SQ_TRY(check_fp8_gemm(wq, w_scale, m, n, k, y, yt, ldy));
+  SQ_TRY(check_vec_matrix(x, xt, m, k, ldx));
+  if (m == 0 || n == 0) return SQ_OK;
+  if (!ws || ws_bytes < sq_fp8_linear_dyn_workspace_size(m, n, k)) return SQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SQ_ERR_ALIGN;
+  uint8_t* xq = reinterpret_cast<uint8_t*>(ws);
+  float* dx = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + round_up((size_t)m * (size_t)k));
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = sqh::quant_f8_rows(x, xt, m, k, ldx, xq, dx, s);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(sqh::gemm_f8(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, s));
+}
+
 size_t sq_outlier_detect_workspace_size(int64_t k) { return k > 0 ? round_up((size_t)k * 4) : 0; }
 
 sq_status sq_outlier_detect(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, float threshold,

@@ -49,6 +49,14 @@ hipError_t silu_quant(const void* gate, const void* up, int64_t m, int64_t k, in
                       const float* smooth, int8_t* xq, float* x_scale, hipStream_t s, uint32_t* zero = nullptr,
                       int64_t nzero = 0);
 
+// FP8 (E4M3) quantisers and GEMM.
+hipError_t quant_f8_rows(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, uint8_t* xq, float* x_scale,
+                         hipStream_t s);
+hipError_t quant_f8_weights(const void* w, sq_dtype wt, int64_t k, int64_t n, int64_t ldw, float* colmax,
+                            uint8_t* wq, float* w_scale, hipStream_t s);
+hipError_t gemm_f8(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
+                   int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, hipStream_t s);
+
 hipError_t gemm_i8(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
                    int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec,
                    hipStream_t s);
