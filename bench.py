@@ -25,6 +25,10 @@ The ``silu_*`` workloads start from the gate/up projection's bf16 outputs:
 the first kernel is the fused SiLU(gate) * up + smoothing + per-token
 quantisation, the second the down projection's GEMM. Their smoothing factors
 come from calibration rows of h made by plain torch ops at load time.
+
+The ``fp8_*`` workloads run the FP8 (E4M3) variant on the same shapes: a
+step is the per-token E4M3 quantisation and the E4M3 GEMM with its
+dequantisation; the weights are quantised per channel at load time.
 """
 from __future__ import annotations
 
@@ -42,6 +46,7 @@ if ROOT not in sys.path:
 METRIC = "W8A8 linear TOPS (quant+int8 GEMM+dequant), 8B shapes, % int8 MFMA peak"
 PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, TOP/s
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, GB/s
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, TFLOP/s
 PROFILE_PMC = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
@@ -56,7 +61,8 @@ def parse():
                         "starts from the residual stream: fused RMSNorm with the folded gain + quantisation, "
                         "then the GEMM); silu_down_prefill, silu_decode_down (the step starts from the gate/up "
                         "projection's bf16 outputs: fused SiLU(gate)*up + smoothing + quantisation, then the "
-                        "down projection GEMM)")
+                        "down projection GEMM); fp8_qkv_prefill, fp8_decode_up (the FP8 E4M3 variant: per-token "
+                        "E4M3 quantisation, then the E4M3 GEMM; no smoothing)")
     p.add_argument("--eps", type=float, default=1e-5, help="RMSNorm epsilon (rmsnorm_* workloads)")
     p.add_argument("--m", type=int, default=None, help="override the token count (decode workloads)")
     p.add_argument("--alpha", type=float, default=None)
@@ -221,6 +227,107 @@ def cpu_baseline_silu(c, gu, budget_s: float):
                       f"all N={c.n} outputs, K={c.k}), {t_total:.1f} s of numpy/BLAS work"}
 
 
+def bench_fp8(args, dev):
+    """FP8 (E4M3) W8A8: quantise X per token, E4M3 GEMM with dequantisation."""
+    import numpy as np
+    import torch
+
+    import workloads
+    import w8a8_int8_quantization_amd as sq
+
+    base = {"fp8_qkv_prefill": "qkv_prefill", "fp8_decode_up": "decode_up"}[args.workload]
+    c = workloads.linear_case(base, m=args.m)
+    to = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
+    x, w = to(c.x), to(c.w)
+    wq, sw = sq.sq_quant_weights_fp8(w)
+    xq = torch.empty((c.m, c.k), dtype=torch.uint8, device=dev)
+    dx = torch.empty(c.m, dtype=torch.float32, device=dev)
+    y = torch.empty((c.m, c.n), dtype=torch.bfloat16, device=dev)
+    decode = c.m <= 64
+    n_w = -(-(768 << 20) // wq.numel()) if decode else 1
+    wqs = [wq] + [wq.clone() for _ in range(n_w - 1)]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    q_fn, g_fn = sq.raw["sq_quant_act_fp8"], sq.raw["sq_fp8_linear"]
+    q_args = (x.data_ptr(), sq.SQ_BF16, c.m, c.k, c.k, xq.data_ptr(), dx.data_ptr(), stream)
+    g_args = [(xq.data_ptr(), dx.data_ptr(), w_i.data_ptr(), sw.data_ptr(), c.m, c.n, c.k, y.data_ptr(), sq.SQ_BF16,
+               c.n, stream) for w_i in wqs]
+    hip = HipEvents(sq._lib, stream)
+    print(f"[bench] workload {args.workload} M={c.m} K={c.k} N={c.n}", file=sys.stderr, flush=True)
+
+    def run(steps, evs=None):
+        bad = 0
+        for i in range(steps):
+            if evs:
+                hip.record(evs[i][0])
+            bad |= q_fn(*q_args)
+            if evs:
+                hip.record(evs[i][1])
+            bad |= g_fn(*g_args[i % n_w])
+            if evs:
+                hip.record(evs[i][2])
+        if bad:
+            raise RuntimeError(f"a C-ABI call failed (status bits {bad})")
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    t0, t1 = hip.create(), hip.create()
+    hip.record(t0)
+    run(args.steps)
+    hip.record(t1)
+    torch.cuda.synchronize()
+    total_ms = hip.elapsed(t0, t1)
+    evs = [[hip.create() for _ in range(3)] for _ in range(args.steps)]
+    run(args.steps, evs)
+    torch.cuda.synchronize()
+    quant_ms = float(np.mean([hip.elapsed(e[0], e[1]) for e in evs]))
+    gemm_ms = float(np.mean([hip.elapsed(e[1], e[2]) for e in evs]))
+    hip.destroy_all()
+    ops = 2.0 * c.m * c.n * c.k
+    ms = total_ms / args.steps
+    gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
+    gemm_bytes = c.m * c.k + c.n * c.k + 4 * c.m + 4 * c.n + 2 * c.m * c.n
+    if decode:
+        roof = {"bound": "hbm", "achieved": gemm_bytes / (gemm_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "bytes_per_launch": gemm_bytes}
+    else:
+        roof = {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "ops_per_launch": ops}
+    roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": pmc_traffic(args.workload, "gemm_f8.hip"),
+                 "kernel": "gemm_f8_kernel", "launch_us": gemm_ms * 1e3})
+    result = {
+        "metric": METRIC, "value": ops / (ms * 1e-3) / 1e12, "unit": "TOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e4m3", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: X bf16 [{c.m} x {c.k}] -> E4M3 per token, W [{c.k} x {c.n}] E4M3 "
+                               f"per channel, bf16 out", "M": c.m, "K": c.k, "N": c.n},
+        "gemm_only_tops": gemm_tops, "gemm_us": gemm_ms * 1e3, "quant_us": quant_ms * 1e3,
+        "weight_copies": n_w, "roofline": roof, "cpu_baseline": None if args.no_cpu_baseline else
+        cpu_baseline_fp8(c, args.cpu_seconds),
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_fp8(c, budget_s: float):
+    """The CPU oracle's FP8 path (E4M3 quantisation, exact product, dequantisation) on row chunks of X."""
+    import oracle
+
+    threads = _blas_threads()
+    wq, sw = oracle.quantize_weights_fp8(c.w)
+    rows, t_total, start, chunk = 0, 0.0, 0, 16
+    while t_total < budget_s:
+        r1 = min(c.m, start + chunk)
+        t0 = time.perf_counter()
+        xq, dx = oracle.quantize_activations_fp8(c.x[start:r1])
+        oracle.fp8_linear(xq, dx, wq, sw, "bf16")
+        t_total += time.perf_counter() - t0
+        rows += r1 - start
+        start = 0 if r1 == c.m else r1
+        chunk = min(chunk * 2, 256)
+    return {"value": 2.0 * rows * c.n * c.k / t_total / 1e12, "unit": "TOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} rows of X ({rows / c.m:.2f} passes over the {c.m}-row workload, all N={c.n} outputs, "
+                      f"K={c.k}), {t_total:.1f} s of numpy/BLAS work"}
+
+
 def bench_llm_int8(args, dev):
     """LLM.int8() decomposition, fp16 in and out: a step is outlier detection
     (column max + selection), the masked row-wise quantisation, and the int8
@@ -350,6 +457,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload == "llm_int8":
         bench_llm_int8(args, dev)
+        return
+    if args.workload.startswith("fp8_"):
+        bench_fp8(args, dev)
         return
     norm = args.workload.startswith("rmsnorm_")
     silu = args.workload.startswith("silu_")
