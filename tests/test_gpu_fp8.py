@@ -104,3 +104,49 @@ def test_fp8_linear_dyn_equals_two_calls():
     ws = torch.full((nb,), 0x5C, dtype=torch.uint8, device=dev())
     y1 = sq.sq_fp8_linear_dyn(x, wq, sw, ws=ws)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+# Prefill-sized problems (M >= 256, N >= 192, M N >= 2^20) run on the
+# 256-row-tile pipeline: ragged tiles in both directions, one and three k
+# stages, every output type.
+@pytest.mark.parametrize("m,n,k,out", [(1030, 1100, 1152, "f16"), (4096, 512, 128, "bf16"), (512, 2112, 384, "f32"),
+                                       (777, 4000, 2176, "bf16"), (2048, 6144, 4096, "f16")])
+def test_fp8_linear_prefill_tiles(m, n, k, out):
+    log("fp8 prefill gemm", m, n, k, out)
+    c = workloads.random_linear_case(m=m, k=k, n=n, seed=3 * m + n + k, dtype="bf16", calib_rows=8)
+    xq, d = oracle.quantize_activations_fp8(c.x)
+    wq, sw = oracle.quantize_weights_fp8(c.w)
+    _check_gemm(xq, d, wq, sw, out)
+
+
+def test_fp8_linear_prefill_random_codes():
+    """Every finite E4M3 code in both operands (products from 2^-18 to 448^2),
+    on the prefill pipeline."""
+    m, n, k = 512, 2048, 1024
+    rng = np.random.default_rng(77)
+    xq = rng.integers(0, 256, size=(m, k), dtype=np.uint8)
+    wq = rng.integers(0, 256, size=(n, k), dtype=np.uint8)
+    xq[(xq & 0x7F) == 0x7F] = 0x00
+    wq[(wq & 0x7F) == 0x7F] = 0x80
+    d = rng.uniform(0.25, 4.0, size=m).astype(np.float32) * np.float32(2.0 ** -10)
+    sw = rng.uniform(0.25, 4.0, size=n).astype(np.float32) * np.float32(2.0 ** -10)
+    _check_gemm(xq, d, wq, sw, "f32")
+
+
+@pytest.mark.parametrize("pad", [3, 8])
+def test_fp8_linear_prefill_strided_output(pad):
+    """Output rows with a pitch of n + pad elements: unaligned rows take the
+    direct stores, aligned ones the staged rows; the padding is left alone."""
+    m, n, k = 640, 1920, 512
+    c = workloads.random_linear_case(m=m, k=k, n=n, seed=pad, dtype="bf16", calib_rows=8)
+    xq, d = oracle.quantize_activations_fp8(c.x)
+    wq, sw = oracle.quantize_weights_fp8(c.w)
+    big = torch.full((m, n + pad), -7.0, dtype=torch.bfloat16, device=dev())
+    y = big[:, :n]
+    sq.sq_fp8_linear(torch.from_numpy(xq).to(dev()), torch.from_numpy(d).to(dev()), torch.from_numpy(wq).to(dev()),
+                     torch.from_numpy(sw).to(dev()), y=y)
+    ref = sq.sq_fp8_linear(torch.from_numpy(xq).to(dev()), torch.from_numpy(d).to(dev()),
+                           torch.from_numpy(wq).to(dev()), torch.from_numpy(sw).to(dev()))
+    assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
+    assert bool((big[:, n:] == -7.0).all())
+    _check_gemm(xq, d, wq, sw, "bf16")

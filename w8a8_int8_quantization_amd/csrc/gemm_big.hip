@@ -31,6 +31,8 @@
 //  * Workgroups are dispatched round-robin over the 8 XCDs; the tile order
 //    gives each XCD a contiguous range of tiles, grouped 4 tile-rows at a time,
 //    so that tiles sharing Xq and Wq panels run under the same L2.
+#include <type_traits>
+
 #include "sq_common.hpp"
 #include "sq_launch.hpp"
 
@@ -121,10 +123,19 @@ __device__ __forceinline__ void store4(void* y, int64_t off, const float* v, con
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int BN, int kOut, bool kVec>
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// kF8: E4M3 operands (one code per byte) on v_mfma_scale_f32_32x32x64_f8f6f4
+// with binary32 accumulators, two 64-k substeps per stage instead of four
+// 32-k ones; everything else is shared with the int8 kernel.
+template <int BN, int kOut, bool kVec, bool kF8 = false>
 __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
                                                           int M, int N, int K, BigEpi ep) {
   using C = BigCfg<BN>;
+  using AccT = typename std::conditional<kF8, v16f, v16i>::type;
+  using FragT = typename std::conditional<kF8, v8i, v4i>::type;
+  constexpr int kSub = kF8 ? 2 : 4;  // MFMA k-substeps per 128-byte stage
   __shared__ __attribute__((aligned(1024))) int8_t smem[kBigStages * C::kStage];
   // LLM.int8(): the tile's fp16 outlier slices of X and W, gathered once
   __shared__ uint16_t slice_x[kOut == kBigDecomp ? kBigBM * kSliceCols : 1];
@@ -178,7 +189,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
       __builtin_amdgcn_global_load_lds((const void*)(src[i] + koff), (lds_void*)(stage + dst[i]), 16, 0, 0);
   };
 
-  v16i acc[C::kFN][C::kFM];
+  AccT acc[C::kFN][C::kFM];
 #pragma unroll
   for (int j = 0; j < C::kFN; ++j)
 #pragma unroll
@@ -191,16 +202,25 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
 
   const int frow = lane & 31;
   const int fhalf = lane >> 5;
-  // Fragments of one 32-k substep: Xq blocks for this wave's 128 tokens and
-  // Wq blocks for its BN/2 output channels.
-  auto read_frags = [&](const int8_t* stage, int ks, v4i* xf, v4i* wf) {
-    const int c = 2 * ks + fhalf;
+  // Fragment of tile row r for substep ks: int8, 16 bytes (chunk 2 ks + half);
+  // E4M3, 32 bytes (chunks 4 ks + 2 half and the next one).
+  auto frag = [&](const int8_t* base, int r, int ks) -> FragT {
+    if constexpr (kF8) {
+      const int c = 4 * ks + 2 * fhalf;
+      const v4i lo = *reinterpret_cast<const v4i*>(base + big_lds_off(r, c));
+      const v4i hi = *reinterpret_cast<const v4i*>(base + big_lds_off(r, c + 1));
+      return FragT{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    } else {
+      return *reinterpret_cast<const v4i*>(base + big_lds_off(r, 2 * ks + fhalf));
+    }
+  };
+  // Fragments of one substep: Xq blocks for this wave's tokens and Wq blocks
+  // for its BN/2 output channels.
+  auto read_frags = [&](const int8_t* stage, int ks, FragT* xf, FragT* wf) {
 #pragma unroll
-    for (int i = 0; i < C::kFM; ++i)
-      xf[i] = *reinterpret_cast<const v4i*>(stage + big_lds_off(wm * C::kWM + 32 * i + frow, c));
+    for (int i = 0; i < C::kFM; ++i) xf[i] = frag(stage, wm * C::kWM + 32 * i + frow, ks);
 #pragma unroll
-    for (int j = 0; j < C::kFN; ++j)
-      wf[j] = *reinterpret_cast<const v4i*>(stage + C::kStageA + big_lds_off(wn * C::kWN + 32 * j + frow, c));
+    for (int j = 0; j < C::kFN; ++j) wf[j] = frag(stage + C::kStageA, wn * C::kWN + 32 * j + frow, ks);
   };
   auto stage_ptr = [&](int kt) { return smem + (kt & 1) * C::kStage; };
 
@@ -219,15 +239,13 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
     __builtin_amdgcn_global_load_lds((const void*)(src[i] + (int64_t)kt * kBigBK), (lds_void*)(stage + dst[i]), 16, 0,
                                      0);
   };
-  auto frag_one = [&](const int8_t* stage, int ks, int q, v4i* xf, v4i* wf) {
-    const int c = 2 * ks + fhalf;
+  auto frag_one = [&](const int8_t* stage, int ks, int q, FragT* xf, FragT* wf) {
     if (q < C::kFM)
-      xf[q] = *reinterpret_cast<const v4i*>(stage + big_lds_off(wm * C::kWM + 32 * q + frow, c));
+      xf[q] = frag(stage, wm * C::kWM + 32 * q + frow, ks);
     else
-      wf[q - C::kFM] = *reinterpret_cast<const v4i*>(
-          stage + C::kStageA + big_lds_off(wn * C::kWN + 32 * (q - C::kFM) + frow, c));
+      wf[q - C::kFM] = frag(stage + C::kStageA, wn * C::kWN + 32 * (q - C::kFM) + frow, ks);
   };
-  v4i fx[2][C::kFM], fw[2][C::kFN];
+  FragT fx[2][C::kFM], fw[2][C::kFN];
   if (nk > 1)
     wait_vmcnt<C::kDma>();
   else
@@ -238,22 +256,26 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
   for (int kt = 0; kt < nk; ++kt) {
     const int8_t* cur = stage_ptr(kt);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < kSub; ++ks) {
       const int p = ks & 1;
-      const bool trans = ks == 3 && kt + 1 < nk;
+      const bool trans = ks == kSub - 1 && kt + 1 < nk;
       const bool more_dma = trans && kt + 2 < nk;
       if (trans) {
         wait_vmcnt<0>();
         lds_barrier();
       }
-      const int8_t* nstage = ks < 3 ? cur : stage_ptr(kt + 1);
-      const int nks = ks < 3 ? ks + 1 : 0;
-      const bool do_frag = ks < 3 || trans;
+      const int8_t* nstage = ks < kSub - 1 ? cur : stage_ptr(kt + 1);
+      const int nks = ks < kSub - 1 ? ks + 1 : 0;
+      const bool do_frag = ks < kSub - 1 || trans;
 #pragma unroll
       for (int q = 0; q < kQ; ++q) {
         if (q < C::kFN * C::kFM) {
           const int j = q / C::kFM, i = q % C::kFM;
-          acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[p][j], fx[p][i], acc[j][i], 0, 0, 0);
+          if constexpr (kF8)
+            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[p][j], fx[p][i], acc[j][i], 0, 0, 0, 127, 0,
+                                                                       127);
+          else
+            acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[p][j], fx[p][i], acc[j][i], 0, 0, 0);
         }
         if (do_frag && q < C::kFM + C::kFN) frag_one(nstage, nks, q, fx[p ^ 1], fw[p ^ 1]);
         if (more_dma && q < C::kDma) dma_one(kt + 2, q);
@@ -358,8 +380,15 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
   auto out_values = [&](int j, int i, int rg, const float* ws, const float (*yo)[16], float* v, int* a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      a[e] = acc[j][i][4 * rg + e];
-      v[e] = __fmul_rn(__fmul_rn((float)a[e], xs[i]), ws[e]);
+      float av;
+      if constexpr (kF8) {
+        a[e] = 0;
+        av = acc[j][i][4 * rg + e];
+      } else {
+        a[e] = acc[j][i][4 * rg + e];
+        av = (float)a[e];
+      }
+      v[e] = __fmul_rn(__fmul_rn(av, xs[i]), ws[e]);
       if (kOut == kBigDecomp) {
         const float yi = f16_to_f32(f32_to_f16(v[e]));
         v[e] = __fadd_rn(yi, f16_to_f32(f32_to_f16(yo[i][4 * rg + e])));
@@ -461,19 +490,20 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
   }
 }
 
-template <int BN, int kOut, bool kVec>
+template <int BN, int kOut, bool kVec, bool kF8 = false>
 static void launch_big(const int8_t* xq, const int8_t* wq, int M, int N, int K, const BigEpi& ep, hipStream_t s) {
   const int tiles = ((M + kBigBM - 1) / kBigBM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_big_kernel<BN, kOut, kVec>), dim3(tiles), dim3(kBigThreads), 0, s, xq, wq, M, N, K, ep);
+  hipLaunchKernelGGL((gemm_big_kernel<BN, kOut, kVec, kF8>), dim3(tiles), dim3(kBigThreads), 0, s, xq, wq, M, N, K,
+                     ep);
 }
 
-template <int BN, int kOut>
+template <int BN, int kOut, bool kF8 = false>
 static void launch_big_v(const int8_t* xq, const int8_t* wq, int M, int N, int K, const BigEpi& ep, bool vec,
                          hipStream_t s) {
   if (vec)
-    launch_big<BN, kOut, true>(xq, wq, M, N, K, ep, s);
+    launch_big<BN, kOut, true, kF8>(xq, wq, M, N, K, ep, s);
   else
-    launch_big<BN, kOut, false>(xq, wq, M, N, K, ep, s);
+    launch_big<BN, kOut, false, kF8>(xq, wq, M, N, K, ep, s);
 }
 
 template <int BN>
@@ -485,6 +515,17 @@ static void launch_big_o(const int8_t* xq, const int8_t* wq, int M, int N, int K
     case kBigF16: launch_big_v<BN, kBigF16>(xq, wq, M, N, K, ep, vec, s); break;
     case kBigI32: launch_big_v<BN, kBigI32>(xq, wq, M, N, K, ep, vec, s); break;
     default: launch_big_v<BN, kBigDecomp>(xq, wq, M, N, K, ep, vec, s); break;
+  }
+}
+
+// E4M3 operands: floating-point outputs only
+template <int BN>
+static void launch_big_f8(const int8_t* xq, const int8_t* wq, int M, int N, int K, const BigEpi& ep, int out,
+                          bool vec, hipStream_t s) {
+  switch (out) {
+    case kBigF32: launch_big_v<BN, kBigF32, true>(xq, wq, M, N, K, ep, vec, s); break;
+    case kBigBF16: launch_big_v<BN, kBigBF16, true>(xq, wq, M, N, K, ep, vec, s); break;
+    default: launch_big_v<BN, kBigF16, true>(xq, wq, M, N, K, ep, vec, s); break;
   }
 }
 
@@ -538,6 +579,23 @@ hipError_t gemm_i8_big(const int8_t* xq, const float* x_scale, const int8_t* wq,
     sqk::launch_big_o<192>(xq, wq, M, N, K, ep, out, vec, s);
   else
     sqk::launch_big_o<256>(xq, wq, M, N, K, ep, out, vec, s);
+  return hipGetLastError();
+}
+
+hipError_t gemm_f8_big(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
+                       int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, hipStream_t s) {
+  sqk::BigEpi ep{x_scale, w_scale, y, ldy, DecompArgs{}, false};
+  const int out = yt == SQ_F32 ? sqk::kBigF32 : (yt == SQ_BF16 ? sqk::kBigBF16 : sqk::kBigF16);
+  const int eb = yt == SQ_F32 ? 4 : 2;
+  const bool vec = (ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % (uintptr_t)(4 * eb) == 0) &&
+                   reinterpret_cast<uintptr_t>(w_scale) % 16 == 0;
+  ep.rows16 = (ldy * eb) % 16 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0;
+  const int M = (int)m, N = (int)n, K = (int)k;
+  // 192-column tiles only: the E4M3 fragments are twice the int8 ones, and
+  // with 256 columns the accumulators and two fragment sets exceed the 256
+  // registers a lane has at two waves per SIMD
+  sqk::launch_big_f8<192>(reinterpret_cast<const int8_t*>(xq), reinterpret_cast<const int8_t*>(wq), M, N, K, ep, out,
+                          vec, s);
   return hipGetLastError();
 }
 

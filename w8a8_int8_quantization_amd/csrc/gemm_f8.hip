@@ -25,6 +25,8 @@
 // XOR-swizzled with (row >> 1) & 7; the next step's global loads are issued
 // before the MFMAs of the current one. Lane l supplies row l % 32 and the 32
 // k-bytes 32 * (l / 32) .. +31 of a 64-k half-step (two 16-byte chunks).
+#include <cstdlib>
+
 #include "sq_common.hpp"
 #include "sq_launch.hpp"
 
@@ -165,9 +167,19 @@ __global__ __launch_bounds__(256) void gemm_f8_kernel(const uint8_t* __restrict_
 
 namespace sqh {
 
+// SQ_F8_BIG=0 keeps prefill-sized problems on the 128 x 128 kernel (for comparisons)
+static bool f8_big_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("SQ_F8_BIG");
+    return !(e && e[0] == '0');
+  }();
+  return on;
+}
+
 hipError_t gemm_f8(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
                    int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, hipStream_t s) {
   if (m <= 0 || n <= 0) return hipSuccess;
+  if (gemm_big_suits(m, n, k) && f8_big_enabled()) return gemm_f8_big(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, s);
   const int64_t tiles = ((m + sqk::kF8BM - 1) / sqk::kF8BM) * ((n + sqk::kF8BN - 1) / sqk::kF8BN);
   const dim3 grid((unsigned)tiles), block(256);
   const int M = (int)m, N = (int)n, K = (int)k;

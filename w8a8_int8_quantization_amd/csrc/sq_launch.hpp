@@ -66,6 +66,9 @@ bool gemm_big_suits(int64_t m, int64_t n, int64_t k);
 hipError_t gemm_i8_big(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
                        int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec,
                        hipStream_t s);
+// The same kernel on E4M3 operands (binary32 accumulators); gemm_f8 routes to it when it suits.
+hipError_t gemm_f8_big(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
+                       int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, hipStream_t s);
 
 // Decode GEMM (M <= 64): split-K over workgroups, partial tiles and ticket
 // counters in the workspace. The counters must be zero at launch.
