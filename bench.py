@@ -249,8 +249,10 @@ def bench_fp8(args, dev):
     stream = torch.cuda.current_stream(dev).cuda_stream
     q_fn, g_fn = sq.raw["sq_quant_act_fp8"], sq.raw["sq_fp8_linear"]
     q_args = (x.data_ptr(), sq.SQ_BF16, c.m, c.k, c.k, xq.data_ptr(), dx.data_ptr(), stream)
+    gws = sq.fp8_linear_workspace(c.m, c.n, c.k, dev)  # split-K partials and counters (decode shapes)
+    gws_p, gws_n = (gws.data_ptr(), gws.numel()) if gws is not None else (None, 0)
     g_args = [(xq.data_ptr(), dx.data_ptr(), w_i.data_ptr(), sw.data_ptr(), c.m, c.n, c.k, y.data_ptr(), sq.SQ_BF16,
-               c.n, stream) for w_i in wqs]
+               c.n, gws_p, gws_n, stream) for w_i in wqs]
     hip = HipEvents(sq._lib, stream)
     print(f"[bench] workload {args.workload} M={c.m} K={c.k} N={c.n}", file=sys.stderr, flush=True)
 

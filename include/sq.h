@@ -319,16 +319,27 @@ sq_status sq_silu_mul_w8a8_linear(const void* gate, const void* up, sq_dtype t, 
  *            of |products| per 64-term instruction, measured)
  *   y[i][n] = out(fl32(fl32(acc_in * x_scale_i) * w_scale_n)), yt = SQ_F32,
  *   SQ_BF16 or SQ_F16. K % 128 == 0, K <= SQ_MAX_K_FP8.
+ *   ws: sq_fp8_linear_workspace_size(m, n, k) bytes, 16-byte aligned (NULL
+ *   when that is 0), with the contract of sq_w8a8_linear's workspace: for
+ *   decode shapes (M <= 64) whose K is split over several workgroups it
+ *   holds binary32 partial tiles and the ticket counters, which the caller
+ *   zero-fills once and every call leaves at zero; one call at a time per
+ *   workspace. The partial tiles are added in a fixed order (deterministic
+ *   results), each sum rounded to binary32.
  * sq_fp8_linear_dyn: sq_quant_act_fp8 then sq_fp8_linear on the same stream,
- *   with the codes and row scales in ws (sq_fp8_linear_dyn_workspace_size).
+ *   with the codes, row scales and the GEMM's workspace in ws
+ *   (sq_fp8_linear_dyn_workspace_size; no initialisation needed: the
+ *   quantisation launch clears the split-K counters).
  */
 sq_status sq_quant_act_fp8(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, uint8_t* xq,
                            float* x_scale, sq_stream_t stream);
 size_t sq_quant_weights_fp8_workspace_size(int64_t k, int64_t n);
 sq_status sq_quant_weights_fp8(const void* w, sq_dtype wt, int64_t k, int64_t n, int64_t ldw, uint8_t* wq,
                                float* w_scale, void* ws, size_t ws_bytes, sq_stream_t stream);
+size_t sq_fp8_linear_workspace_size(int64_t m, int64_t n, int64_t k);
 sq_status sq_fp8_linear(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
-                        int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, sq_stream_t stream);
+                        int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, size_t ws_bytes,
+                        sq_stream_t stream);
 size_t sq_fp8_linear_dyn_workspace_size(int64_t m, int64_t n, int64_t k);
 sq_status sq_fp8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const uint8_t* wq, const float* w_scale,
                             int64_t m, int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws,

@@ -236,12 +236,19 @@ def test_validation_fp8(sq):
     assert g(P, sq.SQ_BF16, 128, 192, 192, None, P, P, nb, None) == NULL
     assert g(P, sq.SQ_BF16, 128, 192, 196, P, P, P, nb, None) == ALIGN      # row pitch
     h = sq.raw["sq_fp8_linear"]
-    assert h(P, P, P, P, 4, 64, 192, P, sq.SQ_BF16, 64, None) == SHAPE      # K % 128
-    assert h(P, P, P, P, 4, 64, 32768 + 128, P, sq.SQ_BF16, 64, None) == RANGE
-    assert h(P, P, P, P, 4, 64, 256, P, sq.SQ_I32, 64, None) == DTYPE
-    assert h(None, P, P, P, 4, 64, 256, P, sq.SQ_BF16, 64, None) == NULL
-    assert h(P, P, P, P, 4, 64, 256, P, sq.SQ_BF16, 32, None) == SHAPE      # ldy < N
-    assert h(None, None, None, None, 0, 64, 256, None, sq.SQ_BF16, 64, None) == OK
+    nbw = sq.raw["sq_fp8_linear_workspace_size"](4, 64, 256)
+    assert nbw > 0                                                          # decode shape, K split
+    assert nbw == sq.raw["sq_w8a8_linear_workspace_size"](4, 64, 256)
+    assert sq.raw["sq_fp8_linear_workspace_size"](2048, 6144, 4096) == 0
+    assert h(P, P, P, P, 4, 64, 192, P, sq.SQ_BF16, 64, P, nbw, None) == SHAPE      # K % 128
+    assert h(P, P, P, P, 4, 64, 32768 + 128, P, sq.SQ_BF16, 64, P, nbw, None) == RANGE
+    assert h(P, P, P, P, 4, 64, 256, P, sq.SQ_I32, 64, P, nbw, None) == DTYPE
+    assert h(None, P, P, P, 4, 64, 256, P, sq.SQ_BF16, 64, P, nbw, None) == NULL
+    assert h(P, P, P, P, 4, 64, 256, P, sq.SQ_BF16, 32, P, nbw, None) == SHAPE      # ldy < N
+    assert h(P, P, P, P, 4, 64, 256, P, sq.SQ_BF16, 64, P, nbw - 1, None) == WS
+    assert h(P, P, P, P, 4, 64, 256, P, sq.SQ_BF16, 64, None, 0, None) == WS
+    assert h(P, P, P, P, 4, 64, 256, P, sq.SQ_BF16, 64, BAD, nbw, None) == ALIGN
+    assert h(None, None, None, None, 0, 64, 256, None, sq.SQ_BF16, 64, None, 0, None) == OK
     dyn = sq.raw["sq_fp8_linear_dyn"]
     nbd = sq.raw["sq_fp8_linear_dyn_workspace_size"](4, 64, 256)
     assert dyn(P, sq.SQ_BF16, 256, P, P, 4, 64, 256, P, sq.SQ_BF16, 64, P, nbd - 1, None) == WS

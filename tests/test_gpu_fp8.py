@@ -150,3 +150,54 @@ def test_fp8_linear_prefill_strided_output(pad):
     assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
     assert bool((big[:, n:] == -7.0).all())
     _check_gemm(xq, d, wq, sw, "bf16")
+
+
+# Decode shapes (M <= 64) run on the split-K decode kernel: one, two and four
+# 16-token blocks, K split over up to 16 slices or not at all (N >= 12288,
+# M > 16), ragged N.
+@pytest.mark.parametrize("m,n,k,out", [(1, 4096, 4096, "bf16"), (16, 1000, 2048, "f16"), (32, 2112, 1152, "f32"),
+                                       (64, 14336, 4096, "bf16"), (48, 200, 14336, "bf16"), (7, 64, 128, "f32")])
+def test_fp8_linear_decode(m, n, k, out):
+    log("fp8 decode gemm", m, n, k, out, "workspace bytes", sq.raw["sq_fp8_linear_workspace_size"](m, n, k))
+    c = workloads.random_linear_case(m=m, k=k, n=n, seed=5 * m + n + k, dtype="bf16", calib_rows=8)
+    xq, d = oracle.quantize_activations_fp8(c.x)
+    wq, sw = oracle.quantize_weights_fp8(c.w)
+    _check_gemm(xq, d, wq, sw, out)
+
+
+def test_fp8_linear_decode_workspace_reuse():
+    """The split-K counters are left at zero: the same workspace serves the
+    next call, at this shape and at a smaller one, with identical results."""
+    m, n, k = 8, 1024, 4096
+    assert sq.raw["sq_fp8_linear_workspace_size"](m, n, k) > 0
+    c = workloads.random_linear_case(m=m, k=k, n=n, seed=21, dtype="bf16", calib_rows=8)
+    xq, d = oracle.quantize_activations_fp8(c.x)
+    wq, sw = oracle.quantize_weights_fp8(c.w)
+    args = [torch.from_numpy(a).to(dev()) for a in (xq, d, wq, sw)]
+    ws = sq.fp8_linear_workspace(m, n, k, dev())
+    y1 = sq.sq_fp8_linear(*args, ws=ws)
+    y2 = sq.sq_fp8_linear(*args, ws=ws)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert int(ws[:256].view(torch.int32)[: (n + 63) // 64].abs().sum()) == 0
+    y3 = sq.sq_fp8_linear(args[0][:3], args[1][:3], *args[2:], ws=ws)
+    assert torch.equal(y3.view(torch.int16), y1[:3].view(torch.int16))
+    _check_gemm(xq, d, wq, sw, "bf16")
+
+
+@pytest.mark.parametrize("m", [1, 40])
+def test_fp8_linear_dyn_decode_garbage_workspace(m):
+    """The one-call path clears the split-K counters itself: a workspace full
+    of garbage gives the result of the two separate calls."""
+    n, k = 768, 2048
+    c = workloads.random_linear_case(m=m, k=k, n=n, seed=m, dtype="bf16", calib_rows=8)
+    x = to_dev(c.x, "bf16")
+    wq, sw = sq.sq_quant_weights_fp8(to_dev(c.w, "bf16"))
+    xq, d = sq.sq_quant_act_fp8(x)
+    y2 = sq.sq_fp8_linear(xq, d, wq, sw)
+    nb = sq.raw["sq_fp8_linear_dyn_workspace_size"](m, n, k)
+    assert nb > sq.raw["sq_fp8_linear_workspace_size"](m, n, k) > 0
+    ws = torch.full((nb,), 0xA7, dtype=torch.uint8, device=dev())
+    y1 = sq.sq_fp8_linear_dyn(x, wq, sw, ws=ws)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    y1b = sq.sq_fp8_linear_dyn(x, wq, sw, ws=ws)
+    assert torch.equal(y1b.view(torch.int16), y2.view(torch.int16))

@@ -22,7 +22,7 @@ __all__ = [
     "sq_w8a8_linear_dyn", "sq_outlier_detect", "sq_quant_act_rows_masked", "sq_int8_decomp_linear",
     "sq_int8_decomp_gemm", "linear_workspace", "sq_fold_norm_gain", "sq_rmsnorm_quant", "sq_rmsnorm_w8a8_linear",
     "sq_silu_mul_quant", "sq_silu_mul_w8a8_linear", "sq_quant_act_fp8", "sq_quant_weights_fp8", "sq_fp8_linear",
-    "sq_fp8_linear_dyn",
+    "sq_fp8_linear_dyn", "fp8_linear_workspace",
     "SMOOTH_COMPUTE", "SMOOTH_GIVEN", "SMOOTH_NONE", "MAX_K_INT32", "EXPORTED_SYMBOLS",
 ]
 
@@ -68,7 +68,8 @@ _SIGS = {
     "sq_quant_act_fp8": (_st, [_p, _st, _i64, _i64, _i64, _p, _p, _p]),
     "sq_quant_weights_fp8_workspace_size": (_sz, [_i64, _i64]),
     "sq_quant_weights_fp8": (_st, [_p, _st, _i64, _i64, _i64, _p, _p, _p, _sz, _p]),
-    "sq_fp8_linear": (_st, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _st, _i64, _p]),
+    "sq_fp8_linear_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "sq_fp8_linear": (_st, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _st, _i64, _p, _sz, _p]),
     "sq_fp8_linear_dyn_workspace_size": (_sz, [_i64, _i64, _i64]),
     "sq_fp8_linear_dyn": (_st, [_p, _st, _i64, _p, _p, _i64, _i64, _i64, _p, _st, _i64, _p, _sz, _p]),
     "sq_outlier_detect_workspace_size": (_sz, [_i64]),
@@ -316,15 +317,27 @@ def sq_quant_weights_fp8(w: torch.Tensor):
     return wq, w_scale
 
 
+def fp8_linear_workspace(m: int, n: int, k: int, device) -> Optional[torch.Tensor]:
+    """A zero-filled workspace for ``sq_fp8_linear`` at this shape (None if it needs none);
+    reusable across calls at the same shape."""
+    nb = raw["sq_fp8_linear_workspace_size"](m, n, k)
+    return torch.zeros(nb, dtype=torch.uint8, device=device) if nb else None
+
+
 def sq_fp8_linear(xq: torch.Tensor, x_scale: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
-                  out_dtype=torch.bfloat16, y: Optional[torch.Tensor] = None):
-    """E4M3 GEMM on the matrix cores with the per-token x per-channel dequantisation."""
+                  out_dtype=torch.bfloat16, y: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """E4M3 GEMM on the matrix cores with the per-token x per-channel dequantisation.
+
+    ``ws``: a workspace from :func:`fp8_linear_workspace`; a fresh one is allocated when None."""
     m, k, _ = _rows(xq)
     n = wq.shape[0]
     y = torch.empty((m, n), dtype=out_dtype, device=xq.device) if y is None else y
     _, _, ldy = _rows(y)
+    if ws is None:
+        ws = fp8_linear_workspace(m, n, k, xq.device)
     _check("sq_fp8_linear", raw["sq_fp8_linear"](
-        _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), m, n, k, _ptr(y), _dt(y), ldy, _stream(xq.device)))
+        _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), m, n, k, _ptr(y), _dt(y), ldy, _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(xq.device)))
     return y
 
 

@@ -362,19 +362,32 @@ static sq_status check_fp8_gemm(const uint8_t* wq, const float* w_scale, int64_t
   return SQ_OK;
 }
 
+size_t sq_fp8_linear_workspace_size(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0) return 0;
+  return sqh::gemm_decode_workspace(m, n, k);
+}
+
 sq_status sq_fp8_linear(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
-                        int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, sq_stream_t stream) {
+                        int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, size_t ws_bytes,
+                        sq_stream_t stream) {
   SQ_TRY(check_fp8_gemm(wq, w_scale, m, n, k, y, yt, ldy));
   if (m == 0 || n == 0) return SQ_OK;
   if (!xq || !x_scale) return SQ_ERR_NULL;
   if (!aligned16(xq)) return SQ_ERR_ALIGN;
-  return hip_status(sqh::gemm_f8(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, (hipStream_t)stream));
+  const size_t need = sq_fp8_linear_workspace_size(m, n, k);
+  if (need > 0 && (!ws || ws_bytes < need)) return SQ_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return SQ_ERR_ALIGN;
+  const hipStream_t s = (hipStream_t)stream;
+  // decode shapes: the workspace's split-K counters are zero on entry (the
+  // caller's contract) and restored to zero by the kernel
+  if (sqh::gemm_decode_suits(m, n, k))
+    return hip_status(sqh::gemm_f8_decode(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, ws, s));
+  return hip_status(sqh::gemm_f8(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, s));
 }
 
 size_t sq_fp8_linear_dyn_workspace_size(int64_t m, int64_t n, int64_t k) {
-  (void)n;
   if (m <= 0 || k <= 0) return 0;
-  return round_up((size_t)m * (size_t)k) + round_up((size_t)m * 4);
+  return round_up((size_t)m * (size_t)k) + round_up((size_t)m * 4) + sq_fp8_linear_workspace_size(m, n, k);
 }
 
 sq_status sq_fp8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const uint8_t* wq, const float* w_scale,
@@ -387,7 +400,17 @@ sq_status sq_fp8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const uint8
   if (!aligned16(ws)) return SQ_ERR_ALIGN;
   uint8_t* xq = reinterpret_cast<uint8_t*>(ws);
   float* dx = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + round_up((size_t)m * (size_t)k));
+  void* gws = reinterpret_cast<char*>(ws) + round_up((size_t)m * (size_t)k) + round_up((size_t)m * 4);
   const hipStream_t s = (hipStream_t)stream;
+  if (sqh::gemm_decode_suits(m, n, k)) {
+    // the quantisation launch also clears the GEMM's split-K counters
+    uint32_t* counters;
+    int64_t ncount;
+    sqh::gemm_decode_counters(m, n, k, gws, &counters, &ncount);
+    hipError_t e = sqh::quant_f8_rows(x, xt, m, k, ldx, xq, dx, s, counters, ncount);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(sqh::gemm_f8_decode(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, gws, s));
+  }
   hipError_t e = sqh::quant_f8_rows(x, xt, m, k, ldx, xq, dx, s);
   if (e != hipSuccess) return hip_status(e);
   return hip_status(sqh::gemm_f8(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, s));

@@ -32,6 +32,14 @@
 //    product bit for bit. The counters must be zero at launch; the last
 //    workgroup of a tile sets its counter back to zero, so a zeroed workspace
 //    stays zeroed from call to call.
+//  * The same kernel takes E4M3 operands (kF8): one
+//    v_mfma_scale_f32_16x16x128_f8f6f4 per 128-byte step (lane l: row l%16,
+//    the 32 bytes at k-offset 32*(l/16)), binary32 accumulators and partial
+//    tiles. The waves' tiles and the slices' partials are added in a fixed
+//    order (wave 0..3, slice 0..S-1), so results are deterministic; they
+//    differ from an unsplit product by binary32 roundings of those sums.
+#include <type_traits>
+
 #include "sq_common.hpp"
 #include "sq_launch.hpp"
 
@@ -63,6 +71,11 @@ struct DecodeArgs {
   int out;             // 0 f32, 1 bf16, 2 f16, 3 i32
 };
 
+typedef int v8i_d __attribute__((ext_vector_type(8)));
+typedef float v4f_d __attribute__((ext_vector_type(4)));
+
+// acc: int32 sums, or (kF8) the bits of binary32 sums
+template <bool kF8>
 __device__ __forceinline__ void dec_epilogue(const DecodeArgs& a, int m, int n, const int32_t* acc) {
   if (m >= a.M || n >= a.N) return;
   const int nv = min(4, a.N - n);
@@ -79,7 +92,10 @@ __device__ __forceinline__ void dec_epilogue(const DecodeArgs& a, int m, int n, 
   const float xs = a.x_scale[m];
   float v[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = e < nv ? __fmul_rn(__fmul_rn((float)acc[e], xs), a.w_scale[n + e]) : 0.f;
+  for (int e = 0; e < 4; ++e) {
+    const float av = kF8 ? __int_as_float(acc[e]) : (float)acc[e];
+    v[e] = e < nv ? __fmul_rn(__fmul_rn(av, xs), a.w_scale[n + e]) : 0.f;
+  }
   if (a.out == 0) {
     float* p = reinterpret_cast<float*>(a.y) + off;
     if (nv == 4 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
@@ -101,8 +117,9 @@ __device__ __forceinline__ void dec_epilogue(const DecodeArgs& a, int m, int n, 
   }
 }
 
-template <int kMB, int kNS>
+template <int kMB, int kNS, bool kF8>
 __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
+  using AccT = typename std::conditional<kF8, v4f_d, v4i>::type;
   constexpr int kTok = 16 * kMB;
   // steps of loads in flight: all of them when the registers allow (the
   // workgroup's whole share of Wq is requested at once); the caps are the
@@ -121,7 +138,10 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
   const int step0 = slice * a.slice_steps;
   const int nsl = min(a.slice_steps, a.K / kDecStep - step0);  // >= 1 by construction of S
 
-  const int kb = 16 * (lane >> 4);
+  // the lane's k bytes of a step: int8, [kb, kb+16) and [64+kb, 64+kb+16);
+  // E4M3, [kb, kb+32)
+  const int kb = (kF8 ? 32 : 16) * (lane >> 4);
+  constexpr int kHalf = kF8 ? 16 : 64;
   const int8_t* wp[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) wp[g] = a.wq + (int64_t)min(n0 + 16 * g + (lane & 15), a.N - 1) * a.K + kb;
@@ -129,11 +149,11 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) xp[mb] = a.xq + (int64_t)min(16 * mb + (lane & 15), a.M - 1) * a.K + kb;
 
-  v4i acc[4][kMB];
+  AccT acc[4][kMB];
 #pragma unroll
   for (int g = 0; g < 4; ++g)
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) acc[g][mb] = v4i{0, 0, 0, 0};
+    for (int mb = 0; mb < kMB; ++mb) acc[g][mb] = AccT{0, 0, 0, 0};
 
   u32x4 wb[kDepth][4][2];
   u32x4 xb[kDepth][kMB][2];
@@ -144,12 +164,12 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       wb[slot][g][0] = load16(wp[g] + off);
-      wb[slot][g][1] = load16(wp[g] + off + 64);
+      wb[slot][g][1] = load16(wp[g] + off + kHalf);
     }
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
       xb[slot][mb][0] = load16(xp[mb] + off);
-      xb[slot][mb][1] = load16(xp[mb] + off + 64);
+      xb[slot][mb][1] = load16(xp[mb] + off + kHalf);
     }
   };
 #pragma unroll
@@ -179,14 +199,26 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
       x[mb][0] = valid ? x[mb][0] : u32x4{0u, 0u, 0u, 0u};
       x[mb][1] = valid ? x[mb][1] : u32x4{0u, 0u, 0u, 0u};
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
+    if constexpr (kF8) {
+      auto cat = [](const u32x4& lo, const u32x4& hi) {
+        return v8i_d{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      };
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
-          acc[g][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, w[g][h]),
-                                                             __builtin_bit_cast(v4i, x[mb][h]), acc[g][mb], 0, 0, 0);
+          acc[g][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cat(w[g][0], w[g][1]), cat(x[mb][0], x[mb][1]),
+                                                                        acc[g][mb], 0, 0, 0, 127, 0, 127);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb)
+            acc[g][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, w[g][h]),
+                                                               __builtin_bit_cast(v4i, x[mb][h]), acc[g][mb], 0, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -200,7 +232,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
     for (int mb = 0; mb < kMB; ++mb) {
       const int tok = 16 * mb + (lane & 15);
       const int quad = (4 * g + (lane >> 4)) ^ (tok & 15);
-      *reinterpret_cast<v4i*>(&red[wid][tok][4 * quad]) = acc[g][mb];
+      *reinterpret_cast<v4i*>(&red[wid][tok][4 * quad]) = __builtin_bit_cast(v4i, acc[g][mb]);
     }
   __syncthreads();
 
@@ -210,15 +242,16 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
   for (int j = 0; j < kMB; ++j) {
     const int tok = (tid >> 4) + 16 * j;
     const int sq = q ^ (tok & 15);
-    v4i s = *reinterpret_cast<const v4i*>(&red[0][tok][4 * sq]);
+    AccT s = __builtin_bit_cast(AccT, *reinterpret_cast<const v4i*>(&red[0][tok][4 * sq]));
 #pragma unroll
-    for (int w = 1; w < kDecWaves; ++w) s += *reinterpret_cast<const v4i*>(&red[w][tok][4 * sq]);
-    sum[j][0] = s[0]; sum[j][1] = s[1]; sum[j][2] = s[2]; sum[j][3] = s[3];
+    for (int w = 1; w < kDecWaves; ++w) s += __builtin_bit_cast(AccT, *reinterpret_cast<const v4i*>(&red[w][tok][4 * sq]));
+    const v4i sb = __builtin_bit_cast(v4i, s);
+    sum[j][0] = sb[0]; sum[j][1] = sb[1]; sum[j][2] = sb[2]; sum[j][3] = sb[3];
   }
   const int n = n0 + 4 * q;
   if (a.S == 1) {
 #pragma unroll
-    for (int j = 0; j < kMB; ++j) dec_epilogue(a, (tid >> 4) + 16 * j, n, sum[j]);
+    for (int j = 0; j < kMB; ++j) dec_epilogue<kF8>(a, (tid >> 4) + 16 * j, n, sum[j]);
     return;
   }
 
@@ -258,7 +291,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
   for (int j = 0; j < kMB; ++j) {
     const int m = (tid >> 4) + 16 * j;
     if (m >= a.M || n >= a.N) continue;
-    v4i t = {0, 0, 0, 0};
+    AccT t = {0, 0, 0, 0};
     const uint32_t off0 = (uint32_t)(((size_t)m * a.N + n) * 4);
     const uint32_t sstride = (uint32_t)((size_t)a.M * a.N * 4);
     if (vec) {
@@ -270,16 +303,24 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
         for (int u = 0; u < 8; ++u)
           part[u] = __builtin_amdgcn_raw_buffer_load_b128(pr, off0 + (uint32_t)(s + u) * sstride, 0, kCoherent);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) t += part[u];
+        for (int u = 0; u < 8; ++u)
+          if (!kF8 || s + u < a.S) t += __builtin_bit_cast(AccT, part[u]);
       }
     } else {
       for (int s = 0; s < a.S; ++s)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (n + e < a.N) t[e] += __builtin_amdgcn_raw_buffer_load_b32(pr, off0 + s * sstride + 4 * e, 0, kCoherent);
+          if (n + e < a.N) {
+            const int32_t pv = __builtin_amdgcn_raw_buffer_load_b32(pr, off0 + s * sstride + 4 * e, 0, kCoherent);
+            if constexpr (kF8)
+              t[e] += __int_as_float(pv);
+            else
+              t[e] += pv;
+          }
     }
-    const int32_t tt[4] = {t[0], t[1], t[2], t[3]};
-    dec_epilogue(a, m, n, tt);
+    const v4i tb = __builtin_bit_cast(v4i, t);
+    const int32_t tt[4] = {tb[0], tb[1], tb[2], tb[3]};
+    dec_epilogue<kF8>(a, m, n, tt);
   }
   // every ticket of this tile has been drawn: restore the counter for the next call
   if (tid == 0) __hip_atomic_store(a.counter + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -326,19 +367,43 @@ DecodePlan decode_plan(int64_t m, int64_t n, int64_t k) {
 
 size_t counter_bytes(int tiles) { return ((size_t)tiles * 4 + 255) / 256 * 256; }
 
-template <int kMB>
+template <int kMB, bool kF8>
 hipError_t launch_decode(const sqk::DecodeArgs& a, int ns, dim3 grid, hipStream_t s) {
   switch (ns) {
-    case 1: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 2>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 3>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 4>), grid, dim3(256), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 5>), grid, dim3(256), 0, s, a); break;
-    case 6: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 6>), grid, dim3(256), 0, s, a); break;
-    case 7: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 7>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 8>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 1, kF8>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 2, kF8>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 3, kF8>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 4, kF8>), grid, dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 5, kF8>), grid, dim3(256), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 6, kF8>), grid, dim3(256), 0, s, a); break;
+    case 7: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 7, kF8>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((sqk::gemm_decode_kernel<kMB, 8, kF8>), grid, dim3(256), 0, s, a); break;
   }
   return hipGetLastError();
+}
+
+template <bool kF8>
+hipError_t decode_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
+                       int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, hipStream_t s) {
+  const DecodePlan p = decode_plan(m, n, k);
+  sqk::DecodeArgs a{};
+  a.xq = xq; a.wq = wq; a.x_scale = x_scale; a.w_scale = w_scale; a.y = y; a.ldy = ldy;
+  a.M = (int)m; a.N = (int)n; a.K = (int)k;
+  a.S = p.S;
+  a.slice_steps = p.slice_steps;
+  a.out = yt == SQ_F32 ? 0 : yt == SQ_BF16 ? 1 : yt == SQ_F16 ? 2 : 3;
+  if (p.S > 1) {
+    a.counter = reinterpret_cast<uint32_t*>(ws);
+    a.partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + counter_bytes(p.tiles));
+  }
+  const dim3 grid((unsigned)p.tiles, (unsigned)p.S);
+  bool mb1 = m <= 16;
+#ifdef SQ_TUNE
+  if (getenv("SQ_DECODE_MB2")) mb1 = false;
+#endif
+  if (mb1) return launch_decode<1, kF8>(a, p.ns, grid, s);
+  if (m <= 32) return launch_decode<2, kF8>(a, p.ns, grid, s);
+  return launch_decode<4, kF8>(a, p.ns, grid, s);
 }
 
 }  // namespace
@@ -366,25 +431,13 @@ void gemm_decode_counters(int64_t m, int64_t n, int64_t k, void* ws, uint32_t** 
 
 hipError_t gemm_i8_decode(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
                           int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, hipStream_t s) {
-  const DecodePlan p = decode_plan(m, n, k);
-  sqk::DecodeArgs a{};
-  a.xq = xq; a.wq = wq; a.x_scale = x_scale; a.w_scale = w_scale; a.y = y; a.ldy = ldy;
-  a.M = (int)m; a.N = (int)n; a.K = (int)k;
-  a.S = p.S;
-  a.slice_steps = p.slice_steps;
-  a.out = yt == SQ_F32 ? 0 : yt == SQ_BF16 ? 1 : yt == SQ_F16 ? 2 : 3;
-  if (p.S > 1) {
-    a.counter = reinterpret_cast<uint32_t*>(ws);
-    a.partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + counter_bytes(p.tiles));
-  }
-  const dim3 grid((unsigned)p.tiles, (unsigned)p.S);
-  bool mb1 = m <= 16;
-#ifdef SQ_TUNE
-  if (getenv("SQ_DECODE_MB2")) mb1 = false;
-#endif
-  if (mb1) return launch_decode<1>(a, p.ns, grid, s);
-  if (m <= 32) return launch_decode<2>(a, p.ns, grid, s);
-  return launch_decode<4>(a, p.ns, grid, s);
+  return decode_gemm<false>(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, ws, s);
+}
+
+hipError_t gemm_f8_decode(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
+                          int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, hipStream_t s) {
+  return decode_gemm<true>(reinterpret_cast<const int8_t*>(xq), x_scale, reinterpret_cast<const int8_t*>(wq), w_scale,
+                           m, n, k, y, yt, ldy, ws, s);
 }
 
 }  // namespace sqh

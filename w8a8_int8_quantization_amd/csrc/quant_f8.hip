@@ -32,7 +32,8 @@ __device__ __forceinline__ uint32_t f8x4(float a, float b, float c, float d) {
 template <class In, int kCh, int kT>
 __global__ __launch_bounds__(kT) void quant_f8_rows_kernel(const uint8_t* __restrict__ x, int64_t m, int nvec,
                                                            int64_t ldx_bytes, uint8_t* __restrict__ xq,
-                                                           float* __restrict__ x_scale) {
+                                                           float* __restrict__ x_scale, uint32_t* __restrict__ zero,
+                                                           int nzero) {
   constexpr int V = In::kVec;
   constexpr int kW = kT / 64;
   __shared__ uint32_t red[kW];
@@ -40,6 +41,8 @@ __global__ __launch_bounds__(kT) void quant_f8_rows_kernel(const uint8_t* __rest
   const int lane = tid & 63;
   const int wid = tid >> 6;
   const int64_t k = (int64_t)nvec * V;
+  if (blockIdx.x == 0)
+    for (int i = tid; i < nzero; i += kT) zero[i] = 0u;
   for (int64_t row = blockIdx.x; row < m; row += gridDim.x) {
     const uint8_t* xr = x + row * ldx_bytes;
     float f[kCh][V];
@@ -121,37 +124,39 @@ namespace sqh {
 
 template <class In, int kCh, int kT>
 static void launch_f8_rows(const void* x, int64_t m, int64_t nvec, int64_t ldb, uint8_t* xq, float* x_scale,
-                           hipStream_t s) {
+                           hipStream_t s, uint32_t* zero, int nzero) {
   const int64_t grid = m < 1024 ? m : 1024;
   hipLaunchKernelGGL((sqk::quant_f8_rows_kernel<In, kCh, kT>), dim3((unsigned)grid), dim3(kT), 0, s,
-                     (const uint8_t*)x, m, (int)nvec, ldb, xq, x_scale);
+                     (const uint8_t*)x, m, (int)nvec, ldb, xq, x_scale, zero, nzero);
 }
 
 template <class In>
-static void quant_f8_t(const void* x, int64_t m, int64_t k, int64_t ldx, uint8_t* xq, float* x_scale, hipStream_t s) {
+static void quant_f8_t(const void* x, int64_t m, int64_t k, int64_t ldx, uint8_t* xq, float* x_scale, hipStream_t s,
+                       uint32_t* zero, int nzero) {
   const int64_t nvec = k / In::kVec;
   const int64_t ldb = ldx * In::kBytes;
   const int64_t per_thread = (nvec + 255) / 256;
   if ((m < 1024 && nvec > 256) || per_thread > 4) {
     const int64_t pt = (nvec + 1023) / 1024;
-    if (pt <= 1) launch_f8_rows<In, 1, 1024>(x, m, nvec, ldb, xq, x_scale, s);
-    else if (pt <= 2) launch_f8_rows<In, 2, 1024>(x, m, nvec, ldb, xq, x_scale, s);
-    else if (pt <= 4) launch_f8_rows<In, 4, 1024>(x, m, nvec, ldb, xq, x_scale, s);
-    else launch_f8_rows<In, 8, 1024>(x, m, nvec, ldb, xq, x_scale, s);
+    if (pt <= 1) launch_f8_rows<In, 1, 1024>(x, m, nvec, ldb, xq, x_scale, s, zero, nzero);
+    else if (pt <= 2) launch_f8_rows<In, 2, 1024>(x, m, nvec, ldb, xq, x_scale, s, zero, nzero);
+    else if (pt <= 4) launch_f8_rows<In, 4, 1024>(x, m, nvec, ldb, xq, x_scale, s, zero, nzero);
+    else launch_f8_rows<In, 8, 1024>(x, m, nvec, ldb, xq, x_scale, s, zero, nzero);
     return;
   }
-  if (per_thread <= 1) launch_f8_rows<In, 1, 256>(x, m, nvec, ldb, xq, x_scale, s);
-  else if (per_thread <= 2) launch_f8_rows<In, 2, 256>(x, m, nvec, ldb, xq, x_scale, s);
-  else launch_f8_rows<In, 4, 256>(x, m, nvec, ldb, xq, x_scale, s);
+  if (per_thread <= 1) launch_f8_rows<In, 1, 256>(x, m, nvec, ldb, xq, x_scale, s, zero, nzero);
+  else if (per_thread <= 2) launch_f8_rows<In, 2, 256>(x, m, nvec, ldb, xq, x_scale, s, zero, nzero);
+  else launch_f8_rows<In, 4, 256>(x, m, nvec, ldb, xq, x_scale, s, zero, nzero);
 }
 
 hipError_t quant_f8_rows(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, uint8_t* xq, float* x_scale,
-                         hipStream_t s) {
+                         hipStream_t s, uint32_t* zero, int64_t nzero) {
   if (m <= 0) return hipSuccess;
+  const int nz = (int)nzero;
   switch (xt) {
-    case SQ_F32: quant_f8_t<sqk::F32In>(x, m, k, ldx, xq, x_scale, s); break;
-    case SQ_BF16: quant_f8_t<sqk::BF16In>(x, m, k, ldx, xq, x_scale, s); break;
-    default: quant_f8_t<sqk::F16In>(x, m, k, ldx, xq, x_scale, s); break;
+    case SQ_F32: quant_f8_t<sqk::F32In>(x, m, k, ldx, xq, x_scale, s, zero, nz); break;
+    case SQ_BF16: quant_f8_t<sqk::BF16In>(x, m, k, ldx, xq, x_scale, s, zero, nz); break;
+    default: quant_f8_t<sqk::F16In>(x, m, k, ldx, xq, x_scale, s, zero, nz); break;
   }
   return hipGetLastError();
 }

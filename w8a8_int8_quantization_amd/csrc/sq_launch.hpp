@@ -50,8 +50,9 @@ hipError_t silu_quant(const void* gate, const void* up, int64_t m, int64_t k, in
                       int64_t nzero = 0);
 
 // FP8 (E4M3) quantisers and GEMM.
+// zero[0 .. nzero-1] are cleared on the way (the decode GEMM's split-K counters).
 hipError_t quant_f8_rows(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, uint8_t* xq, float* x_scale,
-                         hipStream_t s);
+                         hipStream_t s, uint32_t* zero = nullptr, int64_t nzero = 0);
 hipError_t quant_f8_weights(const void* w, sq_dtype wt, int64_t k, int64_t n, int64_t ldw, float* colmax,
                             uint8_t* wq, float* w_scale, hipStream_t s);
 hipError_t gemm_f8(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
@@ -76,6 +77,9 @@ bool gemm_decode_suits(int64_t m, int64_t n, int64_t k);
 size_t gemm_decode_workspace(int64_t m, int64_t n, int64_t k);
 void gemm_decode_counters(int64_t m, int64_t n, int64_t k, void* ws, uint32_t** counters, int64_t* count);
 hipError_t gemm_i8_decode(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
+                          int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, hipStream_t s);
+// The same decode GEMM on E4M3 operands (binary32 partial tiles in the same workspace layout).
+hipError_t gemm_f8_decode(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
                           int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, hipStream_t s);
 
 }  // namespace sqh
