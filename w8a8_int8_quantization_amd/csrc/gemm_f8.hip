@@ -167,13 +167,18 @@ __global__ __launch_bounds__(256) void gemm_f8_kernel(const uint8_t* __restrict_
 
 namespace sqh {
 
-// SQ_F8_BIG=0 keeps prefill-sized problems on the 128 x 128 kernel (for comparisons)
+// Tuning builds (-DSQ_TUNE) only: SQ_F8_BIG=0 keeps prefill-sized problems on
+// the 128 x 128 kernel, for comparisons.
 static bool f8_big_enabled() {
+#ifdef SQ_TUNE
   static const bool on = [] {
     const char* e = getenv("SQ_F8_BIG");
     return !(e && e[0] == '0');
   }();
   return on;
+#else
+  return true;
+#endif
 }
 
 hipError_t gemm_f8(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
