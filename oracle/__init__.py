@@ -1,6 +1,6 @@
 """CPU oracle for the SmoothQuant W8A8 linear layer, the RMSNorm that carries its
-smoothing factor, the gated activation feeding the down projection, the FP8 (E4M3)
-variant and the LLM.int8() variant.
+smoothing factor, the gated activation feeding the down projection, GPTQ weight
+rounding, the FP8 (E4M3) variant and the LLM.int8() variant.
 
 TEST INFRASTRUCTURE ONLY. This package is the plain, slow, obviously correct
 definition of what the HIP path computes; it exists to check that path. Only
@@ -34,6 +34,7 @@ from .rmsnorm import fold_norm_gain, rms_inverse, apply_gain, rmsnorm, rmsnorm_q
 from .silu import exp32, silu32, gated_activation, silu_mul_quantize
 from .fp8 import (e4m3_values, e4m3_encode, e4m3_decode, quantize_activations_fp8, quantize_weights_fp8,
                   fp8_matmul, fp8_linear)
+from .gptq import GPTQ_DAMP, gptq_hessian, gptq_quantize, gptq_smooth_quantize
 
 __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "round_bf16", "round_f16", "round_to",
@@ -44,4 +45,5 @@ __all__ = [
     "fp16_outlier_product", "int8_decomp_linear", "fold_norm_gain", "rms_inverse", "apply_gain", "rmsnorm",
     "rmsnorm_quantize", "exp32", "silu32", "gated_activation", "silu_mul_quantize", "e4m3_values", "e4m3_encode",
     "e4m3_decode", "quantize_activations_fp8", "quantize_weights_fp8", "fp8_matmul", "fp8_linear",
+    "GPTQ_DAMP", "gptq_hessian", "gptq_quantize", "gptq_smooth_quantize",
 ]

@@ -20,6 +20,7 @@ from tests import oracle_pins
 o_rms = importlib.import_module("oracle.rmsnorm")
 o_silu = importlib.import_module("oracle.silu")
 o_fp8 = importlib.import_module("oracle.fp8")
+o_gptq = importlib.import_module("oracle.gptq")
 
 F32 = np.float32
 
@@ -296,6 +297,67 @@ def _fp8_w_scale_per_row(w):
     return np.ascontiguousarray(codes.T), np.resize(s, w.shape[1]).astype(F32)
 
 
+def _gptq_variant(sign=1.0, divide=True, factor="upper_inverse", damp=True, reach=None, half_away=False,
+                  error_from_original=False):
+    """gptq_quantize with one mistake: the update's sign, the division by U_jj,
+    the factor used (lower Cholesky of H, or of H^-1), no damping, errors
+    passed only ``reach`` weights on, ties rounded away from zero, or the
+    error measured against the original rather than the compensated weight."""
+    def f(w_folded, h, damp_frac=0.01, trace=False):
+        w = np.asarray(w_folded, dtype=F32).astype(np.float64)
+        w0 = w.copy()
+        k, n = w.shape
+        h = np.array(h, dtype=np.float64, copy=True)
+        dead = np.diag(h) == 0
+        h[dead, dead] = 1.0
+        w[dead, :] = 0.0
+        sw = (np.abs(w.astype(F32)).max(axis=0).astype(F32) / F32(127)).astype(F32)
+        sw64 = sw.astype(np.float64)
+        if damp:
+            h[np.diag_indices(k)] += damp_frac * np.mean(np.diag(h))
+        if factor == "upper_inverse":
+            u = np.linalg.cholesky(np.linalg.inv(h)).T
+        elif factor == "lower_inverse":
+            u = np.linalg.cholesky(np.linalg.inv(h))
+        else:
+            u = np.linalg.cholesky(h).T
+        codes = np.zeros((k, n), np.int8)
+        z = np.zeros((k, n))
+        for j in range(k):
+            wj = w[j].copy()
+            z[j] = wj
+            with np.errstate(all="ignore"):
+                r = wj / sw64
+                q = np.sign(r) * np.floor(np.abs(r) + 0.5) if half_away else np.rint(r)
+                q = np.where(sw64 > 0, np.clip(q, -127, 127), 0.0)
+            codes[j] = q.astype(np.int8)
+            base = w0[j] if error_from_original else wj
+            err = (base - q * sw64) / (u[j, j] if divide else 1.0)
+            end = k if reach is None else min(k, j + 1 + reach)
+            w[j + 1:end] -= sign * np.outer(u[j, j + 1:end], err)
+        out = (np.ascontiguousarray(codes.T), sw)
+        return out + (z,) if trace else out
+    return f
+
+
+def _gptq_hessian_unsmoothed(x_cal, s=None):
+    x = np.asarray(x_cal, F32).astype(np.float64)
+    return x.T @ x
+
+
+def _gptq_hessian_times_s(x_cal, s=None):
+    x = np.asarray(x_cal, F32)
+    if s is not None:
+        x = (x * np.asarray(s, F32)[None, :]).astype(F32)
+    x = x.astype(np.float64)
+    return x.T @ x
+
+
+def _gptq_hessian_rows(x_cal, s=None):
+    x = o_sq.smooth_activations(x_cal, s).astype(np.float64)
+    return x @ x.T
+
+
 MUTANTS = {
     "s_exponents_swapped": (o_sq, "smoothing_factors", _smooth_swapped),
     "s_product_not_quotient": (o_sq, "smoothing_factors", _smooth_product),
@@ -338,6 +400,17 @@ MUTANTS = {
     "e4m3_truncates": (o_fp8, "e4m3_encode", _e4m3_truncate),
     "fp8_act_scale_127": (o_fp8, "quantize_activations_fp8", _fp8_act_scale_127),
     "fp8_weight_scale_per_row": (o_fp8, "quantize_weights_fp8", _fp8_w_scale_per_row),
+    "gptq_update_sign": (o_gptq, "gptq_quantize", _gptq_variant(sign=-1.0)),
+    "gptq_no_division_by_ujj": (o_gptq, "gptq_quantize", _gptq_variant(divide=False)),
+    "gptq_cholesky_of_h": (o_gptq, "gptq_quantize", _gptq_variant(factor="upper_h")),
+    "gptq_lower_factor": (o_gptq, "gptq_quantize", _gptq_variant(factor="lower_inverse")),
+    "gptq_no_damping": (o_gptq, "gptq_quantize", _gptq_variant(damp=False)),
+    "gptq_error_to_next_only": (o_gptq, "gptq_quantize", _gptq_variant(reach=1)),
+    "gptq_round_half_away": (o_gptq, "gptq_quantize", _gptq_variant(half_away=True)),
+    "gptq_error_from_original_weight": (o_gptq, "gptq_quantize", _gptq_variant(error_from_original=True)),
+    "gptq_hessian_unsmoothed": (o_gptq, "gptq_hessian", _gptq_hessian_unsmoothed),
+    "gptq_hessian_multiplies_s": (o_gptq, "gptq_hessian", _gptq_hessian_times_s),
+    "gptq_hessian_over_tokens": (o_gptq, "gptq_hessian", _gptq_hessian_rows),
 }
 
 
@@ -347,7 +420,7 @@ def _plant(monkeypatch, module, name, fn):
     if hasattr(oracle, name):
         monkeypatch.setattr(oracle, name, fn)
     # functions re-exported through another submodule's namespace
-    for mod in (o_sq, o_int8, o_num, o_rms, o_silu, o_fp8):
+    for mod in (o_sq, o_int8, o_num, o_rms, o_silu, o_fp8, o_gptq):
         if mod is not module and name in mod.__dict__:
             monkeypatch.setitem(mod.__dict__, name, fn)
 
