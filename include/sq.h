@@ -77,6 +77,8 @@ typedef enum sq_dtype {
 #define SQ_MAX_K_SILU 32768
 /* Longest K of the FP8 entry points (their quantiser keeps rows in registers). */
 #define SQ_MAX_K_FP8 32768
+/* Largest K of the GPTQ calls (the K x K binary64 Hessian and its factor). */
+#define SQ_MAX_K_GPTQ 32768
 
 /* Flags of sq_smooth_fold_weights. */
 #define SQ_SMOOTH_COMPUTE 0u /* compute s from absmax and W, write it to `smooth` */
@@ -344,6 +346,49 @@ size_t sq_fp8_linear_dyn_workspace_size(int64_t m, int64_t n, int64_t k);
 sq_status sq_fp8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const uint8_t* wq, const float* w_scale,
                             int64_t m, int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws,
                             size_t ws_bytes, sq_stream_t stream);
+
+/*
+ * GPTQ weight rounding, the weight half of the pages' compression pipeline,
+ * run once at load time in place of round-to-nearest.
+ * [W8A8] "How GPTQ improves on naive quantization" (quantise one weight,
+ * measure its error, spread it over the weights not yet quantised as the
+ * Hessian of the calibration activations directs); "How the smoothing
+ * factor is computed" (it starts from the smoothed weights); the GPTQ paper
+ * cited there (input order, damping by 1% of the mean diagonal).
+ *
+ * sq_gptq_hessian:   h[a][b] += sum_t xh_ta * xh_tb,  xh = fl32(x / s_j)
+ *   (x itself when smooth == NULL), in binary64. Call it once per batch of
+ *   calibration rows; the caller zero-fills h once before the first call.
+ *   x: [T x ldx] SQ_F32, SQ_BF16 or SQ_F16, element-aligned. smooth: [K] or
+ *   NULL. h: [K x K] binary64, row-major, 8-byte aligned, written whole and
+ *   symmetric. K % 128 == 0 and K <= SQ_MAX_K_GPTQ (SQ_ERR_SHAPE /
+ *   SQ_ERR_RANGE otherwise).
+ *
+ * sq_gptq_quantize: from h and the weights W [K x N] (row j = input j):
+ *   W'_jn = fl32(s_j * W_jn) (W itself when smooth == NULL); inputs with
+ *   h_jj == 0 are dead: W'_j = 0 and h_jj taken as 1;
+ *   sw_n  = fl32(max_j |W'_jn| / 127), as sq_smooth_fold_weights;
+ *   lambda = damp * mean_j h_jj, added to the diagonal;
+ *   for j = 0 .. K-1, every n:  q_jn = clamp(round_half_even(z_jn / sw_n), -127, 127)
+ *   where z_jn is W'_jn plus the errors of the earlier inputs of channel n
+ *   passed on through the damped h (the GPTQ update), all in binary64.
+ *   Only the lower triangle of h (row >= column) is read. The result is
+ *   deterministic; it equals a sequential binary64 GPTQ except where a
+ *   quotient lies within rounding of a half-integer.
+ *   w: [K x ldw] SQ_F32, SQ_BF16 or SQ_F16, element-aligned. damp: in
+ *   (0, 1] (SQ_ERR_RANGE otherwise; 0.01 is the usual value). wq: [N x K]
+ *   int8 output (transposed, like sq_smooth_fold_weights), 16-byte aligned.
+ *   w_scale: [N] binary32 output. ws: sq_gptq_quantize_workspace_size(k, n)
+ *   bytes, 16-byte aligned, no initialisation needed (it holds the K x K
+ *   factor, W' and the running corrections: 12 K N + 8 K^2 bytes and a
+ *   little more). About 3 K/64 + 4 launches.
+ */
+sq_status sq_gptq_hessian(const void* x, sq_dtype xt, int64_t t, int64_t k, int64_t ldx, const float* smooth,
+                          double* h, sq_stream_t stream);
+size_t sq_gptq_quantize_workspace_size(int64_t k, int64_t n);
+sq_status sq_gptq_quantize(const double* h, const void* w, sq_dtype wt, int64_t k, int64_t n, int64_t ldw,
+                           const float* smooth, float damp, int8_t* wq, float* w_scale, void* ws, size_t ws_bytes,
+                           sq_stream_t stream);
 
 /*
  * LLM.int8() outlier detection over the feature columns of X.

@@ -252,3 +252,28 @@ def test_validation_fp8(sq):
     dyn = sq.raw["sq_fp8_linear_dyn"]
     nbd = sq.raw["sq_fp8_linear_dyn_workspace_size"](4, 64, 256)
     assert dyn(P, sq.SQ_BF16, 256, P, P, 4, 64, 256, P, sq.SQ_BF16, 64, P, nbd - 1, None) == WS
+
+
+def test_validation_gptq(sq):
+    f = sq.raw["sq_gptq_hessian"]
+    assert f(P, sq.SQ_BF16, 16, 192, 192, None, P, None) == SHAPE            # K % 128
+    assert f(P, sq.SQ_BF16, 16, 32768 + 128, 32768 + 128, None, P, None) == RANGE
+    assert f(P, sq.SQ_I8, 16, 128, 128, None, P, None) == DTYPE
+    assert f(P, sq.SQ_BF16, 16, 128, 100, None, P, None) == SHAPE            # ldx < K
+    assert f(P, sq.SQ_BF16, 16, 128, 128, None, None, None) == NULL
+    assert f(P, sq.SQ_BF16, 16, 128, 128, None, P + 4, None) == ALIGN        # h not 8-byte aligned
+    assert f(None, sq.SQ_BF16, 0, 128, 128, None, None, None) == OK          # no rows: nothing to do
+    g = sq.raw["sq_gptq_quantize"]
+    nb = sq.raw["sq_gptq_quantize_workspace_size"](256, 96)
+    assert nb >= 256 * 256 * 8 + 12 * 256 * 96
+    assert sq.raw["sq_gptq_quantize_workspace_size"](0, 96) == 0
+    assert g(P, P, sq.SQ_BF16, 192, 96, 96, None, 0.01, P, P, P, nb, None) == SHAPE      # K % 128
+    assert g(P, P, sq.SQ_BF16, 256, 96, 64, None, 0.01, P, P, P, nb, None) == SHAPE      # ldw < N
+    assert g(P, P, sq.SQ_BF16, 256, 96, 96, None, 0.0, P, P, P, nb, None) == RANGE       # damp
+    assert g(P, P, sq.SQ_BF16, 256, 96, 96, None, 1.5, P, P, P, nb, None) == RANGE
+    assert g(P, P, sq.SQ_I32, 256, 96, 96, None, 0.01, P, P, P, nb, None) == DTYPE
+    assert g(None, P, sq.SQ_BF16, 256, 96, 96, None, 0.01, P, P, P, nb, None) == NULL
+    assert g(P, P, sq.SQ_BF16, 256, 96, 96, None, 0.01, BAD, P, P, nb, None) == ALIGN    # wq 16-byte
+    assert g(P, P, sq.SQ_BF16, 256, 96, 96, None, 0.01, P, P, P, nb - 1, None) == WS
+    assert g(P, P, sq.SQ_BF16, 256, 96, 96, None, 0.01, P, P, BAD, nb, None) == ALIGN
+    assert g(None, None, sq.SQ_BF16, 256, 0, 0, None, 0.01, None, None, None, 0, None) == OK

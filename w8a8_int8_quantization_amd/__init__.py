@@ -22,7 +22,7 @@ __all__ = [
     "sq_w8a8_linear_dyn", "sq_outlier_detect", "sq_quant_act_rows_masked", "sq_int8_decomp_linear",
     "sq_int8_decomp_gemm", "linear_workspace", "sq_fold_norm_gain", "sq_rmsnorm_quant", "sq_rmsnorm_w8a8_linear",
     "sq_silu_mul_quant", "sq_silu_mul_w8a8_linear", "sq_quant_act_fp8", "sq_quant_weights_fp8", "sq_fp8_linear",
-    "sq_fp8_linear_dyn", "fp8_linear_workspace",
+    "sq_fp8_linear_dyn", "fp8_linear_workspace", "sq_gptq_hessian", "sq_gptq_quantize", "MAX_K_GPTQ",
     "SMOOTH_COMPUTE", "SMOOTH_GIVEN", "SMOOTH_NONE", "MAX_K_INT32", "EXPORTED_SYMBOLS",
 ]
 
@@ -39,6 +39,7 @@ _lib = ctypes.CDLL(lib_path)
 SQ_F32, SQ_BF16, SQ_F16, SQ_I32, SQ_I8 = 0, 1, 2, 3, 4
 SMOOTH_COMPUTE, SMOOTH_GIVEN, SMOOTH_NONE = 0, 1, 2
 MAX_K_INT32 = 133144
+MAX_K_GPTQ = 32768
 
 _i64, _u32, _sz, _p, _f, _d = ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float, \
     ctypes.c_double
@@ -71,6 +72,9 @@ _SIGS = {
     "sq_fp8_linear_workspace_size": (_sz, [_i64, _i64, _i64]),
     "sq_fp8_linear": (_st, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _st, _i64, _p, _sz, _p]),
     "sq_fp8_linear_dyn_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "sq_gptq_hessian": (_st, [_p, _st, _i64, _i64, _i64, _p, _p, _p]),
+    "sq_gptq_quantize_workspace_size": (_sz, [_i64, _i64]),
+    "sq_gptq_quantize": (_st, [_p, _p, _st, _i64, _i64, _i64, _p, _f, _p, _p, _p, _sz, _p]),
     "sq_fp8_linear_dyn": (_st, [_p, _st, _i64, _p, _p, _i64, _i64, _i64, _p, _st, _i64, _p, _sz, _p]),
     "sq_outlier_detect_workspace_size": (_sz, [_i64]),
     "sq_outlier_detect": (_st, [_p, _st, _i64, _i64, _i64, _f, _p, _p, _p, _p, _sz, _p]),
@@ -355,6 +359,31 @@ def sq_fp8_linear_dyn(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, 
         _ptr(x), _dt(x), ldx, _ptr(wq), _ptr(w_scale), m, n, k, _ptr(y), _dt(y), ldy, _ptr(ws),
         ws.numel() if ws is not None else 0, _stream(x.device)))
     return y
+
+
+def sq_gptq_hessian(x: torch.Tensor, smooth: Optional[torch.Tensor] = None, h: Optional[torch.Tensor] = None):
+    """h += Xh^T Xh over the calibration rows x (Xh = fl32(x / smooth)), binary64 [K x K];
+    a zero-filled h is allocated when None. Returns h."""
+    t, k, ldx = _rows(x)
+    h = torch.zeros((k, k), dtype=torch.float64, device=x.device) if h is None else h
+    _check("sq_gptq_hessian", raw["sq_gptq_hessian"](
+        _ptr(x), _dt(x), t, k, ldx, _ptr(smooth), _ptr(h), _stream(x.device)))
+    return h
+
+
+def sq_gptq_quantize(h: torch.Tensor, w: torch.Tensor, smooth: Optional[torch.Tensor] = None, damp: float = 0.01,
+                     ws: Optional[torch.Tensor] = None):
+    """GPTQ of W [K x N] (smoothed by s when given) against h: (Wq [N x K] int8, w_scale [N])."""
+    k, n, ldw = _rows(w)
+    wq = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    w_scale = torch.empty(n, dtype=torch.float32, device=w.device)
+    nb = raw["sq_gptq_quantize_workspace_size"](k, n)
+    if ws is None:
+        ws = _workspace(nb, w.device)
+    _check("sq_gptq_quantize", raw["sq_gptq_quantize"](
+        _ptr(h), _ptr(w), _dt(w), k, n, ldw, _ptr(smooth), float(damp), _ptr(wq), _ptr(w_scale), _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(w.device)))
+    return wq, w_scale
 
 
 def sq_outlier_detect(x: torch.Tensor, threshold: float = 6.0):

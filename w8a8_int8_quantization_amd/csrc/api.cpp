@@ -416,6 +416,50 @@ sq_status sq_fp8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const uint8
   return hip_status(sqh::gemm_f8(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, s));
 }
 
+// ---------------------------------------------------------------- GPTQ
+static sq_status check_gptq_k(int64_t k) {
+  if (k < 128 || k % 128 != 0) return SQ_ERR_SHAPE;
+  if (k > SQ_MAX_K_GPTQ) return SQ_ERR_RANGE;
+  return SQ_OK;
+}
+
+static bool elem_aligned(const void* p, sq_dtype t) {
+  return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)elem_bytes(t)) == 0;
+}
+
+sq_status sq_gptq_hessian(const void* x, sq_dtype xt, int64_t t, int64_t k, int64_t ldx, const float* smooth,
+                          double* h, sq_stream_t stream) {
+  if (!float_input(xt)) return SQ_ERR_DTYPE;
+  SQ_TRY(check_gptq_k(k));
+  if (t < 0 || ldx < k) return SQ_ERR_SHAPE;
+  if (t == 0) return SQ_OK;
+  if (!x || !h) return SQ_ERR_NULL;
+  if (!elem_aligned(x, xt) || (reinterpret_cast<uintptr_t>(h) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(smooth) & 3u) != 0)
+    return SQ_ERR_ALIGN;
+  return hip_status(sqh::gptq_hessian(x, xt, t, k, ldx, smooth, h, (hipStream_t)stream));
+}
+
+size_t sq_gptq_quantize_workspace_size(int64_t k, int64_t n) { return sqh::gptq_workspace(k, n); }
+
+sq_status sq_gptq_quantize(const double* h, const void* w, sq_dtype wt, int64_t k, int64_t n, int64_t ldw,
+                           const float* smooth, float damp, int8_t* wq, float* w_scale, void* ws, size_t ws_bytes,
+                           sq_stream_t stream) {
+  if (!float_input(wt)) return SQ_ERR_DTYPE;
+  SQ_TRY(check_gptq_k(k));
+  if (n < 0 || ldw < n) return SQ_ERR_SHAPE;
+  if (!(damp > 0.f && damp <= 1.f)) return SQ_ERR_RANGE;
+  if (n == 0) return SQ_OK;
+  if (!h || !w || !wq || !w_scale) return SQ_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(h) & 7u) != 0 || !elem_aligned(w, wt) || !aligned16(wq) ||
+      (reinterpret_cast<uintptr_t>(w_scale) & 3u) != 0 || (reinterpret_cast<uintptr_t>(smooth) & 3u) != 0)
+    return SQ_ERR_ALIGN;
+  if (!ws || ws_bytes < sq_gptq_quantize_workspace_size(k, n)) return SQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SQ_ERR_ALIGN;
+  return hip_status(sqh::gptq_quantize(h, w, wt, k, n, ldw, smooth, (double)damp, wq, w_scale, ws,
+                                       (hipStream_t)stream));
+}
+
 size_t sq_outlier_detect_workspace_size(int64_t k) { return k > 0 ? round_up((size_t)k * 4) : 0; }
 
 sq_status sq_outlier_detect(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, float threshold,

@@ -58,6 +58,13 @@ hipError_t quant_f8_weights(const void* w, sq_dtype wt, int64_t k, int64_t n, in
 hipError_t gemm_f8(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
                    int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, hipStream_t s);
 
+// GPTQ (binary64): Hessian accumulation and the quantisation sweep.
+hipError_t gptq_hessian(const void* x, sq_dtype xt, int64_t t, int64_t k, int64_t ldx, const float* smooth, double* h,
+                        hipStream_t s);
+size_t gptq_workspace(int64_t k, int64_t n);
+hipError_t gptq_quantize(const double* h, const void* w, sq_dtype wt, int64_t k, int64_t n, int64_t ldw,
+                         const float* smooth, double damp, int8_t* wq, float* w_scale, void* ws, hipStream_t s);
+
 hipError_t gemm_i8(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
                    int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec,
                    hipStream_t s);

@@ -20,6 +20,12 @@ not available):
 * ``silu_gated``: h = SiLU(a) * b with a, b ~ N(0, 1) independent (the input
   of a gated MLP's down projection), heavy tailed, with the outlier channels
   multiplied by 40.
+* ``correlated_outlier``: X = Z + L M with Z ~ N(0, 1), 32 latent factors
+  L ~ N(0, 1) per row and a fixed mixing M ~ N(0, 0.25) per layer, then the
+  outlier channels multiplied by 60. The channels are correlated, as a real
+  layer's inputs are, so GPTQ's Hessian (its calibration input for "How
+  GPTQ improves on naive quantization") is far from diagonal; with
+  uncorrelated channels GPTQ would pass almost no error on.
 * ``llm_int8``: X ~ N(0, 1) fp16 with 8 columns multiplied by magnitudes
   spread evenly over [6, 60], so every one of them crosses the 6.0 threshold.
 * RMSNorm inputs (``norm_case``): the residual stream before the norm, rows
@@ -40,7 +46,7 @@ Weights are N(0, 0.02) in every configuration.
 from __future__ import annotations
 
 import dataclasses
-from typing import Dict, List, Optional, Sequence
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 import torch
@@ -59,6 +65,8 @@ __all__ = [
     "wide_range_rows",
     "GateUpCase",
     "gate_up_case",
+    "GptqCase",
+    "gptq_case",
     "CONFIGS",
 ]
 
@@ -106,6 +114,14 @@ def activations(rows: int, k: int, model: str, seed: int, role: str,
         b = g.standard_normal((rows, k), dtype=np.float32)
         x = (a / (1.0 + np.exp(-a.astype(np.float64)))).astype(np.float32) * b
         x[:, channels] *= np.float32(40.0)
+    elif model == "correlated_outlier":
+        # channels share 32 latent directions (the same mixing for every row
+        # of a layer), so the calibration Hessian is far from diagonal
+        z = g.standard_normal((rows, k), dtype=np.float32)
+        lat = g.standard_normal((rows, 32), dtype=np.float32)
+        mix = _rng(seed, "extra", 300).standard_normal((32, k), dtype=np.float32) * np.float32(0.5)
+        x = z + lat @ mix
+        x[:, channels] *= np.float32(60.0)
     elif model == "llm_int8":
         x = g.standard_normal((rows, k), dtype=np.float32)
         mags = np.linspace(6.0, 60.0, len(channels)).astype(np.float32)
@@ -200,6 +216,29 @@ def random_linear_case(m: int, k: int, n: int, seed: int, dtype: str = "bf16",
     return LinearCase(name=f"rand_{m}x{k}x{n}_s{seed}", m=m, k=k, n=n, x_dtype=dtype, w_dtype=dtype,
                       y_dtype=y_dtype or dtype, alpha=alpha, channels=ch, x_calib=xc, x=x, w=w,
                       model=model, seed=seed)
+
+
+@dataclasses.dataclass
+class GptqCase:
+    """Calibration rows and the weight of one layer for GPTQ."""
+    k: int
+    n: int
+    t: int
+    dtype: str
+    channels: np.ndarray
+    dead: Tuple[int, ...]  # inputs whose calibration column is zero
+    x_calib: np.ndarray  # [t x k] fp32 holding dtype values
+    w: np.ndarray  # [k x n]
+
+
+def gptq_case(k: int, n: int, t: int, seed: int, dtype: str = "bf16", dead: Sequence[int] = (),
+              model: str = "correlated_outlier") -> GptqCase:
+    ch = outlier_channels(k, seed)
+    xc = activations(t, k, model, seed, "calib", ch, dtype)
+    for j in dead:
+        xc[:, j] = 0.0
+    return GptqCase(k=k, n=n, t=t, dtype=dtype, channels=ch, dead=tuple(dead), x_calib=xc,
+                    w=weights(k, n, seed, dtype))
 
 
 @dataclasses.dataclass
