@@ -47,6 +47,7 @@ METRIC = "W8A8 linear TOPS (quant+int8 GEMM+dequant), 8B shapes, % int8 MFMA pea
 PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, TOP/s
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, GB/s
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, TFLOP/s
+PEAK_FP64_TFLOPS = 78.6   # MI355X binary64 (vector FMA and matrix), TFLOP/s
 PROFILE_PMC = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
@@ -62,7 +63,9 @@ def parse():
                         "then the GEMM); silu_down_prefill, silu_decode_down (the step starts from the gate/up "
                         "projection's bf16 outputs: fused SiLU(gate)*up + smoothing + quantisation, then the "
                         "down projection GEMM); fp8_qkv_prefill, fp8_decode_up (the FP8 E4M3 variant: per-token "
-                        "E4M3 quantisation, then the E4M3 GEMM; no smoothing)")
+                        "E4M3 quantisation, then the E4M3 GEMM; no smoothing); gptq_qkv, gptq_down (GPTQ of one "
+                        "layer at load time: Hessian of 4096 calibration rows, damping, Cholesky, sweep; "
+                        "reports ms per layer)")
     p.add_argument("--eps", type=float, default=1e-5, help="RMSNorm epsilon (rmsnorm_* workloads)")
     p.add_argument("--m", type=int, default=None, help="override the token count (decode workloads)")
     p.add_argument("--alpha", type=float, default=None)
@@ -294,8 +297,11 @@ def bench_fp8(args, dev):
     else:
         roof = {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "ops_per_launch": ops}
-    roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": pmc_traffic(args.workload, "gemm_f8.hip"),
-                 "kernel": "gemm_f8_kernel", "launch_us": gemm_ms * 1e3})
+    # the E4M3 forms of the decode kernel (M <= 64) and of the prefill kernel
+    kfile, kname = (("gemm_decode.hip", "gemm_decode_kernel<kMB, kNS, kF8=true>") if decode else
+                    ("gemm_big.hip", "gemm_big_kernel<192, bf16, kVec, kF8=true>"))
+    roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": pmc_traffic(args.workload, kfile),
+                 "kernel": kname, "launch_us": gemm_ms * 1e3})
     result = {
         "metric": METRIC, "value": ops / (ms * 1e-3) / 1e12, "unit": "TOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -307,6 +313,126 @@ def bench_fp8(args, dev):
         cpu_baseline_fp8(c, args.cpu_seconds),
     }
     print(json.dumps(result), flush=True)
+
+
+GPTQ_SHAPES = {"gptq_qkv": (4096, 6144), "gptq_down": (14336, 4096)}  # K, N; 8 x 512 calibration rows
+
+
+def bench_gptq(args, dev):
+    """GPTQ of one layer at load time: the Hessian of 4096 calibration rows,
+    then damping, Cholesky and the sweep (codes and scales), all in binary64."""
+    import numpy as np
+    import torch
+
+    import workloads
+    import w8a8_int8_quantization_amd as sq
+
+    k, n = GPTQ_SHAPES[args.workload]
+    t = 8 * 512
+    c = workloads.gptq_case(k, n, t, seed=0)
+    x = torch.from_numpy(c.x_calib).to(torch.bfloat16).to(dev)
+    w = torch.from_numpy(c.w).to(torch.bfloat16).to(dev)
+    # SmoothQuant's calibration first (alpha 0.5): GPTQ starts from the smoothed layer
+    absmax = sq.sq_calibrate_absmax(x, torch.zeros(k, dtype=torch.float32, device=dev))
+    sd, _, _ = sq.sq_smooth_fold_weights(w, alpha=0.5, absmax=absmax)
+    h = torch.zeros((k, k), dtype=torch.float64, device=dev)
+    wq = torch.empty((n, k), dtype=torch.int8, device=dev)
+    w_scale = torch.empty(n, dtype=torch.float32, device=dev)
+    ws = torch.empty(sq.raw["sq_gptq_quantize_workspace_size"](k, n), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    h_fn, q_fn = sq.raw["sq_gptq_hessian"], sq.raw["sq_gptq_quantize"]
+    h_args = (x.data_ptr(), sq.SQ_BF16, t, k, k, sd.data_ptr(), h.data_ptr(), stream)
+    q_args = (h.data_ptr(), w.data_ptr(), sq.SQ_BF16, k, n, n, sd.data_ptr(), 0.01, wq.data_ptr(),
+              w_scale.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+    hip = HipEvents(sq._lib, stream)
+    print(f"[bench] workload {args.workload} K={k} N={n} T={t}", file=sys.stderr, flush=True)
+
+    def run(steps, evs=None):
+        bad = 0
+        for i in range(steps):
+            h.zero_()
+            if evs:
+                hip.record(evs[i][0])
+            bad |= h_fn(*h_args)
+            if evs:
+                hip.record(evs[i][1])
+            bad |= q_fn(*q_args)
+            if evs:
+                hip.record(evs[i][2])
+        if bad:
+            raise RuntimeError(f"a C-ABI call failed (status bits {bad})")
+
+    steps = max(1, min(args.steps, 20))
+    run(min(args.warmup, 2))
+    torch.cuda.synchronize()
+    t0, t1 = hip.create(), hip.create()
+    hip.record(t0)
+    run(steps)
+    hip.record(t1)
+    torch.cuda.synchronize()
+    total_ms = hip.elapsed(t0, t1) / steps
+    evs = [[hip.create() for _ in range(3)] for _ in range(steps)]
+    run(steps, evs)
+    torch.cuda.synchronize()
+    hess_ms = float(np.median([hip.elapsed(e[0], e[1]) for e in evs]))
+    quant_ms = float(np.median([hip.elapsed(e[1], e[2]) for e in evs]))
+    hip.destroy_all()
+    # algorithmic binary64 flops: the Hessian's distinct entries K(K+1)/2, 2T
+    # flops each; Cholesky K^3/3; the sweep's compensation K^2 N (each of the
+    # N channels passes every error on to every later input)
+    f_hess = float(t) * k * (k + 1)
+    f_chol = k ** 3 / 3.0
+    f_sweep = float(k) * k * n
+    roof = {"bound": "fp64", "achieved": f_hess / (hess_ms * 1e-3) / 1e12, "peak": PEAK_FP64_TFLOPS,
+            "unit": "TFLOP/s", "frac": f_hess / (hess_ms * 1e-3) / 1e12 / PEAK_FP64_TFLOPS, "traffic": None,
+            "kernel": "gptq_hessian_kernel", "launch_us": hess_ms * 1e3, "flops_per_launch": f_hess}
+    result = {
+        "metric": "GPTQ time per layer (Hessian of the calibration rows + damping + Cholesky + sweep)",
+        "value": total_ms, "unit": "ms", "n_gpus": 1, "steps": steps, "warmup": min(args.warmup, 2),
+        "ms_per_step": total_ms, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: calibration X bf16 [{t} x {k}] (correlated channels, smoothed), "
+                               f"W bf16 [{k} x {n}] -> GPTQ int8 [{n} x {k}] + per-channel scales",
+                   "K": k, "N": n, "T": t, "damp": 0.01},
+        "hessian_ms": hess_ms, "quantize_ms": quant_ms,
+        "quantize_fp64_tflops": (f_chol + f_sweep) / (quant_ms * 1e-3) / 1e12,
+        "roofline": roof,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_gptq(c, args.cpu_seconds),
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_gptq(c, budget_s: float):
+    """The oracle's GPTQ: its smoothing factors, Hessian and factorisation in
+    full, its sweep on as many output channels as the budget allows,
+    extrapolated to all N (the channels are independent given H)."""
+    import oracle
+
+    threads = _blas_threads()
+    s = oracle.smoothing_factors(oracle.calibrate_absmax(c.x_calib), oracle.weight_row_absmax(c.w), 0.5)
+    t0 = time.perf_counter()
+    h = oracle.gptq_hessian(c.x_calib, s)
+    t_h = time.perf_counter() - t0
+    wf = oracle.fold_weights(c.w, s)
+    done, t_sw, chunk = 0, 0.0, 4
+    while t_h + t_sw < budget_s and done < c.n:
+        cols = slice(done, min(c.n, done + chunk))
+        t0 = time.perf_counter()
+        oracle.gptq_quantize(wf[:, cols], h)
+        t_sw += time.perf_counter() - t0
+        done = cols.stop
+        chunk = min(chunk * 2, 64)
+    # every call repeats the damping, inverse and Cholesky; time them once more on their own
+    t0 = time.perf_counter()
+    oracle.gptq_quantize(wf[:, :1], h)
+    t_fact = time.perf_counter() - t0
+    calls = max(1, (done + 63) // 64)
+    per_channel = max(0.0, t_sw - calls * t_fact) / done
+    est = t_h + t_fact + per_channel * c.n
+    return {"value": est * 1e3, "unit": "ms", "cores": threads, "kind": "oracle",
+            "sample": f"Hessian of all {c.t} rows ({t_h:.1f} s), damping+inverse+Cholesky ({t_fact:.1f} s), sweep "
+                      f"of {done} of {c.n} channels ({t_sw:.1f} s incl. per-call factorisations), per-channel "
+                      f"sweep time scaled to all {c.n}"}
 
 
 def cpu_baseline_fp8(c, budget_s: float):
@@ -462,6 +588,9 @@ def main():
         return
     if args.workload.startswith("fp8_"):
         bench_fp8(args, dev)
+        return
+    if args.workload.startswith("gptq_"):
+        bench_gptq(args, dev)
         return
     norm = args.workload.startswith("rmsnorm_")
     silu = args.workload.startswith("silu_")

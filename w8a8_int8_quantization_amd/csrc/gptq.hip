@@ -32,7 +32,8 @@
 //     (dead diagonal entries counted as 1), and A = P (H + dead + lambda I) P
 //     with P the index reversal;
 //  4. blocked lower Cholesky of A, 64 columns at a time: diagonal block in
-//     LDS, panel by forward substitution, trailing update as an fp64 GEMM;
+//     LDS (one wave, left-looking), panel by forward substitution, trailing
+//     update as an fp64 GEMM;
 //  5. gptq_unit_kernel: C_ij = V_ij / V_jj into the upper triangle;
 //  6. per block of 64 inputs: gptq_block_kernel (codes, deltas; one lane per
 //     output channel), then gptq_trailing_kernel (Z += C^T D for the later
@@ -41,6 +42,22 @@
 #include "sq_launch.hpp"
 
 namespace sqk {
+
+// v - sum_{p<c} x(p) * y(p) over four interleaved partial sums (four
+// independent FMA chains instead of one), added in a fixed order
+template <class X, class Y>
+__device__ __forceinline__ double dot_sub(double v, int c, X x, Y y) {
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  int p = 0;
+  for (; p + 4 <= c; p += 4) {
+    s0 = __builtin_fma(x(p), y(p), s0);
+    s1 = __builtin_fma(x(p + 1), y(p + 1), s1);
+    s2 = __builtin_fma(x(p + 2), y(p + 2), s2);
+    s3 = __builtin_fma(x(p + 3), y(p + 3), s3);
+  }
+  for (; p < c; ++p) s0 = __builtin_fma(x(p), y(p), s0);
+  return v - ((s0 + s1) + (s2 + s3));
+}
 
 constexpr int kGB = 64;   // Cholesky panel width and sweep block
 constexpr int kGT = 128;  // GEMM output tile
@@ -174,29 +191,25 @@ __global__ __launch_bounds__(256) void gptq_reverse_kernel(const double* __restr
 }
 
 // ---- 4. blocked Cholesky (lower) of A, panel kb
-__global__ __launch_bounds__(256) void chol_diag_kernel(double* __restrict__ a, int64_t k, int64_t o) {
+// Diagonal block, left-looking, one wave: lane r owns row r;
+// column c: v_r = A_rc - sum_{p<c} L_rp L_cp, L_cc = sqrt(v_c), L_rc = v_r / L_cc.
+__global__ __launch_bounds__(64) void chol_diag_kernel(double* __restrict__ a, int64_t k, int64_t o) {
   __shared__ double l[kGB][kGB + 1];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < kGB * kGB; e += 256) {
-    const int r = e / kGB, c = e % kGB;
-    l[r][c] = c <= r ? a[(o + r) * k + (o + c)] : 0.0;
-  }
+  const int r = threadIdx.x;
+#pragma unroll 16
+  for (int i = 0; i < kGB; ++i) l[i][r] = r <= i ? a[(o + i) * k + (o + r)] : 0.0;
   __syncthreads();
   for (int c = 0; c < kGB; ++c) {
-    if (tid == 0) l[c][c] = sqrt(l[c][c]);
+    double v = 0.0;
+    if (r >= c) v = dot_sub(l[r][c], c, [&](int p) { return l[r][p]; }, [&](int p) { return l[c][p]; });
+    if (r == c) l[c][c] = sqrt(v);
     __syncthreads();
-    if (tid > c && tid < kGB) l[tid][c] = l[tid][c] / l[c][c];
-    __syncthreads();
-    for (int e = tid; e < kGB * kGB; e += 256) {
-      const int r = e / kGB, r2 = e % kGB;
-      if (r2 > c && r2 <= r) l[r][r2] = __builtin_fma(-l[r][c], l[r2][c], l[r][r2]);
-    }
+    if (r > c) l[r][c] = v / l[c][c];
     __syncthreads();
   }
-  for (int e = tid; e < kGB * kGB; e += 256) {
-    const int r = e / kGB, c = e % kGB;
-    if (c <= r) a[(o + r) * k + (o + c)] = l[r][c];
-  }
+#pragma unroll 16
+  for (int i = 0; i < kGB; ++i)
+    if (r <= i) a[(o + i) * k + (o + r)] = l[i][r];
 }
 
 // rows i0 .. i0+63 below the diagonal block: L21 = A21 L11^-T, one thread per row
@@ -205,17 +218,20 @@ __global__ __launch_bounds__(64) void chol_panel_kernel(double* __restrict__ a, 
   __shared__ double p[kGB][kGB + 1];  // p[c][r]: column c of row r
   const int r = threadIdx.x;
   const int64_t i0 = o + kGB + (int64_t)blockIdx.x * kGB;
-  for (int c = 0; c < kGB; ++c) {
-    l11[c][r] = r <= c ? a[(o + c) * k + (o + r)] : 0.0;
-    p[c][r] = a[(i0 + r) * k + (o + c)];
+  // row by row, the 64 lanes reading one row's 64 consecutive columns
+#pragma unroll 16
+  for (int i = 0; i < kGB; ++i) {
+    l11[i][r] = r <= i ? a[(o + i) * k + (o + r)] : 0.0;
+    p[r][i] = a[(i0 + i) * k + (o + r)];
   }
   __syncthreads();
   for (int c = 0; c < kGB; ++c) {
-    double v = p[c][r];
-    for (int c2 = 0; c2 < c; ++c2) v = __builtin_fma(-p[c2][r], l11[c][c2], v);
+    const double v = dot_sub(p[c][r], c, [&](int q) { return p[q][r]; }, [&](int q) { return l11[c][q]; });
     p[c][r] = v / l11[c][c];
   }
-  for (int c = 0; c < kGB; ++c) a[(i0 + r) * k + (o + c)] = p[c][r];
+  __syncthreads();
+#pragma unroll 16
+  for (int i = 0; i < kGB; ++i) a[(i0 + i) * k + (o + r)] = p[r][i];
 }
 
 // trailing update of rows/columns [s, K), s = o + 64: A[r][c] -= sum_p L[r][o+p] L[c][o+p], lower tiles
@@ -275,7 +291,8 @@ __global__ __launch_bounds__(64) void gptq_block_kernel(const float* __restrict_
                                                         int64_t j0, double* __restrict__ dblk,
                                                         int8_t* __restrict__ wq, float* __restrict__ w_scale) {
   __shared__ double cb[kGB][kGB];  // cb[p][q] = C[j0+p][j0+q], p < q
-  __shared__ double ds[kGB][64];   // ds[p][lane] = delta_p of this lane's channel
+  __shared__ double ds[kGB][64];   // ds[q][lane]: z_q's running correction, then delta_q
+  __shared__ float wsh[kGB][64];   // this lane's smoothed weights of the block
   __shared__ uint32_t cs[kGB][64];  // codes, one per word
   const int lane = threadIdx.x;
   for (int e = lane; e < kGB * kGB; e += 64) {
@@ -288,10 +305,15 @@ __global__ __launch_bounds__(64) void gptq_block_kernel(const float* __restrict_
   const float sw = __uint_as_float(colmax[col]) / 127.f;
   if (j0 == 0) w_scale[col] = sw;
   const double sw64 = (double)sw;
+  // the block's corrections and weights of this channel, every load in flight at once
+#pragma unroll 16
   for (int q = 0; q < kGB; ++q) {
-    double acc = z[(j0 + q) * n + col];
-    for (int p = 0; p < q; ++p) acc = __builtin_fma(cb[p][q], ds[p][lane], acc);
-    const double w = (double)wp[(j0 + q) * n + col];
+    ds[q][lane] = z[(j0 + q) * n + col];
+    wsh[q][lane] = wp[(j0 + q) * n + col];
+  }
+  for (int q = 0; q < kGB; ++q) {
+    const double acc = -dot_sub(-ds[q][lane], q, [&](int p) { return cb[p][q]; }, [&](int p) { return ds[p][lane]; });
+    const double w = (double)wsh[q][lane];
     const double zq = w + acc;
     double code = 0.0;
     if (sw > 0.f) code = fmin(fmax(rint(zq / sw64), -127.0), 127.0);
@@ -433,7 +455,7 @@ hipError_t gptq_quantize(const double* h, const void* w, sq_dtype wt, int64_t k,
   const int64_t nb = k / sqk::kGB;
   for (int64_t b = 0; b < nb; ++b) {
     const int64_t o = b * sqk::kGB;
-    hipLaunchKernelGGL(sqk::chol_diag_kernel, dim3(1), dim3(256), 0, s, a, k, o);
+    hipLaunchKernelGGL(sqk::chol_diag_kernel, dim3(1), dim3(64), 0, s, a, k, o);
     if (b + 1 < nb) {
       hipLaunchKernelGGL(sqk::chol_panel_kernel, dim3((unsigned)(nb - 1 - b)), dim3(64), 0, s, a, k, o);
       const int64_t nt = (k - o - sqk::kGB + sqk::kGT - 1) / sqk::kGT;
