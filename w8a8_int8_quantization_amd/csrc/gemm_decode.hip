@@ -122,9 +122,13 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
   using AccT = typename std::conditional<kF8, v4f_d, v4i>::type;
   constexpr int kTok = 16 * kMB;
   // steps of loads in flight: all of them when the registers allow (the
-  // workgroup's whole share of Wq is requested at once); the caps are the
-  // deepest pipelines the compiler allocates without spilling
-  constexpr int kMaxDepth = kMB == 4 ? 6 : 8;
+  // workgroup's whole share of Wq is requested at once). The caps keep the
+  // compiler from spilling: measured on MI355X, the int8 form at 64 tokens
+  // with depth 6 spilled 12 registers and ran its 64 x 4096 x 14336 GEMM in
+  // 26.4 us, with depth 4 in 23.5 us; at 16 tokens depth 8 spilled (14336 x
+  // 4096 down projection, M 1: 17.5 -> 16.5 us with depth 5). The E4M3 form
+  // (one MFMA per step) fits depth 6 / 8 without spilling.
+  constexpr int kMaxDepth = kF8 ? (kMB == 4 ? 6 : 8) : (kMB == 4 ? 4 : (kMB == 1 ? 5 : 8));
   constexpr int kDepth = kNS < kMaxDepth ? kNS : kMaxDepth;
   __shared__ int32_t red[kDecWaves][kTok][kDecRows];
   __shared__ uint32_t last_ticket;
