@@ -107,25 +107,31 @@ __global__ __launch_bounds__(256) void gptq_hessian_kernel(const uint8_t* __rest
   const int lc = tid & 127, lr = tid >> 7;
   const float sa_s = kSmooth ? smooth[a0 + lc] : 1.f;
   const float sb_s = kSmooth ? smooth[b0 + lc] : 1.f;
+  // the next chunk's raw values are loaded into registers while the current
+  // one is multiplied out of LDS
+  float ra[kGP / 2], rb[kGP / 2];
+  auto fetch = [&](int64_t t0) {
+#pragma unroll
+    for (int i = 0; i < kGP / 2; ++i) {
+      const int64_t t = t0 + lr + 2 * i;
+      ra[i] = rb[i] = 0.f;
+      if (t < t_rows) {
+        const uint8_t* row = x + t * ldx_bytes;
+        ra[i] = In::load1(row + (a0 + lc) * In::kBytes);
+        rb[i] = In::load1(row + (b0 + lc) * In::kBytes);
+      }
+    }
+  };
+  fetch(0);
   for (int64_t t0 = 0; t0 < t_rows; t0 += kGP) {
 #pragma unroll
     for (int i = 0; i < kGP / 2; ++i) {
       const int p = lr + 2 * i;
-      const int64_t t = t0 + p;
-      float va = 0.f, vb = 0.f;
-      if (t < t_rows) {
-        const uint8_t* row = x + t * ldx_bytes;
-        va = In::load1(row + (a0 + lc) * In::kBytes);
-        vb = In::load1(row + (b0 + lc) * In::kBytes);
-        if (kSmooth) {
-          va = va / sa_s;
-          vb = vb / sb_s;
-        }
-      }
-      sa[p][lc] = (double)va;
-      sb[p][lc] = (double)vb;
+      sa[p][lc] = (double)(kSmooth ? ra[i] / sa_s : ra[i]);
+      sb[p][lc] = (double)(kSmooth ? rb[i] / sb_s : rb[i]);
     }
     __syncthreads();
+    if (t0 + kGP < t_rows) fetch(t0 + kGP);
     tile_fma(sa, sb, ty, tx, acc);
     __syncthreads();
   }
@@ -252,15 +258,24 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ a
   // loader: element (row q of the tile, column p of the panel); 16 consecutive
   // threads read one row's 16 panel columns (128 bytes)
   const int lp = tid & 15, lq = tid >> 4;
+  double va[kGT / 16], vb[kGT / 16];
+  auto fetch = [&](int p0) {
+#pragma unroll
+    for (int i = 0; i < kGT / 16; ++i) {
+      const int64_t ra = r0 + lq + 16 * i, rb = c0 + lq + 16 * i;
+      va[i] = ra < k ? a[ra * k + o + p0 + lp] : 0.0;
+      vb[i] = rb < k ? a[rb * k + o + p0 + lp] : 0.0;
+    }
+  };
+  fetch(0);
   for (int p0 = 0; p0 < kGB; p0 += kGP) {
 #pragma unroll
     for (int i = 0; i < kGT / 16; ++i) {
-      const int q = lq + 16 * i;
-      const int64_t ra = r0 + q, rb = c0 + q;
-      sa[lp][q] = ra < k ? a[ra * k + o + p0 + lp] : 0.0;
-      sb[lp][q] = rb < k ? a[rb * k + o + p0 + lp] : 0.0;
+      sa[lp][lq + 16 * i] = va[i];
+      sb[lp][lq + 16 * i] = vb[i];
     }
     __syncthreads();
+    if (p0 + kGP < kGB) fetch(p0 + kGP);
     tile_fma(sa, sb, ty, tx, acc);
     __syncthreads();
   }
@@ -352,15 +367,25 @@ __global__ __launch_bounds__(256) void gptq_trailing_kernel(const double* __rest
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
   const int lc = tid & 127, lr = tid >> 7;
-  for (int p0 = 0; p0 < kGB; p0 += kGP) {
+  double va[kGP / 2], vb[kGP / 2];
+  auto fetch = [&](int p0) {
+    const int64_t r = r0 + lc, c = c0 + lc;
 #pragma unroll
     for (int i = 0; i < kGP / 2; ++i) {
       const int p = lr + 2 * i;
-      const int64_t r = r0 + lc, c = c0 + lc;
-      sa[p][lc] = r < k ? a[(j0 + p0 + p) * k + r] : 0.0;
-      sb[p][lc] = c < n ? dblk[(int64_t)(p0 + p) * n + c] : 0.0;
+      va[i] = r < k ? a[(j0 + p0 + p) * k + r] : 0.0;
+      vb[i] = c < n ? dblk[(int64_t)(p0 + p) * n + c] : 0.0;
+    }
+  };
+  fetch(0);
+  for (int p0 = 0; p0 < kGB; p0 += kGP) {
+#pragma unroll
+    for (int i = 0; i < kGP / 2; ++i) {
+      sa[lr + 2 * i][lc] = va[i];
+      sb[lr + 2 * i][lc] = vb[i];
     }
     __syncthreads();
+    if (p0 + kGP < kGB) fetch(p0 + kGP);
     tile_fma(sa, sb, ty, tx, acc);
     __syncthreads();
   }
