@@ -87,6 +87,7 @@ def test_gptq_hessian(dtype, t, k):
     (512, 200, 1024, "f16", (), False),
     (1024, 130, 2048, "f32", (0, 1023), True),
     (128, 1, 64, "bf16", (), True),
+    (2176, 999, 700, "bf16", (17, 2175), True),
 ])
 def test_gptq_quantize(k, n, t, dtype, dead, smooth):
     log("gptq", k, n, t, dtype, dead, smooth)
@@ -134,3 +135,4 @@ def test_gptq_full_size_sampled_channels():
     wq_ref, sw_ref, z_ref = oracle.gptq_quantize(wf[:, cols], h_ref, trace=True)
     _compare(wq[cols], sw[cols], wq_ref, sw_ref, z_ref)
     assert np.all(np.abs(wq.astype(np.int64)) <= 127) and np.all(sw > 0)
+
