@@ -110,16 +110,17 @@ __global__ __launch_bounds__(256) void gptq_hessian_kernel(const uint8_t* __rest
   // the next chunk's raw values are loaded into registers while the current
   // one is multiplied out of LDS
   float ra[kGP / 2], rb[kGP / 2];
+  // loads from a clamped (valid) row, then a select: unconditional loads are
+  // issued together instead of one branch and one wait each
   auto fetch = [&](int64_t t0) {
 #pragma unroll
     for (int i = 0; i < kGP / 2; ++i) {
       const int64_t t = t0 + lr + 2 * i;
-      ra[i] = rb[i] = 0.f;
-      if (t < t_rows) {
-        const uint8_t* row = x + t * ldx_bytes;
-        ra[i] = In::load1(row + (a0 + lc) * In::kBytes);
-        rb[i] = In::load1(row + (b0 + lc) * In::kBytes);
-      }
+      const uint8_t* row = x + (t < t_rows ? t : t_rows - 1) * ldx_bytes;
+      const float va = In::load1(row + (a0 + lc) * In::kBytes);
+      const float vb = In::load1(row + (b0 + lc) * In::kBytes);
+      ra[i] = t < t_rows ? va : 0.f;
+      rb[i] = t < t_rows ? vb : 0.f;
     }
   };
   fetch(0);
@@ -135,14 +136,24 @@ __global__ __launch_bounds__(256) void gptq_hessian_kernel(const uint8_t* __rest
     tile_fma(sa, sb, ty, tx, acc);
     __syncthreads();
   }
+  // read-modify-write a row of 8 at a time: the 8 (16) loads go out together
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 8; ++i) {
+    const int64_t a = a0 + 8 * ty + i;
+    double o1[8], o2[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int64_t a = a0 + 8 * ty + i, b = b0 + 8 * tx + j;
-      h[a * k + b] += acc[i][j];
-      if (ti != tj) h[b * k + a] += acc[i][j];
+      const int64_t b = b0 + 8 * tx + j;
+      o1[j] = h[a * k + b];
+      o2[j] = h[b * k + a];
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t b = b0 + 8 * tx + j;
+      h[a * k + b] = o1[j] + acc[i][j];
+      if (ti != tj) h[b * k + a] = o2[j] + acc[i][j];
+    }
+  }
 }
 
 // ---- 2. smoothed weights (binary32) and their column maxima
@@ -202,8 +213,12 @@ __global__ __launch_bounds__(256) void gptq_reverse_kernel(const double* __restr
 __global__ __launch_bounds__(64) void chol_diag_kernel(double* __restrict__ a, int64_t k, int64_t o) {
   __shared__ double l[kGB][kGB + 1];
   const int r = threadIdx.x;
+  // unconditional loads (every address is inside the block), then a select
 #pragma unroll 16
-  for (int i = 0; i < kGB; ++i) l[i][r] = r <= i ? a[(o + i) * k + (o + r)] : 0.0;
+  for (int i = 0; i < kGB; ++i) {
+    const double v = a[(o + i) * k + (o + r)];
+    l[i][r] = r <= i ? v : 0.0;
+  }
   __syncthreads();
   for (int c = 0; c < kGB; ++c) {
     double v = 0.0;
@@ -227,7 +242,8 @@ __global__ __launch_bounds__(64) void chol_panel_kernel(double* __restrict__ a, 
   // row by row, the 64 lanes reading one row's 64 consecutive columns
 #pragma unroll 16
   for (int i = 0; i < kGB; ++i) {
-    l11[i][r] = r <= i ? a[(o + i) * k + (o + r)] : 0.0;
+    const double v = a[(o + i) * k + (o + r)];
+    l11[i][r] = r <= i ? v : 0.0;
     p[r][i] = a[(i0 + i) * k + (o + r)];
   }
   __syncthreads();
@@ -263,8 +279,10 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ a
 #pragma unroll
     for (int i = 0; i < kGT / 16; ++i) {
       const int64_t ra = r0 + lq + 16 * i, rb = c0 + lq + 16 * i;
-      va[i] = ra < k ? a[ra * k + o + p0 + lp] : 0.0;
-      vb[i] = rb < k ? a[rb * k + o + p0 + lp] : 0.0;
+      const double x0 = a[(ra < k ? ra : k - 1) * k + o + p0 + lp];
+      const double x1 = a[(rb < k ? rb : k - 1) * k + o + p0 + lp];
+      va[i] = ra < k ? x0 : 0.0;
+      vb[i] = rb < k ? x1 : 0.0;
     }
   };
   fetch(0);
@@ -280,12 +298,21 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ a
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = r0 + 8 * ty + i;
+    const int64_t rr = r < k ? r : k - 1;
+    double old[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int64_t r = r0 + 8 * ty + i, c = c0 + 8 * tx + j;
-      if (r < k && c <= r) a[r * k + c] -= acc[i][j];
+      const int64_t c = c0 + 8 * tx + j;
+      old[j] = a[rr * k + (c < k ? c : k - 1)];
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t c = c0 + 8 * tx + j;
+      if (r < k && c <= r) a[r * k + c] = old[j] - acc[i][j];
+    }
+  }
 }
 
 // ---- 5. C[i][j] = V_ij / V_jj for i < j, with V_ij = L[K-1-i][K-1-j], into the upper triangle
@@ -370,11 +397,14 @@ __global__ __launch_bounds__(256) void gptq_trailing_kernel(const double* __rest
   double va[kGP / 2], vb[kGP / 2];
   auto fetch = [&](int p0) {
     const int64_t r = r0 + lc, c = c0 + lc;
+    const int64_t rr = r < k ? r : k - 1, cc = c < n ? c : n - 1;
 #pragma unroll
     for (int i = 0; i < kGP / 2; ++i) {
       const int p = lr + 2 * i;
-      va[i] = r < k ? a[(j0 + p0 + p) * k + r] : 0.0;
-      vb[i] = c < n ? dblk[(int64_t)(p0 + p) * n + c] : 0.0;
+      const double x0 = a[(j0 + p0 + p) * k + rr];
+      const double x1 = dblk[(int64_t)(p0 + p) * n + cc];
+      va[i] = r < k ? x0 : 0.0;
+      vb[i] = c < n ? x1 : 0.0;
     }
   };
   fetch(0);
@@ -390,12 +420,21 @@ __global__ __launch_bounds__(256) void gptq_trailing_kernel(const double* __rest
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = r0 + 8 * ty + i;
+    const int64_t rr = r < k ? r : k - 1;
+    double old[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int64_t r = r0 + 8 * ty + i, c = c0 + 8 * tx + j;
-      if (r < k && c < n) z[r * n + c] += acc[i][j];
+      const int64_t c = c0 + 8 * tx + j;
+      old[j] = z[rr * n + (c < n ? c : n - 1)];
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t c = c0 + 8 * tx + j;
+      if (r < k && c < n) z[r * n + c] = old[j] + acc[i][j];
+    }
+  }
 }
 
 }  // namespace sqk
