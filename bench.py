@@ -48,6 +48,30 @@ PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, TOP/s
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, GB/s
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, TFLOP/s
 PEAK_FP64_TFLOPS = 78.6   # MI355X binary64 (vector FMA and matrix), TFLOP/s
+
+
+def decode_kernel_runs(m: int, n: int, k: int) -> bool:
+    """Whether the library routes this GEMM to its decode kernel (the
+    dispatch rule of the C ABI, repeated here to label the measured kernel):
+    M <= 64, or up to 256 tokens when the tiled kernels would have at most 128
+    units of 128 x 128 outputs."""
+    if k % 128 or m < 1:
+        return False
+    if m <= 64:
+        return True
+    if m > 256:
+        return False
+    big = m >= 256 and m * n >= (1 << 20)
+    units = (-(-m // 256)) * (-(-n // 192)) * 3 if big else (-(-m // 128)) * (-(-n // 128))
+    return units <= 128
+
+
+def hbm_bound(m: int, n: int, k: int, out_bytes: int) -> bool:
+    """Below the ridge point (dense int8 / FP8 peak over HBM bandwidth) the
+    GEMM is bound by streaming its operands."""
+    ops = 2.0 * m * n * k
+    bytes_ = m * k + n * k + 4 * m + 4 * n + out_bytes * m * n
+    return ops / bytes_ < PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 PROFILE_PMC = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
@@ -246,8 +270,11 @@ def bench_fp8(args, dev):
     xq = torch.empty((c.m, c.k), dtype=torch.uint8, device=dev)
     dx = torch.empty(c.m, dtype=torch.float32, device=dev)
     y = torch.empty((c.m, c.n), dtype=torch.bfloat16, device=dev)
-    decode = c.m <= 64
-    n_w = -(-(768 << 20) // wq.numel()) if decode else 1
+    decode = decode_kernel_runs(c.m, c.n, c.k)
+    streamed = hbm_bound(c.m, c.n, c.k, 2)
+    # weight-streaming shapes rotate through >= 768 MiB of weight copies so
+    # that every step reads its weights from HBM, not the last-level cache
+    n_w = -(-(768 << 20) // wq.numel()) if streamed else 1
     wqs = [wq] + [wq.clone() for _ in range(n_w - 1)]
     stream = torch.cuda.current_stream(dev).cuda_stream
     q_fn, g_fn = sq.raw["sq_quant_act_fp8"], sq.raw["sq_fp8_linear"]
@@ -291,15 +318,17 @@ def bench_fp8(args, dev):
     ms = total_ms / args.steps
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
     gemm_bytes = c.m * c.k + c.n * c.k + 4 * c.m + 4 * c.n + 2 * c.m * c.n
-    if decode:
+    if streamed:
         roof = {"bound": "hbm", "achieved": gemm_bytes / (gemm_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "bytes_per_launch": gemm_bytes}
     else:
         roof = {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "ops_per_launch": ops}
-    # the E4M3 forms of the decode kernel (M <= 64) and of the prefill kernel
+    # the E4M3 forms of the decode kernel and of the prefill kernel, or the 128 x 128 kernel
+    big = c.m >= 256 and c.n >= 192 and c.k % 128 == 0 and c.m * c.n >= (1 << 20)
     kfile, kname = (("gemm_decode.hip", "gemm_decode_kernel<kMB, kNS, kF8=true>") if decode else
-                    ("gemm_big.hip", "gemm_big_kernel<192, bf16, kVec, kF8=true>"))
+                    ("gemm_big.hip", "gemm_big_kernel<192, bf16, kVec, kF8=true>") if big else
+                    ("gemm_f8.hip", "gemm_f8_kernel"))
     roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": pmc_traffic(args.workload, kfile),
                  "kernel": kname, "launch_us": gemm_ms * 1e3})
     result = {
@@ -640,11 +669,12 @@ def main():
     dx = torch.empty(c.m, dtype=torch.float32, device=dev)
     y = torch.empty((c.m, c.n), dtype=out_dt, device=dev)
     ws = sq.linear_workspace(c.m, c.n, c.k, dev)
-    decode = c.m <= 64
-    # Decode steps stream the whole weight matrix once; with one copy it would
-    # stay in the 256 MiB last-level cache between steps. Rotating through
-    # copies totalling >= 768 MiB makes every step read its weights from HBM.
-    n_w = -(-(768 << 20) // wq.numel()) if decode else 1
+    decode = decode_kernel_runs(c.m, c.n, c.k)
+    streamed = hbm_bound(c.m, c.n, c.k, {"f32": 4, "bf16": 2}[c.y_dtype])
+    # Weight-streaming steps read the whole weight matrix once; with one copy
+    # it would stay in the 256 MiB last-level cache between steps. Rotating
+    # through copies totalling >= 768 MiB makes every step read it from HBM.
+    n_w = -(-(768 << 20) // wq.numel()) if streamed else 1
     wqs = [wq] + [wq.clone() for _ in range(n_w - 1)]
 
     # The timed loop calls the C ABI directly with pre-marshalled arguments and
@@ -722,7 +752,7 @@ def main():
                     ("gemm_big.hip", "gemm_big_kernel") if big else ("gemm.hip", "gemm_i8_kernel"))
     tag = args.workload if args.m is None else f"{args.workload}_m{c.m}"
     traffic = pmc_traffic(tag, kfile)
-    if decode:
+    if streamed:
         roof = {"bound": "hbm", "achieved": gemm_bytes / (gemm_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "kernel": kname, "bytes_per_launch": gemm_bytes}
     else:

@@ -177,9 +177,10 @@ sq_status sq_quant_act_per_token(const void* x, sq_dtype xt, int64_t m, int64_t 
  * K must not exceed SQ_MAX_K_INT32.
  * ws: workspace of sq_w8a8_linear_workspace_size(m, n, k) bytes, 16-byte
  *     aligned; NULL when that size is 0. The size is non-zero for decode
- *     shapes (M <= 64, K % 128 == 0) whose K is split over several
+ *     shapes (K % 128 == 0 and M <= 64, or M <= 256 where the tiled kernels
+ *     would cover few compute units) whose K is split over several
  *     workgroups: the workspace then holds int32 partial tiles and one ticket
- *     counter per 64 output columns. The caller zero-fills the workspace once,
+ *     counter per 64 output columns and 64 tokens. The caller zero-fills the workspace once,
  *     before its first use; every call leaves the counters at zero again, so
  *     later calls need no clearing. One workspace serves one call at a time
  *     (calls in flight together on different streams need their own).

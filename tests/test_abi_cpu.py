@@ -119,7 +119,10 @@ def test_validation_linear(sq):
     assert f(P, P, P, P, 4, 4096, 14336, P, sq.SQ_BF16, 4096, None, 0, None) == WS
     assert f(P, P, P, P, 4, 4096, 14336, P, sq.SQ_BF16, 4096, P, need - 1, None) == WS
     assert f(P, P, P, P, 4, 4096, 14336, P, sq.SQ_BF16, 4096, BAD, need, None) == ALIGN
-    assert sq.raw["sq_w8a8_linear_workspace_size"](65, 4096, 14336) == 0   # prefill-sized M
+    # 65..256 tokens: the decode kernel only where the tiled kernels get few tiles
+    assert sq.raw["sq_w8a8_linear_workspace_size"](128, 4096, 14336) > 0       # down projection shape
+    assert sq.raw["sq_w8a8_linear_workspace_size"](192, 14336, 4096) == 0      # up projection: tiled
+    assert sq.raw["sq_w8a8_linear_workspace_size"](257, 4096, 14336) == 0      # prefill-sized M
     d = sq.raw["sq_w8a8_linear_dyn"]
     need = sq.raw["sq_w8a8_linear_dyn_workspace_size"](4, 4, 64)
     assert need >= 4 * 64 + 16

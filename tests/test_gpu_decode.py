@@ -1,4 +1,5 @@
-"""Parity of the decode-shaped GEMM (M <= 64 tokens, K a multiple of 128).
+"""Parity of the decode-shaped GEMM (M <= 64 tokens, K a multiple of 128, and
+65..256 tokens where the decode kernel is chosen, one grid layer per 64).
 
 These shapes run the split-K decode kernel: per-slice int32 partial tiles in
 the workspace, ticket counters, the last workgroup of a tile reducing. The
@@ -22,6 +23,8 @@ sq = pytest.importorskip("w8a8_int8_quantization_amd")
 # the int32 limit (hundreds of slices).
 NK = [(64, 128), (99, 256), (301, 1152), (130, 8192), (4096, 14336), (14336, 4096), (64, 133120)]
 MS = [1, 5, 16, 17, 33, 64]
+# more than one 64-token block (ragged last block)
+MS_WIDE = [65, 100, 128, 200, 256]
 
 
 def _dev_i8(a):
@@ -40,8 +43,20 @@ def test_decode_int32_exact(m, n, k):
     assert np.array_equal(host(acc), oracle.int8_matmul(xq, wq))
 
 
+@pytest.mark.parametrize("n,k", [(4096, 14336), (14336, 4096), (301, 1152), (64, 128)])
+@pytest.mark.parametrize("m", MS_WIDE)
+def test_decode_int32_exact_wide(m, n, k):
+    """Token blocks beyond the first (the shapes the decode kernel takes
+    above 64 tokens, and the others through whichever kernel they route to)."""
+    log("decode i32 wide", m, n, k, "ws", sq.raw["sq_w8a8_linear_workspace_size"](m, n, k))
+    xq = workloads.uniform_int8((m, k), seed=m * 3 + n + k, stream=14)
+    wq = workloads.uniform_int8((n, k), seed=m * 3 + n + k, stream=15)
+    acc = sq.sq_w8a8_linear(_dev_i8(xq), None, _dev_i8(wq), None, out_dtype=torch.int32)
+    assert np.array_equal(host(acc), oracle.int8_matmul(xq, wq))
+
+
 @pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("m,n,k", [(1, 4096, 14336), (8, 301, 1152), (32, 14336, 4096), (64, 99, 256)])
+@pytest.mark.parametrize("m,n,k", [(1, 4096, 14336), (8, 301, 1152), (32, 14336, 4096), (64, 99, 256), (100, 4096, 14336), (256, 14336, 4096)])
 def test_decode_dequant(out, m, n, k):
     log("decode dequant", out, m, n, k)
     xq = workloads.uniform_int8((m, k), seed=m + n, stream=12)
@@ -54,11 +69,13 @@ def test_decode_dequant(out, m, n, k):
     log("  exact fraction", frac)
 
 
-def test_decode_workspace_reuse():
+@pytest.mark.parametrize("m", [24, 128])
+def test_decode_workspace_reuse(m):
     """sq_w8a8_linear: a workspace zero-filled once stays usable (the kernel
-    restores its ticket counters). sq_w8a8_linear_dyn: a workspace full of
-    garbage works (the quantisation launch clears the counters)."""
-    m, n, k = 24, 4096, 14336
+    restores its ticket counters, one per 64 columns and 64-token block).
+    sq_w8a8_linear_dyn: a workspace full of garbage works (the quantisation
+    launch clears the counters)."""
+    n, k = 4096, 14336
     nb = sq.raw["sq_w8a8_linear_workspace_size"](m, n, k)
     assert nb > 0
     xq = workloads.uniform_int8((m, k), seed=5, stream=14)
@@ -69,7 +86,7 @@ def test_decode_workspace_reuse():
     for _ in range(3):
         acc = sq.sq_w8a8_linear(x_d, None, w_d, None, out_dtype=torch.int32, ws=ws)
         assert np.array_equal(host(acc), ref)
-        assert not host(ws[:4 * ((n + 63) // 64)]).any(), "ticket counters not restored"
+        assert not host(ws[:4 * ((n + 63) // 64) * ((m + 63) // 64)]).any(), "ticket counters not restored"
     c = workloads.random_linear_case(m=m, k=k, n=n, seed=3, dtype="bf16", calib_rows=64)
     s_ref = oracle.smoothing_factors(oracle.calibrate_absmax(c.x_calib), oracle.weight_row_absmax(c.w), 0.5)
     s = torch.from_numpy(s_ref).to(dev())

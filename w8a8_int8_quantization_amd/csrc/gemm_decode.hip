@@ -1,5 +1,6 @@
-// Decode-shaped int8 GEMM (M <= 64 tokens): Y = dequant(Xq . Wq^T), where the
-// cost is streaming the weight matrix Wq [N x K] from HBM once.
+// Decode-shaped int8 GEMM (M <= 64 tokens, and up to 256 where the tiled
+// kernels would cover few CUs): Y = dequant(Xq . Wq^T), where the cost is
+// streaming the weight matrix Wq [N x K] from HBM.
 //
 // The LLM.int8() page, "The architecture: every piece explained" (int8
 // operands, int32 accumulation, dequantisation by the outer product of the row
@@ -139,6 +140,10 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
   const int tile = blockIdx.x;
   const int slice = blockIdx.y;
   const int n0 = tile * kDecRows;
+  // tokens m0 .. m0 + 63 (blockIdx.z: one grid layer per 64 tokens; every
+  // layer streams the same Wq, whose re-reads hit the last-level cache)
+  const int m0 = (int)blockIdx.z * 64;
+  const int ctr = (int)blockIdx.z * (int)gridDim.x + tile;
   const int step0 = slice * a.slice_steps;
   const int nsl = min(a.slice_steps, a.K / kDecStep - step0);  // >= 1 by construction of S
 
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
   for (int g = 0; g < 4; ++g) wp[g] = a.wq + (int64_t)min(n0 + 16 * g + (lane & 15), a.N - 1) * a.K + kb;
   const int8_t* xp[kMB];
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) xp[mb] = a.xq + (int64_t)min(16 * mb + (lane & 15), a.M - 1) * a.K + kb;
+  for (int mb = 0; mb < kMB; ++mb) xp[mb] = a.xq + (int64_t)min(m0 + 16 * mb + (lane & 15), a.M - 1) * a.K + kb;
 
   AccT acc[4][kMB];
 #pragma unroll
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
   const int n = n0 + 4 * q;
   if (a.S == 1) {
 #pragma unroll
-    for (int j = 0; j < kMB; ++j) dec_epilogue<kF8>(a, (tid >> 4) + 16 * j, n, sum[j]);
+    for (int j = 0; j < kMB; ++j) dec_epilogue<kF8>(a, m0 + (tid >> 4) + 16 * j, n, sum[j]);
     return;
   }
 
@@ -272,7 +277,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
   const bool vec = (a.N & 3) == 0;
 #pragma unroll
   for (int j = 0; j < kMB; ++j) {
-    const int m = (tid >> 4) + 16 * j;
+    const int m = m0 + (tid >> 4) + 16 * j;
     if (m < a.M && n < a.N) {
       const uint32_t off = (uint32_t)((((size_t)slice * a.M + m) * a.N + n) * 4);
       if (vec) {
@@ -288,12 +293,12 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0)
-    last_ticket = __hip_atomic_fetch_add(a.counter + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_ticket = __hip_atomic_fetch_add(a.counter + ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (last_ticket != (uint32_t)(a.S - 1)) return;
 #pragma unroll
   for (int j = 0; j < kMB; ++j) {
-    const int m = (tid >> 4) + 16 * j;
+    const int m = m0 + (tid >> 4) + 16 * j;
     if (m >= a.M || n >= a.N) continue;
     AccT t = {0, 0, 0, 0};
     const uint32_t off0 = (uint32_t)(((size_t)m * a.N + n) * 4);
@@ -327,7 +332,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
     dec_epilogue<kF8>(a, m, n, tt);
   }
   // every ticket of this tile has been drawn: restore the counter for the next call
-  if (tid == 0) __hip_atomic_store(a.counter + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(a.counter + ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace sqk
@@ -341,20 +346,23 @@ struct DecodePlan {
   int slice_steps = 0;
   int ns = 0;      // steps per wave
   int tiles = 0;
+  int tb = 1;      // 64-token blocks (grid z)
 };
 
 DecodePlan decode_plan(int64_t m, int64_t n, int64_t k) {
   DecodePlan p;
   const int steps = (int)(k / sqk::kDecStep);
   p.tiles = (int)((n + sqk::kDecRows - 1) / sqk::kDecRows);
+  p.tb = (int)((m + 63) / 64);
   // at least one workgroup per CU (256 CUs), with at most kDecMaxNS steps
   // per wave; measured on MI355X, more slices than that only add partial-tile
   // traffic and reduction latency. Above 16 tokens the partial tiles grow
   // (S x M x N x 4 bytes written and read back), and three workgroups in four
   // of the CUs streaming unsplit K are faster (14336 columns: M 64 26.8 ->
   // 22.9 us, M 32 18.3 -> 16.4 us).
-  int want = (256 + p.tiles - 1) / p.tiles;
-  if (m > 16 && p.tiles >= 192) want = 1;
+  const int wgs = p.tiles * p.tb;
+  int want = (256 + wgs - 1) / wgs;
+  if (m > 16 && wgs >= 192) want = 1;
 #ifdef SQ_TUNE
   if (const char* e = getenv("SQ_DECODE_SPLIT")) want = atoi(e);
 #endif
@@ -398,9 +406,9 @@ hipError_t decode_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
   a.out = yt == SQ_F32 ? 0 : yt == SQ_BF16 ? 1 : yt == SQ_F16 ? 2 : 3;
   if (p.S > 1) {
     a.counter = reinterpret_cast<uint32_t*>(ws);
-    a.partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + counter_bytes(p.tiles));
+    a.partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + counter_bytes(p.tiles * p.tb));
   }
-  const dim3 grid((unsigned)p.tiles, (unsigned)p.S);
+  const dim3 grid((unsigned)p.tiles, (unsigned)p.S, (unsigned)p.tb);
   bool mb1 = m <= 16;
 #ifdef SQ_TUNE
   if (getenv("SQ_DECODE_MB2")) mb1 = false;
@@ -412,15 +420,39 @@ hipError_t decode_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
 
 }  // namespace
 
+// Up to 256 tokens the decode kernel runs one grid layer per 64 tokens.
+constexpr int64_t kDecodeMaxM = 256;
+
+// Whether 65..256 tokens go to the decode kernel rather than the tiled
+// kernels. The decode kernel streams Wq once per 64-token layer (time grows
+// about linearly with the layers); the tiled kernels are slow when their
+// output tiles cover few CUs. Counted in 128 x 128 tile units (a 256 x 192
+// prefill tile is 3), decode wins when the tiled kernel has at most 128 units:
+// measured on MI355X (GEMM us, tiled -> decode), 4096 -> 14336 columns:
+// M 96 42.4 -> 36.0, M 128 43.5 -> 39.8 (decode), M 192 43.3 vs 57.5, M 256
+// 43.9 vs 75.0 (tiled); 14336 -> 4096: M 96 113.8 -> 42.7, M 128 125.2 ->
+// 47.6, M 192 111.8 -> 68.3, M 256 114.4 -> 88.6 (decode).
+static bool decode_beats_prefill(int64_t m, int64_t n) {
+  const bool big = m >= 256 && m * n >= ((int64_t)1 << 20);
+  const int64_t units = big ? ((m + 255) / 256) * ((n + 191) / 192) * 3 : ((m + 127) / 128) * ((n + 127) / 128);
+  return units <= 128;
+}
+
 bool gemm_decode_suits(int64_t m, int64_t n, int64_t k) {
-  return m >= 1 && m <= 64 && n >= 1 && k % sqk::kDecStep == 0;
+  if (!(m >= 1 && m <= kDecodeMaxM && n >= 1 && n <= INT32_MAX && k % sqk::kDecStep == 0)) return false;
+  if (m <= 64) return true;
+  // beyond one 64-token block only where the prefill kernels get few tiles
+  // (see the dispatch notes); the partial tiles must fit 32-bit offsets
+  const DecodePlan p = decode_plan(m, n, k);
+  if ((size_t)p.S * (size_t)m * (size_t)n * 4 >= ((size_t)1 << 31)) return false;
+  return decode_beats_prefill(m, n);
 }
 
 size_t gemm_decode_workspace(int64_t m, int64_t n, int64_t k) {
   if (!gemm_decode_suits(m, n, k)) return 0;
   const DecodePlan p = decode_plan(m, n, k);
   if (p.S == 1) return 0;
-  return counter_bytes(p.tiles) + (size_t)p.S * (size_t)m * (size_t)n * 4;
+  return counter_bytes(p.tiles * p.tb) + (size_t)p.S * (size_t)m * (size_t)n * 4;
 }
 
 void gemm_decode_counters(int64_t m, int64_t n, int64_t k, void* ws, uint32_t** counters, int64_t* count) {
@@ -430,7 +462,7 @@ void gemm_decode_counters(int64_t m, int64_t n, int64_t k, void* ws, uint32_t** 
   const DecodePlan p = decode_plan(m, n, k);
   if (p.S == 1) return;
   *counters = reinterpret_cast<uint32_t*>(ws);
-  *count = p.tiles;
+  *count = (int64_t)p.tiles * p.tb;
 }
 
 hipError_t gemm_i8_decode(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
