@@ -176,16 +176,18 @@ sq_status sq_quant_act_per_token(const void* x, sq_dtype xt, int64_t m, int64_t 
  * xq: [M x K], wq: [N x K] (K-contiguous, rows 16-byte aligned), y: [M x ldy].
  * K must not exceed SQ_MAX_K_INT32.
  * ws: workspace of sq_w8a8_linear_workspace_size(m, n, k) bytes, 16-byte
- *     aligned; NULL when that size is 0. The size is non-zero for decode
- *     shapes (K % 128 == 0 and M <= 64, or M <= 256 where the tiled kernels
- *     would cover few compute units) whose K is split over several
- *     workgroups: the workspace then holds int32 partial tiles and one ticket
- *     counter per 64 output columns and 64 tokens. The caller zero-fills the workspace once,
- *     before its first use; every call leaves the counters at zero again, so
- *     later calls need no clearing. One workspace serves one call at a time
- *     (calls in flight together on different streams need their own).
- *     The split changes only how the exact int32 sum is formed, never its
- *     value.
+ *     aligned; NULL when that size is 0. The size is non-zero where K is
+ *     split over several workgroups: decode shapes (K % 128 == 0 and
+ *     M <= 64, or M <= 256 where the tiled kernels would cover few compute
+ *     units; one ticket counter per 64 output columns and 64 tokens) and
+ *     prefill shapes whose 256-row tiles number fewer than 128 (up to 4
+ *     slices of at least 1024 K each; one ticket counter per output tile).
+ *     The workspace then holds the counters and int32 partial tiles. The
+ *     caller zero-fills the workspace once, before its first use; every call
+ *     leaves the counters at zero again, so later calls need no clearing.
+ *     One workspace serves one call at a time (calls in flight together on
+ *     different streams need their own). The split changes only how the
+ *     exact int32 sum is formed, never its value.
  */
 size_t sq_w8a8_linear_workspace_size(int64_t m, int64_t n, int64_t k);
 sq_status sq_w8a8_linear(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
@@ -324,8 +326,9 @@ sq_status sq_silu_mul_w8a8_linear(const void* gate, const void* up, sq_dtype t, 
  *   SQ_BF16 or SQ_F16. K % 128 == 0, K <= SQ_MAX_K_FP8.
  *   ws: sq_fp8_linear_workspace_size(m, n, k) bytes, 16-byte aligned (NULL
  *   when that is 0), with the contract of sq_w8a8_linear's workspace: for
- *   decode shapes (M <= 64) whose K is split over several workgroups it
- *   holds binary32 partial tiles and the ticket counters, which the caller
+ *   shapes whose K is split over several workgroups (the decode and prefill
+ *   cases of sq_w8a8_linear) it holds binary32 partial tiles and the ticket
+ *   counters, which the caller
  *   zero-fills once and every call leaves at zero; one call at a time per
  *   workspace. The partial tiles are added in a fixed order (deterministic
  *   results), each sum rounded to binary32.

@@ -1,0 +1,194 @@
+"""Prefill GEMMs with K split over several workgroups, against the oracle.
+
+Where the 256-row tiles number fewer than 128 (the down projection's 4096
+output columns at up to 1792 tokens, say) the prefill kernel splits K into up
+to 4 slices; the last workgroup of each tile adds the slices' partial tiles
+in slice order. int32 accumulators must stay bit-exact (the split changes
+only the order of an exact sum), outputs within 1 ulp of the oracle, E4M3
+outputs within the bound of the FP8 tests, and every path deterministic.
+Every call goes through the C ABI via the ctypes binding.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import assert_out_close, bits16, dev, host, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+sq = pytest.importorskip("w8a8_int8_quantization_amd")
+
+TDT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+# (M, N, K): 2 to 4 slices, ragged M and N tails, a last slice shorter than
+# the others (K 3200 = 25 stages of 128 in slices of 9, 9, 7), the down
+# projection of the 8B model at 257 and 512 tokens
+SPLIT_SHAPES = [(256, 8192, 2048), (300, 4000, 4096), (1000, 1100, 3200), (257, 4096, 14336),
+                (512, 4096, 14336), (640, 1920, 8192)]
+
+
+def _d(a):
+    return torch.from_numpy(a).to(dev())
+
+
+@pytest.mark.parametrize("m,n,k", SPLIT_SHAPES)
+def test_split_int32_exact(m, n, k):
+    need = sq.raw["sq_w8a8_linear_workspace_size"](m, n, k)
+    log("split-K gemm i32", m, n, k, "workspace bytes", need)
+    assert need > 0, "shape expected to split K"
+    xq = workloads.uniform_int8((m, k), seed=m + n + k, stream=10)
+    wq = workloads.uniform_int8((n, k), seed=m + n + k, stream=11)
+    acc = sq.sq_w8a8_linear(_d(xq), None, _d(wq), None, out_dtype=torch.int32)
+    assert np.array_equal(host(acc), oracle.int8_matmul(xq, wq))
+
+
+def test_split_extremes():
+    """Rows of +-127 at K 14336 in 4 slices: partial sums of +-57,806,336 per
+    slice add up to +-231,225,344 exactly."""
+    m, n, k = 300, 4096, 14336
+    rng = np.random.default_rng(8)
+    si = rng.choice([-1, 1], size=m).astype(np.int64)
+    tn = rng.choice([-1, 1], size=n).astype(np.int64)
+    xq = (si[:, None] * np.full((m, k), 127)).astype(np.int8)
+    wq = (tn[:, None] * np.full((n, k), 127)).astype(np.int8)
+    acc = host(sq.sq_w8a8_linear(_d(xq), None, _d(wq), None, out_dtype=torch.int32))
+    assert np.array_equal(acc.astype(np.int64), 127 * 127 * k * (si[:, None] * tn[None, :]))
+
+
+@pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("m,n,k", [(300, 4000, 4096), (512, 4096, 14336)])
+def test_split_dequant(out, m, n, k):
+    log("split-K gemm dequant", out, m, n, k)
+    xq = workloads.uniform_int8((m, k), seed=5 * m + n, stream=12)
+    wq = workloads.uniform_int8((n, k), seed=5 * m + n, stream=13)
+    dx = workloads.positive_scales(m, seed=m, stream=4)
+    dw = workloads.positive_scales(n, seed=n, stream=5) * np.float32(1e-3)
+    y = sq.sq_w8a8_linear(_d(xq), _d(dx), _d(wq), _d(dw), out_dtype=TDT[out])
+    frac = assert_out_close(y, oracle.w8a8_linear(xq, dx, wq, dw, out), out)
+    log("  exact fraction", frac)
+
+
+def test_split_padded_output():
+    """Output rows with a pitch of N + 5: the padding is left alone."""
+    m, n, k = 300, 4000, 4096
+    xq = workloads.uniform_int8((m, k), seed=2, stream=14)
+    wq = workloads.uniform_int8((n, k), seed=2, stream=15)
+    dx = workloads.positive_scales(m, seed=6)
+    dw = workloads.positive_scales(n, seed=7)
+    big = torch.full((m, n + 5), -7.0, dtype=torch.float32, device=dev())
+    y = big[:, :n]
+    sq.sq_w8a8_linear(_d(xq), _d(dx), _d(wq), _d(dw), out_dtype=torch.float32, y=y)
+    assert np.array_equal(host(y), oracle.w8a8_linear(xq, dx, wq, dw, "f32"))
+    assert np.all(host(big)[:, n:] == -7.0)
+
+
+def test_split_workspace_reuse():
+    """The tile counters are left at zero: one workspace serves repeated calls
+    at this shape and then a smaller one, with identical results."""
+    m, n, k = 512, 4096, 14336
+    xq = _d(workloads.uniform_int8((m, k), seed=31, stream=16))
+    wq = _d(workloads.uniform_int8((n, k), seed=31, stream=17))
+    ws = sq.linear_workspace(m, n, k, dev())
+    assert ws is not None
+    first = host(sq.sq_w8a8_linear(xq, None, wq, None, out_dtype=torch.int32, ws=ws))
+    for _ in range(3):
+        assert np.array_equal(host(sq.sq_w8a8_linear(xq, None, wq, None, out_dtype=torch.int32, ws=ws)), first)
+    # 2 x 22 tiles of 256 x 192: the counters fill the first 176 bytes
+    assert int(ws[:256].view(torch.int32).abs().sum()) == 0
+    m2 = 300
+    assert 0 < sq.raw["sq_w8a8_linear_workspace_size"](m2, n, k) <= ws.numel()
+    acc2 = host(sq.sq_w8a8_linear(xq[:m2], None, wq, None, out_dtype=torch.int32, ws=ws))
+    assert np.array_equal(acc2, first[:m2])
+
+
+@pytest.mark.parametrize("path", ["dyn", "rmsnorm", "silu"])
+def test_split_fused_calls_garbage_workspace(path):
+    """The one-call paths clear the tile counters in their quantisation
+    launch: a workspace full of garbage gives the two-call result."""
+    m, k, n = 400, 14336, 4096
+    c = workloads.random_linear_case(m=m, k=k, n=n, seed=41, dtype="bf16", calib_rows=64)
+    s_ref = oracle.smoothing_factors(oracle.calibrate_absmax(c.x_calib), oracle.weight_row_absmax(c.w), 0.5)
+    s = torch.from_numpy(s_ref).to(dev())
+    _, wq, sw = sq.sq_smooth_fold_weights(to_dev(c.w, "bf16"), smooth=s, flags=sq.SMOOTH_GIVEN)
+    x = to_dev(c.x, "bf16")
+    name = {"dyn": "sq_w8a8_linear_dyn", "rmsnorm": "sq_rmsnorm_w8a8_linear",
+            "silu": "sq_silu_mul_w8a8_linear"}[path]
+    nb = sq.raw[name + "_workspace_size"](m, n, k)
+    assert nb > m * k + sq.raw["sq_w8a8_linear_workspace_size"](m, n, k) > m * k
+    ws = torch.full((nb,), 0xA7, dtype=torch.uint8, device=dev())
+    if path == "dyn":
+        y1 = sq.sq_w8a8_linear_dyn(x, s, wq, sw, ws=ws)
+        xq, dx = sq.sq_quant_act_per_token(x, s)
+    elif path == "rmsnorm":
+        gain = (1.0 / s).contiguous()
+        y1 = sq.sq_rmsnorm_w8a8_linear(x, gain, 1e-6, wq, sw, ws=ws)
+        xq, dx = sq.sq_rmsnorm_quant(x, gain, 1e-6)
+    else:
+        up = to_dev(c.x[::-1].copy(), "bf16")
+        y1 = sq.sq_silu_mul_w8a8_linear(x, up, s, wq, sw, ws=ws)
+        xq, dx = sq.sq_silu_mul_quant(x, up, s)
+    y2 = sq.sq_w8a8_linear(xq, dx, wq, sw)
+    assert np.array_equal(bits16(y1), bits16(y2))
+    acc = host(sq.sq_w8a8_linear(xq, None, wq, None, out_dtype=torch.int32))
+    assert np.array_equal(acc, oracle.int8_matmul(host(xq), host(wq)))
+
+
+# ----------------------------------------------------------------------------- E4M3
+def _fp8_case(m, n, k, seed):
+    c = workloads.random_linear_case(m=m, k=k, n=n, seed=seed, dtype="bf16", calib_rows=8)
+    xq, d = oracle.quantize_activations_fp8(c.x)
+    wq, sw = oracle.quantize_weights_fp8(c.w)
+    return xq, d, wq, sw
+
+
+def _fp8_check(y, xq, d, wq, sw, out):
+    """|y - exact| within the E4M3 accumulation bound: 2^-11 of the sum of
+    |products| (binary32 sums of up to 64 exact products, then of the
+    partials), one ulp of the output type and two binary32 roundings of the
+    scaling."""
+    g = host(y.float()).astype(np.float64)
+    a = oracle.e4m3_decode(xq).astype(np.float64)
+    b = oracle.e4m3_decode(wq).astype(np.float64)
+    sc = d.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :]
+    exact = (a @ b.T) * sc
+    mag = (np.abs(a) @ np.abs(b).T) * sc
+    ulp_bits = {"bf16": 8, "f16": 11, "f32": 24}[out]
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(exact), 1e-38))) - (ulp_bits - 1))
+    bound = 2.0 ** -11 * mag + ulp + 2.0 ** -22 * np.abs(exact)
+    err = np.abs(g - exact)
+    log("  max err/bound", float(np.max(err / bound)))
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("m,n,k,out", [(512, 4096, 14336, "bf16"), (300, 4000, 4096, "f32"),
+                                       (777, 4000, 2176, "f16")])
+def test_fp8_split(m, n, k, out):
+    need = sq.raw["sq_fp8_linear_workspace_size"](m, n, k)
+    log("split-K fp8 gemm", m, n, k, out, "workspace bytes", need)
+    assert need > 0
+    xq, d, wq, sw = _fp8_case(m, n, k, seed=m + n + k)
+    args = [torch.from_numpy(a).to(dev()) for a in (xq, d, wq, sw)]
+    ws = sq.fp8_linear_workspace(m, n, k, dev())
+    y = sq.sq_fp8_linear(*args, out_dtype=TDT[out], ws=ws)
+    _fp8_check(y, xq, d, wq, sw, out)
+    # deterministic: the partial tiles are added in slice order
+    y2 = sq.sq_fp8_linear(*args, out_dtype=TDT[out], ws=ws)
+    assert torch.equal(y.view(torch.int16 if out != "f32" else torch.int32),
+                       y2.view(torch.int16 if out != "f32" else torch.int32))
+
+
+def test_fp8_split_dyn_garbage_workspace():
+    m, n, k = 512, 4096, 14336
+    c = workloads.random_linear_case(m=m, k=k, n=n, seed=5, dtype="bf16", calib_rows=8)
+    x = to_dev(c.x, "bf16")
+    wq, sw = sq.sq_quant_weights_fp8(to_dev(c.w, "bf16"))
+    xq, d = sq.sq_quant_act_fp8(x)
+    y2 = sq.sq_fp8_linear(xq, d, wq, sw)
+    nb = sq.raw["sq_fp8_linear_dyn_workspace_size"](m, n, k)
+    assert nb > m * k + sq.raw["sq_fp8_linear_workspace_size"](m, n, k) > m * k
+    ws = torch.full((nb,), 0x5C, dtype=torch.uint8, device=dev())
+    y1 = sq.sq_fp8_linear_dyn(x, wq, sw, ws=ws)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    _fp8_check(y1, host(xq), host(d), host(wq), host(sw), "bf16")

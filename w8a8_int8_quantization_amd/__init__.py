@@ -142,7 +142,8 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 def linear_workspace(m: int, n: int, k: int, device) -> Optional[torch.Tensor]:
     """A zero-filled workspace for ``sq_w8a8_linear`` at this shape (None if it needs none).
 
-    Reusable across calls at the same shape: each call leaves it zero-filled."""
+    Reusable across calls at the same shape: each call restores its counter
+    words to zero (the rest is scratch that every call writes before reading)."""
     nb = raw["sq_w8a8_linear_workspace_size"](m, n, k)
     return torch.zeros(nb, dtype=torch.uint8, device=device) if nb else None
 

@@ -72,9 +72,13 @@ sq_status quant_then_gemm(Quant quant, const int8_t* wq, const float* w_scale, i
     if (e != hipSuccess) return hip_status(e);
     return hip_status(sqh::gemm_i8_decode(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, gws, s));
   }
-  hipError_t e = quant(xq, dx, nullptr, 0);
+  // prefill shapes split over K: the quantisation launch clears the tile counters
+  uint32_t* counters;
+  int64_t ncount;
+  sqh::gemm_big_counters(m, n, k, false, gws, &counters, &ncount);
+  hipError_t e = quant(xq, dx, counters, ncount);
   if (e != hipSuccess) return hip_status(e);
-  return hip_status(sqh::gemm_i8(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, nullptr, s));
+  return hip_status(sqh::gemm_i8(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, nullptr, gws, s));
 }
 
 }  // namespace
@@ -151,7 +155,8 @@ sq_status sq_quant_act_per_token(const void* x, sq_dtype xt, int64_t m, int64_t 
 
 size_t sq_w8a8_linear_workspace_size(int64_t m, int64_t n, int64_t k) {
   if (m <= 0 || n <= 0 || k <= 0 || k % 64 != 0) return 0;
-  return sqh::gemm_decode_workspace(m, n, k);
+  if (sqh::gemm_decode_suits(m, n, k)) return sqh::gemm_decode_workspace(m, n, k);
+  return sqh::gemm_big_workspace(m, n, k, false);
 }
 
 // Shapes, output type and the weight-side pointers of the GEMM.
@@ -194,7 +199,8 @@ sq_status sq_w8a8_linear(const int8_t* xq, const float* x_scale, const int8_t* w
   // caller's contract) and restored to zero by the kernel
   if (sqh::gemm_decode_suits(m, n, k))
     return hip_status(sqh::gemm_i8_decode(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, ws, s));
-  return hip_status(sqh::gemm_i8(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, nullptr, s));
+  // prefill shapes split over K: the same contract for the tile counters
+  return hip_status(sqh::gemm_i8(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, nullptr, ws, s));
 }
 
 size_t sq_w8a8_linear_dyn_workspace_size(int64_t m, int64_t n, int64_t k) {
@@ -364,7 +370,8 @@ static sq_status check_fp8_gemm(const uint8_t* wq, const float* w_scale, int64_t
 
 size_t sq_fp8_linear_workspace_size(int64_t m, int64_t n, int64_t k) {
   if (m <= 0 || n <= 0 || k <= 0) return 0;
-  return sqh::gemm_decode_workspace(m, n, k);
+  if (sqh::gemm_decode_suits(m, n, k)) return sqh::gemm_decode_workspace(m, n, k);
+  return sqh::gemm_big_workspace(m, n, k, true);
 }
 
 sq_status sq_fp8_linear(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
@@ -382,7 +389,7 @@ sq_status sq_fp8_linear(const uint8_t* xq, const float* x_scale, const uint8_t* 
   // caller's contract) and restored to zero by the kernel
   if (sqh::gemm_decode_suits(m, n, k))
     return hip_status(sqh::gemm_f8_decode(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, ws, s));
-  return hip_status(sqh::gemm_f8(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, s));
+  return hip_status(sqh::gemm_f8(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, ws, s));
 }
 
 size_t sq_fp8_linear_dyn_workspace_size(int64_t m, int64_t n, int64_t k) {
@@ -411,9 +418,12 @@ sq_status sq_fp8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const uint8
     if (e != hipSuccess) return hip_status(e);
     return hip_status(sqh::gemm_f8_decode(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, gws, s));
   }
-  hipError_t e = sqh::quant_f8_rows(x, xt, m, k, ldx, xq, dx, s);
+  uint32_t* counters;
+  int64_t ncount;
+  sqh::gemm_big_counters(m, n, k, true, gws, &counters, &ncount);
+  hipError_t e = sqh::quant_f8_rows(x, xt, m, k, ldx, xq, dx, s, counters, ncount);
   if (e != hipSuccess) return hip_status(e);
-  return hip_status(sqh::gemm_f8(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, s));
+  return hip_status(sqh::gemm_f8(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, gws, s));
 }
 
 // ---------------------------------------------------------------- GPTQ
@@ -533,7 +543,7 @@ sq_status sq_int8_decomp_linear(const void* x, int64_t ldx, const int8_t* wq, co
   if (e != hipSuccess) return hip_status(e);
   if (m == 0 || n == 0) return SQ_OK;
   sqh::DecompArgs d{(const uint16_t*)x, ldx, (const uint16_t*)w16, ldw16, idx, n_outliers};
-  return hip_status(sqh::gemm_i8(xq, dx, wq, w_scale, m, n, k, y, SQ_F16, ldy, &d, s));
+  return hip_status(sqh::gemm_i8(xq, dx, wq, w_scale, m, n, k, y, SQ_F16, ldy, &d, nullptr, s));
 }
 
 sq_status sq_int8_decomp_gemm(const int8_t* xq, const float* x_scale, const void* x, int64_t ldx, const int8_t* wq,
@@ -552,7 +562,7 @@ sq_status sq_int8_decomp_gemm(const int8_t* xq, const float* x_scale, const void
       (reinterpret_cast<uintptr_t>(y) & 1u))
     return SQ_ERR_ALIGN;
   sqh::DecompArgs d{(const uint16_t*)x, ldx, (const uint16_t*)w16, ldw16, idx, n_outliers};
-  return hip_status(sqh::gemm_i8(xq, x_scale, wq, w_scale, m, n, k, y, SQ_F16, ldy, &d, (hipStream_t)stream));
+  return hip_status(sqh::gemm_i8(xq, x_scale, wq, w_scale, m, n, k, y, SQ_F16, ldy, &d, nullptr, (hipStream_t)stream));
 }
 
 }  // extern "C"

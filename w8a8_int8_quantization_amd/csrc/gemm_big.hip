@@ -31,6 +31,7 @@
 //  * Workgroups are dispatched round-robin over the 8 XCDs; the tile order
 //    gives each XCD a contiguous range of tiles, grouped 4 tile-rows at a time,
 //    so that tiles sharing Xq and Wq panels run under the same L2.
+#include <cstdlib>
 #include <type_traits>
 
 #include "sq_common.hpp"
@@ -84,7 +85,22 @@ struct BigEpi {
   int64_t ldy;
   sqh::DecompArgs dec;
   bool rows16;  // y and every output row start 16-byte aligned: staged full-row stores
+  // split K (kSplit kernels): S slices of slice_stages stages each; partial
+  // tiles [S][M][N] (int32, or binary32 bits) and one ticket counter per tile,
+  // zero at launch and restored to zero by the tile's last workgroup
+  int32_t* partial;
+  uint32_t* counter;
+  int S;
+  int slice_stages;
 };
+
+// Buffer descriptor word 3 of a raw byte buffer on gfx9, and the cache-policy
+// operand of device-coherent (sc1) buffer accesses: partial tiles cross XCDs,
+// whose L2 caches are not coherent with each other.
+constexpr int kBigBufDword3 = 0x00020000;
+// at most this many K slices per output tile
+constexpr int kBigMaxSplit = 4;
+constexpr int kBigCoherent = 16;
 
 // s_waitcnt vmcnt(n) with the lgkm and exp counters left alone (gfx9 encoding).
 template <int kN>
@@ -129,7 +145,9 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // kF8: E4M3 operands (one code per byte) on v_mfma_scale_f32_32x32x64_f8f6f4
 // with binary32 accumulators, two 64-k substeps per stage instead of four
 // 32-k ones; everything else is shared with the int8 kernel.
-template <int BN, int kOut, bool kVec, bool kF8 = false>
+// kSplit: the K range is split over blockIdx.y (see BigEpi); the tile's last
+// workgroup adds the S partial tiles in slice order, then runs the epilogue.
+template <int BN, int kOut, bool kVec, bool kF8 = false, bool kSplit = false>
 __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
                                                           int M, int N, int K, BigEpi ep) {
   using C = BigCfg<BN>;
@@ -159,6 +177,9 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
   const int tm = first_m + (t % in_group) % gm;
   const int tn = (t % in_group) / gm;
   const int m0 = tm * kBigBM, n0 = tn * BN;
+  // this workgroup's stages: kt0 .. kt0 + nk - 1
+  const int kt0 = kSplit ? (int)blockIdx.y * ep.slice_stages : 0;
+  const int nk = kSplit ? min(ep.slice_stages, K / kBigBK - kt0) : K / kBigBK;
 
   // ---- direct-to-LDS transfers: lane L of a 1 KiB transfer fills LDS bytes
   // [16L, 16L+16) of an 8-row block, i.e. row L/8, physical chunk L%8, so it
@@ -173,14 +194,13 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
     const int r = blk * 8 + (lane >> 3);
     const int c = (lane & 7) ^ big_swz(r);
     if (is_a) {
-      src[i] = A + (int64_t)min(m0 + r, M - 1) * K + c * 16;
+      src[i] = A + (int64_t)min(m0 + r, M - 1) * K + (int64_t)kt0 * kBigBK + c * 16;
       dst[i] = blk * 1024;
     } else {
-      src[i] = B + (int64_t)min(n0 + r, N - 1) * K + c * 16;
+      src[i] = B + (int64_t)min(n0 + r, N - 1) * K + (int64_t)kt0 * kBigBK + c * 16;
       dst[i] = C::kStageA + blk * 1024;
     }
   }
-  const int nk = K / kBigBK;
   auto issue = [&](int kt) {
     int8_t* stage = smem + (kt % kBigStages) * C::kStage;
     const int64_t koff = (int64_t)kt * kBigBK;
@@ -285,6 +305,90 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
       // the next substep uses them
       wait_lgkmcnt0();
     }
+  }
+
+  if constexpr (kSplit) {
+    // ---- split K: publish this slice's tile (coherent buffer stores), take
+    // a ticket; the last workgroup of the tile adds all S slices in order
+    __shared__ uint32_t last_ticket;
+    const uint32_t pbytes = (uint32_t)((size_t)ep.S * M * N * 4);
+    const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(ep.partial, (short)0, pbytes, kBigBufDword3);
+    const uint32_t sstride = (uint32_t)((size_t)M * N * 4);
+    // byte offset of the 4 outputs (j, i, rg) within a slice, or ~0u where
+    // the row is past M; columns past N are handled one by one
+    auto part_off = [&](int j, int i, int rg) -> uint32_t {
+      const int m = m0 + wm * C::kWM + 32 * i + frow;
+      const int n = n0 + wn * C::kWN + 32 * j + 8 * rg + 4 * fhalf;
+      return (m < M && n < N) ? (uint32_t)(((size_t)m * N + n) * 4) : ~0u;
+    };
+    auto ncols = [&](int j, int rg) { return min(4, N - (n0 + wn * C::kWN + 32 * j + 8 * rg + 4 * fhalf)); };
+    const uint32_t soff = (uint32_t)blockIdx.y * sstride;
+#pragma unroll
+    for (int j = 0; j < C::kFN; ++j)
+#pragma unroll
+      for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const uint32_t off = part_off(j, i, rg);
+          if (off == ~0u) continue;
+          // bit_cast the whole accumulator, then pick elements: a bit_cast of
+          // one vector element reads element 0 of the vector in this compiler
+          const v16i bits = __builtin_bit_cast(v16i, acc[j][i]);
+          const v4i v = {bits[4 * rg], bits[4 * rg + 1], bits[4 * rg + 2], bits[4 * rg + 3]};
+          const int nv = ncols(j, rg);
+          if (nv == 4) {
+            __builtin_amdgcn_raw_buffer_store_b128(v, pr, soff + off, 0, kBigCoherent);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (e < nv) __builtin_amdgcn_raw_buffer_store_b32(v[e], pr, soff + off + 4 * e, 0, kBigCoherent);
+          }
+        }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int tile_id = tm * nbn + tn;
+    if (tid == 0)
+      last_ticket = __hip_atomic_fetch_add(ep.counter + tile_id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (last_ticket != (uint32_t)(ep.S - 1)) return;
+    // slice by slice, in order (binary32 sums in a fixed order: deterministic
+    // results), the loads of one column block of the tile in flight together.
+    // Rows past M load from row 0 of the slice and add zero; in a ragged last
+    // column group the 16-byte load runs into the next row (or past the
+    // buffer's end, where it reads zeros): those columns are never stored.
+    uint32_t offv[C::kFN][C::kFM][4];
+#pragma unroll
+    for (int j = 0; j < C::kFN; ++j)
+#pragma unroll
+      for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          offv[j][i][rg] = part_off(j, i, rg);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[j][i][4 * rg + e] = 0;
+        }
+    for (int sl = 0; sl < ep.S; ++sl) {
+      const uint32_t base = (uint32_t)sl * sstride;
+#pragma unroll
+      for (int j = 0; j < C::kFN; ++j)
+#pragma unroll
+        for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const uint32_t off = offv[j][i][rg];
+            const bool ok = off != ~0u;
+            const v4i t = __builtin_amdgcn_raw_buffer_load_b128(pr, base + (ok ? off : 0u), 0, kBigCoherent);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if constexpr (kF8)
+                acc[j][i][4 * rg + e] += ok ? __int_as_float(t[e]) : 0.f;
+              else
+                acc[j][i][4 * rg + e] += ok ? t[e] : 0;
+            }
+          }
+    }
+    // every ticket of this tile has been drawn: restore the counter
+    if (tid == 0) __hip_atomic_store(ep.counter + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- epilogue: lane holds D[n][m] with m = l%32 and n = 8*(r/4) + 4*(l/32) + r%4 of each 32x32 block
@@ -493,8 +597,12 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
 template <int BN, int kOut, bool kVec, bool kF8 = false>
 static void launch_big(const int8_t* xq, const int8_t* wq, int M, int N, int K, const BigEpi& ep, hipStream_t s) {
   const int tiles = ((M + kBigBM - 1) / kBigBM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_big_kernel<BN, kOut, kVec, kF8>), dim3(tiles), dim3(kBigThreads), 0, s, xq, wq, M, N, K,
-                     ep);
+  if (ep.S > 1 && kOut != kBigDecomp)
+    hipLaunchKernelGGL((gemm_big_kernel<BN, kOut, kVec, kF8, kOut != kBigDecomp>), dim3(tiles, ep.S),
+                       dim3(kBigThreads), 0, s, xq, wq, M, N, K, ep);
+  else
+    hipLaunchKernelGGL((gemm_big_kernel<BN, kOut, kVec, kF8>), dim3(tiles), dim3(kBigThreads), 0, s, xq, wq, M, N,
+                       K, ep);
 }
 
 template <int BN, int kOut, bool kF8 = false>
@@ -533,9 +641,42 @@ static void launch_big_f8(const int8_t* xq, const int8_t* wq, int M, int N, int 
 
 namespace sqh {
 
+bool gemm_big_suits(int64_t m, int64_t n, int64_t k) {
+  return m >= 256 && n >= 192 && k % sqk::kBigBK == 0 && m * n >= ((int64_t)1 << 20);
+}
+
+namespace {
+
+using sqk::kBigMaxSplit;
+
+struct BigSplit {
+  int bn = 256;
+  int S = 1;
+  int slice_stages = 0;
+  int64_t tiles = 0;
+};
+
+// K slices for `tiles` output tiles: split when the tiles cover at most half
+// of the 256 CUs, into as many slices as fill them (at most kBigMaxSplit),
+// each of at least 8 stages. The partial tiles (S x M x N x 4 bytes, written
+// and read back once) stay small against the operands at these shapes.
+int split_for(int64_t tiles, int stages, int64_t m, int64_t n) {
+  int want = tiles <= 128 ? (int)(256 / tiles) : 1;
+#ifdef SQ_TUNE
+  if (const char* e = getenv("SQ_BIG_SPLIT")) want = atoi(e);
+#endif
+  if (want > kBigMaxSplit) want = kBigMaxSplit;
+  if (want > stages / 8) want = stages / 8;
+  if (want < 2) return 1;
+  const int per = (stages + want - 1) / want;
+  const int S = (stages + per - 1) / per;
+  if ((size_t)S * (size_t)m * (size_t)n * 4 >= ((size_t)1 << 31)) return 1;
+  return S;
+}
+
 // Output tile width that fills the 256 CUs best: useful outputs over the
 // outputs that the scheduled waves of workgroups could compute.
-static int pick_bn(int64_t m, int64_t n) {
+int pick_bn(int64_t m, int64_t n) {
   const int cands[2] = {256, 192};
   int best = 256;
   double best_eff = -1.0;
@@ -548,17 +689,60 @@ static int pick_bn(int64_t m, int64_t n) {
       best = bn;
     }
   }
+#ifdef SQ_TUNE
+  if (const char* e = getenv("SQ_BIG_BN")) best = atoi(e);
+#endif
   return best;
 }
 
-bool gemm_big_suits(int64_t m, int64_t n, int64_t k) {
-  return m >= 256 && n >= 192 && k % sqk::kBigBK == 0 && m * n >= ((int64_t)1 << 20);
+// Tile width, then the K split for that many tiles. Measured on the
+// 14336 -> 4096 projection (GEMM alone): the split pays while all
+// workgroups fit in one wave of the 256 CUs (512 tokens: 116 -> 83 us with 4
+// slices; 768: 110 -> 88 us with 3; 1024: 111 -> 96 us with 2), and costs
+// once they do not (1024 tokens with 3 slices: 133 us). 256-column tiles
+// with a split lose to 192-column ones at every size tried.
+BigSplit big_split(int64_t m, int64_t n, int64_t k, bool f8, bool split_ok = true) {
+  BigSplit p;
+  p.bn = f8 ? 192 : pick_bn(m, n);
+  p.tiles = ((m + sqk::kBigBM - 1) / sqk::kBigBM) * ((n + p.bn - 1) / p.bn);
+  const int stages = (int)(k / sqk::kBigBK);
+  p.S = split_ok ? split_for(p.tiles, stages, m, n) : 1;
+  p.slice_stages = (stages + p.S - 1) / p.S;
+  return p;
+}
+
+size_t big_counter_bytes(int64_t tiles) { return ((size_t)tiles * 4 + 255) / 256 * 256; }
+
+}  // namespace
+
+size_t gemm_big_workspace(int64_t m, int64_t n, int64_t k, bool f8) {
+  if (!gemm_big_suits(m, n, k)) return 0;
+  const BigSplit p = big_split(m, n, k, f8);
+  if (p.S == 1) return 0;
+  return big_counter_bytes(p.tiles) + (size_t)p.S * (size_t)m * (size_t)n * 4;
+}
+
+void gemm_big_counters(int64_t m, int64_t n, int64_t k, bool f8, void* ws, uint32_t** counters, int64_t* count) {
+  *counters = nullptr;
+  *count = 0;
+  if (!gemm_big_suits(m, n, k)) return;
+  const BigSplit p = big_split(m, n, k, f8);
+  if (p.S == 1) return;
+  *counters = reinterpret_cast<uint32_t*>(ws);
+  *count = p.tiles;
 }
 
 hipError_t gemm_i8_big(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
-                       int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec,
+                       int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec, void* ws,
                        hipStream_t s) {
-  sqk::BigEpi ep{x_scale, w_scale, y, ldy, dec ? *dec : DecompArgs{}, false};
+  sqk::BigEpi ep{x_scale, w_scale, y, ldy, dec ? *dec : DecompArgs{}, false, nullptr, nullptr, 1, 0};
+  const BigSplit sp = big_split(m, n, k, false, dec == nullptr);
+  if (sp.S > 1) {
+    ep.S = sp.S;
+    ep.slice_stages = sp.slice_stages;
+    ep.counter = reinterpret_cast<uint32_t*>(ws);
+    ep.partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + big_counter_bytes(sp.tiles));
+  }
   int out;
   int eb;
   if (dec) {
@@ -575,7 +759,7 @@ hipError_t gemm_i8_big(const int8_t* xq, const float* x_scale, const int8_t* wq,
                    (out == sqk::kBigI32 || reinterpret_cast<uintptr_t>(w_scale) % 16 == 0);
   ep.rows16 = (ldy * eb) % 16 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0;
   const int M = (int)m, N = (int)n, K = (int)k;
-  if (pick_bn(m, n) == 192)
+  if (sp.bn == 192)
     sqk::launch_big_o<192>(xq, wq, M, N, K, ep, out, vec, s);
   else
     sqk::launch_big_o<256>(xq, wq, M, N, K, ep, out, vec, s);
@@ -583,8 +767,15 @@ hipError_t gemm_i8_big(const int8_t* xq, const float* x_scale, const int8_t* wq,
 }
 
 hipError_t gemm_f8_big(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
-                       int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, hipStream_t s) {
-  sqk::BigEpi ep{x_scale, w_scale, y, ldy, DecompArgs{}, false};
+                       int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, hipStream_t s) {
+  sqk::BigEpi ep{x_scale, w_scale, y, ldy, DecompArgs{}, false, nullptr, nullptr, 1, 0};
+  const BigSplit sp = big_split(m, n, k, true);
+  if (sp.S > 1) {
+    ep.S = sp.S;
+    ep.slice_stages = sp.slice_stages;
+    ep.counter = reinterpret_cast<uint32_t*>(ws);
+    ep.partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + big_counter_bytes(sp.tiles));
+  }
   const int out = yt == SQ_F32 ? sqk::kBigF32 : (yt == SQ_BF16 ? sqk::kBigBF16 : sqk::kBigF16);
   const int eb = yt == SQ_F32 ? 4 : 2;
   const bool vec = (ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % (uintptr_t)(4 * eb) == 0) &&

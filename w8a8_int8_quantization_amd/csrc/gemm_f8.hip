@@ -182,9 +182,10 @@ static bool f8_big_enabled() {
 }
 
 hipError_t gemm_f8(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
-                   int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, hipStream_t s) {
+                   int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, hipStream_t s) {
   if (m <= 0 || n <= 0) return hipSuccess;
-  if (gemm_big_suits(m, n, k) && f8_big_enabled()) return gemm_f8_big(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, s);
+  if (gemm_big_suits(m, n, k) && f8_big_enabled())
+    return gemm_f8_big(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, ws, s);
   const int64_t tiles = ((m + sqk::kF8BM - 1) / sqk::kF8BM) * ((n + sqk::kF8BN - 1) / sqk::kF8BN);
   const dim3 grid((unsigned)tiles), block(256);
   const int M = (int)m, N = (int)n, K = (int)k;

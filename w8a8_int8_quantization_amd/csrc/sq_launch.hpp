@@ -56,7 +56,7 @@ hipError_t quant_f8_rows(const void* x, sq_dtype xt, int64_t m, int64_t k, int64
 hipError_t quant_f8_weights(const void* w, sq_dtype wt, int64_t k, int64_t n, int64_t ldw, float* colmax,
                             uint8_t* wq, float* w_scale, hipStream_t s);
 hipError_t gemm_f8(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
-                   int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, hipStream_t s);
+                   int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, hipStream_t s);
 
 // GPTQ (binary64): Hessian accumulation and the quantisation sweep.
 hipError_t gptq_hessian(const void* x, sq_dtype xt, int64_t t, int64_t k, int64_t ldx, const float* smooth, double* h,
@@ -65,18 +65,24 @@ size_t gptq_workspace(int64_t k, int64_t n);
 hipError_t gptq_quantize(const double* h, const void* w, sq_dtype wt, int64_t k, int64_t n, int64_t ldw,
                          const float* smooth, double damp, int8_t* wq, float* w_scale, void* ws, hipStream_t s);
 
+// ws: the prefill kernel's split-K workspace (gemm_big_workspace bytes; may
+// be null when that is 0 or when dec is given).
 hipError_t gemm_i8(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
-                   int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec,
+                   int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec, void* ws,
                    hipStream_t s);
 
 // Large-tile prefill GEMM (256-row tiles); gemm_i8 routes to it when it suits.
 bool gemm_big_suits(int64_t m, int64_t n, int64_t k);
 hipError_t gemm_i8_big(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
-                       int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec,
+                       int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec, void* ws,
                        hipStream_t s);
+// Split-K workspace of the prefill kernel (0 when the shape is not split):
+// ticket counters (zero at launch, restored by the kernel) and partial tiles.
+size_t gemm_big_workspace(int64_t m, int64_t n, int64_t k, bool f8);
+void gemm_big_counters(int64_t m, int64_t n, int64_t k, bool f8, void* ws, uint32_t** counters, int64_t* count);
 // The same kernel on E4M3 operands (binary32 accumulators); gemm_f8 routes to it when it suits.
 hipError_t gemm_f8_big(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
-                       int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, hipStream_t s);
+                       int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, hipStream_t s);
 
 // Decode GEMM (M <= 64): split-K over workgroups, partial tiles and ticket
 // counters in the workspace. The counters must be zero at launch.
