@@ -1,9 +1,9 @@
 """Prefill GEMMs with K split over several workgroups, against the oracle.
 
-Where the 256-row tiles number fewer than 128 (the down projection's 4096
-output columns at up to 1792 tokens, say) the prefill kernel splits K into up
-to 4 slices; the last workgroup of each tile adds the slices' partial tiles
-in slice order. int32 accumulators must stay bit-exact (the split changes
+Where the 256-row tiles number at most 128 (the down projection's 4096
+output columns at up to 1280 tokens, say) and K holds at least 2 x 3072, the
+prefill kernel splits K into up to 4 slices; the last workgroup of each tile
+adds the slices' partial tiles in slice order. int32 accumulators must stay bit-exact (the split changes
 only the order of an exact sum), outputs within 1 ulp of the oracle, E4M3
 outputs within the bound of the FP8 tests, and every path deterministic.
 Every call goes through the C ABI via the ctypes binding.
@@ -23,10 +23,10 @@ sq = pytest.importorskip("w8a8_int8_quantization_amd")
 TDT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 # (M, N, K): 2 to 4 slices, ragged M and N tails, a last slice shorter than
-# the others (K 3200 = 25 stages of 128 in slices of 9, 9, 7), the down
-# projection of the 8B model at 257 and 512 tokens
-SPLIT_SHAPES = [(256, 8192, 2048), (300, 4000, 4096), (1000, 1100, 3200), (257, 4096, 14336),
-                (512, 4096, 14336), (640, 1920, 8192)]
+# the others (K 9728 = 76 stages of 128 in slices of 26, 26, 24), the down
+# projection of the 8B model at 257, 512 and 768 tokens
+SPLIT_SHAPES = [(256, 8192, 8192), (300, 4000, 8192), (1000, 1100, 9728), (257, 4096, 14336),
+                (512, 4096, 14336), (640, 1920, 8192), (768, 4096, 14336)]
 
 
 def _d(a):
@@ -58,7 +58,7 @@ def test_split_extremes():
 
 
 @pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("m,n,k", [(300, 4000, 4096), (512, 4096, 14336)])
+@pytest.mark.parametrize("m,n,k", [(300, 4000, 8192), (512, 4096, 14336)])
 def test_split_dequant(out, m, n, k):
     log("split-K gemm dequant", out, m, n, k)
     xq = workloads.uniform_int8((m, k), seed=5 * m + n, stream=12)
@@ -72,7 +72,7 @@ def test_split_dequant(out, m, n, k):
 
 def test_split_padded_output():
     """Output rows with a pitch of N + 5: the padding is left alone."""
-    m, n, k = 300, 4000, 4096
+    m, n, k = 300, 4000, 8192
     xq = workloads.uniform_int8((m, k), seed=2, stream=14)
     wq = workloads.uniform_int8((n, k), seed=2, stream=15)
     dx = workloads.positive_scales(m, seed=6)
@@ -162,8 +162,8 @@ def _fp8_check(y, xq, d, wq, sw, out):
     assert np.all(err <= bound)
 
 
-@pytest.mark.parametrize("m,n,k,out", [(512, 4096, 14336, "bf16"), (300, 4000, 4096, "f32"),
-                                       (777, 4000, 2176, "f16")])
+@pytest.mark.parametrize("m,n,k,out", [(512, 4096, 14336, "bf16"), (300, 4000, 8192, "f32"),
+                                       (777, 4000, 6144, "f16")])
 def test_fp8_split(m, n, k, out):
     need = sq.raw["sq_fp8_linear_workspace_size"](m, n, k)
     log("split-K fp8 gemm", m, n, k, out, "workspace bytes", need)

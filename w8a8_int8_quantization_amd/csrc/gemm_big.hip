@@ -658,15 +658,17 @@ struct BigSplit {
 
 // K slices for `tiles` output tiles: split when the tiles cover at most half
 // of the 256 CUs, into as many slices as fill them (at most kBigMaxSplit),
-// each of at least 8 stages. The partial tiles (S x M x N x 4 bytes, written
-// and read back once) stay small against the operands at these shapes.
+// each of at least 24 stages (3072 K). Publishing and adding the partial
+// tiles (S x M x N x 4 bytes) costs about as much as 10 stages of a slice
+// per slice at these shapes: 4096 -> 14336 at 256 tokens took 44 us
+// unsplit and 72 us in 3 slices of 11 stages.
 int split_for(int64_t tiles, int stages, int64_t m, int64_t n) {
   int want = tiles <= 128 ? (int)(256 / tiles) : 1;
 #ifdef SQ_TUNE
   if (const char* e = getenv("SQ_BIG_SPLIT")) want = atoi(e);
 #endif
   if (want > kBigMaxSplit) want = kBigMaxSplit;
-  if (want > stages / 8) want = stages / 8;
+  if (want > stages / 24) want = stages / 24;
   if (want < 2) return 1;
   const int per = (stages + want - 1) / want;
   const int S = (stages + per - 1) / per;
