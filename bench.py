@@ -53,16 +53,15 @@ PEAK_FP64_TFLOPS = 78.6   # MI355X binary64 (vector FMA and matrix), TFLOP/s
 def decode_kernel_runs(m: int, n: int, k: int) -> bool:
     """Whether the library routes this GEMM to its decode kernel (the
     dispatch rule of the C ABI, repeated here to label the measured kernel):
-    M <= 64, or up to 256 tokens when the tiled kernels would have at most 128
-    units of 128 x 128 outputs."""
+    M <= 64, or up to 256 tokens when the 256-row prefill kernel does not
+    apply and the 128 x 128 tiled kernel would have at most 128 tiles."""
     if k % 128 or m < 1:
         return False
     if m <= 64:
         return True
-    if m > 256:
+    if m > 256 or (m >= 256 and m * n >= (1 << 20)):
         return False
-    big = m >= 256 and m * n >= (1 << 20)
-    units = (-(-m // 256)) * (-(-n // 192)) * 3 if big else (-(-m // 128)) * (-(-n // 128))
+    units = (-(-m // 128)) * (-(-n // 128))
     return units <= 128
 
 

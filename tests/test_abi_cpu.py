@@ -123,8 +123,8 @@ def test_validation_linear(sq):
     assert sq.raw["sq_w8a8_linear_workspace_size"](128, 4096, 14336) > 0       # down projection shape
     assert sq.raw["sq_w8a8_linear_workspace_size"](192, 14336, 4096) == 0      # up projection: tiled
     # prefill with 2 x 22 tiles of 256 x 192: K split 4 ways (28 stages of 128
-    # each), 4 partial tiles of M x N int32 after 256 bytes of tile counters
-    assert sq.raw["sq_w8a8_linear_workspace_size"](257, 4096, 14336) == 256 + 4 * 257 * 4096 * 4
+    # each), 4 x 44 partial int32 tiles after 256 bytes of tile counters
+    assert sq.raw["sq_w8a8_linear_workspace_size"](257, 4096, 14336) == 256 + 4 * 44 * 256 * 192 * 4
     assert sq.raw["sq_w8a8_linear_workspace_size"](4096, 4096, 14336) == 0     # 256 tiles: no split
     d = sq.raw["sq_w8a8_linear_dyn"]
     need = sq.raw["sq_w8a8_linear_dyn_workspace_size"](4, 4, 64)

@@ -1,7 +1,7 @@
 """Prefill GEMMs with K split over several workgroups, against the oracle.
 
-Where the 256-row tiles number at most 128 (the down projection's 4096
-output columns at up to 1280 tokens, say) and K holds at least 2 x 3072, the
+Where the 256-row tiles number fewer than 128 (the down projection's 4096
+output columns at up to 1280 tokens, say) and K holds at least 2 x 1280, the
 prefill kernel splits K into up to 4 slices; the last workgroup of each tile
 adds the slices' partial tiles in slice order. int32 accumulators must stay bit-exact (the split changes
 only the order of an exact sum), outputs within 1 ulp of the oracle, E4M3
@@ -22,11 +22,11 @@ sq = pytest.importorskip("w8a8_int8_quantization_amd")
 
 TDT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
-# (M, N, K): 2 to 4 slices, ragged M and N tails, a last slice shorter than
-# the others (K 9728 = 76 stages of 128 in slices of 26, 26, 24), the down
-# projection of the 8B model at 257, 512 and 768 tokens
-SPLIT_SHAPES = [(256, 8192, 8192), (300, 4000, 8192), (1000, 1100, 9728), (257, 4096, 14336),
-                (512, 4096, 14336), (640, 1920, 8192), (768, 4096, 14336)]
+# (M, N, K): 2, 3 and 4 slices, ragged M and N tails, a last slice shorter
+# than the others (K 9600 = 75 stages of 128 in slices of 19, 19, 19, 18),
+# the down projection of the 8B model at 257, 512, 768 and 1024 tokens
+SPLIT_SHAPES = [(256, 8192, 8192), (300, 4000, 8192), (1000, 1100, 9600), (257, 4096, 14336),
+                (512, 4096, 14336), (640, 1920, 8192), (768, 4096, 14336), (1024, 4096, 4096)]
 
 
 def _d(a):

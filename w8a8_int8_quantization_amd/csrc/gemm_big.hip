@@ -86,8 +86,9 @@ struct BigEpi {
   sqh::DecompArgs dec;
   bool rows16;  // y and every output row start 16-byte aligned: staged full-row stores
   // split K (kSplit kernels): S slices of slice_stages stages each; partial
-  // tiles [S][M][N] (int32, or binary32 bits) and one ticket counter per tile,
-  // zero at launch and restored to zero by the tile's last workgroup
+  // tiles [S][tiles][256 x BN] (int32, or binary32 bits, in accumulator
+  // order) and one ticket counter per tile, zero at launch and restored to
+  // zero by the tile's last workgroup
   int32_t* partial;
   uint32_t* counter;
   int S;
@@ -309,81 +310,67 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
 
   if constexpr (kSplit) {
     // ---- split K: publish this slice's tile (coherent buffer stores), take
-    // a ticket; the last workgroup of the tile adds all S slices in order
+    // a ticket; the last workgroup of the tile adds all S slices in order.
+    // Partial tiles are kept in accumulator order, not as rows of the
+    // output: slice s, tile t, wave w, block (j, i), register group rg, lane
+    // l at 16 bytes each, so every store and load instruction of a wave
+    // covers 1 KiB of consecutive bytes, and ragged tiles need no bounds
+    // (their padding is never stored to y).
     __shared__ uint32_t last_ticket;
-    const uint32_t pbytes = (uint32_t)((size_t)ep.S * M * N * 4);
+    constexpr uint32_t kTileBytes = kBigBM * BN * 4;
+    constexpr uint32_t kWaveBytes = kTileBytes / kBigWaves;
+    const uint32_t pbytes = (uint32_t)ep.S * (uint32_t)total * kTileBytes;
     const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(ep.partial, (short)0, pbytes, kBigBufDword3);
-    const uint32_t sstride = (uint32_t)((size_t)M * N * 4);
-    // byte offset of the 4 outputs (j, i, rg) within a slice, or ~0u where
-    // the row is past M; columns past N are handled one by one
-    auto part_off = [&](int j, int i, int rg) -> uint32_t {
-      const int m = m0 + wm * C::kWM + 32 * i + frow;
-      const int n = n0 + wn * C::kWN + 32 * j + 8 * rg + 4 * fhalf;
-      return (m < M && n < N) ? (uint32_t)(((size_t)m * N + n) * 4) : ~0u;
-    };
-    auto ncols = [&](int j, int rg) { return min(4, N - (n0 + wn * C::kWN + 32 * j + 8 * rg + 4 * fhalf)); };
-    const uint32_t soff = (uint32_t)blockIdx.y * sstride;
+    const int tile_id = tm * nbn + tn;
+    const uint32_t lane_off = (uint32_t)wid * kWaveBytes + (uint32_t)lane * 16;
+    auto slice_base = [&](int sl) { return ((uint32_t)sl * (uint32_t)total + (uint32_t)tile_id) * kTileBytes + lane_off; };
+    {
+      const uint32_t base = slice_base((int)blockIdx.y);
 #pragma unroll
-    for (int j = 0; j < C::kFN; ++j)
+      for (int j = 0; j < C::kFN; ++j)
 #pragma unroll
-      for (int i = 0; i < C::kFM; ++i)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const uint32_t off = part_off(j, i, rg);
-          if (off == ~0u) continue;
+        for (int i = 0; i < C::kFM; ++i) {
           // bit_cast the whole accumulator, then pick elements: a bit_cast of
           // one vector element reads element 0 of the vector in this compiler
           const v16i bits = __builtin_bit_cast(v16i, acc[j][i]);
-          const v4i v = {bits[4 * rg], bits[4 * rg + 1], bits[4 * rg + 2], bits[4 * rg + 3]};
-          const int nv = ncols(j, rg);
-          if (nv == 4) {
-            __builtin_amdgcn_raw_buffer_store_b128(v, pr, soff + off, 0, kBigCoherent);
-          } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (e < nv) __builtin_amdgcn_raw_buffer_store_b32(v[e], pr, soff + off + 4 * e, 0, kBigCoherent);
+          for (int rg = 0; rg < 4; ++rg) {
+            const v4i v = {bits[4 * rg], bits[4 * rg + 1], bits[4 * rg + 2], bits[4 * rg + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(v, pr, base + (uint32_t)((j * C::kFM + i) * 4 + rg) * 1024, 0,
+                                                   kBigCoherent);
           }
         }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const int tile_id = tm * nbn + tn;
     if (tid == 0)
       last_ticket = __hip_atomic_fetch_add(ep.counter + tile_id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (last_ticket != (uint32_t)(ep.S - 1)) return;
     // slice by slice, in order (binary32 sums in a fixed order: deterministic
-    // results), the loads of one column block of the tile in flight together.
-    // Rows past M load from row 0 of the slice and add zero; in a ragged last
-    // column group the 16-byte load runs into the next row (or past the
-    // buffer's end, where it reads zeros): those columns are never stored.
-    uint32_t offv[C::kFN][C::kFM][4];
+    // results), a whole slice's loads in flight together
 #pragma unroll
     for (int j = 0; j < C::kFN; ++j)
 #pragma unroll
       for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          offv[j][i][rg] = part_off(j, i, rg);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[j][i][4 * rg + e] = 0;
-        }
+        for (int r = 0; r < 16; ++r) acc[j][i][r] = 0;
     for (int sl = 0; sl < ep.S; ++sl) {
-      const uint32_t base = (uint32_t)sl * sstride;
+      const uint32_t base = slice_base(sl);
 #pragma unroll
       for (int j = 0; j < C::kFN; ++j)
 #pragma unroll
         for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
           for (int rg = 0; rg < 4; ++rg) {
-            const uint32_t off = offv[j][i][rg];
-            const bool ok = off != ~0u;
-            const v4i t = __builtin_amdgcn_raw_buffer_load_b128(pr, base + (ok ? off : 0u), 0, kBigCoherent);
+            const v4i t = __builtin_amdgcn_raw_buffer_load_b128(
+                pr, base + (uint32_t)((j * C::kFM + i) * 4 + rg) * 1024, 0, kBigCoherent);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               if constexpr (kF8)
-                acc[j][i][4 * rg + e] += ok ? __int_as_float(t[e]) : 0.f;
+                acc[j][i][4 * rg + e] += __int_as_float(t[e]);
               else
-                acc[j][i][4 * rg + e] += ok ? t[e] : 0;
+                acc[j][i][4 * rg + e] += t[e];
             }
           }
     }
@@ -656,23 +643,27 @@ struct BigSplit {
   int64_t tiles = 0;
 };
 
-// K slices for `tiles` output tiles: split when the tiles cover at most half
-// of the 256 CUs, into as many slices as fill them (at most kBigMaxSplit),
-// each of at least 24 stages (3072 K). Publishing and adding the partial
-// tiles (S x M x N x 4 bytes) costs about as much as 10 stages of a slice
-// per slice at these shapes: 4096 -> 14336 at 256 tokens took 44 us
-// unsplit and 72 us in 3 slices of 11 stages.
-int split_for(int64_t tiles, int stages, int64_t m, int64_t n) {
-  int want = tiles <= 128 ? (int)(256 / tiles) : 1;
+// K slices for `tiles` output tiles: split when the tiles cover fewer than
+// half of the 256 CUs, into as many slices as keep all workgroups in one wave
+// (at most kBigMaxSplit), each of at least 10 stages (1280 K). Measured,
+// GEMM alone: 14336 -> 4096 at 512 / 1024 / 1280 tokens 116 / 128 / 132 us
+// unsplit, 60 / 89 / 98 us in 4 / 2 / 2 slices; 4096 -> 6144 at 512 tokens
+// 41.6 -> 35.1 us in 3 slices. A second wave of workgroups costs more than
+// the split saves (1024 tokens in 3 slices: 112 us), and so does splitting
+// 128 tiles in two (4096 -> 6144 at 1024 tokens: 43.2 -> 46.5 us).
+int split_for(int64_t tiles, int stages, int bn) {
+  int want = tiles < 128 ? (int)(256 / tiles) : 1;
+  int min_stages = 10;
 #ifdef SQ_TUNE
   if (const char* e = getenv("SQ_BIG_SPLIT")) want = atoi(e);
+  if (const char* e = getenv("SQ_BIG_MINST")) min_stages = atoi(e);
 #endif
   if (want > kBigMaxSplit) want = kBigMaxSplit;
-  if (want > stages / 24) want = stages / 24;
+  if (want > stages / min_stages) want = stages / min_stages;
   if (want < 2) return 1;
   const int per = (stages + want - 1) / want;
   const int S = (stages + per - 1) / per;
-  if ((size_t)S * (size_t)m * (size_t)n * 4 >= ((size_t)1 << 31)) return 1;
+  if ((size_t)S * (size_t)tiles * (size_t)(sqk::kBigBM * bn * 4) >= ((size_t)1 << 31)) return 1;
   return S;
 }
 
@@ -697,18 +688,14 @@ int pick_bn(int64_t m, int64_t n) {
   return best;
 }
 
-// Tile width, then the K split for that many tiles. Measured on the
-// 14336 -> 4096 projection (GEMM alone): the split pays while all
-// workgroups fit in one wave of the 256 CUs (512 tokens: 116 -> 83 us with 4
-// slices; 768: 110 -> 88 us with 3; 1024: 111 -> 96 us with 2), and costs
-// once they do not (1024 tokens with 3 slices: 133 us). 256-column tiles
-// with a split lose to 192-column ones at every size tried.
+// Tile width, then the K split for that many tiles (256-column tiles with a
+// split lost to 192-column ones at every size tried).
 BigSplit big_split(int64_t m, int64_t n, int64_t k, bool f8, bool split_ok = true) {
   BigSplit p;
   p.bn = f8 ? 192 : pick_bn(m, n);
   p.tiles = ((m + sqk::kBigBM - 1) / sqk::kBigBM) * ((n + p.bn - 1) / p.bn);
   const int stages = (int)(k / sqk::kBigBK);
-  p.S = split_ok ? split_for(p.tiles, stages, m, n) : 1;
+  p.S = split_ok ? split_for(p.tiles, stages, p.bn) : 1;
   p.slice_stages = (stages + p.S - 1) / p.S;
   return p;
 }
@@ -721,7 +708,7 @@ size_t gemm_big_workspace(int64_t m, int64_t n, int64_t k, bool f8) {
   if (!gemm_big_suits(m, n, k)) return 0;
   const BigSplit p = big_split(m, n, k, f8);
   if (p.S == 1) return 0;
-  return big_counter_bytes(p.tiles) + (size_t)p.S * (size_t)m * (size_t)n * 4;
+  return big_counter_bytes(p.tiles) + (size_t)p.S * (size_t)p.tiles * (size_t)(sqk::kBigBM * p.bn * 4);
 }
 
 void gemm_big_counters(int64_t m, int64_t n, int64_t k, bool f8, void* ws, uint32_t** counters, int64_t* count) {

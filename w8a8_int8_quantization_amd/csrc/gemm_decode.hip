@@ -431,10 +431,12 @@ constexpr int64_t kDecodeMaxM = 256;
 // measured on MI355X (GEMM us, tiled -> decode), 4096 -> 14336 columns:
 // M 96 42.4 -> 36.0, M 128 43.5 -> 39.8 (decode), M 192 43.3 vs 57.5, M 256
 // 43.9 vs 75.0 (tiled); 14336 -> 4096: M 96 113.8 -> 42.7, M 128 125.2 ->
-// 47.6, M 192 111.8 -> 68.3, M 256 114.4 -> 88.6 (decode).
+// 47.6, M 192 111.8 -> 68.3 (decode). Where the 256-row prefill kernel
+// applies, it splits K over enough workgroups to cover the CUs and beats the
+// decode kernel: 14336 -> 4096 at 256 tokens 60.4 us against 89.6.
 static bool decode_beats_prefill(int64_t m, int64_t n) {
-  const bool big = m >= 256 && m * n >= ((int64_t)1 << 20);
-  const int64_t units = big ? ((m + 255) / 256) * ((n + 191) / 192) * 3 : ((m + 127) / 128) * ((n + 127) / 128);
+  if (m >= 256 && m * n >= ((int64_t)1 << 20)) return false;
+  const int64_t units = ((m + 127) / 128) * ((n + 127) / 128);
   return units <= 128;
 }
 
