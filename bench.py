@@ -50,6 +50,13 @@ PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, TFLOP/s
 PEAK_FP64_TFLOPS = 78.6   # MI355X binary64 (vector FMA and matrix), TFLOP/s
 
 
+def big_kernel_suits(m: int, n: int, k: int) -> bool:
+    """Whether the 256-row prefill kernel takes this GEMM (the C ABI's rule)."""
+    if n < 192 or k % 128:
+        return False
+    return (m >= 256 and m * n >= (1 << 20)) or (m >= 160 and n >= 4096 and k // 128 >= 20)
+
+
 def decode_kernel_runs(m: int, n: int, k: int) -> bool:
     """Whether the library routes this GEMM to its decode kernel (the
     dispatch rule of the C ABI, repeated here to label the measured kernel):
@@ -59,7 +66,7 @@ def decode_kernel_runs(m: int, n: int, k: int) -> bool:
         return False
     if m <= 64:
         return True
-    if m > 256 or (m >= 256 and m * n >= (1 << 20)):
+    if m > 256 or big_kernel_suits(m, n, k):
         return False
     units = (-(-m // 128)) * (-(-n // 128))
     return units <= 128
@@ -324,7 +331,7 @@ def bench_fp8(args, dev):
         roof = {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "ops_per_launch": ops}
     # the E4M3 forms of the decode kernel and of the prefill kernel, or the 128 x 128 kernel
-    big = c.m >= 256 and c.n >= 192 and c.k % 128 == 0 and c.m * c.n >= (1 << 20)
+    big = big_kernel_suits(c.m, c.n, c.k)
     kfile, kname = (("gemm_decode.hip", "gemm_decode_kernel<kMB, kNS, kF8=true>") if decode else
                     ("gemm_big.hip", "gemm_big_kernel<192, bf16, kVec, kF8=true>") if big else
                     ("gemm_f8.hip", "gemm_f8_kernel"))
@@ -746,7 +753,7 @@ def main():
     in_bytes = {"f32": 4, "bf16": 2}[c.x_dtype] * (2 if silu else 1)  # gate and up
     quant_bytes = c.m * c.k * in_bytes + 4 * c.k + c.m * c.k + 4 * c.m
     gemm_bytes = c.m * c.k + c.n * c.k + 4 * c.m + 4 * c.n + c.m * c.n * {"f32": 4, "bf16": 2}[c.y_dtype]
-    big = c.m >= 256 and c.n >= 192 and c.k % 128 == 0 and c.m * c.n >= (1 << 20)
+    big = big_kernel_suits(c.m, c.n, c.k)
     kfile, kname = (("gemm_decode.hip", "gemm_decode_kernel") if decode else
                     ("gemm_big.hip", "gemm_big_kernel") if big else ("gemm.hip", "gemm_i8_kernel"))
     tag = args.workload if args.m is None else f"{args.workload}_m{c.m}"

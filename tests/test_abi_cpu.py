@@ -121,7 +121,10 @@ def test_validation_linear(sq):
     assert f(P, P, P, P, 4, 4096, 14336, P, sq.SQ_BF16, 4096, BAD, need, None) == ALIGN
     # 65..256 tokens: the decode kernel only where the tiled kernels get few tiles
     assert sq.raw["sq_w8a8_linear_workspace_size"](128, 4096, 14336) > 0       # down projection shape
-    assert sq.raw["sq_w8a8_linear_workspace_size"](192, 14336, 4096) == 0      # up projection: tiled
+    # 160..255 tokens over wide layers: the 256-row kernel, K split 3 ways over
+    # its 75 tiles of 256 x 192 (300 bytes of counters, padded to 512)
+    assert sq.raw["sq_w8a8_linear_workspace_size"](192, 14336, 4096) == 512 + 3 * 75 * 256 * 192 * 4
+    assert sq.raw["sq_w8a8_linear_workspace_size"](150, 20000, 4096) == 0      # 128 x 128 tiles
     # prefill with 2 x 22 tiles of 256 x 192: K split 4 ways (28 stages of 128
     # each), 4 x 44 partial int32 tiles after 256 bytes of tile counters
     assert sq.raw["sq_w8a8_linear_workspace_size"](257, 4096, 14336) == 256 + 4 * 44 * 256 * 192 * 4

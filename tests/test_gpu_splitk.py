@@ -24,9 +24,11 @@ TDT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 # (M, N, K): 2, 3 and 4 slices, ragged M and N tails, a last slice shorter
 # than the others (K 9600 = 75 stages of 128 in slices of 19, 19, 19, 18),
-# the down projection of the 8B model at 257, 512, 768 and 1024 tokens
+# the down projection of the 8B model at 257, 512, 768 and 1024 tokens, and
+# 160..255 tokens (one partly filled 256-row tile) over wide layers
 SPLIT_SHAPES = [(256, 8192, 8192), (300, 4000, 8192), (1000, 1100, 9600), (257, 4096, 14336),
-                (512, 4096, 14336), (640, 1920, 8192), (768, 4096, 14336), (1024, 4096, 4096)]
+                (512, 4096, 14336), (640, 1920, 8192), (768, 4096, 14336), (1024, 4096, 4096),
+                (160, 4096, 14336), (192, 14336, 4096), (231, 6100, 2560)]
 
 
 def _d(a):
@@ -58,7 +60,7 @@ def test_split_extremes():
 
 
 @pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("m,n,k", [(300, 4000, 8192), (512, 4096, 14336)])
+@pytest.mark.parametrize("m,n,k", [(300, 4000, 8192), (512, 4096, 14336), (200, 4096, 14336)])
 def test_split_dequant(out, m, n, k):
     log("split-K gemm dequant", out, m, n, k)
     xq = workloads.uniform_int8((m, k), seed=5 * m + n, stream=12)
@@ -163,7 +165,7 @@ def _fp8_check(y, xq, d, wq, sw, out):
 
 
 @pytest.mark.parametrize("m,n,k,out", [(512, 4096, 14336, "bf16"), (300, 4000, 8192, "f32"),
-                                       (777, 4000, 6144, "f16")])
+                                       (777, 4000, 6144, "f16"), (192, 14336, 4096, "bf16")])
 def test_fp8_split(m, n, k, out):
     need = sq.raw["sq_fp8_linear_workspace_size"](m, n, k)
     log("split-K fp8 gemm", m, n, k, out, "workspace bytes", need)

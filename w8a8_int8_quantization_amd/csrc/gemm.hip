@@ -178,7 +178,8 @@ hipError_t gemm_i8(const int8_t* xq, const float* x_scale, const int8_t* wq, con
                    int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec, void* ws,
                    hipStream_t s) {
   if (m <= 0 || n <= 0) return hipSuccess;
-  if (gemm_big_suits(m, n, k)) return gemm_i8_big(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, dec, ws, s);
+  if (gemm_big_suits(m, n, k, dec == nullptr))
+    return gemm_i8_big(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, dec, ws, s);
   const int64_t tiles = ((m + sqk::kBM - 1) / sqk::kBM) * ((n + sqk::kBN - 1) / sqk::kBN);
   const dim3 grid((unsigned)tiles), block(256);
   DecompArgs d{};

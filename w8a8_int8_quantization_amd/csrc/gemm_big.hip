@@ -628,8 +628,15 @@ static void launch_big_f8(const int8_t* xq, const int8_t* wq, int M, int N, int 
 
 namespace sqh {
 
-bool gemm_big_suits(int64_t m, int64_t n, int64_t k) {
-  return m >= 256 && n >= 192 && k % sqk::kBigBK == 0 && m * n >= ((int64_t)1 << 20);
+bool gemm_big_suits(int64_t m, int64_t n, int64_t k, bool split_ok) {
+  if (n < 192 || k % sqk::kBigBK != 0) return false;
+  if (m >= 256 && m * n >= ((int64_t)1 << 20)) return true;
+  // 160..255 tokens over wide layers: one 256-row tile per column block with K
+  // split over the CUs beats the decode and 128 x 128 kernels (GEMM us at 192
+  // tokens, decode / 128 x 128 / this: 14336 -> 4096 69.2 / 138.0 / 57.1,
+  // 4096 -> 14336 55.4 / 49.8 / 39.1, 4096 -> 6144 36.6 / 39.3 / 31.3,
+  // 4096 -> 28672 110.2 / 61.9 / 53.6)
+  return split_ok && m >= 160 && n >= 4096 && k / sqk::kBigBK >= 20;
 }
 
 namespace {

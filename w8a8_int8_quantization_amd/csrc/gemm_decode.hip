@@ -432,10 +432,11 @@ constexpr int64_t kDecodeMaxM = 256;
 // M 96 42.4 -> 36.0, M 128 43.5 -> 39.8 (decode), M 192 43.3 vs 57.5, M 256
 // 43.9 vs 75.0 (tiled); 14336 -> 4096: M 96 113.8 -> 42.7, M 128 125.2 ->
 // 47.6, M 192 111.8 -> 68.3 (decode). Where the 256-row prefill kernel
-// applies, it splits K over enough workgroups to cover the CUs and beats the
-// decode kernel: 14336 -> 4096 at 256 tokens 60.4 us against 89.6.
-static bool decode_beats_prefill(int64_t m, int64_t n) {
-  if (m >= 256 && m * n >= ((int64_t)1 << 20)) return false;
+// applies (gemm_big_suits), it splits K over enough workgroups to cover the
+// CUs and beats the decode kernel: 14336 -> 4096 at 256 tokens 60.4 us
+// against 89.6, at 192 tokens 57.1 against 69.2.
+static bool decode_beats_prefill(int64_t m, int64_t n, int64_t k) {
+  if (gemm_big_suits(m, n, k)) return false;
   const int64_t units = ((m + 127) / 128) * ((n + 127) / 128);
   return units <= 128;
 }
@@ -447,7 +448,7 @@ bool gemm_decode_suits(int64_t m, int64_t n, int64_t k) {
   // (see the dispatch notes); the partial tiles must fit 32-bit offsets
   const DecodePlan p = decode_plan(m, n, k);
   if ((size_t)p.S * (size_t)m * (size_t)n * 4 >= ((size_t)1 << 31)) return false;
-  return decode_beats_prefill(m, n);
+  return decode_beats_prefill(m, n, k);
 }
 
 size_t gemm_decode_workspace(int64_t m, int64_t n, int64_t k) {

@@ -72,7 +72,9 @@ hipError_t gemm_i8(const int8_t* xq, const float* x_scale, const int8_t* wq, con
                    hipStream_t s);
 
 // Large-tile prefill GEMM (256-row tiles); gemm_i8 routes to it when it suits.
-bool gemm_big_suits(int64_t m, int64_t n, int64_t k);
+// Whether the 256-row-tile prefill kernel takes this GEMM (split_ok: the
+// call may split K, i.e. it is not the LLM.int8() epilogue).
+bool gemm_big_suits(int64_t m, int64_t n, int64_t k, bool split_ok = true);
 hipError_t gemm_i8_big(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
                        int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, const DecompArgs* dec, void* ws,
                        hipStream_t s);
