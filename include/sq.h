@@ -180,8 +180,8 @@ sq_status sq_quant_act_per_token(const void* x, sq_dtype xt, int64_t m, int64_t 
  *     split over several workgroups: decode shapes (K % 128 == 0 and
  *     M <= 64, or M <= 256 where the tiled kernels would cover few compute
  *     units; one ticket counter per 64 output columns and 64 tokens) and
- *     prefill shapes whose 256-row tiles number fewer than 128 (up to 4
- *     slices of at least 1280 K each; one ticket counter per output tile).
+ *     prefill shapes whose 256-row tiles number fewer than 128 (up to 8
+ *     slices of at least 1024 K each; one ticket counter per output tile).
  *     The workspace then holds the counters and int32 partial tiles. The
  *     caller zero-fills the workspace once, before its first use; every call
  *     leaves the counters at zero again, so later calls need no clearing.

@@ -2,7 +2,7 @@
 
 Where the 256-row tiles number fewer than 128 (the down projection's 4096
 output columns at up to 1280 tokens, say) and K holds at least 2 x 1280, the
-prefill kernel splits K into up to 4 slices; the last workgroup of each tile
+prefill kernel splits K into up to 8 slices; the last workgroup of each tile
 adds the slices' partial tiles in slice order. int32 accumulators must stay bit-exact (the split changes
 only the order of an exact sum), outputs within 1 ulp of the oracle, E4M3
 outputs within the bound of the FP8 tests, and every path deterministic.
@@ -22,8 +22,8 @@ sq = pytest.importorskip("w8a8_int8_quantization_amd")
 
 TDT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
-# (M, N, K): 2, 3 and 4 slices, ragged M and N tails, a last slice shorter
-# than the others (K 9600 = 75 stages of 128 in slices of 19, 19, 19, 18),
+# (M, N, K): 2 to 7 slices, ragged M and N tails, a last slice shorter than
+# the others (K 9600 = 75 stages of 128 in 6 slices, the last of 10 stages),
 # the down projection of the 8B model at 257, 512, 768 and 1024 tokens, and
 # 160..255 tokens (one partly filled 256-row tile) over wide layers
 SPLIT_SHAPES = [(256, 8192, 8192), (300, 4000, 8192), (1000, 1100, 9600), (257, 4096, 14336),
@@ -47,8 +47,8 @@ def test_split_int32_exact(m, n, k):
 
 
 def test_split_extremes():
-    """Rows of +-127 at K 14336 in 4 slices: partial sums of +-57,806,336 per
-    slice add up to +-231,225,344 exactly."""
+    """Rows of +-127 at K 14336 in 5 slices: partial sums of +-47,483,776 (23
+    stages) and +-41,290,240 (the last 20) add up to +-231,225,344 exactly."""
     m, n, k = 300, 4096, 14336
     rng = np.random.default_rng(8)
     si = rng.choice([-1, 1], size=m).astype(np.int64)
@@ -105,11 +105,12 @@ def test_split_workspace_reuse():
     assert np.array_equal(acc2, first[:m2])
 
 
+@pytest.mark.parametrize("m", [400, 192])
 @pytest.mark.parametrize("path", ["dyn", "rmsnorm", "silu"])
-def test_split_fused_calls_garbage_workspace(path):
+def test_split_fused_calls_garbage_workspace(path, m):
     """The one-call paths clear the tile counters in their quantisation
     launch: a workspace full of garbage gives the two-call result."""
-    m, k, n = 400, 14336, 4096
+    k, n = 14336, 4096
     c = workloads.random_linear_case(m=m, k=k, n=n, seed=41, dtype="bf16", calib_rows=64)
     s_ref = oracle.smoothing_factors(oracle.calibrate_absmax(c.x_calib), oracle.weight_row_absmax(c.w), 0.5)
     s = torch.from_numpy(s_ref).to(dev())
@@ -181,8 +182,9 @@ def test_fp8_split(m, n, k, out):
                        y2.view(torch.int16 if out != "f32" else torch.int32))
 
 
-def test_fp8_split_dyn_garbage_workspace():
-    m, n, k = 512, 4096, 14336
+@pytest.mark.parametrize("m", [512, 200])
+def test_fp8_split_dyn_garbage_workspace(m):
+    n, k = 4096, 14336
     c = workloads.random_linear_case(m=m, k=k, n=n, seed=5, dtype="bf16", calib_rows=8)
     x = to_dev(c.x, "bf16")
     wq, sw = sq.sq_quant_weights_fp8(to_dev(c.w, "bf16"))

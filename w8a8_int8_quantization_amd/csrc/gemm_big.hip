@@ -100,7 +100,7 @@ struct BigEpi {
 // whose L2 caches are not coherent with each other.
 constexpr int kBigBufDword3 = 0x00020000;
 // at most this many K slices per output tile
-constexpr int kBigMaxSplit = 4;
+constexpr int kBigMaxSplit = 8;
 constexpr int kBigCoherent = 16;
 
 // s_waitcnt vmcnt(n) with the lgkm and exp counters left alone (gfx9 encoding).
@@ -651,22 +651,26 @@ struct BigSplit {
 };
 
 // K slices for `tiles` output tiles: split when the tiles cover fewer than
-// half of the 256 CUs, into as many slices as keep all workgroups in one wave
-// (at most kBigMaxSplit), each of at least 10 stages (1280 K). Measured,
-// GEMM alone: 14336 -> 4096 at 512 / 1024 / 1280 tokens 116 / 128 / 132 us
-// unsplit, 60 / 89 / 98 us in 4 / 2 / 2 slices; 4096 -> 6144 at 512 tokens
-// 41.6 -> 35.1 us in 3 slices. A second wave of workgroups costs more than
-// the split saves (1024 tokens in 3 slices: 112 us), and so does splitting
-// 128 tiles in two (4096 -> 6144 at 1024 tokens: 43.2 -> 46.5 us).
+// half of the 256 CUs, into at most as many slices as keep all workgroups in
+// one wave with a CU to spare (a full 256 measured slower: 4096 -> 6144 at 512
+// tokens, 64 tiles in 3 / 4 slices 34.8 / 37.1 us). Each slice costs its reducer one more partial tile to read and
+// shortens every slice's main loop: with about 1.3 us per 128-deep stage and
+// 3 us per slice (fitted on 14336 -> 4096 at 192 tokens: 4 / 8 / 10 slices
+// 56.6 / 49.9 / 52.1 us), S = sqrt(0.45 x stages) balances the two (7 for
+// K = 14336, 4 for K = 4096; 4096 -> 6144 at 256 tokens: 3 / 4 / 6 slices
+// 32.1 / 31.9 / 34.8 us). Slices keep at least 8 stages. A second wave of
+// workgroups costs more than the split saves (14336 -> 4096 at 1024 tokens
+// in 3 slices: 112 us against 89 in 2), and so does splitting 128 tiles in
+// two (4096 -> 6144 at 1024 tokens: 43.2 -> 46.5 us).
 int split_for(int64_t tiles, int stages, int bn) {
-  int want = tiles < 128 ? (int)(256 / tiles) : 1;
-  int min_stages = 10;
+  int want = tiles < 128 ? (int)(255 / tiles) : 1;
+  int best = (int)(sqrtf(0.45f * (float)stages) + 0.5f);
 #ifdef SQ_TUNE
-  if (const char* e = getenv("SQ_BIG_SPLIT")) want = atoi(e);
-  if (const char* e = getenv("SQ_BIG_MINST")) min_stages = atoi(e);
+  if (const char* e = getenv("SQ_BIG_SPLIT")) want = best = atoi(e);
 #endif
+  if (want > best) want = best;
   if (want > kBigMaxSplit) want = kBigMaxSplit;
-  if (want > stages / min_stages) want = stages / min_stages;
+  if (want > stages / 8) want = stages / 8;
   if (want < 2) return 1;
   const int per = (stages + want - 1) / want;
   const int S = (stages + per - 1) / per;
