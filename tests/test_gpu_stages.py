@@ -197,10 +197,11 @@ def test_quant_act_ties_and_padding():
 
 # --------------------------------------------------------------------------- int8 GEMM
 # Small shapes run the 128 x 128 kernel; from about a million outputs on, the
-# 256-row kernel (BN 256 or 192), including ragged M and N tails.
+# 256-row kernel (BN 256, 192 or 128), including ragged M and N tails.
 GEMM_SHAPES = [(1, 1, 64), (3, 5, 64), (16, 512, 256), (100, 72, 192), (129, 257, 320), (256, 256, 512),
                (300, 130, 4096), (77, 1000, 1088), (1, 4096, 14336), (64, 200, 14336),
-               (1000, 1100, 384), (513, 2050, 1024), (2048, 768, 256), (256, 4096, 128), (777, 1536, 4160)]
+               (1000, 1100, 384), (513, 2050, 1024), (2048, 768, 256), (256, 4096, 128), (777, 1536, 4160),
+               (1000, 6100, 1024), (2048, 4096, 4096), (3072, 4096, 512)]
 
 
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
@@ -229,7 +230,7 @@ def test_gemm_extremes():
 
 @pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("m,n,k", [(5, 64, 128), (129, 257, 320), (200, 300, 4096), (1000, 1100, 384),
-                                   (512, 2048, 256)])
+                                   (512, 2048, 256), (1000, 6100, 1024)])
 def test_gemm_dequant(out, m, n, k):
     log("gemm dequant", out, m, n, k)
     xq = workloads.uniform_int8((m, k), seed=3 * m + n, stream=2)

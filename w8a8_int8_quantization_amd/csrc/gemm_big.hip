@@ -678,37 +678,44 @@ int split_for(int64_t tiles, int stages, int bn) {
   return S;
 }
 
-// Output tile width that fills the 256 CUs best: useful outputs over the
-// outputs that the scheduled waves of workgroups could compute.
-int pick_bn(int64_t m, int64_t n) {
-  const int cands[2] = {256, 192};
-  int best = 256;
-  double best_eff = -1.0;
+// Tile width (256, 192 or 128 columns) and K split, chosen together: the
+// score is the fraction of the scheduled waves' workgroup slots doing useful
+// work, useful outputs x S over (waves of tiles x S) x 256 x 256 x BN, times
+// a measured efficiency: 0.8 for 128-column tiles (less operand reuse per
+// fragment read), 0.8 for a split (0.7 with 256-column tiles). GEMM alone,
+// us, tile width 192 / 256 / 128 (S: split into S slices): 4096 -> 6144 at
+// 1024 tokens 44.2 / 59.4 (S2) / 36.9; 4096 -> 14336 at 512 tokens 47.8 /
+// 63.4 (S2) / 41.6; 14336 -> 4096 at 2048 tokens 134.8 / 146.9 / 126.3, at
+// 1024 tokens 97.5 (S2) / 105.9 (S3) / 118.4, at 3072 tokens 269.3 / 167.3 /
+// 223.7; 4096 -> 6144 at 1536 tokens 46.2 / 52.9 / 71.0. The 128-column
+// tile is taken only unsplit (the combination measured).
+BigSplit big_split(int64_t m, int64_t n, int64_t k, bool f8, bool split_ok = true) {
+  const int stages = (int)(k / sqk::kBigBK);
+  const int cands[3] = {256, 192, 128};
+  BigSplit best;
+  double best_score = -1.0;
   for (int bn : cands) {
-    const int64_t tiles = ((m + sqk::kBigBM - 1) / sqk::kBigBM) * ((n + bn - 1) / bn);
-    const int64_t waves = (tiles + 255) / 256;
-    const double eff = (double)m * (double)n / ((double)waves * 256.0 * sqk::kBigBM * bn);
-    if (eff > best_eff + 1e-9) {
-      best_eff = eff;
-      best = bn;
+    if (f8 && bn != 192) continue;  // E4M3 tiles: 192 columns only
+#ifdef SQ_TUNE
+    if (const char* e = getenv("SQ_BIG_BN"))
+      if (atoi(e) != bn) continue;
+#endif
+    BigSplit p;
+    p.bn = bn;
+    p.tiles = ((m + sqk::kBigBM - 1) / sqk::kBigBM) * ((n + bn - 1) / bn);
+    p.S = split_ok ? split_for(p.tiles, stages, bn) : 1;
+    if (bn == 128 && p.S > 1) continue;
+    p.slice_stages = (stages + p.S - 1) / p.S;
+    const int64_t waves = (p.tiles * p.S + 255) / 256;
+    double score = (double)m * (double)n * p.S / ((double)waves * 256.0 * sqk::kBigBM * bn);
+    if (bn == 128) score *= 0.8;
+    if (p.S > 1) score *= bn == 256 ? 0.7 : 0.8;
+    if (score > best_score + 1e-9) {
+      best = p;
+      best_score = score;
     }
   }
-#ifdef SQ_TUNE
-  if (const char* e = getenv("SQ_BIG_BN")) best = atoi(e);
-#endif
   return best;
-}
-
-// Tile width, then the K split for that many tiles (256-column tiles with a
-// split lost to 192-column ones at every size tried).
-BigSplit big_split(int64_t m, int64_t n, int64_t k, bool f8, bool split_ok = true) {
-  BigSplit p;
-  p.bn = f8 ? 192 : pick_bn(m, n);
-  p.tiles = ((m + sqk::kBigBM - 1) / sqk::kBigBM) * ((n + p.bn - 1) / p.bn);
-  const int stages = (int)(k / sqk::kBigBK);
-  p.S = split_ok ? split_for(p.tiles, stages, p.bn) : 1;
-  p.slice_stages = (stages + p.S - 1) / p.S;
-  return p;
 }
 
 size_t big_counter_bytes(int64_t tiles) { return ((size_t)tiles * 4 + 255) / 256 * 256; }
@@ -759,7 +766,9 @@ hipError_t gemm_i8_big(const int8_t* xq, const float* x_scale, const int8_t* wq,
                    (out == sqk::kBigI32 || reinterpret_cast<uintptr_t>(w_scale) % 16 == 0);
   ep.rows16 = (ldy * eb) % 16 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0;
   const int M = (int)m, N = (int)n, K = (int)k;
-  if (sp.bn == 192)
+  if (sp.bn == 128)
+    sqk::launch_big_o<128>(xq, wq, M, N, K, ep, out, vec, s);
+  else if (sp.bn == 192)
     sqk::launch_big_o<192>(xq, wq, M, N, K, ep, out, vec, s);
   else
     sqk::launch_big_o<256>(xq, wq, M, N, K, ep, out, vec, s);
