@@ -333,7 +333,7 @@ def bench_fp8(args, dev):
     # the E4M3 forms of the decode kernel and of the prefill kernel, or the 128 x 128 kernel
     big = big_kernel_suits(c.m, c.n, c.k)
     kfile, kname = (("gemm_decode.hip", "gemm_decode_kernel<kMB, kNS, kF8=true>") if decode else
-                    ("gemm_big.hip", "gemm_big_kernel<192, bf16, kVec, kF8=true>") if big else
+                    ("gemm_big.hip", "gemm_big_kernel<BN, bf16, kVec, kF8=true>") if big else
                     ("gemm_f8.hip", "gemm_f8_kernel"))
     roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": pmc_traffic(args.workload, kfile),
                  "kernel": kname, "launch_us": gemm_ms * 1e3})

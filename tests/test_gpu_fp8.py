@@ -107,10 +107,11 @@ def test_fp8_linear_dyn_equals_two_calls():
 
 
 # Prefill-sized problems (M >= 256, N >= 192, M N >= 2^20) run on the
-# 256-row-tile pipeline: ragged tiles in both directions, one and three k
-# stages, every output type.
+# 256-row-tile pipeline (192- or 128-column tiles): ragged tiles in both
+# directions, one and three k stages, every output type.
 @pytest.mark.parametrize("m,n,k,out", [(1030, 1100, 1152, "f16"), (4096, 512, 128, "bf16"), (512, 2112, 384, "f32"),
-                                       (777, 4000, 2176, "bf16"), (2048, 6144, 4096, "f16")])
+                                       (777, 4000, 2176, "bf16"), (2048, 6144, 4096, "f16"), (1000, 6100, 1024, "bf16"),
+                                       (2048, 4096, 4096, "f32")])
 def test_fp8_linear_prefill_tiles(m, n, k, out):
     log("fp8 prefill gemm", m, n, k, out)
     c = workloads.random_linear_case(m=m, k=k, n=n, seed=3 * m + n + k, dtype="bf16", calib_rows=8)

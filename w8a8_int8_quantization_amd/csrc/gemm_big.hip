@@ -695,7 +695,7 @@ BigSplit big_split(int64_t m, int64_t n, int64_t k, bool f8, bool split_ok = tru
   BigSplit best;
   double best_score = -1.0;
   for (int bn : cands) {
-    if (f8 && bn != 192) continue;  // E4M3 tiles: 192 columns only
+    if (f8 && bn == 256) continue;  // E4M3 tiles: 192 or 128 columns
 #ifdef SQ_TUNE
     if (const char* e = getenv("SQ_BIG_BN"))
       if (atoi(e) != bn) continue;
@@ -791,11 +791,15 @@ hipError_t gemm_f8_big(const uint8_t* xq, const float* x_scale, const uint8_t* w
                    reinterpret_cast<uintptr_t>(w_scale) % 16 == 0;
   ep.rows16 = (ldy * eb) % 16 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0;
   const int M = (int)m, N = (int)n, K = (int)k;
-  // 192-column tiles only: the E4M3 fragments are twice the int8 ones, and
-  // with 256 columns the accumulators and two fragment sets exceed the 256
-  // registers a lane has at two waves per SIMD
-  sqk::launch_big_f8<192>(reinterpret_cast<const int8_t*>(xq), reinterpret_cast<const int8_t*>(wq), M, N, K, ep, out,
-                          vec, s);
+  // 192- or 128-column tiles: the E4M3 fragments are twice the int8 ones,
+  // and with 256 columns the accumulators and two fragment sets exceed the
+  // 256 registers a lane has at two waves per SIMD
+  if (sp.bn == 128)
+    sqk::launch_big_f8<128>(reinterpret_cast<const int8_t*>(xq), reinterpret_cast<const int8_t*>(wq), M, N, K, ep,
+                            out, vec, s);
+  else
+    sqk::launch_big_f8<192>(reinterpret_cast<const int8_t*>(xq), reinterpret_cast<const int8_t*>(wq), M, N, K, ep,
+                            out, vec, s);
   return hipGetLastError();
 }
 
