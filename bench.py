@@ -54,7 +54,9 @@ def big_kernel_suits(m: int, n: int, k: int) -> bool:
     """Whether the 256-row prefill kernel takes this GEMM (the C ABI's rule)."""
     if n < 192 or k % 128:
         return False
-    return (m >= 256 and m * n >= (1 << 20)) or (m >= 160 and n >= 4096 and k // 128 >= 20)
+    if m >= 256 and m * n >= (1 << 20):
+        return True
+    return n >= 4096 and k // 128 >= 20 and (m >= 176 or (m >= 129 and n * k >= (1 << 25)))
 
 
 def decode_kernel_runs(m: int, n: int, k: int) -> bool:

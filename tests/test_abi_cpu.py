@@ -124,7 +124,7 @@ def test_validation_linear(sq):
     # 160..255 tokens over wide layers: the 256-row kernel, K split 3 ways over
     # its 75 tiles of 256 x 192 (300 bytes of counters, padded to 512)
     assert sq.raw["sq_w8a8_linear_workspace_size"](192, 14336, 4096) == 512 + 3 * 75 * 256 * 192 * 4
-    assert sq.raw["sq_w8a8_linear_workspace_size"](150, 20000, 4096) == 0      # 128 x 128 tiles
+    assert sq.raw["sq_w8a8_linear_workspace_size"](150, 20000, 2048) == 0      # 128 x 128 tiles
     # prefill with 2 x 22 tiles of 256 x 192: K (112 stages of 128) split 5
     # ways, 5 x 44 partial int32 tiles after 256 bytes of tile counters
     assert sq.raw["sq_w8a8_linear_workspace_size"](257, 4096, 14336) == 256 + 5 * 44 * 256 * 192 * 4

@@ -25,10 +25,10 @@ TDT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 # (M, N, K): 2 to 7 slices, ragged M and N tails, a last slice shorter than
 # the others (K 9600 = 75 stages of 128 in 6 slices, the last of 10 stages),
 # the down projection of the 8B model at 257, 512, 768 and 1024 tokens, and
-# 160..255 tokens (one partly filled 256-row tile) over wide layers
+# 129..255 tokens (one partly filled 256-row tile) over wide layers
 SPLIT_SHAPES = [(256, 8192, 8192), (300, 4000, 8192), (1000, 1100, 9600), (257, 4096, 14336),
                 (512, 4096, 14336), (640, 1920, 8192), (768, 4096, 14336), (1024, 4096, 4096),
-                (160, 4096, 14336), (192, 14336, 4096), (231, 6100, 2560)]
+                (160, 4096, 14336), (192, 14336, 4096), (231, 6100, 2560), (137, 14336, 4096)]
 
 
 def _d(a):

@@ -631,12 +631,16 @@ namespace sqh {
 bool gemm_big_suits(int64_t m, int64_t n, int64_t k, bool split_ok) {
   if (n < 192 || k % sqk::kBigBK != 0) return false;
   if (m >= 256 && m * n >= ((int64_t)1 << 20)) return true;
-  // 160..255 tokens over wide layers: one 256-row tile per column block with K
-  // split over the CUs beats the decode and 128 x 128 kernels (GEMM us at 192
-  // tokens, decode / 128 x 128 / this: 14336 -> 4096 69.2 / 138.0 / 57.1,
-  // 4096 -> 14336 55.4 / 49.8 / 39.1, 4096 -> 6144 36.6 / 39.3 / 31.3,
-  // 4096 -> 28672 110.2 / 61.9 / 53.6)
-  return split_ok && m >= 160 && n >= 4096 && k / sqk::kBigBK >= 20;
+  // 129..255 tokens over wide layers: one 256-row tile per column block with
+  // K split over the CUs beats the decode and 128 x 128 kernels (GEMM us at
+  // 136 / 192 tokens, decode / 128 x 128 / this: 14336 -> 4096 60.8 / 136.3 /
+  // 49.9 and 69.2 / 138.0 / 57.1; 4096 -> 14336 48.9 / 48.6 / 38.0 and 55.4 /
+  // 49.8 / 39.1; 4096 -> 28672 91.8 / 60.4 / 47.8 and 110.2 / 61.9 / 53.6),
+  // except that the decode kernel streams weights under 32 MiB fast enough to
+  // stay ahead up to about 176 tokens (4096 -> 6144: 24.0 / 38.6 / 30.9 at
+  // 136 tokens, 36.6 / 39.3 / 31.3 at 192)
+  if (!split_ok || n < 4096 || k / sqk::kBigBK < 20) return false;
+  return m >= 176 || (m >= 129 && n * k >= ((int64_t)1 << 25));
 }
 
 namespace {
