@@ -178,10 +178,12 @@ sq_status sq_quant_act_per_token(const void* x, sq_dtype xt, int64_t m, int64_t 
  * ws: workspace of sq_w8a8_linear_workspace_size(m, n, k) bytes, 16-byte
  *     aligned; NULL when that size is 0. The size is non-zero where K is
  *     split over several workgroups: decode shapes (K % 128 == 0 and
- *     M <= 64, or M <= 256 where the tiled kernels would cover few compute
+ *     M <= 64, or M <= 255 where no tiled kernel would cover the compute
  *     units; one ticket counter per 64 output columns and 64 tokens) and
- *     prefill shapes whose 256-row tiles number fewer than 128 (up to 8
- *     slices of at least 1024 K each; one ticket counter per output tile).
+ *     shapes of the 256-row prefill kernel (M >= 256, or M >= 129 over
+ *     layers at least 4096 wide with K >= 2560) whose tiles number fewer
+ *     than 128 (up to 8 slices of at least 1024 K each; one ticket counter
+ *     per output tile). The size depends on (m, n, k) only.
  *     The workspace then holds the counters and int32 partial tiles. The
  *     caller zero-fills the workspace once, before its first use; every call
  *     leaves the counters at zero again, so later calls need no clearing.
