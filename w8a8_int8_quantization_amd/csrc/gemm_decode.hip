@@ -356,13 +356,14 @@ DecodePlan decode_plan(int64_t m, int64_t n, int64_t k) {
   p.tb = (int)((m + 63) / 64);
   // at least one workgroup per CU (256 CUs), with at most kDecMaxNS steps
   // per wave; measured on MI355X, more slices than that only add partial-tile
-  // traffic and reduction latency. Above 16 tokens the partial tiles grow
-  // (S x M x N x 4 bytes written and read back), and three workgroups in four
-  // of the CUs streaming unsplit K are faster (14336 columns: M 64 26.8 ->
-  // 22.9 us, M 32 18.3 -> 16.4 us).
+  // traffic and reduction latency. Where the unsplit grid already has 192
+  // workgroups, three in four of the CUs streaming unsplit K are faster than a
+  // second round of workgroups (4096 -> 14336, 224 column tiles, GEMM us
+  // unsplit / 2 slices: M 1 13.8 / 15.0, M 8 13.9 / 16.0, M 32 16.4 / 18.4,
+  // M 64 20.6 / 27.0).
   const int wgs = p.tiles * p.tb;
   int want = (256 + wgs - 1) / wgs;
-  if (m > 16 && wgs >= 192) want = 1;
+  if (wgs >= 192) want = 1;
 #ifdef SQ_TUNE
   if (const char* e = getenv("SQ_DECODE_SPLIT")) want = atoi(e);
 #endif
