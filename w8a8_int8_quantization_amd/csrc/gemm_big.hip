@@ -347,15 +347,20 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
       last_ticket = __hip_atomic_fetch_add(ep.counter + tile_id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (last_ticket != (uint32_t)(ep.S - 1)) return;
-    // slice by slice, in order (binary32 sums in a fixed order: deterministic
-    // results), a whole slice's loads in flight together
+    // slice by slice, a whole slice's loads in flight together. E4M3: all S
+    // partials in slice order (binary32 sums in a fixed order: deterministic
+    // results); int8: the own slice stays in registers (int32 sums are exact
+    // in any order)
+    if constexpr (kF8) {
 #pragma unroll
-    for (int j = 0; j < C::kFN; ++j)
+      for (int j = 0; j < C::kFN; ++j)
 #pragma unroll
-      for (int i = 0; i < C::kFM; ++i)
+        for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[j][i][r] = 0;
+          for (int r = 0; r < 16; ++r) acc[j][i][r] = 0;
+    }
     for (int sl = 0; sl < ep.S; ++sl) {
+      if (!kF8 && sl == (int)blockIdx.y) continue;
       const uint32_t base = slice_base(sl);
 #pragma unroll
       for (int j = 0; j < C::kFN; ++j)
