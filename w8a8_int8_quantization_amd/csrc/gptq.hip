@@ -297,6 +297,33 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ a
     tile_fma(sa, sb, ty, tx, acc);
     __syncthreads();
   }
+  // A -= acc on and below the diagonal. With an even K and a 16-byte aligned
+  // A the thread's 8 columns go as four 16-byte accesses (c is even, so
+  // c < k implies c + 1 < k); a pair that straddles the diagonal stores its
+  // first element only.
+  if ((k & 1) == 0 && (reinterpret_cast<uintptr_t>(a) & 15) == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = r0 + 8 * ty + i;
+      const int64_t rr = r < k ? r : k - 1;
+      double2 old[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t c = c0 + 8 * tx + 2 * j;
+        old[j] = *reinterpret_cast<const double2*>(&a[rr * k + (c < k ? c : k - 2)]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t c = c0 + 8 * tx + 2 * j;
+        if (r < k && c + 1 <= r)
+          *reinterpret_cast<double2*>(&a[r * k + c]) =
+              double2{old[j].x - acc[i][2 * j], old[j].y - acc[i][2 * j + 1]};
+        else if (r < k && c == r)
+          a[r * k + c] = old[j].x - acc[i][2 * j];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t r = r0 + 8 * ty + i;
@@ -418,6 +445,30 @@ __global__ __launch_bounds__(256) void gptq_trailing_kernel(const double* __rest
     if (p0 + kGP < kGB) fetch(p0 + kGP);
     tile_fma(sa, sb, ty, tx, acc);
     __syncthreads();
+  }
+  // Z += acc. With an even row length and a 16-byte aligned Z the thread's 8
+  // columns go as four 16-byte accesses (column pairs never straddle the end:
+  // c is even, so c < n implies c + 1 < n); otherwise one element at a time.
+  if ((n & 1) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = r0 + 8 * ty + i;
+      const int64_t rr = r < k ? r : k - 1;
+      double2 old[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t c = c0 + 8 * tx + 2 * j;
+        old[j] = *reinterpret_cast<const double2*>(&z[rr * n + (c < n ? c : n - 2)]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t c = c0 + 8 * tx + 2 * j;
+        if (r < k && c < n)
+          *reinterpret_cast<double2*>(&z[r * n + c]) =
+              double2{old[j].x + acc[i][2 * j], old[j].y + acc[i][2 * j + 1]};
+      }
+    }
+    return;
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
