@@ -164,7 +164,7 @@ sq_status sq_quant_act_per_token(const void* x, sq_dtype xt, int64_t m, int64_t 
  * int8 x int8 -> int32 GEMM with the fused per-token x per-output-channel
  * dequantisation epilogue, on the gfx950 int8 matrix cores.
  * [INT8] "The architecture: every piece explained" (int32 accumulation; the
- * accumulator is scaled by the outer product of row and column scales);
+ * accumulator is scaled by the product of its row and column scales);
  * [W8A8] "Performance After Quantization", Inter-Token Latency (the int8
  * matmul output is converted back to bf16).
  *
@@ -184,11 +184,21 @@ sq_status sq_quant_act_per_token(const void* x, sq_dtype xt, int64_t m, int64_t 
  *     layers at least 4096 wide with K >= 2560) whose tiles number fewer
  *     than 128 (up to 8 slices of at least 1024 K each; one ticket counter
  *     per output tile). The size depends on (m, n, k) only.
- *     The workspace then holds the counters and int32 partial tiles. The
- *     caller zero-fills the workspace once, before its first use; every call
- *     leaves the counters at zero again, so later calls need no clearing.
- *     One workspace serves one call at a time (calls in flight together on
- *     different streams need their own). The split changes only how the
+ *     The workspace then holds the ticket counters, in a fixed region of
+ *     the first 1 KiB, and the int32 partial tiles after it. Contract: the
+ *     counter region reads zero when a call starts. The caller zero-fills
+ *     the workspace once, before its first use; every call leaves its
+ *     counters at zero again, and no call writes partial tiles into the
+ *     counter region, so one zero-filled workspace of the largest size
+ *     needed serves any later sequence of calls, at any shapes, without
+ *     clearing. Failure mode: non-zero counters at the start of a call (a
+ *     workspace never zero-filled, or one shared by calls in flight at the
+ *     same time) let the tile reduction run before every slice has
+ *     published, or never, so Y is wrong or left unwritten; nothing
+ *     detects this. One workspace serves one call at a time (calls in
+ *     flight together on different streams need their own). The one-call
+ *     entry points (sq_w8a8_linear_dyn and the fused norm / gated-MLP
+ *     calls) clear the counters themselves. The split changes only how the
  *     exact int32 sum is formed, never its value.
  */
 size_t sq_w8a8_linear_workspace_size(int64_t m, int64_t n, int64_t k);
@@ -327,13 +337,13 @@ sq_status sq_silu_mul_w8a8_linear(const void* gate, const void* up, sq_dtype t, 
  *   y[i][n] = out(fl32(fl32(acc_in * x_scale_i) * w_scale_n)), yt = SQ_F32,
  *   SQ_BF16 or SQ_F16. K % 128 == 0, K <= SQ_MAX_K_FP8.
  *   ws: sq_fp8_linear_workspace_size(m, n, k) bytes, 16-byte aligned (NULL
- *   when that is 0), with the contract of sq_w8a8_linear's workspace: for
- *   shapes whose K is split over several workgroups (the decode and prefill
- *   cases of sq_w8a8_linear) it holds binary32 partial tiles and the ticket
- *   counters, which the caller
- *   zero-fills once and every call leaves at zero; one call at a time per
- *   workspace. The partial tiles are added in a fixed order (deterministic
- *   results), each sum rounded to binary32.
+ *   when that is 0), with the layout, contract and failure mode of
+ *   sq_w8a8_linear's workspace: for shapes whose K is split over several
+ *   workgroups (the decode and prefill cases of sq_w8a8_linear) it holds the
+ *   ticket counters (first 1 KiB, zero when a call starts: the caller
+ *   zero-fills once, every call leaves them at zero) and binary32 partial
+ *   tiles; one call at a time per workspace. The partial tiles are added in
+ *   a fixed order (deterministic results), each sum rounded to binary32.
  * sq_fp8_linear_dyn: sq_quant_act_fp8 then sq_fp8_linear on the same stream,
  *   with the codes, row scales and the GEMM's workspace in ws
  *   (sq_fp8_linear_dyn_workspace_size; no initialisation needed: the

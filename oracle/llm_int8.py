@@ -8,8 +8,8 @@ explained" and "End-to-end flow", in its order:
 2. column split: outlier columns go to the fp16 path, the rest to int8;
 3. int8 path: one scale per row of X over the regular columns only, one scale
    per column of W (made once at load time over all of W's rows); int8 x int8
-   with an int32 accumulator; dequantisation by the outer product of the
-   scales, to fp16;
+   with an int32 accumulator; dequantisation by the row scale times the
+   column scale, to fp16;
 4. fp16 path: the outlier columns of X times the matching fp16 weight rows;
 5. accumulate: the two fp16 partial products are added.
 

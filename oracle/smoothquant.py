@@ -197,7 +197,7 @@ def dequantize(acc: np.ndarray, x_scale: np.ndarray, w_scale: np.ndarray,
     """y_in = ((float)acc_in * x_scale_i) * w_scale_n in binary32, then the output type.
 
     The LLM.int8() page, "The architecture ...": the accumulator is scaled by
-    the outer product of the row and column scales; the W8A8 post, "Inter-Token
+    the row scale times the column scale; the W8A8 post, "Inter-Token
     Latency": the result is converted back to bf16. ``out`` is 'f32', 'bf16'
     (returned as uint16 bit patterns) or 'f16'.
     """

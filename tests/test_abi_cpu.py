@@ -122,12 +122,15 @@ def test_validation_linear(sq):
     # 65..256 tokens: the decode kernel only where the tiled kernels get few tiles
     assert sq.raw["sq_w8a8_linear_workspace_size"](128, 4096, 14336) > 0       # down projection shape
     # 160..255 tokens over wide layers: the 256-row kernel, K split 3 ways over
-    # its 75 tiles of 256 x 192 (300 bytes of counters, padded to 512)
-    assert sq.raw["sq_w8a8_linear_workspace_size"](192, 14336, 4096) == 512 + 3 * 75 * 256 * 192 * 4
+    # its 75 tiles of 256 x 192, the partial tiles after the fixed 1 KiB
+    # counter region
+    assert sq.raw["sq_w8a8_linear_workspace_size"](192, 14336, 4096) == 1024 + 3 * 75 * 256 * 192 * 4
     assert sq.raw["sq_w8a8_linear_workspace_size"](150, 20000, 2048) == 0      # 128 x 128 tiles
     # prefill with 2 x 22 tiles of 256 x 192: K (112 stages of 128) split 5
-    # ways, 5 x 44 partial int32 tiles after 256 bytes of tile counters
-    assert sq.raw["sq_w8a8_linear_workspace_size"](257, 4096, 14336) == 256 + 5 * 44 * 256 * 192 * 4
+    # ways, 5 x 44 partial int32 tiles after the counter region
+    assert sq.raw["sq_w8a8_linear_workspace_size"](257, 4096, 14336) == 1024 + 5 * 44 * 256 * 192 * 4
+    # decode: 64 columns x 64 tokens per counter, partial tiles [S][M][N] after the region
+    assert sq.raw["sq_w8a8_linear_workspace_size"](64, 4096, 14336) == 1024 + 4 * 64 * 4096 * 4
     assert sq.raw["sq_w8a8_linear_workspace_size"](4096, 4096, 14336) == 0     # 256 tiles: no split
     d = sq.raw["sq_w8a8_linear_dyn"]
     need = sq.raw["sq_w8a8_linear_dyn_workspace_size"](4, 4, 64)

@@ -2,8 +2,10 @@
 
 Calibration statistics, smoothing factors, Wq, w_scale, Xq and x_scale are
 compared in full; the GEMM output on every row for the small configurations
-and on a seeded sample of rows (all columns) for the large ones, which the
-oracle computes row by row.
+and, for the large ones, on a stratified sample of rows (all columns) that the
+oracle computes row by row: one row for every position within the 256-row
+tiles (each from a seeded random tile) plus the last row, so every row slot
+of the kernels' tiles and the ragged tail are checked at full size.
 """
 import numpy as np
 import pytest
@@ -17,7 +19,15 @@ pytestmark = pytest.mark.gpu
 
 sq = pytest.importorskip("w8a8_int8_quantization_amd")
 
-ROW_SAMPLE = 192
+ROW_SAMPLE = 256  # rows per tile of the prefill kernel
+
+
+def _stratified_rows(m: int, seed: int) -> np.ndarray:
+    """One row for each residue mod ROW_SAMPLE (in a random tile), plus m - 1."""
+    rng = np.random.default_rng(seed)
+    rows = [r + ROW_SAMPLE * int(rng.integers(0, (m - r + ROW_SAMPLE - 1) // ROW_SAMPLE))
+            for r in range(min(ROW_SAMPLE, m))]
+    return np.unique(np.array(rows + [m - 1], dtype=np.int64))
 
 
 def _run_linear(c, sample_rows):
@@ -44,8 +54,7 @@ def _run_linear(c, sample_rows):
     xq_ref, dx_ref = oracle.quantize_activations(c.x, s_ref)
     assert np.array_equal(host(dx), dx_ref), "x_scale"
     assert np.array_equal(host(xq), xq_ref), "Xq"
-    rows = np.arange(c.m) if not sample_rows else np.sort(
-        np.random.default_rng(c.m + c.n).choice(c.m, min(sample_rows, c.m), replace=False))
+    rows = np.arange(c.m) if not sample_rows else _stratified_rows(c.m, c.m + c.n)
     acc_ref = oracle.int8_matmul(xq_ref[rows], wq_ref)
     y_ref = oracle.dequantize(acc_ref, dx_ref[rows], sw_ref, c.y_dtype)
     acc = sq.sq_w8a8_linear(xq, dx, wq, sw, out_dtype=torch.int32)
@@ -93,6 +102,6 @@ def test_llm_int8_full():
     xq, dx = sq.sq_quant_act_rows_masked(xh, mask)
     xq_ref, dx_ref = oracle.quantize_rows_regular(cfg.x, mask_ref)
     assert np.array_equal(host(xq), xq_ref) and np.array_equal(host(dx), dx_ref)
-    rows = np.sort(np.random.default_rng(5).choice(cfg.m, ROW_SAMPLE, replace=False))
+    rows = _stratified_rows(cfg.m, 5)
     r = oracle.int8_decomp_linear(cfg.x[rows], wq_ref, sw_ref, cfg.w, cfg.threshold, mask=mask_ref)
     assert np.array_equal(bits16(y)[rows], r["y"].view(np.uint16))

@@ -196,3 +196,31 @@ def test_fp8_split_dyn_garbage_workspace(m):
     y1 = sq.sq_fp8_linear_dyn(x, wq, sw, ws=ws)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     _fp8_check(y1, host(xq), host(d), host(wq), host(sw), "bf16")
+
+
+def test_workspace_shared_across_shapes():
+    """One zero-filled workspace of the largest size serves calls of different
+    shapes in sequence: the ticket counters sit in a fixed region that no
+    shape's partial tiles overwrite (decode shapes split 4 and 2 ways, a
+    65..256-token decode shape, a split prefill shape, then the first shape
+    again), int32 results exact and E4M3 results equal to fresh-workspace calls."""
+    shapes = [(64, 4096, 14336), (64, 6144, 4096), (100, 4096, 14336), (512, 4096, 14336), (8, 4096, 14336),
+              (64, 4096, 14336)]
+    need = max(sq.raw["sq_w8a8_linear_workspace_size"](m, n, k) for m, n, k in shapes)
+    need8 = max(sq.raw["sq_fp8_linear_workspace_size"](m, n, k) for m, n, k in shapes)
+    assert all(sq.raw["sq_w8a8_linear_workspace_size"](m, n, k) > 0 for m, n, k in shapes)
+    ws = torch.zeros(max(need, need8), dtype=torch.uint8, device=dev())
+    for i, (m, n, k) in enumerate(shapes):
+        log("shared workspace, int8", m, n, k)
+        xq = workloads.uniform_int8((m, k), seed=70 + i, stream=1)
+        wq = workloads.uniform_int8((n, k), seed=70 + i, stream=2)
+        acc = sq.sq_w8a8_linear(_d(xq), None, _d(wq), None, out_dtype=torch.int32, ws=ws)
+        assert np.array_equal(host(acc), oracle.int8_matmul(xq, wq)), (m, n, k)
+        assert int(ws[:1024].view(torch.int32).abs().sum()) == 0
+    for i, (m, n, k) in enumerate(shapes):
+        log("shared workspace, e4m3", m, n, k)
+        args = [_d(a) for a in _fp8_case(m, n, k, seed=90 + i)]
+        y_shared = sq.sq_fp8_linear(*args, ws=ws)
+        y_fresh = sq.sq_fp8_linear(*args, ws=sq.fp8_linear_workspace(m, n, k, dev()))
+        assert torch.equal(y_shared.view(torch.int16), y_fresh.view(torch.int16)), (m, n, k)
+        assert int(ws[:1024].view(torch.int32).abs().sum()) == 0

@@ -22,7 +22,7 @@ ARCH = "gfx950"
 # method's definitions are written; fused multiply-adds appear only where a
 # kernel asks for one.  Packed FP32 instructions are disabled.
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
@@ -39,17 +39,37 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build_library(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + [f"-I{INCLUDE}", f"-I{CSRC}", "-o", tmp] + sources()
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _compile(src: str, obj: str) -> str:
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-c", f"-I{INCLUDE}", f"-I{CSRC}", "-o", obj, src]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
-    if verbose and out.strip():
-        print(out)
+        raise RuntimeError(f"hipcc failed on {os.path.basename(src)} ({res.returncode}):\n{out}")
+    return out
+
+
+def build_library(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every source to an object (in parallel), then link libsq.so."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    srcs = sources()
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
+    jobs = jobs or min(len(srcs), max(1, min(os.cpu_count() or 1, 8)))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        outs = list(ex.map(_compile, srcs, objs))
+    if verbose:
+        for o in outs:
+            if o.strip():
+                print(o)
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed ({res.returncode}):\n{res.stdout + res.stderr}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -2,7 +2,7 @@
 // dequantisation epilogue.
 //
 // The LLM.int8() page, "The architecture: every piece explained": int8
-// operands, int32 accumulation, dequantisation by the outer product of the
+// operands, int32 accumulation, dequantisation by the product of the
 // per-row (token) and per-column (output channel) scales; the fp16 outlier
 // slice of the decomposition is added in the same epilogue. "Half the Size,
 // Better Performance, Same Accuracy: Understanding W8A8 INT8 LLM

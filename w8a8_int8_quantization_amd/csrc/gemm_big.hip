@@ -2,7 +2,7 @@
 // dequantisation epilogue (and the LLM.int8() fp16 outlier slice).
 //
 // The LLM.int8() page, "The architecture: every piece explained": int8 x int8
-// products accumulated in int32, scaled by the outer product of the row
+// products accumulated in int32, scaled by the product of the row
 // (token) and column (output channel) scales; the fp16 outlier slice is added
 // to the dequantised product. "Half the Size, Better Performance, Same
 // Accuracy: Understanding W8A8 INT8 LLM Quantization", "Performance After
@@ -31,7 +31,6 @@
 //  * Workgroups are dispatched round-robin over the 8 XCDs; the tile order
 //    gives each XCD a contiguous range of tiles, grouped 4 tile-rows at a time,
 //    so that tiles sharing Xq and Wq panels run under the same L2.
-#include <cstdlib>
 #include <type_traits>
 
 #include "sq_common.hpp"
@@ -40,13 +39,6 @@
 namespace sqk {
 
 constexpr int kBigBM = 256;
-// Eight waves, two per SIMD, in a 4 x 2 grid over the tile: while one wave of
-// a SIMD waits on its fragment reads or the stage barrier, the other keeps the
-// matrix core busy (measured on MI355X against four waves of twice the
-// sub-tile: QKV 62 -> 55 us, gate/up 1010 -> 942 us, down 425 -> 406 us), at
-// the price of ~40% more LDS fragment reads, which the LDS has room for.
-constexpr int kBigWaves = 8;
-constexpr int kBigThreads = 64 * kBigWaves;
 constexpr int kBigBK = 128;    // k bytes per pipeline stage: one 128-byte line per tile row
 constexpr int kBigStages = 2;  // LDS double buffer
 constexpr int kGroupM = 4;
@@ -64,17 +56,23 @@ enum BigOut { kBigF32 = 0, kBigBF16 = 1, kBigF16 = 2, kBigI32 = 3, kBigDecomp = 
 __device__ __forceinline__ int big_swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int big_lds_off(int r, int c) { return r * kBigBK + ((c ^ big_swz(r)) << 4); }
 
-template <int BN>
+// kW waves in a (kW/2) x 2 grid over the 256 x BN tile. Eight waves (two per
+// SIMD, 64 x BN/2 each): while one wave of a SIMD waits on its fragment reads
+// or the stage barrier, the other keeps the matrix core busy. Four waves (one
+// per SIMD, 128 x BN/2 each): every fragment read feeds twice the MFMAs, so
+// the LDS carries less per MFMA, and the schedule alone has to hide waits.
+template <int BN, int kW = 8>
 struct BigCfg {
+  static constexpr int kThreads = 64 * kW;
   static constexpr int kWN = BN / 2;                  // output columns per wave
   static constexpr int kFN = kWN / 32;
-  static constexpr int kWM = kBigBM / (kBigWaves / 2);  // tokens per wave
+  static constexpr int kWM = kBigBM / (kW / 2);        // tokens per wave
   static constexpr int kFM = kWM / 32;
   static constexpr int kStageA = kBigBM * kBigBK;
   static constexpr int kStage = (kBigBM + BN) * kBigBK;
   // 1 KiB direct-to-LDS transfers (8 rows each) per wave and stage
-  static constexpr int kDmaA = kBigBM / 8 / kBigWaves;
-  static constexpr int kDmaB = BN / 8 / kBigWaves;
+  static constexpr int kDmaA = kBigBM / 8 / kW;
+  static constexpr int kDmaB = BN / 8 / kW;
   static constexpr int kDma = kDmaA + kDmaB;
 };
 
@@ -148,17 +146,21 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // 32-k ones; everything else is shared with the int8 kernel.
 // kSplit: the K range is split over blockIdx.y (see BigEpi); the tile's last
 // workgroup adds the S partial tiles in slice order, then runs the epilogue.
-template <int BN, int kOut, bool kVec, bool kF8 = false, bool kSplit = false>
-__global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
-                                                          int M, int N, int K, BigEpi ep) {
-  using C = BigCfg<BN>;
+template <int BN, int kW, int kOut, bool kVec, bool kF8 = false, bool kSplit = false>
+__global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
+                                                              int M, int N, int K, BigEpi ep) {
+  using C = BigCfg<BN, kW>;
   using AccT = typename std::conditional<kF8, v16f, v16i>::type;
   using FragT = typename std::conditional<kF8, v8i, v4i>::type;
   constexpr int kSub = kF8 ? 2 : 4;  // MFMA k-substeps per 128-byte stage
+  // Two stage buffers; stage kt lives in buffer kt % 2. The epilogue stages
+  // its output bands in them as well.
   __shared__ __attribute__((aligned(1024))) int8_t smem[kBigStages * C::kStage];
   // LLM.int8(): the tile's fp16 outlier slices of X and W, gathered once
   __shared__ uint16_t slice_x[kOut == kBigDecomp ? kBigBM * kSliceCols : 1];
   __shared__ __attribute__((aligned(16))) uint16_t slice_w[kOut == kBigDecomp ? kSliceCols * BN : 1];
+  // the tile's output-channel scales, read by the epilogue
+  __shared__ __attribute__((aligned(16))) float scale_w[kOut == kBigI32 ? 4 : BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
 #pragma unroll
   for (int i = 0; i < C::kDma; ++i) {
     const bool is_a = i < C::kDmaA;
-    const int blk = (is_a ? i : i - C::kDmaA) * kBigWaves + wid;  // 8-row block within the operand tile
+    const int blk = (is_a ? i : i - C::kDmaA) * kW + wid;  // 8-row block within the operand tile
     const int r = blk * 8 + (lane >> 3);
     const int c = (lane & 7) ^ big_swz(r);
     if (is_a) {
@@ -202,9 +204,11 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
       dst[i] = C::kStageA + blk * 1024;
     }
   }
+  auto kbyte = [&](int kt) -> int64_t { return (int64_t)kt * kBigBK; };
+  auto stage_ptr = [&](int kt) { return smem + (kt & 1) * C::kStage; };
   auto issue = [&](int kt) {
-    int8_t* stage = smem + (kt % kBigStages) * C::kStage;
-    const int64_t koff = (int64_t)kt * kBigBK;
+    int8_t* stage = stage_ptr(kt);
+    const int64_t koff = kbyte(kt);
 #pragma unroll
     for (int i = 0; i < C::kDma; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(src[i] + koff), (lds_void*)(stage + dst[i]), 16, 0, 0);
@@ -218,10 +222,32 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0;
 
+  // The epilogue's scales are fetched before the first transfers, so that
+  // their latency hides behind the main loop: the lane's token scales in
+  // registers, the tile's channel scales in LDS.
+  const int frow = lane & 31;
+  float xs[C::kFM];
+#pragma unroll
+  for (int i = 0; i < C::kFM; ++i) {
+    const int m = m0 + wm * C::kWM + 32 * i + frow;
+    xs[i] = (kOut != kBigI32 && m < M) ? ep.x_scale[m] : 0.f;
+  }
+  float4 w4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (kOut != kBigI32 && tid < BN / 4) {
+    const int n = n0 + 4 * tid;
+    if (kVec && n + 4 <= N) {
+      w4 = *reinterpret_cast<const float4*>(ep.w_scale + n);
+    } else {
+      if (n < N) w4.x = ep.w_scale[n];
+      if (n + 1 < N) w4.y = ep.w_scale[n + 1];
+      if (n + 2 < N) w4.z = ep.w_scale[n + 2];
+      if (n + 3 < N) w4.w = ep.w_scale[n + 3];
+    }
+  }
+
   issue(0);
   if (nk > 1) issue(1);
 
-  const int frow = lane & 31;
   const int fhalf = lane >> 5;
   // Fragment of tile row r for substep ks: int8, 16 bytes (chunk 2 ks + half);
   // E4M3, 32 bytes (chunks 4 ks + 2 half and the next one).
@@ -243,7 +269,6 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
 #pragma unroll
     for (int j = 0; j < C::kFN; ++j) wf[j] = frag(stage + C::kStageA, wn * C::kWN + 32 * j + frow, ks);
   };
-  auto stage_ptr = [&](int kt) { return smem + (kt & 1) * C::kStage; };
 
   // Software pipeline over the 4 substeps of a stage: the fragments of the
   // next substep are read from LDS while the MFMAs of the current one run,
@@ -256,8 +281,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
   // cores do (issued in one burst they stall the wave for hundreds of cycles).
   constexpr int kQ = C::kFN * C::kFM > C::kDma ? C::kFN * C::kFM : C::kDma;
   auto dma_one = [&](int kt, int i) {
-    int8_t* stage = smem + (kt & 1) * C::kStage;
-    __builtin_amdgcn_global_load_lds((const void*)(src[i] + (int64_t)kt * kBigBK), (lds_void*)(stage + dst[i]), 16, 0,
+    __builtin_amdgcn_global_load_lds((const void*)(src[i] + kbyte(kt)), (lds_void*)(stage_ptr(kt) + dst[i]), 16, 0,
                                      0);
   };
   auto frag_one = [&](const int8_t* stage, int ks, int q, FragT* xf, FragT* wf) {
@@ -274,6 +298,9 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
   lds_barrier();
   read_frags(stage_ptr(0), 0, fx[0], fw[0]);
   wait_lgkmcnt0();
+  // The stage hand-over (transfer wait, barrier) runs in front of the last
+  // substep of every stage but the last; the stage after next is transferred
+  // during that substep when it exists.
   for (int kt = 0; kt < nk; ++kt) {
     const int8_t* cur = stage_ptr(kt);
 #pragma unroll
@@ -318,7 +345,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
     // (their padding is never stored to y).
     __shared__ uint32_t last_ticket;
     constexpr uint32_t kTileBytes = kBigBM * BN * 4;
-    constexpr uint32_t kWaveBytes = kTileBytes / kBigWaves;
+    constexpr uint32_t kWaveBytes = kTileBytes / kW;
     const uint32_t pbytes = (uint32_t)ep.S * (uint32_t)total * kTileBytes;
     const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(ep.partial, (short)0, pbytes, kBigBufDword3);
     const int tile_id = tm * nbn + tn;
@@ -387,11 +414,11 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
   const int mw = m0 + wm * C::kWM;
   const int nw = n0 + wn * C::kWN;
   int mrow[C::kFM];
-  float xs[C::kFM];
 #pragma unroll
-  for (int i = 0; i < C::kFM; ++i) {
-    mrow[i] = mw + 32 * i + frow;
-    xs[i] = (kOut != kBigI32 && mrow[i] < M) ? ep.x_scale[mrow[i]] : 0.f;
+  for (int i = 0; i < C::kFM; ++i) mrow[i] = mw + 32 * i + frow;
+  if (kOut != kBigI32) {
+    if (tid < BN / 4) *reinterpret_cast<float4*>(&scale_w[4 * tid]) = w4;
+    __syncthreads();
   }
   const int cnt = kOut == kBigDecomp ? *ep.dec.count : 0;
   // Up to kSliceCols outlier columns: gather X[tile rows][idx] and
@@ -405,7 +432,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
       for (int c = 0; c < cnt; ++c)
         slice_x[row * kSliceCols + c] = m < M ? ep.dec.x[m * ep.dec.ldx + ep.dec.idx[c]] : (uint16_t)0;
     }
-    for (int e = tid; e < cnt * BN; e += kBigThreads) {
+    for (int e = tid; e < cnt * BN; e += C::kThreads) {
       const int c = e / BN, nl = e - c * BN;
       const int64_t n = (int64_t)n0 + nl;
       slice_w[c * BN + nl] = n < N ? ep.dec.w16[(int64_t)ep.dec.idx[c] * ep.dec.ldw + n] : (uint16_t)0;
@@ -461,15 +488,15 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
     }
   };
   // column scales of the 4 outputs a lane holds in row group rg of block j
+  // (zero past N), from the LDS copy
   auto col_scales = [&](int n, int nvalid, float* ws) {
-    ws[0] = ws[1] = ws[2] = ws[3] = 0.f;
-    if (kOut == kBigI32 || n >= N) return;
-    if (kVec && nvalid == 4) {
-      const float4 w4 = *reinterpret_cast<const float4*>(ep.w_scale + n);
-      ws[0] = w4.x; ws[1] = w4.y; ws[2] = w4.z; ws[3] = w4.w;
-    } else {
-      for (int e = 0; e < nvalid; ++e) ws[e] = ep.w_scale[n + e];
+    if (kOut == kBigI32) {
+      ws[0] = ws[1] = ws[2] = ws[3] = 0.f;
+      return;
     }
+    (void)nvalid;
+    const float4 c4 = *reinterpret_cast<const float4*>(&scale_w[n - n0]);
+    ws[0] = c4.x; ws[1] = c4.y; ws[2] = c4.z; ws[3] = c4.w;
   };
   // output values of fragment (j, i), row group rg: dequantised, plus the
   // outlier slice for LLM.int8()
@@ -493,62 +520,73 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
   };
 
   if (ep.rows16) {
-    // Staged through LDS, one band of tile rows at a time: the lanes' 4-column
-    // pieces are assembled into whole tile rows, which then leave as 16-byte
-    // chunks, consecutive threads writing consecutive chunks of a row (whole
-    // 128-byte lines; written straight from the fragments, 32 rows x 16 bytes
-    // per instruction, the partial lines cost about three times the output
-    // size in HBM writes).
+    // Staged through LDS, one band at a time: the lanes' 4-column pieces are
+    // assembled into whole rows, which then leave as 16-byte chunks,
+    // consecutive threads writing consecutive chunks of a row (whole 128-byte
+    // lines; written straight from the fragments, 32 rows x 16 bytes per
+    // instruction, the partial lines cost about three times the output size
+    // in HBM writes). Band (i, h) holds fragment row block i of every wave
+    // row (kW/2 x 32 tile rows) and, for 4-byte outputs, column half h (all
+    // BN columns for 2-byte outputs). Bands alternate between the two stage
+    // buffers, so one barrier per band separates its writes from its
+    // copy-out: the copy-out of band b and the writes of band b + 1 use
+    // different buffers. Chunk c of staged row r sits at chunk (c + r) mod
+    // kCh, which spreads the 32 rows of a fragment write over the banks.
     constexpr int kEl = (kOut == kBigF32 || kOut == kBigI32) ? 4 : 2;
-    constexpr int kRowB = BN * kEl + 16;  // staged row pitch; the pad spreads the row-strided writes over the banks
-    constexpr int kBand = 128 * kRowB <= kBigStages * C::kStage ? 128 : 64;
-    constexpr int kChunks = BN * kEl / 16;
-    constexpr int kPer = 16 / kEl;  // outputs per chunk
-#pragma unroll 1
-    for (int band = 0; band < kBigBM / kBand; ++band) {
-      __syncthreads();  // every wave is done with the LDS contents
+    constexpr int kRows = (kW / 2) * 32;  // rows per band
+    constexpr int kParts = kRows * BN * kEl <= C::kStage ? 1 : 2;
+    constexpr int kColsB = BN / kParts;  // columns per band
+    constexpr int kRowB = kColsB * kEl;  // staged row bytes
+    constexpr int kCh = kRowB / 16;      // 16-byte chunks per staged row
+    constexpr int kPer = 16 / kEl;       // outputs per chunk
+    static_assert(kRows * kRowB <= C::kStage, "an output band must fit one stage buffer");
+    __syncthreads();  // every wave is done with the stage buffers
 #pragma unroll
-      for (int j = 0; j < C::kFN; ++j) {
-        // fragments of this wave inside the band (the test is uniform per wave)
-        const int i0 = (band * kBand - wm * C::kWM) / 32;
-        const int lo = i0 < 0 ? 0 : i0, hi = min(C::kFM, i0 + kBand / 32);
-        if (lo >= hi) continue;
-        float yo[kOut == kBigDecomp ? C::kFM : 1][16];
-        if (kOut == kBigDecomp) outlier_slice(j, lo, hi, yo);
+    for (int b = 0; b < C::kFM * kParts; ++b) {
+      const int i = b / kParts, h = b % kParts;
+      int8_t* const buf = smem + (b & 1) * C::kStage;
+      if (kParts == 1 || wn == h) {
+        const int lr = wm * 32 + frow;  // row within the band
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int nl = wn * C::kWN + 32 * j + 8 * rg + 4 * fhalf;
-          const int n = n0 + nl;
-          float ws[4];
-          col_scales(n, min(4, N - n), ws);
+        for (int j = 0; j < C::kFN; ++j) {
+          float yo[kOut == kBigDecomp ? C::kFM : 1][16];
+          if (kOut == kBigDecomp) outlier_slice(j, i, i + 1, yo);
 #pragma unroll
-          for (int i = 0; i < C::kFM; ++i) {
-            if (i < lo || i >= hi) continue;
+          for (int rg = 0; rg < 4; ++rg) {
+            const int nl = wn * C::kWN + 32 * j + 8 * rg + 4 * fhalf;
+            float ws[4];
+            col_scales(n0 + nl, 4, ws);
             int a[4];
             float v[4];
             out_values(j, i, rg, ws, yo, v, a);
-            int8_t* dst = smem + (wm * C::kWM + 32 * i + frow - band * kBand) * kRowB + nl * kEl;
+            const int cb = (nl - h * kColsB) * kEl;  // byte offset within the staged row
+            int pc = (cb >> 4) + lr % kCh;
+            if (pc >= kCh) pc -= kCh;
+            int8_t* dst = buf + lr * kRowB + pc * 16 + (cb & 15);
             if (kOut == kBigI32) {
               *reinterpret_cast<int4*>(dst) = make_int4(a[0], a[1], a[2], a[3]);
             } else if (kOut == kBigF32) {
               *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+            } else if (kOut == kBigBF16) {
+              *reinterpret_cast<uint2*>(dst) = make_uint2(bf16x2_rn(v[0], v[1]), bf16x2_rn(v[2], v[3]));
             } else {
-              uint32_t h[4];
+              uint32_t hb[4];
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                h[e] = (kOut == kBigBF16) ? f32_to_bf16(v[e]) : f32_to_f16(v[e]);
-              *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+              for (int e = 0; e < 4; ++e) hb[e] = f32_to_f16(v[e]);
+              *reinterpret_cast<uint2*>(dst) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
             }
           }
         }
       }
       __syncthreads();
-      for (int c = tid; c < kBand * kChunks; c += kBigThreads) {
-        const int r = c / kChunks, ch = c - r * kChunks;
-        const int m = m0 + band * kBand + r;
-        const int n = n0 + ch * kPer;
+      for (int c = tid; c < kRows * kCh; c += C::kThreads) {
+        const int lr = c / kCh, ch = c - lr * kCh;
+        const int m = m0 + (lr >> 5) * C::kWM + 32 * i + (lr & 31);
+        const int n = n0 + h * kColsB + ch * kPer;
         if (m >= M || n >= N) continue;
-        const int8_t* srcp = smem + r * kRowB + ch * 16;
+        int pc = ch + lr % kCh;
+        if (pc >= kCh) pc -= kCh;
+        const int8_t* srcp = buf + lr * kRowB + pc * 16;
         int8_t* dst = reinterpret_cast<int8_t*>(ep.y) + ((int64_t)m * ep.ldy + n) * kEl;
         if (n + kPer <= N) {
           *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(srcp);
@@ -586,46 +624,46 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const int8_t* 
   }
 }
 
-template <int BN, int kOut, bool kVec, bool kF8 = false>
+template <int BN, int kW, int kOut, bool kVec, bool kF8 = false>
 static void launch_big(const int8_t* xq, const int8_t* wq, int M, int N, int K, const BigEpi& ep, hipStream_t s) {
   const int tiles = ((M + kBigBM - 1) / kBigBM) * ((N + BN - 1) / BN);
   if (ep.S > 1 && kOut != kBigDecomp)
-    hipLaunchKernelGGL((gemm_big_kernel<BN, kOut, kVec, kF8, kOut != kBigDecomp>), dim3(tiles, ep.S),
-                       dim3(kBigThreads), 0, s, xq, wq, M, N, K, ep);
+    hipLaunchKernelGGL((gemm_big_kernel<BN, kW, kOut, kVec, kF8, kOut != kBigDecomp>), dim3(tiles, ep.S),
+                       dim3(64 * kW), 0, s, xq, wq, M, N, K, ep);
   else
-    hipLaunchKernelGGL((gemm_big_kernel<BN, kOut, kVec, kF8>), dim3(tiles), dim3(kBigThreads), 0, s, xq, wq, M, N,
-                       K, ep);
+    hipLaunchKernelGGL((gemm_big_kernel<BN, kW, kOut, kVec, kF8, false>), dim3(tiles), dim3(64 * kW), 0, s, xq,
+                       wq, M, N, K, ep);
 }
 
-template <int BN, int kOut, bool kF8 = false>
+template <int BN, int kW, int kOut, bool kF8 = false>
 static void launch_big_v(const int8_t* xq, const int8_t* wq, int M, int N, int K, const BigEpi& ep, bool vec,
                          hipStream_t s) {
   if (vec)
-    launch_big<BN, kOut, true, kF8>(xq, wq, M, N, K, ep, s);
+    launch_big<BN, kW, kOut, true, kF8>(xq, wq, M, N, K, ep, s);
   else
-    launch_big<BN, kOut, false, kF8>(xq, wq, M, N, K, ep, s);
+    launch_big<BN, kW, kOut, false, kF8>(xq, wq, M, N, K, ep, s);
 }
 
-template <int BN>
+template <int BN, int kW = 8>
 static void launch_big_o(const int8_t* xq, const int8_t* wq, int M, int N, int K, const BigEpi& ep, int out, bool vec,
                          hipStream_t s) {
   switch (out) {
-    case kBigF32: launch_big_v<BN, kBigF32>(xq, wq, M, N, K, ep, vec, s); break;
-    case kBigBF16: launch_big_v<BN, kBigBF16>(xq, wq, M, N, K, ep, vec, s); break;
-    case kBigF16: launch_big_v<BN, kBigF16>(xq, wq, M, N, K, ep, vec, s); break;
-    case kBigI32: launch_big_v<BN, kBigI32>(xq, wq, M, N, K, ep, vec, s); break;
-    default: launch_big_v<BN, kBigDecomp>(xq, wq, M, N, K, ep, vec, s); break;
+    case kBigF32: launch_big_v<BN, kW, kBigF32>(xq, wq, M, N, K, ep, vec, s); break;
+    case kBigBF16: launch_big_v<BN, kW, kBigBF16>(xq, wq, M, N, K, ep, vec, s); break;
+    case kBigF16: launch_big_v<BN, kW, kBigF16>(xq, wq, M, N, K, ep, vec, s); break;
+    case kBigI32: launch_big_v<BN, kW, kBigI32>(xq, wq, M, N, K, ep, vec, s); break;
+    default: launch_big_v<BN, kW, kBigDecomp>(xq, wq, M, N, K, ep, vec, s); break;
   }
 }
 
 // E4M3 operands: floating-point outputs only
-template <int BN>
+template <int BN, int kW = 8>
 static void launch_big_f8(const int8_t* xq, const int8_t* wq, int M, int N, int K, const BigEpi& ep, int out,
                           bool vec, hipStream_t s) {
   switch (out) {
-    case kBigF32: launch_big_v<BN, kBigF32, true>(xq, wq, M, N, K, ep, vec, s); break;
-    case kBigBF16: launch_big_v<BN, kBigBF16, true>(xq, wq, M, N, K, ep, vec, s); break;
-    default: launch_big_v<BN, kBigF16, true>(xq, wq, M, N, K, ep, vec, s); break;
+    case kBigF32: launch_big_v<BN, kW, kBigF32, true>(xq, wq, M, N, K, ep, vec, s); break;
+    case kBigBF16: launch_big_v<BN, kW, kBigBF16, true>(xq, wq, M, N, K, ep, vec, s); break;
+    default: launch_big_v<BN, kW, kBigF16, true>(xq, wq, M, N, K, ep, vec, s); break;
   }
 }
 
@@ -674,9 +712,6 @@ struct BigSplit {
 int split_for(int64_t tiles, int stages, int bn) {
   int want = tiles < 128 ? (int)(255 / tiles) : 1;
   int best = (int)(sqrtf(0.45f * (float)stages) + 0.5f);
-#ifdef SQ_TUNE
-  if (const char* e = getenv("SQ_BIG_SPLIT")) want = best = atoi(e);
-#endif
   if (want > best) want = best;
   if (want > kBigMaxSplit) want = kBigMaxSplit;
   if (want > stages / 8) want = stages / 8;
@@ -705,10 +740,6 @@ BigSplit big_split(int64_t m, int64_t n, int64_t k, bool f8, bool split_ok = tru
   double best_score = -1.0;
   for (int bn : cands) {
     if (f8 && bn == 256) continue;  // E4M3 tiles: 192 or 128 columns
-#ifdef SQ_TUNE
-    if (const char* e = getenv("SQ_BIG_BN"))
-      if (atoi(e) != bn) continue;
-#endif
     BigSplit p;
     p.bn = bn;
     p.tiles = ((m + sqk::kBigBM - 1) / sqk::kBigBM) * ((n + bn - 1) / bn);
@@ -727,7 +758,6 @@ BigSplit big_split(int64_t m, int64_t n, int64_t k, bool f8, bool split_ok = tru
   return best;
 }
 
-size_t big_counter_bytes(int64_t tiles) { return ((size_t)tiles * 4 + 255) / 256 * 256; }
 
 }  // namespace
 
@@ -735,7 +765,7 @@ size_t gemm_big_workspace(int64_t m, int64_t n, int64_t k, bool f8) {
   if (!gemm_big_suits(m, n, k)) return 0;
   const BigSplit p = big_split(m, n, k, f8);
   if (p.S == 1) return 0;
-  return big_counter_bytes(p.tiles) + (size_t)p.S * (size_t)p.tiles * (size_t)(sqk::kBigBM * p.bn * 4);
+  return kSplitCounterBytes + (size_t)p.S * (size_t)p.tiles * (size_t)(sqk::kBigBM * p.bn * 4);
 }
 
 void gemm_big_counters(int64_t m, int64_t n, int64_t k, bool f8, void* ws, uint32_t** counters, int64_t* count) {
@@ -757,7 +787,7 @@ hipError_t gemm_i8_big(const int8_t* xq, const float* x_scale, const int8_t* wq,
     ep.S = sp.S;
     ep.slice_stages = sp.slice_stages;
     ep.counter = reinterpret_cast<uint32_t*>(ws);
-    ep.partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + big_counter_bytes(sp.tiles));
+    ep.partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + kSplitCounterBytes);
   }
   int out;
   int eb;
@@ -792,7 +822,7 @@ hipError_t gemm_f8_big(const uint8_t* xq, const float* x_scale, const uint8_t* w
     ep.S = sp.S;
     ep.slice_stages = sp.slice_stages;
     ep.counter = reinterpret_cast<uint32_t*>(ws);
-    ep.partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + big_counter_bytes(sp.tiles));
+    ep.partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + kSplitCounterBytes);
   }
   const int out = yt == SQ_F32 ? sqk::kBigF32 : (yt == SQ_BF16 ? sqk::kBigBF16 : sqk::kBigF16);
   const int eb = yt == SQ_F32 ? 4 : 2;

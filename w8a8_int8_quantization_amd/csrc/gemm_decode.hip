@@ -3,7 +3,7 @@
 // streaming the weight matrix Wq [N x K] from HBM.
 //
 // The LLM.int8() page, "The architecture: every piece explained" (int8
-// operands, int32 accumulation, dequantisation by the outer product of the row
+// operands, int32 accumulation, dequantisation by the product of the row
 // and column scales); "Half the Size, Better Performance, Same Accuracy:
 // Understanding W8A8 INT8 LLM Quantization", "Performance After Quantization"
 // (per decoded token the weights are read once; the layer is memory-bound).
@@ -44,7 +44,6 @@
 #include "sq_common.hpp"
 #include "sq_launch.hpp"
 
-#include <stdlib.h>
 
 namespace sqk {
 
@@ -305,7 +304,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
     const uint32_t sstride = (uint32_t)((size_t)a.M * a.N * 4);
     if (vec) {
       // eight slices per round trip; slices past S read beyond the buffer's
-      // range, which a raw buffer load returns as zero
+      // range (a raw buffer load returns zero there) and are not added
       for (int s = 0; s < a.S; s += 8) {
         v4i part[8];
 #pragma unroll
@@ -313,7 +312,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
           part[u] = __builtin_amdgcn_raw_buffer_load_b128(pr, off0 + (uint32_t)(s + u) * sstride, 0, kCoherent);
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          if (!kF8 || s + u < a.S) t += __builtin_bit_cast(AccT, part[u]);
+          if (s + u < a.S) t += __builtin_bit_cast(AccT, part[u]);
       }
     } else {
       for (int s = 0; s < a.S; ++s)
@@ -364,9 +363,6 @@ DecodePlan decode_plan(int64_t m, int64_t n, int64_t k) {
   const int wgs = p.tiles * p.tb;
   int want = (256 + wgs - 1) / wgs;
   if (wgs >= 192) want = 1;
-#ifdef SQ_TUNE
-  if (const char* e = getenv("SQ_DECODE_SPLIT")) want = atoi(e);
-#endif
   if (want < 1) want = 1;
   if (want > steps) want = steps;
   int per = (steps + want - 1) / want;
@@ -374,11 +370,15 @@ DecodePlan decode_plan(int64_t m, int64_t n, int64_t k) {
   if (per > cap) per = cap;
   p.slice_steps = per;
   p.S = (steps + per - 1) / per;
+  // one ticket counter per column tile and token block, in the fixed region
+  if (p.S > 1 && (int64_t)p.tiles * p.tb > kSplitMaxCounters) {
+    p.S = 1;
+    p.slice_steps = steps;
+  }
   p.ns = (per + sqk::kDecWaves - 1) / sqk::kDecWaves;
   return p;
 }
 
-size_t counter_bytes(int tiles) { return ((size_t)tiles * 4 + 255) / 256 * 256; }
 
 template <int kMB, bool kF8>
 hipError_t launch_decode(const sqk::DecodeArgs& a, int ns, dim3 grid, hipStream_t s) {
@@ -407,14 +407,10 @@ hipError_t decode_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
   a.out = yt == SQ_F32 ? 0 : yt == SQ_BF16 ? 1 : yt == SQ_F16 ? 2 : 3;
   if (p.S > 1) {
     a.counter = reinterpret_cast<uint32_t*>(ws);
-    a.partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + counter_bytes(p.tiles * p.tb));
+    a.partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + kSplitCounterBytes);
   }
   const dim3 grid((unsigned)p.tiles, (unsigned)p.S, (unsigned)p.tb);
-  bool mb1 = m <= 16;
-#ifdef SQ_TUNE
-  if (getenv("SQ_DECODE_MB2")) mb1 = false;
-#endif
-  if (mb1) return launch_decode<1, kF8>(a, p.ns, grid, s);
+  if (m <= 16) return launch_decode<1, kF8>(a, p.ns, grid, s);
   if (m <= 32) return launch_decode<2, kF8>(a, p.ns, grid, s);
   return launch_decode<4, kF8>(a, p.ns, grid, s);
 }
@@ -444,11 +440,13 @@ static bool decode_beats_prefill(int64_t m, int64_t n, int64_t k) {
 
 bool gemm_decode_suits(int64_t m, int64_t n, int64_t k) {
   if (!(m >= 1 && m <= kDecodeMaxM && n >= 1 && n <= INT32_MAX && k % sqk::kDecStep == 0)) return false;
+  // the partial tiles must fit 32-bit offsets (with the reducer's eight-slice
+  // rounds)
+  const DecodePlan p = decode_plan(m, n, k);
+  if ((size_t)(p.S + 7) / 8 * 8 * (size_t)m * (size_t)n * 4 >= ((size_t)1 << 31)) return false;
   if (m <= 64) return true;
   // beyond one 64-token block only where the prefill kernels get few tiles
-  // (see the dispatch notes); the partial tiles must fit 32-bit offsets
-  const DecodePlan p = decode_plan(m, n, k);
-  if ((size_t)p.S * (size_t)m * (size_t)n * 4 >= ((size_t)1 << 31)) return false;
+  // (see the dispatch notes)
   return decode_beats_prefill(m, n, k);
 }
 
@@ -456,7 +454,7 @@ size_t gemm_decode_workspace(int64_t m, int64_t n, int64_t k) {
   if (!gemm_decode_suits(m, n, k)) return 0;
   const DecodePlan p = decode_plan(m, n, k);
   if (p.S == 1) return 0;
-  return counter_bytes(p.tiles * p.tb) + (size_t)p.S * (size_t)m * (size_t)n * 4;
+  return kSplitCounterBytes + (size_t)p.S * (size_t)m * (size_t)n * 4;
 }
 
 void gemm_decode_counters(int64_t m, int64_t n, int64_t k, void* ws, uint32_t** counters, int64_t* count) {

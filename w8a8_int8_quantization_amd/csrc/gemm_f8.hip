@@ -5,7 +5,7 @@
 // LLM Quantization", section "Conclusion": FP8 is the W8A8 alternative that
 // skips calibration and needs newer hardware. The dequantisation is the int8
 // path's (the LLM.int8() page, "The architecture: every piece explained":
-// scale the accumulator by the outer product of row and column scales).
+// scale the accumulator by the product of its row and column scales).
 //
 //   acc_in = sum_k E4M3(xq_ik) * E4M3(wq_nk)        (matrix-core binary32 sums)
 //   y_in   = out(fl32(fl32(acc_in * x_scale_i) * w_scale_n))
@@ -25,7 +25,6 @@
 // XOR-swizzled with (row >> 1) & 7; the next step's global loads are issued
 // before the MFMAs of the current one. Lane l supplies row l % 32 and the 32
 // k-bytes 32 * (l / 32) .. +31 of a 64-k half-step (two 16-byte chunks).
-#include <cstdlib>
 
 #include "sq_common.hpp"
 #include "sq_launch.hpp"
@@ -167,24 +166,10 @@ __global__ __launch_bounds__(256) void gemm_f8_kernel(const uint8_t* __restrict_
 
 namespace sqh {
 
-// Tuning builds (-DSQ_TUNE) only: SQ_F8_BIG=0 keeps prefill-sized problems on
-// the 128 x 128 kernel, for comparisons.
-static bool f8_big_enabled() {
-#ifdef SQ_TUNE
-  static const bool on = [] {
-    const char* e = getenv("SQ_F8_BIG");
-    return !(e && e[0] == '0');
-  }();
-  return on;
-#else
-  return true;
-#endif
-}
-
 hipError_t gemm_f8(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
                    int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, hipStream_t s) {
   if (m <= 0 || n <= 0) return hipSuccess;
-  if (gemm_big_suits(m, n, k) && f8_big_enabled())
+  if (gemm_big_suits(m, n, k))
     return gemm_f8_big(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, ws, s);
   const int64_t tiles = ((m + sqk::kF8BM - 1) / sqk::kF8BM) * ((n + sqk::kF8BN - 1) / sqk::kF8BN);
   const dim3 grid((unsigned)tiles), block(256);

@@ -27,6 +27,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Two binary32 values -> two bf16 (low half = a), round to nearest even, with
+// gfx950's packed conversion (v_cvt_pk_bf16_f32): the same results as
+// f32_to_bf16 on every finite value, in one instruction per pair.
+__device__ __forceinline__ uint32_t bf16x2_rn(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }

@@ -10,6 +10,15 @@
 
 namespace sqh {
 
+// Split-K workspaces (the decode and prefill GEMMs): ticket counters in a
+// fixed region at the start, then the partial tiles. The region has room for
+// every split the dispatch makes (the decode kernel splits only below 192
+// workgroups, the prefill kernel only below 128 tiles), so the partial tiles
+// of one shape never land on the counters of another: one zero-filled
+// workspace serves any sequence of calls, of any shapes, made one at a time.
+constexpr size_t kSplitCounterBytes = 1024;
+constexpr int64_t kSplitMaxCounters = (int64_t)(kSplitCounterBytes / 4);
+
 // Extra inputs of the LLM.int8() epilogue: the fp16 outlier slice.
 struct DecompArgs {
   const uint16_t* x;    // [M x ldx] fp16 activations
