@@ -222,6 +222,28 @@ sq_status sq_w8a8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const floa
                              sq_stream_t stream);
 
 /*
+ * sq_w8a8_linear_dyn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation). It allocates nothing: its scratch (Xq,
+ * the row scales, the split-K counters and partial tiles) is a static device
+ * array of SQ_STATIC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends. Same arguments and results as
+ * sq_w8a8_linear_dyn, without ws / ws_bytes.
+ * Errors: those of sq_w8a8_linear_dyn; SQ_ERR_WORKSPACE when
+ * sq_w8a8_linear_dyn_workspace_size(m, n, k) exceeds SQ_STATIC_SCRATCH_BYTES
+ * (nothing is enqueued); SQ_ERR_HIP when the array's device address cannot be
+ * looked up on the first call on a device (current device >= 64: SQ_ERR_RANGE).
+ * All calls on one GPU share its array: calls that overlap in time on one GPU
+ * (other streams, other host threads) race and give wrong results, so the
+ * caller serialises them. Contents left by an earlier call do not matter (the
+ * call's quantisation launch clears the counters).
+ */
+#define SQ_STATIC_SCRATCH_BYTES (32u << 20)
+sq_status sq_w8a8_linear_dyn_static(const void* x, sq_dtype xt, int64_t ldx, const float* smooth,
+                                    const int8_t* wq, const float* w_scale, int64_t m, int64_t n, int64_t k,
+                                    void* y, sq_dtype yt, int64_t ldy, sq_stream_t stream);
+
+/*
  * The smoothing factor moved into RMSNorm's gain, once at load time.
  * [W8A8] "How the smoothing factor is computed" (SmoothQuant divides the
  * norm's gamma by s and multiplies the matching weight rows by s, which

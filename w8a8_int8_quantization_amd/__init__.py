@@ -58,6 +58,7 @@ _SIGS = {
     "sq_w8a8_linear": (_st, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _st, _i64, _p, _sz, _p]),
     "sq_w8a8_linear_dyn_workspace_size": (_sz, [_i64, _i64, _i64]),
     "sq_w8a8_linear_dyn": (_st, [_p, _st, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _st, _i64, _p, _sz, _p]),
+    "sq_w8a8_linear_dyn_static": (_st, [_p, _st, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _st, _i64, _p]),
     "sq_fold_norm_gain": (_st, [_p, _st, _p, _i64, _p, _p]),
     "sq_rmsnorm_quant": (_st, [_p, _st, _i64, _i64, _i64, _p, _f, _p, _p, _p]),
     "sq_rmsnorm_w8a8_linear_workspace_size": (_sz, [_i64, _i64, _i64]),
@@ -226,6 +227,19 @@ def sq_w8a8_linear_dyn(x: torch.Tensor, smooth: Optional[torch.Tensor], wq: torc
     _check("sq_w8a8_linear_dyn", raw["sq_w8a8_linear_dyn"](
         _ptr(x), _dt(x), ldx, _ptr(smooth), _ptr(wq), _ptr(w_scale), m, n, k, _ptr(y), _dt(y), ldy,
         _ptr(ws), ws.numel() if ws is not None else 0, _stream(x.device)))
+    return y
+
+
+def sq_w8a8_linear_dyn_static(x: torch.Tensor, smooth: Optional[torch.Tensor], wq: torch.Tensor,
+                              w_scale: torch.Tensor, out_dtype=torch.bfloat16, y: Optional[torch.Tensor] = None):
+    """:func:`sq_w8a8_linear_dyn` with the library's static scratch instead of a workspace."""
+    m, k, ldx = _rows(x)
+    n = wq.shape[0]
+    y = torch.empty((m, n), dtype=out_dtype, device=x.device) if y is None else y
+    _, _, ldy = _rows(y)
+    _check("sq_w8a8_linear_dyn_static", raw["sq_w8a8_linear_dyn_static"](
+        _ptr(x), _dt(x), ldx, _ptr(smooth), _ptr(wq), _ptr(w_scale), m, n, k, _ptr(y), _dt(y), ldy,
+        _stream(x.device)))
     return y
 
 

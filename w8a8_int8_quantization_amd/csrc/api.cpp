@@ -83,6 +83,10 @@ sq_status quant_then_gemm(Quant quant, const int8_t* wq, const float* w_scale, i
 
 }  // namespace
 
+namespace sqh {
+void set_last_hip_error(int e) { g_last_hip_error = e; }
+}  // namespace sqh
+
 extern "C" {
 
 const char* sq_status_string(sq_status status) {

@@ -31,6 +31,10 @@ struct DecompArgs {
 
 hipError_t fill_u32(void* p, uint32_t value, int64_t count, hipStream_t s);
 
+// Records the HIP error behind an SQ_ERR_HIP (what sq_last_hip_error() returns
+// on this thread).
+void set_last_hip_error(int e);
+
 hipError_t absmax_cols(const void* x, sq_dtype xt, int64_t t, int64_t k, int64_t ldx, float* absmax,
                        hipStream_t s);
 
