@@ -115,3 +115,55 @@ def test_decode_workspace_validation():
     st = sq.raw["sq_w8a8_linear"](xq.data_ptr(), None, wq.data_ptr(), None, m, n, k, y.data_ptr(), 3, n,
                                   None, 0, None)
     assert st == 6
+
+
+# One token: sq_w8a8_linear_dyn runs the quantisation inside the decode GEMM
+# (one launch) for layers at least 192 x 64 wide, and quantisation + split-K
+# GEMM otherwise. (dtype, n, k): the 8B up projection, ragged N, the longest
+# rows the fused path takes (16384 bf16 / fp16, 8192 binary32), a one-step K,
+# and narrower layers on the two-launch path.
+ONE_TOKEN = [("bf16", 14336, 4096), ("bf16", 12300, 16384), ("f16", 12290, 1152), ("f32", 14336, 8192),
+             ("f32", 12288, 128), ("bf16", 28672, 256), ("bf16", 4096, 14336), ("f16", 300, 1152)]
+
+
+def _one_token_case(dtype, n, k, seed, smooth_kind):
+    c = workloads.random_linear_case(m=1, k=k, n=n, seed=seed, dtype=dtype, calib_rows=8)
+    x = to_dev(c.x, dtype)
+    if smooth_kind == "none":
+        s = None
+    elif smooth_kind == "fast":
+        s = torch.from_numpy(workloads.spread_scales(k, seed=seed, lo_exp=-6, hi_exp=6)).to(dev())
+    else:  # factors outside the quotients' fast range: IEEE division throughout
+        s = torch.from_numpy(workloads.spread_scales(k, seed=seed, lo_exp=-30, hi_exp=30)).to(dev())
+    _, wq, sw = sq.sq_smooth_fold_weights(to_dev(c.w, dtype), flags=sq.SMOOTH_NONE)
+    return x, s, wq, sw
+
+
+@pytest.mark.parametrize("smooth_kind", ["fast", "wide", "none"])
+@pytest.mark.parametrize("dtype,n,k", ONE_TOKEN)
+def test_one_token_fused_equals_two_calls(dtype, n, k, smooth_kind):
+    """Row scale, codes and outputs of the fused one-token step are those of
+    the quantisation kernel followed by the GEMM, bit for bit."""
+    log("one token fused", dtype, n, k, smooth_kind)
+    x, s, wq, sw = _one_token_case(dtype, n, k, seed=n + k, smooth_kind=smooth_kind)
+    for out in (torch.bfloat16, torch.float32, torch.float16):
+        y1 = sq.sq_w8a8_linear_dyn(x, s, wq, sw, out_dtype=out)
+        xq, dx = sq.sq_quant_act_per_token(x, s)
+        y2 = sq.sq_w8a8_linear(xq, dx, wq, sw, out_dtype=out)
+        iv = torch.int32 if out == torch.float32 else torch.int16
+        assert torch.equal(y1.view(iv), y2.view(iv)), out
+
+
+def test_one_token_fused_zero_row_and_oracle():
+    """A zero token gives zero outputs; a real one matches the oracle."""
+    k, n = 4096, 14336
+    c = workloads.linear_case("decode_up", m=1)
+    s_ref = oracle.smoothing_factors(oracle.calibrate_absmax(c.x_calib), oracle.weight_row_absmax(c.w), c.alpha)
+    s = torch.from_numpy(s_ref).to(dev())
+    _, wq, sw = sq.sq_smooth_fold_weights(to_dev(c.w, "bf16"), smooth=s, flags=sq.SMOOTH_GIVEN)
+    y0 = sq.sq_w8a8_linear_dyn(torch.zeros((1, k), dtype=torch.bfloat16, device=dev()), s, wq, sw)
+    assert int((bits16(y0) != 0).sum()) == 0
+    y = sq.sq_w8a8_linear_dyn(to_dev(c.x, "bf16"), s, wq, sw)
+    wq_ref, sw_ref = oracle.quantize_weights_per_channel(oracle.fold_weights(c.w, s_ref))
+    y_ref, _, _, _ = oracle.smoothquant_linear(c.x, s_ref, wq_ref, sw_ref, "bf16")
+    assert_out_close(y, y_ref, "bf16")

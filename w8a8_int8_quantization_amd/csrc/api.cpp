@@ -224,6 +224,10 @@ sq_status sq_w8a8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const floa
   if (!ws || ws_bytes < sq_w8a8_linear_dyn_workspace_size(m, n, k)) return SQ_ERR_WORKSPACE;
   if (!aligned16(ws)) return SQ_ERR_ALIGN;
   const hipStream_t s = (hipStream_t)stream;
+  // one token on the weight-streaming path: one launch (the quantisation
+  // runs inside the GEMM; the workspace is not touched)
+  if (sqh::gemm_decode_suits(m, n, k) && sqh::decode1_suits(m, n, k, xt))
+    return hip_status(sqh::decode1_linear(x, xt, smooth, wq, w_scale, n, k, y, yt, s));
   auto quant = [&](int8_t* xq, float* dx, uint32_t* zero, int64_t nzero) {
     return sqh::quant_rows(x, xt, m, k, ldx, smooth, nullptr, xq, dx, s, zero, nzero);
   };

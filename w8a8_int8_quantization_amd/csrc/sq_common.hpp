@@ -195,14 +195,14 @@ __device__ __forceinline__ float div_mk(float a, float b, float rb) {
   return __builtin_fmaf(e, rb, q0);
 }
 
-// int8 code of one quotient: clamp to [-127, 127], then adding 1.5 * 2^23
+// int8 code of one quotient v = fl32(a / d) with d = fl32(amax / 127) and
+// |a| <= amax (a row's own values): |a / d| <= amax / d <= 127 (1 + 2^-23),
+// so |v| < 127.0001 and round-half-even(v) already lies in [-127, 127]; the
+// clamp of the definition never acts and is not applied. Adding 1.5 * 2^23
 // rounds to the nearest integer with ties to even (the sum lies in
 // [2^23, 2^24), where the binary32 spacing is 1) and leaves the two's-
 // complement code in the low byte of the sum's bit pattern.
-__device__ __forceinline__ uint32_t q_code(float v) {
-  v = __builtin_amdgcn_fmed3f(v, -(float)kQMax, (float)kQMax);
-  return __float_as_uint(v + 12582912.0f);
-}
+__device__ __forceinline__ uint32_t q_code(float v) { return __float_as_uint(v + 12582912.0f); }
 
 // Low bytes of four codes -> one little-endian word (v_perm_b32 picks bytes).
 __device__ __forceinline__ uint32_t pack4(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3) {

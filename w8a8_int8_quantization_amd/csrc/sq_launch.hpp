@@ -99,6 +99,12 @@ void gemm_big_counters(int64_t m, int64_t n, int64_t k, bool f8, void* ws, uint3
 hipError_t gemm_f8_big(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
                        int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, hipStream_t s);
 
+// One-token decode step (quantisation fused into the weight-streaming GEMM;
+// no workspace): whether it takes this shape, and the call.
+bool decode1_suits(int64_t m, int64_t n, int64_t k, sq_dtype xt);
+hipError_t decode1_linear(const void* x, sq_dtype xt, const float* smooth, const int8_t* wq, const float* w_scale,
+                          int64_t n, int64_t k, void* y, sq_dtype yt, hipStream_t s);
+
 // Decode GEMM (M <= 64): split-K over workgroups, partial tiles and ticket
 // counters in the workspace. The counters must be zero at launch.
 bool gemm_decode_suits(int64_t m, int64_t n, int64_t k);
