@@ -74,6 +74,13 @@ def decode_kernel_runs(m: int, n: int, k: int) -> bool:
     return units <= 128
 
 
+def decode_one_token_fused(m: int, n: int, k: int) -> bool:
+    """Whether the one-call path fuses the quantisation into the decode GEMM
+    (the C ABI's rule for bf16 inputs): one token, a layer at least 192 x 64
+    wide, K a multiple of 128 up to 16384."""
+    return decode_kernel_runs(m, n, k) and m == 1 and -(-n // 64) >= 192 and k % 128 == 0 and k <= 16384
+
+
 def hbm_bound(m: int, n: int, k: int, out_bytes: int) -> bool:
     """Below the ridge point (dense int8 / FP8 peak over HBM bandwidth) the
     GEMM is bound by streaming its operands."""
@@ -103,6 +110,21 @@ def parse():
     p.add_argument("--alpha", type=float, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle time budget")
+    p.add_argument("--one-call", action="store_true",
+                   help="time the step as one sq_w8a8_linear_dyn call instead of quantisation + GEMM "
+                        "(the default for the one-token config records)")
+    p.add_argument("--no-configs", action="store_true",
+                   help="default workload only: skip the per-config records of the other configurations")
+    p.add_argument("--ingest-stats", default=None,
+                   help="record a rocprofv3 --stats kernel_stats.csv for --workload in profiles/pmc_traffic.json "
+                        "(with --kernel-match and --kernel-file); no GPU needed")
+    p.add_argument("--pmc-fetch", default=None, help="rocprofv3 --pmc FETCH_SIZE counter_collection.csv to record")
+    p.add_argument("--pmc-write", default=None, help="rocprofv3 --pmc WRITE_SIZE counter_collection.csv to record")
+    p.add_argument("--kernel-match", default="gemm_big_kernel", help="substring of the kernel name to record")
+    p.add_argument("--kernel-file", default="gemm_big.hip", help="source file of that kernel (csrc/)")
+    p.add_argument("--fetch-scale", type=float, default=1.9999,
+                   help="FETCH_SIZE scale factor from the copy probe (profiles/hbm_counter_scale_copy.md)")
+    p.add_argument("--write-scale", type=float, default=1.0, help="WRITE_SIZE scale factor from the copy probe")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain device-to-device copy of 512 MiB (5 times), the known-size "
                         "reference that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
@@ -127,8 +149,8 @@ def kernel_source_hash(name: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def pmc_traffic(workload: str, kernel_file: str):
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, if current."""
+def profile_entry(workload: str, kernel_file: str):
+    """The committed rocprofv3 record of this workload's kernel (profiles/pmc_traffic.json), if its source is current."""
     try:
         with open(PROFILE_PMC) as f:
             d = json.load(f)
@@ -137,7 +159,25 @@ def pmc_traffic(workload: str, kernel_file: str):
     e = d.get(workload)
     if not e or e.get("source_sha256_16") != kernel_source_hash(kernel_file):
         return None
-    return e.get("hbm_bytes_per_launch")
+    return e
+
+
+def pmc_traffic(workload: str, kernel_file: str):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, if current."""
+    e = profile_entry(workload, kernel_file)
+    return e.get("hbm_bytes_per_launch") if e else None
+
+
+def kernel_only(roof: dict, workload: str, kernel_file: str, per_launch: float):
+    """Adds the rocprofv3 kernel-only duration of the committed profile (if
+    current) and the roofline fraction computed from it, beside the
+    event-timed one (HIP events also count the dispatch gap before a launch)."""
+    e = profile_entry(workload, kernel_file)
+    us = e.get("kernel_us") if e else None
+    roof["kernel_us_rocprof"] = us
+    roof["frac_kernel_only"] = (per_launch / (us * 1e-6) / (1e9 if roof["unit"] == "GB/s" else 1e12) / roof["peak"]
+                                if us else None)
+    roof["frac_basis"] = "frac: HIP events around each launch on its stream; frac_kernel_only: rocprofv3 kernel time"
 
 
 class HipEvents:
@@ -349,7 +389,7 @@ def bench_fp8(args, dev):
         "weight_copies": n_w, "roofline": roof, "cpu_baseline": None if args.no_cpu_baseline else
         cpu_baseline_fp8(c, args.cpu_seconds),
     }
-    print(json.dumps(result), flush=True)
+    return result
 
 
 GPTQ_SHAPES = {"gptq_qkv": (4096, 6144), "gptq_down": (14336, 4096)}  # K, N; 8 x 512 calibration rows
@@ -436,7 +476,7 @@ def bench_gptq(args, dev):
         "roofline": roof,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_gptq(c, args.cpu_seconds),
     }
-    print(json.dumps(result), flush=True)
+    return result
 
 
 def cpu_baseline_gptq(c, budget_s: float):
@@ -574,7 +614,8 @@ def bench_llm_int8(args, dev):
                      "ops_per_launch": ops, "launch_us": part[2] * 1e3},
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_decomp(c, args.cpu_seconds),
     }
-    print(json.dumps(result), flush=True)
+    kernel_only(result["roofline"], "llm_int8" if args.m is None else f"llm_int8_m{c.m}", "gemm_big.hip", ops)
+    return result
 
 
 def cpu_baseline_decomp(c, budget_s: float):
@@ -599,36 +640,16 @@ def cpu_baseline_decomp(c, budget_s: float):
                       f"outputs, K={c.k}), {t_total:.1f} s of numpy/BLAS work"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: the W8A8 linear layer is built and measured on a single "
-              "MI355X (no sharding or collectives in this library); use --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-
-    if args.copy_probe:
-        copy_probe()
-        return
-
+def bench_linear(args, dev) -> dict:
+    """The run-time path of one linear layer (quantisation + GEMM, or the
+    fused RMSNorm / gated-activation variants), timed with HIP events."""
     import numpy as np
     import torch
 
     import workloads
     import w8a8_int8_quantization_amd as sq
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    if args.workload == "llm_int8":
-        bench_llm_int8(args, dev)
-        return
-    if args.workload.startswith("fp8_"):
-        bench_fp8(args, dev)
-        return
-    if args.workload.startswith("gptq_"):
-        bench_gptq(args, dev)
-        return
+    one_call = getattr(args, "one_call", False)
     norm = args.workload.startswith("rmsnorm_")
     silu = args.workload.startswith("silu_")
     base = args.workload[len("rmsnorm_"):] if norm else (
@@ -707,16 +728,28 @@ def main():
     g_args = [(xq.data_ptr(), dx.data_ptr(), w_i.data_ptr(), sw.data_ptr(), c.m, c.n, c.k, y.data_ptr(),
                sq._dt(y), c.n, ws.data_ptr() if ws is not None else None, nb, stream) for w_i in wqs]
     hip = HipEvents(sq._lib, stream)
+    dyn_fn = sq.raw["sq_w8a8_linear_dyn"]
+    if one_call:
+        if norm or silu:
+            raise SystemExit("--one-call applies to the plain quantisation + GEMM path")
+        dws = torch.zeros(sq.raw["sq_w8a8_linear_dyn_workspace_size"](c.m, c.n, c.k), dtype=torch.uint8, device=dev)
+        d_args = [(x.data_ptr(), sq._dt(x), ldx, s.data_ptr(), w_i.data_ptr(), sw.data_ptr(), c.m, c.n, c.k,
+                   y.data_ptr(), sq._dt(y), c.n, dws.data_ptr(), dws.numel(), stream) for w_i in wqs]
 
     def run(steps, evs=None):
         bad = 0
         for i in range(steps):
             if evs:
                 hip.record(evs[i][0])
-            bad |= q_fn(*q_args)
-            if evs:
-                hip.record(evs[i][1])
-            bad |= g_fn(*g_args[i % n_w])
+            if one_call:
+                if evs:
+                    hip.record(evs[i][1])
+                bad |= dyn_fn(*d_args[i % n_w])
+            else:
+                bad |= q_fn(*q_args)
+                if evs:
+                    hip.record(evs[i][1])
+                bad |= g_fn(*g_args[i % n_w])
             if evs:
                 hip.record(evs[i][2])
         if bad:
@@ -746,6 +779,17 @@ def main():
     instr_ms = hip.elapsed(i_start, i_end) / args.steps
     quant_ms = float(np.mean([hip.elapsed(e[0], e[1]) for e in evs]))
     gemm_ms = float(np.mean([hip.elapsed(e[1], e[2]) for e in evs]))
+    # the GEMM (or the one call) alone, launches back to back
+    b0, b1 = hip.create(), hip.create()
+    hip.record(b0)
+    for i in range(args.steps):
+        if one_call:
+            dyn_fn(*d_args[i % n_w])
+        else:
+            g_fn(*g_args[i % n_w])
+    hip.record(b1)
+    torch.cuda.synchronize()
+    b2b_ms = hip.elapsed(b0, b1) / args.steps
     hip.destroy_all()
 
     ops = 2.0 * c.m * c.n * c.k
@@ -756,10 +800,15 @@ def main():
     quant_bytes = c.m * c.k * in_bytes + 4 * c.k + c.m * c.k + 4 * c.m
     gemm_bytes = c.m * c.k + c.n * c.k + 4 * c.m + 4 * c.n + c.m * c.n * {"f32": 4, "bf16": 2}[c.y_dtype]
     big = big_kernel_suits(c.m, c.n, c.k)
-    kfile, kname = (("gemm_decode.hip", "gemm_decode_kernel") if decode else
+    fused1 = one_call and decode_one_token_fused(c.m, c.n, c.k)
+    kfile, kname = (("decode_fused.hip", "gemm_decode1_kernel") if fused1 else
+                    ("gemm_decode.hip", "gemm_decode_kernel") if decode else
                     ("gemm_big.hip", "gemm_big_kernel") if big else ("gemm.hip", "gemm_i8_kernel"))
-    tag = args.workload if args.m is None else f"{args.workload}_m{c.m}"
+    tag = (args.workload if args.m is None else f"{args.workload}_m{c.m}") + (":one_call" if one_call else "")
     traffic = pmc_traffic(tag, kfile)
+    if fused1:
+        # one launch reads X, s, Wq and the scales and writes Y (Xq never reaches memory)
+        gemm_bytes = c.m * c.k * in_bytes + 4 * c.k + c.n * c.k + 4 * c.n + c.m * c.n * {"f32": 4, "bf16": 2}[c.y_dtype]
     if streamed:
         roof = {"bound": "hbm", "achieved": gemm_bytes / (gemm_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "kernel": kname, "bytes_per_launch": gemm_bytes}
@@ -769,6 +818,7 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic
     roof["launch_us"] = gemm_ms * 1e3
+    kernel_only(roof, tag, kfile, gemm_bytes if streamed else ops)
     pre = "norm_" if norm else ("silu_" if silu else "")
     norm_roof = None
     if norm or silu:
@@ -792,10 +842,12 @@ def main():
         "pct_int8_peak": 100.0 * value / PEAK_INT8_TOPS,
         "gemm_only_tops": gemm_tops,
         "gemm_us": gemm_ms * 1e3,
-        (pre + "quant_us"): quant_ms * 1e3,
-        (pre + "quant_gbs"): quant_bytes / (quant_ms * 1e-3) / 1e9,
-        (pre + "quant_frac_hbm"): quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "step_gbs_algorithmic": (quant_bytes + gemm_bytes) / (ms_per_step * 1e-3) / 1e9,
+        "gemm_us_back_to_back": b2b_ms * 1e3,
+        "one_call": one_call,
+        (pre + "quant_us"): None if one_call else quant_ms * 1e3,
+        (pre + "quant_gbs"): None if one_call else quant_bytes / (quant_ms * 1e-3) / 1e9,
+        (pre + "quant_frac_hbm"): None if one_call else quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "step_gbs_algorithmic": ((gemm_bytes if fused1 else quant_bytes + gemm_bytes) / (ms_per_step * 1e-3) / 1e9),
         "weight_copies": n_w,
         "host_enqueue_us_per_step": host_us,
         "ms_per_step_with_kernel_events": instr_ms,
@@ -817,6 +869,113 @@ def main():
         result["cpu_baseline"] = cpu_baseline(c, s_ref, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
+    return result
+
+
+# Per-config records of the default run: the other configurations of the
+# workload set (gate/up and down projections at 8192 tokens, alpha 0.5; the
+# decode projections at 1 and 64 tokens; the LLM.int8() layer), each timed
+# like the headline with fewer steps and a short oracle sample.
+EXTRA_CONFIGS = [("gateup_prefill", None, 30), ("down_prefill", None, 40), ("decode_up", 1, 200),
+                 ("decode_down", 1, 200), ("decode_up", 64, 200), ("decode_down", 64, 200), ("llm_int8", None, 40)]
+
+
+def config_records(args, dev) -> list:
+    import copy
+    recs = []
+    for workload, m, steps in EXTRA_CONFIGS:
+        a = copy.copy(args)
+        a.workload, a.m, a.alpha, a.steps, a.warmup = workload, m, None, steps, max(3, steps // 10)
+        a.cpu_seconds = min(args.cpu_seconds, 3.0)
+        a.one_call = m == 1  # one token: the one-call entry point (the fused step where it applies)
+        print(f"[bench] config record {workload} m={m}", file=sys.stderr, flush=True)
+        r = bench_llm_int8(a, dev) if workload == "llm_int8" else bench_linear(a, dev)
+        keep = ("value", "unit", "ms_per_step", "steps", "config", "gemm_only_tops", "gemm_us", "quant_us",
+                "gemm_us_back_to_back", "step_gbs_algorithmic", "detect_us", "outlier_columns", "weight_copies",
+                "roofline", "cpu_baseline", "one_call")
+        recs.append({k: r[k] for k in keep if k in r})
+        import torch
+        torch.cuda.empty_cache()
+    return recs
+
+
+def ingest_profile(args):
+    """Record a rocprofv3 run of one workload in profiles/pmc_traffic.json:
+    the named kernel's average duration from a --stats kernel_stats.csv, and,
+    with --pmc-fetch / --pmc-write, its FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch) scaled by the copy-probe factors, keyed by workload and the
+    kernel source file's hash (the bench ignores an entry once that file has
+    changed)."""
+    import csv
+
+    def rows(path):
+        with open(path) as f:
+            return list(csv.DictReader(f))
+
+    try:
+        with open(PROFILE_PMC) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        d = {}
+    e = dict(d.get(args.workload) or {})
+    if e.get("source_sha256_16") != kernel_source_hash(args.kernel_file):
+        e = {}
+    e.update({"kernel_file": args.kernel_file, "source_sha256_16": kernel_source_hash(args.kernel_file)})
+    if args.ingest_stats:
+        hit = [r for r in rows(args.ingest_stats) if args.kernel_match in r["Name"]]
+        if not hit:
+            raise SystemExit(f"no kernel matching {args.kernel_match!r} in {args.ingest_stats}")
+        r = max(hit, key=lambda r: int(r["Calls"]))
+        e.update({"kernel": r["Name"], "kernel_us": float(r["AverageNs"]) / 1e3, "calls": int(r["Calls"])})
+    for key, path, name in (("fetch_kib", args.pmc_fetch, "FETCH_SIZE"), ("write_kib", args.pmc_write, "WRITE_SIZE")):
+        if not path:
+            continue
+        vals = [float(r["Counter_Value"]) for r in rows(path)
+                if args.kernel_match in r["Kernel_Name"] and r["Counter_Name"] == name]
+        if not vals:
+            raise SystemExit(f"no {name} for {args.kernel_match!r} in {path}")
+        e[key] = sorted(vals)[len(vals) // 2]
+    if "fetch_kib" in e and "write_kib" in e:
+        e.update({"fetch_scale": args.fetch_scale, "write_scale": args.write_scale,
+                  "hbm_bytes_per_launch": 1024.0 * (e["fetch_kib"] * args.fetch_scale +
+                                                    e["write_kib"] * args.write_scale)})
+    d[args.workload] = e
+    with open(PROFILE_PMC, "w") as f:
+        json.dump(d, f, indent=1, sort_keys=True)
+    print(json.dumps({args.workload: e}))
+
+
+def main():
+    args = parse()
+    if args.ingest_stats or args.pmc_fetch or args.pmc_write:
+        ingest_profile(args)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the W8A8 linear layer is built and measured on a single "
+              "MI355X (no sharding or collectives in this library); use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.workload == "llm_int8":
+        result = bench_llm_int8(args, dev)
+    elif args.workload.startswith("fp8_"):
+        result = bench_fp8(args, dev)
+    elif args.workload.startswith("gptq_"):
+        result = bench_gptq(args, dev)
+    else:
+        args.one_call = args.one_call or False
+        result = bench_linear(args, dev)
+        if args.workload == "qkv_prefill" and args.m is None and not args.no_configs:
+            result["configs"] = config_records(args, dev)
     print(json.dumps(result), flush=True)
 
 
