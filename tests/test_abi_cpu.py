@@ -8,7 +8,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sq.h")
-LIB = os.path.join(ROOT, "w8a8_int8_quantization_amd", "libsq.so")
+LIB = os.environ.get("SQ_LIBRARY") or os.path.join(ROOT, "w8a8_int8_quantization_amd", "libsq.so")
 
 
 @pytest.fixture(scope="module")
@@ -289,3 +289,31 @@ def test_validation_gptq(sq):
     assert g(P, P, sq.SQ_BF16, 256, 96, 96, None, 0.01, P, P, P, nb - 1, None) == WS
     assert g(P, P, sq.SQ_BF16, 256, 96, 96, None, 0.01, P, P, BAD, nb, None) == ALIGN
     assert g(None, None, sq.SQ_BF16, 256, 0, 0, None, 0.01, None, None, None, 0, None) == OK
+
+
+def test_out_of_range_enums_rejected(sq):
+    """A C caller may pass any int for an enum argument: out-of-range element
+    types are rejected with SQ_ERR_DTYPE before anything else is looked at, and
+    an unknown status has a string (the host-sanitized build checks that no
+    such value is ever loaded as the enum)."""
+    r, BADT = sq.raw, 17
+    assert r["sq_status_string"](-5).decode() == "unknown status"
+    calls = [
+        ("sq_calibrate_absmax", (P, BADT, 4, 64, 64, P, None)),
+        ("sq_smooth_fold_weights", (P, P, BADT, 64, 64, 64, 0.5, 0, P, P, P, P, 1 << 20, None)),
+        ("sq_quant_act_per_token", (P, BADT, 4, 64, 64, None, P, P, None)),
+        ("sq_w8a8_linear", (P, P, P, P, 4, 64, 64, P, BADT, 64, None, 0, None)),
+        ("sq_w8a8_linear_dyn", (P, BADT, 64, None, P, P, 4, 64, 64, P, sq.SQ_BF16, 64, P, 1 << 20, None)),
+        ("sq_w8a8_linear_dyn", (P, sq.SQ_BF16, 64, None, P, P, 4, 64, 64, P, BADT, 64, P, 1 << 20, None)),
+        ("sq_w8a8_linear_dyn_static", (P, BADT, 64, None, P, P, 4, 64, 64, P, sq.SQ_BF16, 64, None)),
+        ("sq_fold_norm_gain", (P, BADT, None, 64, P, None)),
+        ("sq_rmsnorm_quant", (P, BADT, 4, 64, 64, P, 1e-5, P, P, None)),
+        ("sq_silu_mul_quant", (P, P, BADT, 4, 64, 64, 64, None, P, P, None)),
+        ("sq_quant_act_fp8", (P, BADT, 4, 64, 64, P, P, None)),
+        ("sq_fp8_linear", (P, P, P, P, 4, 64, 128, P, BADT, 64, None, 0, None)),
+        ("sq_gptq_hessian", (P, BADT, 4, 128, 128, None, P, None)),
+        ("sq_outlier_detect", (P, BADT, 4, 64, 64, 6.0, P, P, P, P, 1 << 20, None)),
+        ("sq_quant_act_rows_masked", (P, BADT, 4, 64, 64, P, P, P, None)),
+    ]
+    for name, args in calls:
+        assert r[name](*args) == DTYPE, name

@@ -27,7 +27,9 @@ __all__ = [
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-lib_path = os.path.join(_PKG, "libsq.so")
+# SQ_LIBRARY selects another build of the same library (the host-sanitized
+# one that the CPU tests load); by default the in-tree libsq.so.
+lib_path = os.environ.get("SQ_LIBRARY") or os.path.join(_PKG, "libsq.so")
 
 if not os.path.exists(lib_path):
     raise ImportError(

@@ -39,8 +39,8 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _compile(src: str, obj: str) -> str:
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-c", f"-I{INCLUDE}", f"-I{CSRC}", "-o", obj, src]
+def _compile(src: str, obj: str, extra=()) -> str:
+    cmd = [hipcc()] + HIPCC_FLAGS + list(extra) + ["-c", f"-I{INCLUDE}", f"-I{CSRC}", "-o", obj, src]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:
@@ -48,31 +48,53 @@ def _compile(src: str, obj: str) -> str:
     return out
 
 
-def build_library(verbose: bool = False, jobs: int = 0) -> str:
-    """Compile every source to an object (in parallel), then link libsq.so."""
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the same
+# sources (libsq_san.so, for the CPU tests of the C-ABI layer): each
+# -fsanitize= applies to the host compilation only (-Xarch_host), the gfx950
+# device code is built as usual.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_LIB = os.path.join(PKG, "libsq_san.so")
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime that a host process must preload to load libsq_san.so."""
+    clang = os.path.join(os.path.dirname(hipcc()), "..", "lib", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    out = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return out.stdout.strip()
+
+
+def build_library(verbose: bool = False, jobs: int = 0, sanitize: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link libsq.so
+    (libsq_san.so with sanitize=True)."""
     from concurrent.futures import ThreadPoolExecutor
 
     srcs = sources()
-    objdir = os.path.join(PKG, "_build")
+    objdir = os.path.join(PKG, "_build_san" if sanitize else "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
     jobs = jobs or min(len(srcs), max(1, min(os.cpu_count() or 1, 8)))
+    extra = SAN_FLAGS if sanitize else []
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        outs = list(ex.map(_compile, srcs, objs))
+        outs = list(ex.map(lambda so: _compile(so[0], so[1], extra), zip(srcs, objs)))
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    lib = SAN_LIB if sanitize else LIB
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + (
+        SAN_FLAGS + ["-shared-libsan"] if sanitize else []) + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed ({res.returncode}):\n{res.stdout + res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build_library(verbose="-v" in sys.argv))
+    print(build_library(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 
 #include "sq.h"
 #include "sq_launch.hpp"
@@ -12,6 +13,23 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// A C caller may pass any int for an enum argument, but in C++ an enum object
+// holds only values within its enumerators' bit range (loading another is
+// undefined behaviour, which the host-sanitized build reports). Enum
+// arguments are therefore read as plain ints (memcpy, not a load of the enum)
+// and range-checked before any other use.
+template <class E>
+int enum_value(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "enum arguments are int-sized");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+bool dtype_in_range(const sq_dtype& t) {
+  const int v = enum_value(t);
+  return v >= (int)SQ_F32 && v <= (int)SQ_I8;
+}
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -90,7 +108,7 @@ void set_last_hip_error(int e) { g_last_hip_error = e; }
 extern "C" {
 
 const char* sq_status_string(sq_status status) {
-  switch (status) {
+  switch (enum_value(status)) {
     case SQ_OK: return "ok";
     case SQ_ERR_NULL: return "a required pointer is NULL";
     case SQ_ERR_DTYPE: return "element type not supported by this call";
@@ -109,6 +127,7 @@ int sq_version(void) { return 10000; }
 
 sq_status sq_calibrate_absmax(const void* x, sq_dtype xt, int64_t t, int64_t k, int64_t ldx, float* absmax,
                               sq_stream_t stream) {
+  if (!dtype_in_range(xt)) return SQ_ERR_DTYPE;
   SQ_TRY(check_k(k));
   SQ_TRY(check_vec_matrix(x, xt, t, k, ldx));
   if (!absmax) return SQ_ERR_NULL;
@@ -124,6 +143,7 @@ size_t sq_smooth_fold_workspace_size(int64_t k, int64_t n) {
 sq_status sq_smooth_fold_weights(const float* absmax, const void* w, sq_dtype wt, int64_t k, int64_t n, int64_t ldw,
                                  double alpha, uint32_t flags, float* smooth, int8_t* wq, float* w_scale, void* ws,
                                  size_t ws_bytes, sq_stream_t stream) {
+  if (!dtype_in_range(wt)) return SQ_ERR_DTYPE;
   SQ_TRY(check_k(k));
   if (n < 0) return SQ_ERR_SHAPE;
   if (!float_input(wt)) return SQ_ERR_DTYPE;
@@ -149,6 +169,7 @@ sq_status sq_smooth_fold_weights(const float* absmax, const void* w, sq_dtype wt
 
 sq_status sq_quant_act_per_token(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, const float* smooth,
                                  int8_t* xq, float* x_scale, sq_stream_t stream) {
+  if (!dtype_in_range(xt)) return SQ_ERR_DTYPE;
   SQ_TRY(check_k(k));
   SQ_TRY(check_vec_matrix(x, xt, m, k, ldx));
   if (m == 0) return SQ_OK;
@@ -193,6 +214,7 @@ static sq_status check_linear(const int8_t* xq, const float* x_scale, const int8
 sq_status sq_w8a8_linear(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
                          int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, size_t ws_bytes,
                          sq_stream_t stream) {
+  if (!dtype_in_range(yt)) return SQ_ERR_DTYPE;
   SQ_TRY(check_linear(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy));
   if (m == 0 || n == 0) return SQ_OK;
   const size_t need = sq_w8a8_linear_workspace_size(m, n, k);
@@ -215,6 +237,8 @@ size_t sq_w8a8_linear_dyn_workspace_size(int64_t m, int64_t n, int64_t k) {
 sq_status sq_w8a8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const float* smooth, const int8_t* wq,
                              const float* w_scale, int64_t m, int64_t n, int64_t k, void* y, sq_dtype yt,
                              int64_t ldy, void* ws, size_t ws_bytes, sq_stream_t stream) {
+  if (!dtype_in_range(xt)) return SQ_ERR_DTYPE;
+  if (!dtype_in_range(yt)) return SQ_ERR_DTYPE;
   SQ_TRY(check_k(k));
   SQ_TRY(check_vec_matrix(x, xt, m, k, ldx));
   if (yt == SQ_I32) return SQ_ERR_DTYPE;
@@ -249,6 +273,7 @@ static sq_status check_norm(const void* x, sq_dtype xt, int64_t m, int64_t k, in
 
 sq_status sq_fold_norm_gain(const void* gamma, sq_dtype gt, const float* smooth, int64_t k, float* gain,
                             sq_stream_t stream) {
+  if (!dtype_in_range(gt)) return SQ_ERR_DTYPE;
   if (k < 0) return SQ_ERR_SHAPE;
   if (!float_input(gt)) return SQ_ERR_DTYPE;
   if (k == 0) return SQ_OK;
@@ -261,6 +286,7 @@ sq_status sq_fold_norm_gain(const void* gamma, sq_dtype gt, const float* smooth,
 
 sq_status sq_rmsnorm_quant(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, const float* gain,
                            float eps, int8_t* xq, float* x_scale, sq_stream_t stream) {
+  if (!dtype_in_range(xt)) return SQ_ERR_DTYPE;
   SQ_TRY(check_norm(x, xt, m, k, ldx, gain, eps));
   if (m == 0) return SQ_OK;
   if (!xq || !x_scale) return SQ_ERR_NULL;
@@ -275,6 +301,8 @@ size_t sq_rmsnorm_w8a8_linear_workspace_size(int64_t m, int64_t n, int64_t k) {
 sq_status sq_rmsnorm_w8a8_linear(const void* x, sq_dtype xt, int64_t ldx, const float* gain, float eps,
                                  const int8_t* wq, const float* w_scale, int64_t m, int64_t n, int64_t k, void* y,
                                  sq_dtype yt, int64_t ldy, void* ws, size_t ws_bytes, sq_stream_t stream) {
+  if (!dtype_in_range(xt)) return SQ_ERR_DTYPE;
+  if (!dtype_in_range(yt)) return SQ_ERR_DTYPE;
   SQ_TRY(check_norm(x, xt, m, k, ldx, gain, eps));
   if (yt == SQ_I32) return SQ_ERR_DTYPE;
   SQ_TRY(check_gemm_common(wq, w_scale, m, n, k, y, yt, ldy));
@@ -302,6 +330,7 @@ static sq_status check_silu(const void* gate, const void* up, sq_dtype t, int64_
 
 sq_status sq_silu_mul_quant(const void* gate, const void* up, sq_dtype t, int64_t m, int64_t k, int64_t ldg,
                             int64_t ldu, const float* smooth, int8_t* xq, float* x_scale, sq_stream_t stream) {
+  if (!dtype_in_range(t)) return SQ_ERR_DTYPE;
   SQ_TRY(check_silu(gate, up, t, m, k, ldg, ldu, smooth));
   if (m == 0) return SQ_OK;
   if (!xq || !x_scale) return SQ_ERR_NULL;
@@ -317,6 +346,8 @@ sq_status sq_silu_mul_w8a8_linear(const void* gate, const void* up, sq_dtype t, 
                                   const float* smooth, const int8_t* wq, const float* w_scale, int64_t m, int64_t n,
                                   int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, size_t ws_bytes,
                                   sq_stream_t stream) {
+  if (!dtype_in_range(t)) return SQ_ERR_DTYPE;
+  if (!dtype_in_range(yt)) return SQ_ERR_DTYPE;
   SQ_TRY(check_silu(gate, up, t, m, k, ldg, ldu, smooth));
   if (yt == SQ_I32) return SQ_ERR_DTYPE;
   SQ_TRY(check_gemm_common(wq, w_scale, m, n, k, y, yt, ldy));
@@ -333,6 +364,7 @@ sq_status sq_silu_mul_w8a8_linear(const void* gate, const void* up, sq_dtype t, 
 // ---------------------------------------------------------------- FP8 (E4M3) variant
 sq_status sq_quant_act_fp8(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, uint8_t* xq,
                            float* x_scale, sq_stream_t stream) {
+  if (!dtype_in_range(xt)) return SQ_ERR_DTYPE;
   SQ_TRY(check_k(k));
   if (k > SQ_MAX_K_FP8) return SQ_ERR_RANGE;
   SQ_TRY(check_vec_matrix(x, xt, m, k, ldx));
@@ -349,6 +381,7 @@ size_t sq_quant_weights_fp8_workspace_size(int64_t k, int64_t n) {
 
 sq_status sq_quant_weights_fp8(const void* w, sq_dtype wt, int64_t k, int64_t n, int64_t ldw, uint8_t* wq,
                                float* w_scale, void* ws, size_t ws_bytes, sq_stream_t stream) {
+  if (!dtype_in_range(wt)) return SQ_ERR_DTYPE;
   if (k < 0) return SQ_ERR_SHAPE;
   // the column maxima read W with 16-byte vectors along N
   SQ_TRY(check_k(n));
@@ -385,6 +418,7 @@ size_t sq_fp8_linear_workspace_size(int64_t m, int64_t n, int64_t k) {
 sq_status sq_fp8_linear(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
                         int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, size_t ws_bytes,
                         sq_stream_t stream) {
+  if (!dtype_in_range(yt)) return SQ_ERR_DTYPE;
   SQ_TRY(check_fp8_gemm(wq, w_scale, m, n, k, y, yt, ldy));
   if (m == 0 || n == 0) return SQ_OK;
   if (!xq || !x_scale) return SQ_ERR_NULL;
@@ -408,6 +442,8 @@ size_t sq_fp8_linear_dyn_workspace_size(int64_t m, int64_t n, int64_t k) {
 sq_status sq_fp8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const uint8_t* wq, const float* w_scale,
                             int64_t m, int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws,
                             size_t ws_bytes, sq_stream_t stream) {
+  if (!dtype_in_range(xt)) return SQ_ERR_DTYPE;
+  if (!dtype_in_range(yt)) return SQ_ERR_DTYPE;
   SQ_TRY(check_fp8_gemm(wq, w_scale, m, n, k, y, yt, ldy));
   SQ_TRY(check_vec_matrix(x, xt, m, k, ldx));
   if (m == 0 || n == 0) return SQ_OK;
@@ -447,6 +483,7 @@ static bool elem_aligned(const void* p, sq_dtype t) {
 
 sq_status sq_gptq_hessian(const void* x, sq_dtype xt, int64_t t, int64_t k, int64_t ldx, const float* smooth,
                           double* h, sq_stream_t stream) {
+  if (!dtype_in_range(xt)) return SQ_ERR_DTYPE;
   if (!float_input(xt)) return SQ_ERR_DTYPE;
   SQ_TRY(check_gptq_k(k));
   if (t < 0 || ldx < k) return SQ_ERR_SHAPE;
@@ -463,6 +500,7 @@ size_t sq_gptq_quantize_workspace_size(int64_t k, int64_t n) { return sqh::gptq_
 sq_status sq_gptq_quantize(const double* h, const void* w, sq_dtype wt, int64_t k, int64_t n, int64_t ldw,
                            const float* smooth, float damp, int8_t* wq, float* w_scale, void* ws, size_t ws_bytes,
                            sq_stream_t stream) {
+  if (!dtype_in_range(wt)) return SQ_ERR_DTYPE;
   if (!float_input(wt)) return SQ_ERR_DTYPE;
   SQ_TRY(check_gptq_k(k));
   if (n < 0 || ldw < n) return SQ_ERR_SHAPE;
@@ -483,6 +521,7 @@ size_t sq_outlier_detect_workspace_size(int64_t k) { return k > 0 ? round_up((si
 sq_status sq_outlier_detect(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx, float threshold,
                             uint8_t* mask, int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
                             sq_stream_t stream) {
+  if (!dtype_in_range(xt)) return SQ_ERR_DTYPE;
   SQ_TRY(check_k(k));
   SQ_TRY(check_vec_matrix(x, xt, m, k, ldx));
   if (std::isnan(threshold)) return SQ_ERR_RANGE;
@@ -498,6 +537,7 @@ sq_status sq_outlier_detect(const void* x, sq_dtype xt, int64_t m, int64_t k, in
 
 sq_status sq_quant_act_rows_masked(const void* x, sq_dtype xt, int64_t m, int64_t k, int64_t ldx,
                                    const uint8_t* mask, int8_t* xq, float* x_scale, sq_stream_t stream) {
+  if (!dtype_in_range(xt)) return SQ_ERR_DTYPE;
   SQ_TRY(check_k(k));
   SQ_TRY(check_vec_matrix(x, xt, m, k, ldx));
   if (!mask) return SQ_ERR_NULL;

@@ -14,6 +14,7 @@
 // own quantisation launch.
 #include <hip/hip_runtime.h>
 
+#include <cstring>
 #include <mutex>
 
 #include "sq.h"
@@ -55,6 +56,12 @@ sq_status device_scratch(void** out) {
 extern "C" sq_status sq_w8a8_linear_dyn_static(const void* x, sq_dtype xt, int64_t ldx, const float* smooth,
                                                const int8_t* wq, const float* w_scale, int64_t m, int64_t n,
                                                int64_t k, void* y, sq_dtype yt, int64_t ldy, sq_stream_t stream) {
+  // enum arguments are checked as ints before they are used (a C caller may
+  // pass any int; see the C-ABI layer)
+  int xv, yv;
+  std::memcpy(&xv, &xt, sizeof xv);
+  std::memcpy(&yv, &yt, sizeof yv);
+  if (xv < (int)SQ_F32 || xv > (int)SQ_I8 || yv < (int)SQ_F32 || yv > (int)SQ_I8) return SQ_ERR_DTYPE;
   // empty problems and bad shapes go straight to the workspace entry point's
   // validation (it needs no scratch for them)
   const size_t need = sq_w8a8_linear_dyn_workspace_size(m, n, k);
