@@ -40,8 +40,11 @@ def test_abi_checks_clean_under_asan_ubsan():
     if not rt or not os.path.exists(rt):
         pytest.skip("clang AddressSanitizer runtime not found")
     env = dict(os.environ)
+    # the AddressSanitizer runtime must come first; whatever the environment
+    # already preloads stays after it
+    pre = os.environ.get("LD_PRELOAD", "")
     env.update(
-        LD_PRELOAD=rt,
+        LD_PRELOAD=rt + (":" + pre if pre else ""),
         ASAN_OPTIONS="detect_leaks=0:abort_on_error=0",
         UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1",
         SQ_LIBRARY=b.SAN_LIB,

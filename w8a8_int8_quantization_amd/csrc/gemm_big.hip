@@ -38,43 +38,22 @@
 
 namespace sqk {
 
-constexpr int kBigBM = 256;
-constexpr int kBigBK = 128;    // k bytes per pipeline stage: one 128-byte line per tile row
-constexpr int kBigStages = 2;  // LDS double buffer
-constexpr int kGroupM = 4;
+using sqi::BigCfg;
+using sqi::kBigBK;
+using sqi::kBigBM;
+using sqi::kBigMaxSplit;
+using sqi::kBigStages;
 constexpr int kSliceCols = 16;  // outlier columns staged in LDS by the LLM.int8() epilogue
 
 enum BigOut { kBigF32 = 0, kBigBF16 = 1, kBigF16 = 2, kBigI32 = 3, kBigDecomp = 4 };
 
-// Byte offset of 16-byte chunk c (0..7) of tile row r in a stage (128-byte
-// rows). The chunk index is XOR-ed with (r >> 1) & 7: a 128-byte row covers
-// half of the 64 banks, so rows r and r+1 fall in different halves, and the
-// eight even (odd) rows of a 16-lane group get eight distinct chunks. Without
-// it every lane of a half-wave would hit the same bank group; with r & 7,
-// rows r and r + 8 collided (measured: 3.96M bank-conflict cycles per QKV
-// dispatch, 0.29M with this one).
-__device__ __forceinline__ int big_swz(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int big_lds_off(int r, int c) { return r * kBigBK + ((c ^ big_swz(r)) << 4); }
-
-// kW waves in a (kW/2) x 2 grid over the 256 x BN tile. Eight waves (two per
-// SIMD, 64 x BN/2 each): while one wave of a SIMD waits on its fragment reads
-// or the stage barrier, the other keeps the matrix core busy. Four waves (one
-// per SIMD, 128 x BN/2 each): every fragment read feeds twice the MFMAs, so
-// the LDS carries less per MFMA, and the schedule alone has to hide waits.
-template <int BN, int kW = 8>
-struct BigCfg {
-  static constexpr int kThreads = 64 * kW;
-  static constexpr int kWN = BN / 2;                  // output columns per wave
-  static constexpr int kFN = kWN / 32;
-  static constexpr int kWM = kBigBM / (kW / 2);        // tokens per wave
-  static constexpr int kFM = kWM / 32;
-  static constexpr int kStageA = kBigBM * kBigBK;
-  static constexpr int kStage = (kBigBM + BN) * kBigBK;
-  // 1 KiB direct-to-LDS transfers (8 rows each) per wave and stage
-  static constexpr int kDmaA = kBigBM / 8 / kW;
-  static constexpr int kDmaB = BN / 8 / kW;
-  static constexpr int kDma = kDmaA + kDmaB;
-};
+// LDS layout of a stage: 128-byte rows, 16-byte chunks XOR-swizzled by
+// (row >> 1) & 7 (sqi::big_lds_off). kW waves in a (kW/2) x 2 grid over the
+// 256 x BN tile (sqi::BigCfg). Eight waves (two per SIMD, 64 x BN/2 each):
+// while one wave of a SIMD waits on its fragment reads or the stage barrier,
+// the other keeps the matrix core busy. Four waves (one per SIMD, 128 x BN/2
+// each): every fragment read feeds twice the MFMAs, so the LDS carries less
+// per MFMA, and the schedule alone has to hide waits.
 
 struct BigEpi {
   const float* x_scale;
@@ -97,8 +76,6 @@ struct BigEpi {
 // operand of device-coherent (sc1) buffer accesses: partial tiles cross XCDs,
 // whose L2 caches are not coherent with each other.
 constexpr int kBigBufDword3 = 0x00020000;
-// at most this many K slices per output tile
-constexpr int kBigMaxSplit = 8;
 constexpr int kBigCoherent = 16;
 
 // s_waitcnt vmcnt(n) with the lgkm and exp counters left alone (gfx9 encoding).
@@ -171,38 +148,23 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
   const int nbm = (M + kBigBM - 1) / kBigBM;
   const int nbn = (N + BN - 1) / BN;
   const int total = nbm * nbn;
-  int t = blockIdx.x;
-  const int full = total & ~7;
-  if (t < full) t = (t & 7) * (full >> 3) + (t >> 3);
-  const int in_group = kGroupM * nbn;
-  const int first_m = (t / in_group) * kGroupM;
-  const int gm = min(nbm - first_m, kGroupM);
-  const int tm = first_m + (t % in_group) % gm;
-  const int tn = (t % in_group) / gm;
+  const sqi::BigTile tile = sqi::big_tile((int)blockIdx.x, nbm, nbn);
+  const int tm = tile.tm, tn = tile.tn;
   const int m0 = tm * kBigBM, n0 = tn * BN;
   // this workgroup's stages: kt0 .. kt0 + nk - 1
-  const int kt0 = kSplit ? (int)blockIdx.y * ep.slice_stages : 0;
-  const int nk = kSplit ? min(ep.slice_stages, K / kBigBK - kt0) : K / kBigBK;
+  const sqi::BigSlice slice = sqi::big_slice(kSplit, (int)blockIdx.y, ep.slice_stages, K / kBigBK);
+  const int kt0 = slice.kt0;
+  const int nk = slice.nk;
 
   // ---- direct-to-LDS transfers: lane L of a 1 KiB transfer fills LDS bytes
-  // [16L, 16L+16) of an 8-row block, i.e. row L/8, physical chunk L%8, so it
-  // fetches the logical chunk (L%8) ^ swizzle(row) of that row from HBM; the
-  // 8 lanes of a row read one whole 128-byte line.
+  // [16L, 16L+16) of an 8-row block (sqi::big_dma)
   const int8_t* src[C::kDma];
   int dst[C::kDma];
 #pragma unroll
   for (int i = 0; i < C::kDma; ++i) {
-    const bool is_a = i < C::kDmaA;
-    const int blk = (is_a ? i : i - C::kDmaA) * kW + wid;  // 8-row block within the operand tile
-    const int r = blk * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ big_swz(r);
-    if (is_a) {
-      src[i] = A + (int64_t)min(m0 + r, M - 1) * K + (int64_t)kt0 * kBigBK + c * 16;
-      dst[i] = blk * 1024;
-    } else {
-      src[i] = B + (int64_t)min(n0 + r, N - 1) * K + (int64_t)kt0 * kBigBK + c * 16;
-      dst[i] = C::kStageA + blk * 1024;
-    }
+    const sqi::BigDma d = sqi::big_dma<BN, kW>(i, wid, lane);
+    src[i] = d.a ? A + sqi::big_dma_src(m0, d.row, M, K, kt0, d.chunk) : B + sqi::big_dma_src(n0, d.row, N, K, kt0, d.chunk);
+    dst[i] = d.dst;
   }
   auto kbyte = [&](int kt) -> int64_t { return (int64_t)kt * kBigBK; };
   auto stage_ptr = [&](int kt) { return smem + (kt & 1) * C::kStage; };
@@ -229,7 +191,7 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
   float xs[C::kFM];
 #pragma unroll
   for (int i = 0; i < C::kFM; ++i) {
-    const int m = m0 + wm * C::kWM + 32 * i + frow;
+    const int m = m0 + sqi::big_frag_row<BN, kW>(wm, i, frow);
     xs[i] = (kOut != kBigI32 && m < M) ? ep.x_scale[m] : 0.f;
   }
   float4 w4 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -254,20 +216,20 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
   auto frag = [&](const int8_t* base, int r, int ks) -> FragT {
     if constexpr (kF8) {
       const int c = 4 * ks + 2 * fhalf;
-      const v4i lo = *reinterpret_cast<const v4i*>(base + big_lds_off(r, c));
-      const v4i hi = *reinterpret_cast<const v4i*>(base + big_lds_off(r, c + 1));
+      const v4i lo = *reinterpret_cast<const v4i*>(base + sqi::big_lds_off(r, c));
+      const v4i hi = *reinterpret_cast<const v4i*>(base + sqi::big_lds_off(r, c + 1));
       return FragT{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     } else {
-      return *reinterpret_cast<const v4i*>(base + big_lds_off(r, 2 * ks + fhalf));
+      return *reinterpret_cast<const v4i*>(base + sqi::big_lds_off(r, 2 * ks + fhalf));
     }
   };
   // Fragments of one substep: Xq blocks for this wave's tokens and Wq blocks
   // for its BN/2 output channels.
   auto read_frags = [&](const int8_t* stage, int ks, FragT* xf, FragT* wf) {
 #pragma unroll
-    for (int i = 0; i < C::kFM; ++i) xf[i] = frag(stage, wm * C::kWM + 32 * i + frow, ks);
+    for (int i = 0; i < C::kFM; ++i) xf[i] = frag(stage, sqi::big_frag_row<BN, kW>(wm, i, frow), ks);
 #pragma unroll
-    for (int j = 0; j < C::kFN; ++j) wf[j] = frag(stage + C::kStageA, wn * C::kWN + 32 * j + frow, ks);
+    for (int j = 0; j < C::kFN; ++j) wf[j] = frag(stage + C::kStageA, sqi::big_wfrag_row<BN, kW>(wn, j, frow), ks);
   };
 
   // Software pipeline over the 4 substeps of a stage: the fragments of the
@@ -286,9 +248,9 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
   };
   auto frag_one = [&](const int8_t* stage, int ks, int q, FragT* xf, FragT* wf) {
     if (q < C::kFM)
-      xf[q] = frag(stage, wm * C::kWM + 32 * q + frow, ks);
+      xf[q] = frag(stage, sqi::big_frag_row<BN, kW>(wm, q, frow), ks);
     else
-      wf[q - C::kFM] = frag(stage + C::kStageA, wn * C::kWN + 32 * (q - C::kFM) + frow, ks);
+      wf[q - C::kFM] = frag(stage + C::kStageA, sqi::big_wfrag_row<BN, kW>(wn, q - C::kFM, frow), ks);
   };
   FragT fx[2][C::kFM], fw[2][C::kFN];
   if (nk > 1)
@@ -344,15 +306,11 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
     // covers 1 KiB of consecutive bytes, and ragged tiles need no bounds
     // (their padding is never stored to y).
     __shared__ uint32_t last_ticket;
-    constexpr uint32_t kTileBytes = kBigBM * BN * 4;
-    constexpr uint32_t kWaveBytes = kTileBytes / kW;
-    const uint32_t pbytes = (uint32_t)ep.S * (uint32_t)total * kTileBytes;
+    const uint32_t pbytes = (uint32_t)ep.S * (uint32_t)total * C::kTileBytes;
     const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(ep.partial, (short)0, pbytes, kBigBufDword3);
     const int tile_id = tm * nbn + tn;
-    const uint32_t lane_off = (uint32_t)wid * kWaveBytes + (uint32_t)lane * 16;
-    auto slice_base = [&](int sl) { return ((uint32_t)sl * (uint32_t)total + (uint32_t)tile_id) * kTileBytes + lane_off; };
     {
-      const uint32_t base = slice_base((int)blockIdx.y);
+      const int sl = (int)blockIdx.y;
 #pragma unroll
       for (int j = 0; j < C::kFN; ++j)
 #pragma unroll
@@ -363,8 +321,9 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
 #pragma unroll
           for (int rg = 0; rg < 4; ++rg) {
             const v4i v = {bits[4 * rg], bits[4 * rg + 1], bits[4 * rg + 2], bits[4 * rg + 3]};
-            __builtin_amdgcn_raw_buffer_store_b128(v, pr, base + (uint32_t)((j * C::kFM + i) * 4 + rg) * 1024, 0,
-                                                   kBigCoherent);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                v, pr, sqi::big_partial_off<BN, kW>(sl, total, tile_id, wid, lane, j * C::kFM + i, rg), 0,
+                kBigCoherent);
           }
         }
     }
@@ -388,7 +347,6 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
     }
     for (int sl = 0; sl < ep.S; ++sl) {
       if (!kF8 && sl == (int)blockIdx.y) continue;
-      const uint32_t base = slice_base(sl);
 #pragma unroll
       for (int j = 0; j < C::kFN; ++j)
 #pragma unroll
@@ -396,7 +354,8 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
 #pragma unroll
           for (int rg = 0; rg < 4; ++rg) {
             const v4i t = __builtin_amdgcn_raw_buffer_load_b128(
-                pr, base + (uint32_t)((j * C::kFM + i) * 4 + rg) * 1024, 0, kBigCoherent);
+                pr, sqi::big_partial_off<BN, kW>(sl, total, tile_id, wid, lane, j * C::kFM + i, rg), 0,
+                kBigCoherent);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               if constexpr (kF8)
@@ -411,11 +370,9 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
   }
 
   // ---- epilogue: lane holds D[n][m] with m = l%32 and n = 8*(r/4) + 4*(l/32) + r%4 of each 32x32 block
-  const int mw = m0 + wm * C::kWM;
-  const int nw = n0 + wn * C::kWN;
   int mrow[C::kFM];
 #pragma unroll
-  for (int i = 0; i < C::kFM; ++i) mrow[i] = mw + 32 * i + frow;
+  for (int i = 0; i < C::kFM; ++i) mrow[i] = m0 + sqi::big_frag_row<BN, kW>(wm, i, frow);
   if (kOut != kBigI32) {
     if (tid < BN / 4) *reinterpret_cast<float4*>(&scale_w[4 * tid]) = w4;
     __syncthreads();
@@ -450,10 +407,10 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
         float xv[C::kFM];
 #pragma unroll
         for (int i = 0; i < C::kFM; ++i)
-          xv[i] = (i >= i0 && i < i1) ? f16_to_f32(slice_x[(wm * C::kWM + 32 * i + frow) * kSliceCols + c]) : 0.f;
+          xv[i] = (i >= i0 && i < i1) ? f16_to_f32(slice_x[sqi::big_frag_row<BN, kW>(wm, i, frow) * kSliceCols + c]) : 0.f;
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-          const int nl = wn * C::kWN + 32 * j + 8 * rg + 4 * fhalf;
+          const int nl = sqi::big_frag_col<BN, kW>(wn, j, rg, fhalf);
           const uint2 wp = *reinterpret_cast<const uint2*>(&slice_w[c * BN + nl]);
           const float wv[4] = {f16_to_f32((uint16_t)(wp.x & 0xFFFFu)), f16_to_f32((uint16_t)(wp.x >> 16)),
                                f16_to_f32((uint16_t)(wp.y & 0xFFFFu)), f16_to_f32((uint16_t)(wp.y >> 16))};
@@ -476,7 +433,7 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
       const uint16_t* wrow = ep.dec.w16 + jc * ep.dec.ldw;
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const int n = nw + 32 * j + 8 * rg + 4 * fhalf;
+        const int n = n0 + sqi::big_frag_col<BN, kW>(wn, j, rg, fhalf);
         float wv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) wv[e] = n + e < N ? f16_to_f32(wrow[n + e]) : 0.f;
@@ -533,13 +490,13 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
     // different buffers. Chunk c of staged row r sits at chunk (c + r) mod
     // kCh, which spreads the 32 rows of a fragment write over the banks.
     constexpr int kEl = (kOut == kBigF32 || kOut == kBigI32) ? 4 : 2;
-    constexpr int kRows = (kW / 2) * 32;  // rows per band
-    constexpr int kParts = kRows * BN * kEl <= C::kStage ? 1 : 2;
-    constexpr int kColsB = BN / kParts;  // columns per band
-    constexpr int kRowB = kColsB * kEl;  // staged row bytes
-    constexpr int kCh = kRowB / 16;      // 16-byte chunks per staged row
-    constexpr int kPer = 16 / kEl;       // outputs per chunk
-    static_assert(kRows * kRowB <= C::kStage, "an output band must fit one stage buffer");
+    using Band = sqi::BigBand<BN, kW, kEl>;
+    constexpr int kRows = Band::kRows;    // rows per band
+    constexpr int kParts = Band::kParts;  // column parts per band row block
+    constexpr int kColsB = Band::kColsB;  // columns per band
+    constexpr int kRowB = Band::kRowB;    // staged row bytes
+    constexpr int kCh = Band::kCh;        // 16-byte chunks per staged row
+    constexpr int kPer = Band::kPer;      // outputs per chunk
     __syncthreads();  // every wave is done with the stage buffers
 #pragma unroll
     for (int b = 0; b < C::kFM * kParts; ++b) {
@@ -553,15 +510,14 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
           if (kOut == kBigDecomp) outlier_slice(j, i, i + 1, yo);
 #pragma unroll
           for (int rg = 0; rg < 4; ++rg) {
-            const int nl = wn * C::kWN + 32 * j + 8 * rg + 4 * fhalf;
+            const int nl = sqi::big_frag_col<BN, kW>(wn, j, rg, fhalf);
             float ws[4];
             col_scales(n0 + nl, 4, ws);
             int a[4];
             float v[4];
             out_values(j, i, rg, ws, yo, v, a);
             const int cb = (nl - h * kColsB) * kEl;  // byte offset within the staged row
-            int pc = (cb >> 4) + lr % kCh;
-            if (pc >= kCh) pc -= kCh;
+            const int pc = sqi::band_chunk(cb >> 4, lr, kCh);
             int8_t* dst = buf + lr * kRowB + pc * 16 + (cb & 15);
             if (kOut == kBigI32) {
               *reinterpret_cast<int4*>(dst) = make_int4(a[0], a[1], a[2], a[3]);
@@ -581,12 +537,10 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
       __syncthreads();
       for (int c = tid; c < kRows * kCh; c += C::kThreads) {
         const int lr = c / kCh, ch = c - lr * kCh;
-        const int m = m0 + (lr >> 5) * C::kWM + 32 * i + (lr & 31);
+        const int m = m0 + sqi::band_tile_row<BN, kW>(lr, i);
         const int n = n0 + h * kColsB + ch * kPer;
         if (m >= M || n >= N) continue;
-        int pc = ch + lr % kCh;
-        if (pc >= kCh) pc -= kCh;
-        const int8_t* srcp = buf + lr * kRowB + pc * 16;
+        const int8_t* srcp = buf + lr * kRowB + sqi::band_chunk(ch, lr, kCh) * 16;
         int8_t* dst = reinterpret_cast<int8_t*>(ep.y) + ((int64_t)m * ep.ldy + n) * kEl;
         if (n + kPer <= N) {
           *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(srcp);
@@ -605,7 +559,7 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
     if (kOut == kBigDecomp) outlier_slice(j, 0, C::kFM, yo);
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
-      const int n = nw + 32 * j + 8 * rg + 4 * fhalf;
+      const int n = n0 + sqi::big_frag_col<BN, kW>(wn, j, rg, fhalf);
       if (n >= N) continue;
       const int nvalid = min(4, N - n);
       float ws[4];
@@ -671,101 +625,18 @@ static void launch_big_f8(const int8_t* xq, const int8_t* wq, int M, int N, int 
 
 namespace sqh {
 
-bool gemm_big_suits(int64_t m, int64_t n, int64_t k, bool split_ok) {
-  if (n < 192 || k % sqk::kBigBK != 0) return false;
-  if (m >= 256 && m * n >= ((int64_t)1 << 20)) return true;
-  // 129..255 tokens over wide layers: one 256-row tile per column block with
-  // K split over the CUs beats the decode and 128 x 128 kernels (GEMM us at
-  // 136 / 192 tokens, decode / 128 x 128 / this: 14336 -> 4096 60.8 / 136.3 /
-  // 49.9 and 69.2 / 138.0 / 57.1; 4096 -> 14336 48.9 / 48.6 / 38.0 and 55.4 /
-  // 49.8 / 39.1; 4096 -> 28672 91.8 / 60.4 / 47.8 and 110.2 / 61.9 / 53.6),
-  // except that the decode kernel streams weights under 32 MiB fast enough to
-  // stay ahead up to about 176 tokens (4096 -> 6144: 24.0 / 38.6 / 30.9 at
-  // 136 tokens, 36.6 / 39.3 / 31.3 at 192)
-  if (!split_ok || n < 4096 || k / sqk::kBigBK < 20) return false;
-  return m >= 176 || (m >= 129 && n * k >= ((int64_t)1 << 25));
-}
+bool gemm_big_suits(int64_t m, int64_t n, int64_t k, bool split_ok) { return sqi::big_suits(m, n, k, split_ok); }
 
 namespace {
-
-using sqk::kBigMaxSplit;
-
-struct BigSplit {
-  int bn = 256;
-  int S = 1;
-  int slice_stages = 0;
-  int64_t tiles = 0;
-};
-
-// K slices for `tiles` output tiles: split when the tiles cover fewer than
-// half of the 256 CUs, into at most as many slices as keep all workgroups in
-// one wave with a CU to spare (a full 256 measured slower: 4096 -> 6144 at 512
-// tokens, 64 tiles in 3 / 4 slices 34.8 / 37.1 us). Each slice costs its reducer one more partial tile to read and
-// shortens every slice's main loop: with about 1.3 us per 128-deep stage and
-// 3 us per slice (fitted on 14336 -> 4096 at 192 tokens: 4 / 8 / 10 slices
-// 56.6 / 49.9 / 52.1 us), S = sqrt(0.45 x stages) balances the two (7 for
-// K = 14336, 4 for K = 4096; 4096 -> 6144 at 256 tokens: 3 / 4 / 6 slices
-// 32.1 / 31.9 / 34.8 us). Slices keep at least 8 stages. A second wave of
-// workgroups costs more than the split saves (14336 -> 4096 at 1024 tokens
-// in 3 slices: 112 us against 89 in 2), and so does splitting 128 tiles in
-// two (4096 -> 6144 at 1024 tokens: 43.2 -> 46.5 us).
-int split_for(int64_t tiles, int stages, int bn) {
-  int want = tiles < 128 ? (int)(255 / tiles) : 1;
-  int best = (int)(sqrtf(0.45f * (float)stages) + 0.5f);
-  if (want > best) want = best;
-  if (want > kBigMaxSplit) want = kBigMaxSplit;
-  if (want > stages / 8) want = stages / 8;
-  if (want < 2) return 1;
-  const int per = (stages + want - 1) / want;
-  const int S = (stages + per - 1) / per;
-  if ((size_t)S * (size_t)tiles * (size_t)(sqk::kBigBM * bn * 4) >= ((size_t)1 << 31)) return 1;
-  return S;
-}
-
-// Tile width (256, 192 or 128 columns) and K split, chosen together: the
-// score is the fraction of the scheduled waves' workgroup slots doing useful
-// work, useful outputs x S over (waves of tiles x S) x 256 x 256 x BN, times
-// a measured efficiency: 0.8 for 128-column tiles (less operand reuse per
-// fragment read), 0.8 for a split (0.7 with 256-column tiles). GEMM alone,
-// us, tile width 192 / 256 / 128 (S: split into S slices): 4096 -> 6144 at
-// 1024 tokens 44.2 / 59.4 (S2) / 36.9; 4096 -> 14336 at 512 tokens 47.8 /
-// 63.4 (S2) / 41.6; 14336 -> 4096 at 2048 tokens 134.8 / 146.9 / 126.3, at
-// 1024 tokens 97.5 (S2) / 105.9 (S3) / 118.4, at 3072 tokens 269.3 / 167.3 /
-// 223.7; 4096 -> 6144 at 1536 tokens 46.2 / 52.9 / 71.0. The 128-column
-// tile is taken only unsplit (the combination measured).
+using sqi::BigSplit;
 BigSplit big_split(int64_t m, int64_t n, int64_t k, bool f8, bool split_ok = true) {
-  const int stages = (int)(k / sqk::kBigBK);
-  const int cands[3] = {256, 192, 128};
-  BigSplit best;
-  double best_score = -1.0;
-  for (int bn : cands) {
-    if (f8 && bn == 256) continue;  // E4M3 tiles: 192 or 128 columns
-    BigSplit p;
-    p.bn = bn;
-    p.tiles = ((m + sqk::kBigBM - 1) / sqk::kBigBM) * ((n + bn - 1) / bn);
-    p.S = split_ok ? split_for(p.tiles, stages, bn) : 1;
-    if (bn == 128 && p.S > 1) continue;
-    p.slice_stages = (stages + p.S - 1) / p.S;
-    const int64_t waves = (p.tiles * p.S + 255) / 256;
-    double score = (double)m * (double)n * p.S / ((double)waves * 256.0 * sqk::kBigBM * bn);
-    if (bn == 128) score *= 0.8;
-    if (p.S > 1) score *= bn == 256 ? 0.7 : 0.8;
-    if (score > best_score + 1e-9) {
-      best = p;
-      best_score = score;
-    }
-  }
-  return best;
+  return sqi::big_split(m, n, k, f8, split_ok);
 }
-
-
 }  // namespace
 
 size_t gemm_big_workspace(int64_t m, int64_t n, int64_t k, bool f8) {
   if (!gemm_big_suits(m, n, k)) return 0;
-  const BigSplit p = big_split(m, n, k, f8);
-  if (p.S == 1) return 0;
-  return kSplitCounterBytes + (size_t)p.S * (size_t)p.tiles * (size_t)(sqk::kBigBM * p.bn * 4);
+  return sqi::big_workspace_bytes(big_split(m, n, k, f8));
 }
 
 void gemm_big_counters(int64_t m, int64_t n, int64_t k, bool f8, void* ws, uint32_t** counters, int64_t* count) {

@@ -47,10 +47,10 @@
 
 namespace sqk {
 
-constexpr int kDecRows = 64;    // Wq rows per workgroup
-constexpr int kDecStep = 128;   // k bytes per pipeline step
-constexpr int kDecWaves = 4;
-constexpr int kDecMaxNS = 8;    // most steps per wave (template range)
+using sqi::kDecMaxNS;
+using sqi::kDecRows;
+using sqi::kDecStep;
+using sqi::kDecWaves;
 // Buffer descriptor word 3 of a raw byte buffer on gfx9 (32-bit data format),
 // and the cache-policy operand of device-coherent (sc1) buffer accesses.
 constexpr int kBufDword3 = 0x00020000;
@@ -143,19 +143,20 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
   // layer streams the same Wq, whose re-reads hit the last-level cache)
   const int m0 = (int)blockIdx.z * 64;
   const int ctr = (int)blockIdx.z * (int)gridDim.x + tile;
-  const int step0 = slice * a.slice_steps;
-  const int nsl = min(a.slice_steps, a.K / kDecStep - step0);  // >= 1 by construction of S
+  const sqi::DecSlice sl = sqi::dec_slice(slice, a.slice_steps, a.K);
+  const int step0 = sl.step0;
+  const int nsl = sl.nsl;  // >= 1 by construction of S
 
   // the lane's k bytes of a step: int8, [kb, kb+16) and [64+kb, 64+kb+16);
   // E4M3, [kb, kb+32)
-  const int kb = (kF8 ? 32 : 16) * (lane >> 4);
-  constexpr int kHalf = kF8 ? 16 : 64;
+  const int kb = sqi::dec_kb(kF8, lane);
+  constexpr int kHalf = sqi::dec_khalf(kF8);
   const int8_t* wp[4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) wp[g] = a.wq + (int64_t)min(n0 + 16 * g + (lane & 15), a.N - 1) * a.K + kb;
+  for (int g = 0; g < 4; ++g) wp[g] = a.wq + (int64_t)sqi::dec_w_row(n0, g, lane, a.N) * a.K + kb;
   const int8_t* xp[kMB];
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) xp[mb] = a.xq + (int64_t)min(m0 + 16 * mb + (lane & 15), a.M - 1) * a.K + kb;
+  for (int mb = 0; mb < kMB; ++mb) xp[mb] = a.xq + (int64_t)sqi::dec_x_row(m0, mb, lane, a.M) * a.K + kb;
 
   AccT acc[4][kMB];
 #pragma unroll
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
   // step i of this wave is slice step wid + 4 i; past the slice end it reloads
   // the last step (valid memory) and its product is skipped
   auto load = [&](int i, int slot) {
-    const int64_t off = (int64_t)(step0 + min(wid + kDecWaves * i, nsl - 1)) * kDecStep;
+    const int64_t off = (int64_t)(step0 + sqi::dec_step(wid, i, nsl)) * kDecStep;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       wb[slot][g][0] = load16(wp[g] + off);
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
     if (i + kDepth < kNS) load(i + kDepth, slot);
     // a step past the slice end contributes zero (a select, not a branch, so
     // that the compiler keeps every load at its place in the pipeline)
-    const bool valid = wid + kDecWaves * i < nsl;
+    const bool valid = sqi::dec_step_valid(wid, i, nsl);
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
       x[mb][0] = valid ? x[mb][0] : u32x4{0u, 0u, 0u, 0u};
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
       const int tok = 16 * mb + (lane & 15);
-      const int quad = (4 * g + (lane >> 4)) ^ (tok & 15);
+      const int quad = sqi::dec_red_quad(g, lane, tok);
       *reinterpret_cast<v4i*>(&red[wid][tok][4 * quad]) = __builtin_bit_cast(v4i, acc[g][mb]);
     }
   __syncthreads();
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
   for (int j = 0; j < kMB; ++j) {
     const int m = m0 + (tid >> 4) + 16 * j;
     if (m < a.M && n < a.N) {
-      const uint32_t off = (uint32_t)((((size_t)slice * a.M + m) * a.N + n) * 4);
+      const uint32_t off = sqi::dec_partial_off(slice, a.M, a.N, m, n);
       if (vec) {
         const v4i v = {sum[j][0], sum[j][1], sum[j][2], sum[j][3]};
         __builtin_amdgcn_raw_buffer_store_b128(v, pr, off, 0, kCoherent);
@@ -300,8 +301,8 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
     const int m = m0 + (tid >> 4) + 16 * j;
     if (m >= a.M || n >= a.N) continue;
     AccT t = {0, 0, 0, 0};
-    const uint32_t off0 = (uint32_t)(((size_t)m * a.N + n) * 4);
-    const uint32_t sstride = (uint32_t)((size_t)a.M * a.N * 4);
+    const uint32_t off0 = sqi::dec_partial_off(0, a.M, a.N, m, n);
+    const uint32_t sstride = sqi::dec_partial_off(1, a.M, a.N, 0, 0);
     if (vec) {
       // eight slices per round trip; slices past S read beyond the buffer's
       // range (a raw buffer load returns zero there) and are not added
@@ -340,45 +341,8 @@ namespace sqh {
 
 namespace {
 
-struct DecodePlan {
-  int S = 1;
-  int slice_steps = 0;
-  int ns = 0;      // steps per wave
-  int tiles = 0;
-  int tb = 1;      // 64-token blocks (grid z)
-};
-
-DecodePlan decode_plan(int64_t m, int64_t n, int64_t k) {
-  DecodePlan p;
-  const int steps = (int)(k / sqk::kDecStep);
-  p.tiles = (int)((n + sqk::kDecRows - 1) / sqk::kDecRows);
-  p.tb = (int)((m + 63) / 64);
-  // at least one workgroup per CU (256 CUs), with at most kDecMaxNS steps
-  // per wave; measured on MI355X, more slices than that only add partial-tile
-  // traffic and reduction latency. Where the unsplit grid already has 192
-  // workgroups, three in four of the CUs streaming unsplit K are faster than a
-  // second round of workgroups (4096 -> 14336, 224 column tiles, GEMM us
-  // unsplit / 2 slices: M 1 13.8 / 15.0, M 8 13.9 / 16.0, M 32 16.4 / 18.4,
-  // M 64 20.6 / 27.0).
-  const int wgs = p.tiles * p.tb;
-  int want = (256 + wgs - 1) / wgs;
-  if (wgs >= 192) want = 1;
-  if (want < 1) want = 1;
-  if (want > steps) want = steps;
-  int per = (steps + want - 1) / want;
-  const int cap = sqk::kDecWaves * sqk::kDecMaxNS;
-  if (per > cap) per = cap;
-  p.slice_steps = per;
-  p.S = (steps + per - 1) / per;
-  // one ticket counter per column tile and token block, in the fixed region
-  if (p.S > 1 && (int64_t)p.tiles * p.tb > kSplitMaxCounters) {
-    p.S = 1;
-    p.slice_steps = steps;
-  }
-  p.ns = (per + sqk::kDecWaves - 1) / sqk::kDecWaves;
-  return p;
-}
-
+using sqi::decode_plan;
+using sqi::DecodePlan;
 
 template <int kMB, bool kF8>
 hipError_t launch_decode(const sqk::DecodeArgs& a, int ns, dim3 grid, hipStream_t s) {
@@ -417,44 +381,11 @@ hipError_t decode_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
 
 }  // namespace
 
-// Up to 256 tokens the decode kernel runs one grid layer per 64 tokens.
-constexpr int64_t kDecodeMaxM = 256;
-
-// Whether 65..256 tokens go to the decode kernel rather than the tiled
-// kernels. The decode kernel streams Wq once per 64-token layer (time grows
-// about linearly with the layers); the tiled kernels are slow when their
-// output tiles cover few CUs. Counted in 128 x 128 tile units (a 256 x 192
-// prefill tile is 3), decode wins when the tiled kernel has at most 128 units:
-// measured on MI355X (GEMM us, tiled -> decode), 4096 -> 14336 columns:
-// M 96 42.4 -> 36.0, M 128 43.5 -> 39.8 (decode), M 192 43.3 vs 57.5, M 256
-// 43.9 vs 75.0 (tiled); 14336 -> 4096: M 96 113.8 -> 42.7, M 128 125.2 ->
-// 47.6, M 192 111.8 -> 68.3 (decode). Where the 256-row prefill kernel
-// applies (gemm_big_suits), it splits K over enough workgroups to cover the
-// CUs and beats the decode kernel: 14336 -> 4096 at 256 tokens 60.4 us
-// against 89.6, at 192 tokens 57.1 against 69.2.
-static bool decode_beats_prefill(int64_t m, int64_t n, int64_t k) {
-  if (gemm_big_suits(m, n, k)) return false;
-  const int64_t units = ((m + 127) / 128) * ((n + 127) / 128);
-  return units <= 128;
-}
-
-bool gemm_decode_suits(int64_t m, int64_t n, int64_t k) {
-  if (!(m >= 1 && m <= kDecodeMaxM && n >= 1 && n <= INT32_MAX && k % sqk::kDecStep == 0)) return false;
-  // the partial tiles must fit 32-bit offsets (with the reducer's eight-slice
-  // rounds)
-  const DecodePlan p = decode_plan(m, n, k);
-  if ((size_t)(p.S + 7) / 8 * 8 * (size_t)m * (size_t)n * 4 >= ((size_t)1 << 31)) return false;
-  if (m <= 64) return true;
-  // beyond one 64-token block only where the prefill kernels get few tiles
-  // (see the dispatch notes)
-  return decode_beats_prefill(m, n, k);
-}
+bool gemm_decode_suits(int64_t m, int64_t n, int64_t k) { return sqi::decode_suits(m, n, k); }
 
 size_t gemm_decode_workspace(int64_t m, int64_t n, int64_t k) {
   if (!gemm_decode_suits(m, n, k)) return 0;
-  const DecodePlan p = decode_plan(m, n, k);
-  if (p.S == 1) return 0;
-  return kSplitCounterBytes + (size_t)p.S * (size_t)m * (size_t)n * 4;
+  return sqi::dec_workspace_bytes(decode_plan(m, n, k), m, n);
 }
 
 void gemm_decode_counters(int64_t m, int64_t n, int64_t k, void* ws, uint32_t** counters, int64_t* count) {

@@ -6,18 +6,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gemm_index.hpp"
 #include "sq.h"
 
 namespace sqh {
 
-// Split-K workspaces (the decode and prefill GEMMs): ticket counters in a
-// fixed region at the start, then the partial tiles. The region has room for
-// every split the dispatch makes (the decode kernel splits only below 192
-// workgroups, the prefill kernel only below 128 tiles), so the partial tiles
-// of one shape never land on the counters of another: one zero-filled
-// workspace serves any sequence of calls, of any shapes, made one at a time.
-constexpr size_t kSplitCounterBytes = 1024;
-constexpr int64_t kSplitMaxCounters = (int64_t)(kSplitCounterBytes / 4);
+// Split-K workspaces: fixed counter region, then partial tiles (see
+// gemm_index.hpp).
+using sqi::kSplitCounterBytes;
+using sqi::kSplitMaxCounters;
 
 // Extra inputs of the LLM.int8() epilogue: the fp16 outlier slice.
 struct DecompArgs {
