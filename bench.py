@@ -33,6 +33,7 @@ dequantisation; the weights are quantised per channel at load time.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -75,10 +76,10 @@ def decode_kernel_runs(m: int, n: int, k: int) -> bool:
 
 
 def decode_one_token_fused(m: int, n: int, k: int) -> bool:
-    """Whether the one-call path fuses the quantisation into the decode GEMM
-    (the C ABI's rule for bf16 inputs): one token, a layer at least 192 x 64
-    wide, K a multiple of 128 up to 16384."""
-    return decode_kernel_runs(m, n, k) and m == 1 and -(-n // 64) >= 192 and k % 128 == 0 and k <= 16384
+    """Whether the one-call path fuses the quantisation into the one-token
+    product (the C ABI's rule): one token, a layer at least 2048 wide, K a
+    multiple of 128 up to 16384."""
+    return decode_kernel_runs(m, n, k) and m == 1 and n >= 2048 and k % 128 == 0 and k <= 16384
 
 
 def hbm_bound(m: int, n: int, k: int, out_bytes: int) -> bool:
@@ -125,6 +126,12 @@ def parse():
     p.add_argument("--fetch-scale", type=float, default=1.9999,
                    help="FETCH_SIZE scale factor from the copy probe (profiles/hbm_counter_scale_copy.md)")
     p.add_argument("--write-scale", type=float, default=1.0, help="WRITE_SIZE scale factor from the copy probe")
+    p.add_argument("--probe", choices=["mfma", "stream", "lds", "fp8sum"], default=None,
+                   help="only run one measurement probe (libsq_probes.so) and print its JSON line: mfma = "
+                        "int8 matrix-core rate and shader clock with constant and changing operands; stream = "
+                        "single-kernel streaming read / read+write ceilings at the workloads' sizes; lds = "
+                        "fragment-read rate of the prefill GEMM's LDS pattern beside the MFMA rate; fp8sum = "
+                        "summation error of the E4M3 matrix instructions against exact sums")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain device-to-device copy of 512 MiB (5 times), the known-size "
                         "reference that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
@@ -143,10 +150,214 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
 
 
+def probe_lib():
+    """The measurement probes (w8a8_int8_quantization_amd/probes/probes.hip)."""
+    import ctypes
+
+    path = os.path.join(ROOT, "w8a8_int8_quantization_amd", "libsq_probes.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is not built: python w8a8_int8_quantization_amd/build.py --probes")
+    lib = ctypes.CDLL(path)
+    P, I, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    for name, argt in (("sqp_mfma_rate", [P, P, I, I, I, P]), ("sqp_stream", [P, L, P, L, P, I, I, P]),
+                       ("sqp_lds_rate", [P, P, I, I, I, P]), ("sqp_fp8_mfma", [P, P, P, I, I, P])):
+        fn = getattr(lib, name)
+        fn.argtypes = argt
+        fn.restype = I
+    return lib
+
+
+def _probe_time(torch, launch, reps, inner=1):
+    """Median HIP-event time (us) per launch over `reps` rounds of `inner`
+    launches back to back on the current stream (inner > 1 hides the
+    dispatch gap in front of each launch, as in a steady stream of kernels)."""
+    st = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(inner):
+            rc = launch()
+            if rc != 0:
+                raise SystemExit(f"probe launch failed: HIP error {rc}")
+        e1.record(st)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / inner)
+    return sorted(times)[len(times) // 2]
+
+
+def _sclk_ghz(clocks):
+    """Shader clock (GHz) per workgroup from its s_memtime / s_memrealtime (100 MHz) deltas."""
+    c = clocks.cpu().numpy().reshape(-1, 4).astype("float64")
+    ticks, real = c[:, 2] - c[:, 0], c[:, 3] - c[:, 1]
+    ok = real > 0
+    ghz = (ticks[ok] / real[ok]) * 0.1
+    real_us = real[ok] / 100.0
+    import numpy as np
+    return float(np.median(ghz)), float(np.median(real_us))
+
+
+def run_probe(args):
+    import numpy as np
+    import torch
+
+    lib = probe_lib()
+    dev = torch.device("cuda:0")
+    stream = lambda: ctypes_stream(torch)
+    out = {"probe": args.probe, "device": torch.cuda.get_device_name(0)}
+    if args.probe == "mfma":
+        blocks, iters = 256, 20000
+        clocks = torch.zeros(blocks * 4, dtype=torch.int64, device=dev)
+        sink = torch.zeros(blocks * 256, dtype=torch.int32, device=dev)
+        ops = blocks * 4 * iters * 16 * 2 * 32 * 32 * 32
+        for name, rnd in (("constant_operands", 0), ("changing_operands", 1)):
+            launch = lambda: lib.sqp_mfma_rate(clocks.data_ptr(), sink.data_ptr(), blocks, iters, rnd, stream())
+            _probe_time(torch, launch, 2)
+            us = _probe_time(torch, launch, 7)
+            ghz, real_us = _sclk_ghz(clocks)
+            out[name] = {"us": us, "pops": ops / us / 1e6, "frac_of_5_pops": ops / us / 1e6 / 5000.0,
+                         "sclk_ghz": ghz, "in_kernel_us": real_us,
+                         "pops_at_sclk_per_cu_clk": ops / (real_us * 1e-6) / (ghz * 1e9) / 256}
+        out["setup"] = (f"{blocks} workgroups x 4 waves (one per SIMD), {iters} x 16 v_mfma_i32_32x32x32_i8 per wave, "
+                        "8 independent accumulators; changing operands: 16 A and 16 B fragments of hashed bytes "
+                        "combined in rotation, so no two consecutive MFMAs share operands")
+    elif args.probe == "stream":
+        res = {}
+        sink = torch.zeros(4096 * 256, dtype=torch.int32, device=dev)
+        # decode: 58.7 MB of weights per launch, rotating over copies that exceed the 256 MiB last-level cache
+        wbytes = 14336 * 4096
+        ncopy = 14
+        bufs = [torch.empty(wbytes, dtype=torch.uint8, device=dev).fill_(i + 1) for i in range(ncopy)]
+        dummy = torch.empty(16, dtype=torch.uint8, device=dev)
+        best = None
+        for depth in (4, 8, 16):
+            for grid in (256, 512, 1024, 2048):
+                it = {"i": 0}
+
+                def launch(grid=grid, depth=depth, it=it):
+                    b = bufs[it["i"] % ncopy]
+                    it["i"] += 1
+                    return lib.sqp_stream(b.data_ptr(), wbytes, dummy.data_ptr(), 0, sink.data_ptr(), grid, depth,
+                                          stream())
+                _probe_time(torch, launch, 2, ncopy)
+                us = _probe_time(torch, launch, 7, ncopy)
+                r = {"us": us, "tbs": wbytes / us / 1e6, "grid": grid, "depth": depth}
+                res[f"read_58.7MB_grid{grid}_depth{depth}"] = r
+                best = r if best is None or us < best["us"] else best
+        res["read_58.7MB_best"] = best
+        del bufs
+        # prefill quantisation shapes: read bf16 [M x K], write int8 [M x K]
+        for name, m, k in (("qkv_2048x4096", 2048, 4096), ("gateup_8192x4096", 8192, 4096),
+                           ("down_8192x14336", 8192, 14336)):
+            src = torch.empty(m * k * 2, dtype=torch.uint8, device=dev).fill_(3)
+            dst = torch.empty(m * k, dtype=torch.uint8, device=dev)
+            best = None
+            for depth in (4, 8, 16):
+                for grid in (512, 1024, 2048, 4096):
+                    launch = lambda grid=grid, depth=depth: lib.sqp_stream(
+                        src.data_ptr(), m * k * 2, dst.data_ptr(), m * k, sink.data_ptr(), grid, depth, stream())
+                    _probe_time(torch, launch, 2, 10)
+                    us = _probe_time(torch, launch, 7, 20)
+                    r = {"us": us, "tbs": 3 * m * k / us / 1e6, "grid": grid, "depth": depth}
+                    res[f"rw_{name}_grid{grid}_depth{depth}"] = r
+                    best = r if best is None or us < best["us"] else best
+            res[f"rw_{name}_best"] = best
+            del src, dst
+        out["results"] = res
+        out["setup"] = ("16-byte loads, per thread a contiguous run of 16-byte vectors with `depth` loads in flight, "
+                        "256-thread workgroups, launches back to back (time per launch); the read-only "
+                        "case rotates over 14 copies (822 MB) so that every launch streams from HBM; the read+write "
+                        "cases read M x K bf16 and write M x K bytes (the activation quantiser's traffic) with "
+                        "operands that fit the last-level cache between launches")
+    elif args.probe == "lds":
+        blocks, iters = 256, 20000
+        clocks = torch.zeros(blocks * 4, dtype=torch.int64, device=dev)
+        sink = torch.zeros(blocks * 512, dtype=torch.int32, device=dev)
+        for name, mode in (("reads_only", 0), ("mfma_only", 1), ("reads_and_mfma", 2), ("linear_reads_only", 3)):
+            launch = lambda: lib.sqp_lds_rate(clocks.data_ptr(), sink.data_ptr(), blocks, iters, mode, stream())
+            _probe_time(torch, launch, 2)
+            us = _probe_time(torch, launch, 7)
+            ghz, real_us = _sclk_ghz(clocks)
+            cycles = real_us * 1e-6 * ghz * 1e9
+            r = {"us": us, "sclk_ghz": ghz, "in_kernel_us": real_us}
+            if mode != 1:
+                r["lds_bytes_per_clk_per_cu"] = 8 * 64 * 5 * 16 * iters / cycles
+            if mode in (1, 2):
+                ops = blocks * 8 * 6 * iters * 2 * 32 * 32 * 32
+                r["pops"] = ops / us / 1e6
+                r["frac_of_5_pops"] = ops / us / 1e6 / 5000.0
+            out[name] = r
+        out["setup"] = (f"{blocks} workgroups x 8 waves (two per SIMD), 64 KiB LDS; per iteration and wave 5 "
+                        "ds_read_b128 fragment reads in the prefill GEMM's swizzled 128-byte-row pattern and/or "
+                        "6 v_mfma_i32_32x32x32_i8 with constant operands (the kernel's 5 reads per 6 MFMAs)")
+    else:
+        res = {}
+        tiles = 4096
+        # E4M3 (OCP) values of all 256 codes; 0x7F and 0xFF are NaN
+        codes = np.arange(256)
+        e, mnt, sgn = (codes >> 3) & 15, codes & 7, np.where(codes >> 7, -1.0, 1.0)
+        val = np.where(e == 0, mnt / 8.0 * 2.0 ** -6, (1 + mnt / 8.0) * 2.0 ** (e - 7.0)) * sgn
+        finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F])
+        pos = np.array([c for c in range(128) if c != 0x7F])
+        rng = np.random.default_rng(20240)
+
+        def nearest_codes(x):
+            # nearest finite E4M3 value (input data only: ties are immaterial here)
+            a = np.abs(x)
+            order = np.argsort(val[pos])
+            sv = val[pos][order]
+            j = np.clip(np.searchsorted(sv, a), 1, len(sv) - 1)
+            pick = np.where(np.abs(sv[j] - a) < np.abs(sv[j - 1] - a), j, j - 1)
+            c = pos[order][pick]
+            return np.where(x < 0, c | 0x80, c).astype(np.uint8)
+
+        for dname in ("every_finite_code", "quantised_gaussian"):
+            for form, (rows, kk) in ((0, (32, 64)), (1, (16, 128))):
+                if dname == "every_finite_code":
+                    a8 = rng.choice(finite, size=(tiles, rows, kk)).astype(np.uint8)
+                    b8 = rng.choice(finite, size=(tiles, rows, kk)).astype(np.uint8)
+                else:
+                    g = rng.standard_normal((2, tiles, rows, kk))
+                    g = g / np.abs(g).max(axis=-1, keepdims=True) * 448.0
+                    a8, b8 = nearest_codes(g[0]), nearest_codes(g[1])
+                av, bv = val[a8], val[b8]
+                exact = np.einsum("tnk,tmk->tnm", av, bv)
+                mag = np.einsum("tnk,tmk->tnm", np.abs(av), np.abs(bv))
+                ta = torch.from_numpy(a8.reshape(-1)).to(dev)
+                tb = torch.from_numpy(b8.reshape(-1)).to(dev)
+                td = torch.empty(tiles * rows * rows, dtype=torch.float32, device=dev)
+                rc = lib.sqp_fp8_mfma(ta.data_ptr(), tb.data_ptr(), td.data_ptr(), tiles, form, stream())
+                torch.cuda.synchronize()
+                if rc != 0:
+                    raise SystemExit(f"probe launch failed: HIP error {rc}")
+                got = td.cpu().numpy().astype(np.float64).reshape(tiles, rows, rows)
+                err = np.abs(got - exact)
+                rel = np.where(mag > 0, err / np.where(mag > 0, mag, 1.0), 0.0)
+                res[f"{dname}_{'32x32x64' if form == 0 else '16x16x128'}"] = {
+                    "max_err_over_sum_abs_products": float(rel.max()),
+                    "max_in_units_of_2^-12": float(rel.max() * 4096.0),
+                    "p99_err_over_sum_abs_products": float(np.quantile(rel, 0.99)),
+                    "exact_fraction": float((err == 0).mean()),
+                    "layout_ok": bool(rel.max() < 2.0 ** -6),
+                }
+        out["results"] = res
+        out["setup"] = (f"{tiles} tiles per case, one E4M3 MFMA each with zero accumulators and unit scales; "
+                        "exact sums in binary64 (every E4M3 product and these sums are exact there)")
+    print(json.dumps(out), flush=True)
+
+
+def ctypes_stream(torch):
+    return torch.cuda.current_stream().cuda_stream
+
+
 def kernel_source_hash(name: str) -> str:
-    path = os.path.join(ROOT, "w8a8_int8_quantization_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel's source file and of the shared headers it includes."""
+    csrc = os.path.join(ROOT, "w8a8_int8_quantization_amd", "csrc")
+    h = hashlib.sha256()
+    for path in [os.path.join(csrc, name)] + sorted(glob.glob(os.path.join(csrc, "*.hpp"))):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def profile_entry(workload: str, kernel_file: str):
@@ -801,7 +1012,7 @@ def bench_linear(args, dev) -> dict:
     gemm_bytes = c.m * c.k + c.n * c.k + 4 * c.m + 4 * c.n + c.m * c.n * {"f32": 4, "bf16": 2}[c.y_dtype]
     big = big_kernel_suits(c.m, c.n, c.k)
     fused1 = one_call and decode_one_token_fused(c.m, c.n, c.k)
-    kfile, kname = (("decode_fused.hip", "gemm_decode1_kernel") if fused1 else
+    kfile, kname = (("decode_fused.hip", "gemv_decode1_kernel") if fused1 else
                     ("gemm_decode.hip", "gemm_decode_kernel") if decode else
                     ("gemm_big.hip", "gemm_big_kernel") if big else ("gemm.hip", "gemm_i8_kernel"))
     tag = (args.workload if args.m is None else f"{args.workload}_m{c.m}") + (":one_call" if one_call else "")
@@ -957,6 +1168,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.probe:
+        run_probe(args)
         return
 
     import torch

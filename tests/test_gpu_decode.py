@@ -117,13 +117,15 @@ def test_decode_workspace_validation():
     assert st == 6
 
 
-# One token: sq_w8a8_linear_dyn runs the quantisation inside the decode GEMM
-# (one launch) for layers at least 192 x 64 wide, and quantisation + split-K
-# GEMM otherwise. (dtype, n, k): the 8B up projection, ragged N, the longest
-# rows the fused path takes (16384 bf16 / fp16, 8192 binary32), a one-step K,
-# and narrower layers on the two-launch path.
+# One token: sq_w8a8_linear_dyn runs the quantisation inside the one-token
+# product (one launch) for layers at least 2048 wide, and quantisation +
+# split-K decode GEMM otherwise. (dtype, n, k): the 8B up and down
+# projections, ragged N, the longest rows the fused path takes (16384 values,
+# with 4, 8 and 16 waves per workgroup), one-step K, the narrowest fused
+# layer, and a narrower layer on the two-launch path.
 ONE_TOKEN = [("bf16", 14336, 4096), ("bf16", 12300, 16384), ("f16", 12290, 1152), ("f32", 14336, 8192),
-             ("f32", 12288, 128), ("bf16", 28672, 256), ("bf16", 4096, 14336), ("f16", 300, 1152)]
+             ("f32", 12288, 128), ("bf16", 28672, 256), ("bf16", 4096, 14336), ("f16", 300, 1152),
+             ("f32", 2050, 16384), ("bf16", 2048, 128), ("f16", 6150, 5120)]
 
 
 def _one_token_case(dtype, n, k, seed, smooth_kind):

@@ -16,6 +16,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsq.so")
+# measurement probes for the benchmark's probe modes (not part of the layer)
+PROBE_SRC = os.path.join(PKG, "probes", "probes.hip")
+PROBE_LIB = os.path.join(PKG, "libsq_probes.so")
 ARCH = "gfx950"
 
 # -ffp-contract=off: every binary32 multiply and add rounds on its own, as the
@@ -96,5 +99,25 @@ def build_library(verbose: bool = False, jobs: int = 0, sanitize: bool = False) 
     return lib
 
 
+def build_probes(verbose: bool = False) -> str:
+    """Compile the measurement probes (probes/probes.hip) to libsq_probes.so."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    obj = os.path.join(objdir, "probes.hip.o")
+    out = _compile(PROBE_SRC, obj)
+    if verbose and out.strip():
+        print(out)
+    tmp = PROBE_LIB + ".tmp"
+    res = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"probe link failed ({res.returncode}):\n{res.stdout + res.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
+    if "--probes" in sys.argv:
+        print(build_probes(verbose="-v" in sys.argv))
+        sys.exit(0)
     print(build_library(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))
