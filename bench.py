@@ -77,8 +77,8 @@ def decode_kernel_runs(m: int, n: int, k: int) -> bool:
 
 def decode_one_token_fused(m: int, n: int, k: int) -> bool:
     """Whether the one-call path fuses the quantisation into the one-token
-    product (the C ABI's rule): one token, a layer at least 2048 wide, K a
-    multiple of 128 up to 16384."""
+    product (the C ABI's rule for bf16 inputs): one token, a layer at least
+    2048 wide, K a multiple of 128 up to 16384."""
     return decode_kernel_runs(m, n, k) and m == 1 and n >= 2048 and k % 128 == 0 and k <= 16384
 
 

@@ -120,9 +120,10 @@ def test_decode_workspace_validation():
 # One token: sq_w8a8_linear_dyn runs the quantisation inside the one-token
 # product (one launch) for layers at least 2048 wide, and quantisation +
 # split-K decode GEMM otherwise. (dtype, n, k): the 8B up and down
-# projections, ragged N, the longest rows the fused path takes (16384 values,
-# with 4, 8 and 16 waves per workgroup), one-step K, the narrowest fused
-# layer, and a narrower layer on the two-launch path.
+# projections, ragged N, the longest rows the fused path takes (16384 bf16 /
+# fp16 values with 16 waves, 8192 binary32 with 8), one-step K, the narrowest
+# fused layer, and layers on the two-launch path (narrower, or binary32 rows
+# of 16384).
 ONE_TOKEN = [("bf16", 14336, 4096), ("bf16", 12300, 16384), ("f16", 12290, 1152), ("f32", 14336, 8192),
              ("f32", 12288, 128), ("bf16", 28672, 256), ("bf16", 4096, 14336), ("f16", 300, 1152),
              ("f32", 2050, 16384), ("bf16", 2048, 128), ("f16", 6150, 5120)]
@@ -169,3 +170,24 @@ def test_one_token_fused_zero_row_and_oracle():
     wq_ref, sw_ref = oracle.quantize_weights_per_channel(oracle.fold_weights(c.w, s_ref))
     y_ref, _, _, _ = oracle.smoothquant_linear(c.x, s_ref, wq_ref, sw_ref, "bf16")
     assert_out_close(y, y_ref, "bf16")
+
+
+@pytest.mark.parametrize("dtype,n,k", [("bf16", 14336, 4096), ("bf16", 4096, 14336), ("f32", 2050, 16384)])
+def test_one_token_fused_workspace_reuse(dtype, n, k):
+    """The one-launch step publishes the row's codes and scale through the
+    workspace: a workspace full of garbage, one reused call after call (with
+    different inputs and layers of different K), and the library's static
+    scratch all give the two-call result, bit for bit."""
+    log("one token workspace reuse", dtype, n, k)
+    nb = sq.raw["sq_w8a8_linear_dyn_workspace_size"](1, n, 16384)
+    ws = torch.randint(0, 256, (nb,), dtype=torch.uint8, device=dev())
+    layers = [_one_token_case(dtype, n, k, seed=11 + i, smooth_kind="fast") for i in range(3)]
+    layers.append(_one_token_case(dtype, n, 4096 if k != 4096 else 8192, seed=23, smooth_kind="fast"))
+    for rep in range(2):
+        for x, s, wq, sw in layers:
+            xq, dx = sq.sq_quant_act_per_token(x, s)
+            y2 = sq.sq_w8a8_linear(xq, dx, wq, sw, out_dtype=torch.bfloat16)
+            y1 = sq.sq_w8a8_linear_dyn(x, s, wq, sw, out_dtype=torch.bfloat16, ws=ws)
+            y3 = sq.sq_w8a8_linear_dyn_static(x, s, wq, sw, out_dtype=torch.bfloat16)
+            assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), rep
+            assert torch.equal(y3.view(torch.int16), y2.view(torch.int16)), rep

@@ -14,15 +14,15 @@
 // the matrix cores would idle on 15 of their 16 token columns; the dot
 // products run on the vector ALUs instead (v_dot4_i32_i8: four int8 products
 // summed into an int32 per instruction), and the weight stream is laid out
-// for full cache lines. A workgroup of kW waves owns 16 rows of Wq (output
-// columns); within a wave, lanes 8r .. 8r + 7 read the 16-byte pieces of one
-// 128-byte line of row r, so each load instruction covers 8 whole lines
-// (the matrix-core layout reads half lines, 16 rows x 64 bytes, and needs two
-// requests per line). The waves take the 128-byte k-steps round-robin (wave w:
-// steps w, w + kW, ...), eight steps per wave with every load of the wave in
-// flight before the first product; kW grows with K (4, 8 or 16 waves for K up
-// to 4096, 8192 or 16384) so that the row's quantisation below is spread over
-// enough threads.
+// for full cache lines. A workgroup of kW waves owns 8 or 16 rows of Wq
+// (output columns); within a wave, lanes 8r .. 8r + 7 read the 16-byte pieces
+// of one 128-byte line of row r, so each load instruction covers 8 whole
+// lines (the matrix-core layout reads half lines, 16 rows x 64 bytes, and
+// needs two requests per line). The waves take the 128-byte k-steps round-
+// robin (wave w: steps w, w + kW, ...), up to eight steps per wave with every
+// load of the wave in flight before the first product; kW grows with K (8
+// waves for K up to 8192, 16 up to 16384) so that the row's quantisation
+// below is spread over enough threads.
 //
 // Before its first product every workgroup reads the token's row of X and the
 // smoothing factors (L2-resident after the first workgroup), forms the row
@@ -51,17 +51,16 @@ struct Decode1Args {
   int out;              // 0 f32, 1 bf16, 2 f16
 };
 
-constexpr int kD1Rows = 16;   // Wq rows (outputs) per workgroup: two 8-row groups
-constexpr int kD1Steps = 8;   // 128-byte k-steps per wave (all loads in flight)
-
-// kW waves; each thread keeps kC 16-byte vectors of the row (16 / bytes per
-// value, so K <= 64 kW x 16 values).
-template <class In, bool kSmooth, int kW>
+// kW waves of kNS 128-byte k-steps each (all loads in flight; K <= 128 kW
+// kNS) over kG 8-row groups of Wq; each thread keeps kC 16-byte vectors of
+// the row (16 / bytes per value, so K <= 64 kW x 16 values).
+template <class In, bool kSmooth, int kW, int kG, int kNS>
 __global__ __launch_bounds__(64 * kW, 1) void gemv_decode1_kernel(Decode1Args a) {
   constexpr int kT = 64 * kW;
   constexpr int V = In::kVec;
   constexpr int kC = 16 / V;
-  constexpr int kG = kD1Rows / 8;
+  constexpr int kD1Rows = 8 * kG;  // Wq rows (outputs) of the workgroup
+  constexpr int kD1Steps = kNS;
   constexpr int kMaxK = kT * kC * V;
   __shared__ __attribute__((aligned(16))) int8_t codes[kMaxK];
   __shared__ int32_t red[kW][kD1Rows];
@@ -95,7 +94,7 @@ __global__ __launch_bounds__(64 * kW, 1) void gemv_decode1_kernel(Decode1Args a)
     }
   }
 
-  // ---- Wq: all kD1Steps steps of this wave for both row groups; steps past
+  // ---- Wq: all kD1Steps steps of this wave for its row groups; steps past
   // the end reload the last step (valid memory; their products are skipped)
   const int piece = 16 * (lane & 7);
   const int8_t* wp[kG];
@@ -231,17 +230,28 @@ namespace sqh {
 
 namespace {
 
+// 8 waves of 4 steps and 8 rows per workgroup up to K = 4096, 8 waves of 8
+// steps up to 8192, 16 waves of 8 steps and 16 rows up to 16384. Measured on
+// MI355X, us per one-call step back to back, 4096 -> 14336 / 14336 -> 4096
+// layers: 8 rows and 8 waves 13.9 / -, 16 rows and 4 waves 15.4 / -, 16 rows
+// and 16 waves - / 14.7, 8 rows and 16 waves - / 17.2 (two rounds of
+// workgroups, each quantising the row; without the quantisation the product
+// alone takes 10.7 / 11.4 with 8 rows against 14.1 / 12.3 with 16, and a plain
+// stream of the same bytes 10.1-10.4). Publishing the codes from one
+// workgroup to the others through the workspace measured slower (15.6 / 16.1:
+// the publication adds two dependent memory round trips to every later
+// workgroup's path).
 template <class In, bool kSmooth>
 void launch_d1(const sqk::Decode1Args& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.N + sqk::kD1Rows - 1) / sqk::kD1Rows));
-  const int nvec = a.K / In::kVec;
-  constexpr int kC = 16 / In::kVec;
-  if (nvec <= 256 * kC)
-    hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, 4>), grid, dim3(256), 0, s, a);
-  else if (nvec <= 512 * kC)
-    hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, 8>), grid, dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, 16>), grid, dim3(1024), 0, s, a);
+  if (a.K <= 4096)
+    hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, 8, 1, 4>), dim3((unsigned)((a.N + 7) / 8)), dim3(512),
+                       0, s, a);
+  else if (a.K <= 8192)
+    hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, 8, 1, 8>), dim3((unsigned)((a.N + 7) / 8)), dim3(512),
+                       0, s, a);
+  else if constexpr (In::kVec == 8)  // binary32 rows stop at 8192 (decode1_suits)
+    hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, 16, 2, 8>), dim3((unsigned)((a.N + 15) / 16)),
+                       dim3(1024), 0, s, a);
 }
 
 template <class In>
@@ -259,8 +269,9 @@ hipError_t decode1(const sqk::Decode1Args& a, bool smooth, hipStream_t s) {
 // 16 values; the eight k-steps per wave then cover K), and layers at least
 // 2048 wide (128 workgroups or more).
 bool decode1_suits(int64_t m, int64_t n, int64_t k, sq_dtype xt) {
-  (void)xt;
-  return m == 1 && n >= 2048 && n <= INT32_MAX && k % 128 == 0 && k <= 16384;
+  // binary32 rows up to 8192 (beyond, the 16-wave form would need more
+  // registers than it has)
+  return m == 1 && n >= 2048 && n <= INT32_MAX && k % 128 == 0 && k <= (xt == SQ_F32 ? 8192 : 16384);
 }
 
 hipError_t decode1_linear(const void* x, sq_dtype xt, const float* smooth, const int8_t* wq, const float* w_scale,
