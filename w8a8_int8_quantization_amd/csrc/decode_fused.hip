@@ -20,9 +20,9 @@
 // lines (the matrix-core layout reads half lines, 16 rows x 64 bytes, and
 // needs two requests per line). The waves take the 128-byte k-steps round-
 // robin (wave w: steps w, w + kW, ...), up to eight steps per wave with every
-// load of the wave in flight before the first product; kW grows with K (8
-// waves for K up to 8192, 16 up to 16384) so that the row's quantisation
-// below is spread over enough threads.
+// load of the wave in flight before the first product; kW grows with K (4
+// waves for K up to 4096, 8 up to 8192, 16 up to 16384) so that the row's
+// quantisation below is spread over enough threads.
 //
 // Before its first product every workgroup reads the token's row of X and the
 // smoothing factors (L2-resident after the first workgroup), forms the row
@@ -230,21 +230,23 @@ namespace sqh {
 
 namespace {
 
-// 8 waves of 4 steps and 8 rows per workgroup up to K = 4096, 8 waves of 8
+// 4 waves of 8 steps and 8 rows per workgroup up to K = 4096, 8 waves of 8
 // steps up to 8192, 16 waves of 8 steps and 16 rows up to 16384. Measured on
-// MI355X, us per one-call step back to back, 4096 -> 14336 / 14336 -> 4096
-// layers: 8 rows and 8 waves 13.9 / -, 16 rows and 4 waves 15.4 / -, 16 rows
-// and 16 waves - / 14.7, 8 rows and 16 waves - / 17.2 (two rounds of
-// workgroups, each quantising the row; without the quantisation the product
-// alone takes 10.7 / 11.4 with 8 rows against 14.1 / 12.3 with 16, and a plain
-// stream of the same bytes 10.1-10.4). Publishing the codes from one
-// workgroup to the others through the workspace measured slower (15.6 / 16.1:
-// the publication adds two dependent memory round trips to every later
+// MI355X, us per launch back to back over rotating weight copies, 4096 ->
+// 14336 layer (waves / rows per workgroup / steps per wave): 4/8/8 13.5,
+// 8/8/4 14.2, 8/16/4 13.8, 16/16/2 14.8, 16/32/2 14.2, 16/8/2 18.5; 14336 ->
+// 4096 layer: 16/16/8 15.2, 16/8/8 17.5 (two rounds of workgroups, each
+// quantising the row), 16/24/8 23.7 and 16/32/8 32.8 (registers spilled).
+// Without the quantisation the product alone takes 10.7-11.0 / 11.4 with 8
+// rows, and a plain stream of the same bytes 10.1-10.4: the row's
+// quantisation in every workgroup costs the rest. Publishing the codes from
+// one workgroup to the others through the workspace measured slower (15.6 /
+// 16.1: the publication adds two dependent memory round trips to every other
 // workgroup's path).
 template <class In, bool kSmooth>
 void launch_d1(const sqk::Decode1Args& a, hipStream_t s) {
   if (a.K <= 4096)
-    hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, 8, 1, 4>), dim3((unsigned)((a.N + 7) / 8)), dim3(512),
+    hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, 4, 1, 8>), dim3((unsigned)((a.N + 7) / 8)), dim3(256),
                        0, s, a);
   else if (a.K <= 8192)
     hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, 8, 1, 8>), dim3((unsigned)((a.N + 7) / 8)), dim3(512),
