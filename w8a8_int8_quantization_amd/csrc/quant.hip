@@ -379,13 +379,6 @@ static void launch_quant(const void* x, int64_t m, int64_t k, int64_t ldx, const
   const int64_t nvec = k / In::kVec;
   const int64_t ldb = ldx * In::kBytes;
   const uint8_t* xb = (const uint8_t*)x;
-  // prefill rows of 1025..1792 vectors (the 14336-wide down projection's
-  // input): 448 threads of 4 vectors (8192 x 14336 bf16: 76.8 us against
-  // 80.9 with 1024 threads of 2, back to back)
-  if (m >= 1024 && nvec > 1024 && nvec <= 1792) {
-    launch_rows<In, 4, 448, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s, zero, nzero);
-    return;
-  }
   // 1024 threads per row: decode-sized inputs (the row's work lands on one
   // CU), and rows too long to keep in registers at 256 threads
   if (nvec <= 2048 && ((m < 1024 && nvec > 256) || nvec > 1024)) {
