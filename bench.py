@@ -60,12 +60,33 @@ def big_kernel_suits(m: int, n: int, k: int) -> bool:
     return n >= 4096 and k // 128 >= 20 and (m >= 176 or (m >= 129 and n * k >= (1 << 25)))
 
 
-def decode_kernel_runs(m: int, n: int, k: int) -> bool:
+def decode_steps_per_wave(m: int, n: int, k: int) -> int:
+    """Steps per wave of the decode plan (the C ABI's plan, repeated here)."""
+    steps = k // 128
+    tiles, tb = -(-n // 64), -(-m // 64)
+    wgs = tiles * tb
+    want = 1 if wgs >= 192 else -(-256 // wgs)
+    want = max(1, min(want, steps))
+    per = min(-(-steps // want), 32)
+    if -(-steps // per) > 1 and tiles * tb > 256:
+        per = steps  # no room for the split's counters: K is not split
+    return -(-per // 4)
+
+
+def decode_ring(m: int, f8: bool = False) -> bool:
+    """Whether the decode GEMM runs its LDS-ring form (int8, 17 tokens and more)."""
+    return not f8 and m >= 17
+
+
+def decode_kernel_runs(m: int, n: int, k: int, f8: bool = False) -> bool:
     """Whether the library routes this GEMM to its decode kernel (the
     dispatch rule of the C ABI, repeated here to label the measured kernel):
     M <= 64, or up to 256 tokens when the 256-row prefill kernel does not
-    apply and the 128 x 128 tiled kernel would have at most 128 tiles."""
+    apply and the 128 x 128 tiled kernel would have at most 128 tiles; the
+    unrolled form only where its 8 steps per wave cover a K slice."""
     if k % 128 or m < 1:
+        return False
+    if not decode_ring(m, f8) and decode_steps_per_wave(m, n, k) > 8:
         return False
     if m <= 64:
         return True
@@ -79,7 +100,7 @@ def decode_one_token_fused(m: int, n: int, k: int) -> bool:
     """Whether the one-call path fuses the quantisation into the one-token
     product (the C ABI's rule for bf16 inputs): one token, a layer at least
     2048 wide, K a multiple of 128 up to 16384."""
-    return decode_kernel_runs(m, n, k) and m == 1 and n >= 2048 and k % 128 == 0 and k <= 16384
+    return m == 1 and n >= 2048 and k % 128 == 0 and k <= 16384
 
 
 def hbm_bound(m: int, n: int, k: int, out_bytes: int) -> bool:
@@ -529,7 +550,7 @@ def bench_fp8(args, dev):
     xq = torch.empty((c.m, c.k), dtype=torch.uint8, device=dev)
     dx = torch.empty(c.m, dtype=torch.float32, device=dev)
     y = torch.empty((c.m, c.n), dtype=torch.bfloat16, device=dev)
-    decode = decode_kernel_runs(c.m, c.n, c.k)
+    decode = decode_kernel_runs(c.m, c.n, c.k, f8=True)
     streamed = hbm_bound(c.m, c.n, c.k, 2)
     # weight-streaming shapes rotate through >= 768 MiB of weight copies so
     # that every step reads its weights from HBM, not the last-level cache
@@ -1013,7 +1034,8 @@ def bench_linear(args, dev) -> dict:
     big = big_kernel_suits(c.m, c.n, c.k)
     fused1 = one_call and decode_one_token_fused(c.m, c.n, c.k)
     kfile, kname = (("decode_fused.hip", "gemv_decode1_kernel") if fused1 else
-                    ("gemm_decode.hip", "gemm_decode_kernel") if decode else
+                    ("gemm_decode.hip", "gemm_decode_ring_kernel" if decode_ring(c.m) else "gemm_decode_kernel")
+                    if decode else
                     ("gemm_big.hip", "gemm_big_kernel") if big else ("gemm.hip", "gemm_i8_kernel"))
     tag = (args.workload if args.m is None else f"{args.workload}_m{c.m}") + (":one_call" if one_call else "")
     traffic = pmc_traffic(tag, kfile)

@@ -17,7 +17,14 @@
 //     loads inside the rows, the LDS reduction (each quad read where it was
 //     written), partial tiles and the reducer's eight-slice rounds (inside
 //     32-bit offsets, reads past the last slice never land inside the
-//     buffer), ticket counters inside the fixed region, and the output stores.
+//     buffer), ticket counters inside the fixed region, and the output stores;
+//   decode ring form: every LDS byte of a stage written once by the
+//     transfers, every fragment read finding its row and k chunk (the four
+//     waves' quarters covering each row's eight chunks once), the reduction
+//     slots (written once, each output read from the slot that holds it),
+//     transfers inside the operands over the whole slice, partial tiles
+//     (inside the workspace, every 16-byte slot once per call) and the
+//     output stores (every output once).
 // Prints "OK <checks>" and exits 0, or prints the first failures and exits 1.
 #include <stdio.h>
 #include <stdlib.h>
@@ -381,11 +388,163 @@ static void big_shape(const Shape& sh, bool every_tile) {
 
 // ------------------------------------------------------------------- decode
 
+// Configuration checks of the ring form (all tiles alike).
+template <int kTok>
+static void ring_config_checks() {
+  using C = RingCfg<kTok>;
+  g_ctx = "ring config tok=" + std::to_string(kTok);
+  CHECK(C::kLds + 16 <= 160 * 1024, "LDS %d bytes", C::kLds + 16);
+  CHECK(C::kLds >= C::kRing * C::kStage && C::kLds >= C::kRedBytes, "LDS holds the ring and the reduction");
+  CHECK(C::kStage % 1024 == 0, "stage size %d", C::kStage);
+  CHECK((C::kRing - 2) * C::kDma <= 63 && C::kRing >= 2, "vmcnt range");
+  // one stage of transfers: every 16-byte slot once, with its tag
+  std::vector<Tag> lds(C::kStage / 16);
+  for (int wid = 0; wid < kDecWaves; ++wid)
+    for (int lane = 0; lane < 64; ++lane)
+      for (int i = 0; i < C::kDma; ++i) {
+        const RingDma d = ring_dma<kTok>(i, wid, lane);
+        const int off = d.dst + 16 * lane;
+        CHECK(d.dst % 1024 == 0, "transfer block at %d", d.dst);
+        CHECK(d.row >= 0 && d.row < (d.w ? C::kRows : kTok), "row %d", d.row);
+        CHECK(d.chunk >= 0 && d.chunk < 8, "chunk %d", d.chunk);
+        CHECK(off >= (d.w ? 0 : C::kStageW) && off + 16 <= (d.w ? C::kStageW : C::kStage), "lds off %d", off);
+        if (off < 0 || off + 16 > C::kStage) continue;
+        CHECK(off - (d.w ? 0 : C::kStageW) == big_lds_off(d.row, d.chunk), "transfer slot vs fragment layout");
+        Tag& t = lds[off / 16];
+        CHECK(t.op == -1, "LDS slot %d written twice", off);
+        t.op = d.w ? 1 : 0;
+        t.row = d.row;
+        t.chunk = d.chunk;
+      }
+  for (size_t e = 0; e < lds.size(); ++e) CHECK(lds[e].op != -1, "LDS slot %zu never written", e);
+  // fragment reads: wave q reads chunks 2q, 2q+1 of every row of its blocks
+  std::vector<int> wseen((size_t)C::kRows * 8, 0), xseen((size_t)kTok * 8, 0);
+  for (int q = 0; q < kDecWaves; ++q)
+    for (int lane = 0; lane < 64; ++lane) {
+      for (int bn = 0; bn < C::kNB; ++bn) {
+        const int off = ring_frag_w<kTok>(bn, q, lane);
+        CHECK(off >= 0 && off + 16 <= C::kStageW && off % 16 == 0, "w frag off %d", off);
+        if (off < 0 || off + 16 > C::kStageW) continue;
+        const Tag& t = lds[off / 16];
+        const int row = 32 * bn + (lane & 31), chunk = 2 * q + (lane >> 5);
+        CHECK(t.op == 1 && t.row == row && t.chunk == chunk, "w frag finds (%d,%d,%d)", t.op, t.row, t.chunk);
+        ++wseen[(size_t)row * 8 + chunk];
+      }
+      for (int bm = 0; bm < C::kMB; ++bm) {
+        const int off = ring_frag_x<kTok>(bm, q, lane);
+        CHECK(off >= C::kStageW && off + 16 <= C::kStage && off % 16 == 0, "x frag off %d", off);
+        if (off < C::kStageW || off + 16 > C::kStage) continue;
+        const Tag& t = lds[off / 16];
+        const int row = 32 * bm + (lane & 31), chunk = 2 * q + (lane >> 5);
+        CHECK(t.op == 0 && t.row == row && t.chunk == chunk, "x frag finds (%d,%d,%d)", t.op, t.row, t.chunk);
+        ++xseen[(size_t)row * 8 + chunk];
+      }
+    }
+  for (int v : wseen) CHECK(v == 1, "w chunk read %d times", v);
+  for (int v : xseen) CHECK(v == 1, "x chunk read %d times", v);
+  // reduction slots: what each holds, and where the epilogue reads
+  std::vector<int> holds(C::kSlots, -1);  // token * 64 + first output
+  for (int bn = 0; bn < C::kNB; ++bn)
+    for (int bm = 0; bm < C::kMB; ++bm)
+      for (int rg = 0; rg < 4; ++rg)
+        for (int lane = 0; lane < 64; ++lane) {
+          const int slot = ring_slot<kTok>(bn, bm, rg, lane);
+          CHECK(slot >= 0 && slot < C::kSlots, "slot %d", slot);
+          if (slot < 0 || slot >= C::kSlots) continue;
+          CHECK(holds[slot] == -1, "slot %d written twice", slot);
+          holds[slot] = (32 * bm + (lane & 31)) * 64 + 32 * bn + 8 * rg + 4 * (lane >> 5);
+        }
+  std::vector<int> outs((size_t)kTok * 64, 0);
+  for (int tid = 0; tid < 256; ++tid)
+    for (int g = 0; g < C::kNG; ++g) {
+      const int ml = ring_tok<kTok>(tid), nl = ring_col<kTok>(tid, g);
+      CHECK(ml >= 0 && ml < kTok && nl >= 0 && nl + 4 <= 64 && nl % 4 == 0, "epilogue (%d,%d)", ml, nl);
+      if (ml < 0 || ml >= kTok || nl < 0 || nl + 4 > 64) continue;
+      const int slot = ring_read_slot<kTok>(ml, nl);
+      CHECK(slot >= 0 && slot < C::kSlots && holds[slot] == ml * 64 + nl, "read slot %d", slot);
+      if (g > 0) CHECK(nl == ring_col<kTok>(tid, g - 1) + 4, "a thread's outputs are consecutive");
+      for (int e = 0; e < 4; ++e) ++outs[(size_t)ml * 64 + nl + e];
+    }
+  for (int v : outs) CHECK(v == 1, "tile output covered %d times", v);
+}
+
+// One shape of the ring form.
+template <int kTok>
+static void ring_shape(int M, int N, int K, const DecodePlan& p) {
+  using C = RingCfg<kTok>;
+  CHECK(p.tb == 1 || kTok == 64, "token layers with %d-token tiles", kTok);
+  CHECK(dec_ring_tok(M) == kTok, "token tile");
+  const int steps = K / kDecStep;
+  // transfers over each slice, inside the operands
+  for (int s = 0; s < p.S; ++s) {
+    const DecSlice sl = dec_slice(s, p.slice_steps, K);
+    CHECK(sl.nsl >= 1 && sl.step0 + sl.nsl <= steps, "slice %d", s);
+    for (int wid = 0; wid < kDecWaves; ++wid)
+      for (int lane = 0; lane < 64; ++lane)
+        for (int i = 0; i < C::kDma; ++i) {
+          const RingDma d = ring_dma<kTok>(i, wid, lane);
+          for (int tile = 0; tile < p.tiles; tile += (p.tiles > 2 ? p.tiles - 1 : 1))
+            for (int z = 0; z < p.tb; ++z) {
+              const int64_t base = d.w ? big_dma_src(tile * C::kRows, d.row, N, K, sl.step0, d.chunk)
+                                       : big_dma_src(z * 64, d.row, M, K, sl.step0, d.chunk);
+              const int64_t last = base + (int64_t)(sl.nsl - 1) * kDecStep;
+              const int64_t size = (int64_t)(d.w ? N : M) * K;
+              CHECK(base >= 0 && last + 16 <= size, "transfer outside the operand");
+            }
+        }
+  }
+  // partial tiles and outputs
+  const bool split = p.S > 1;
+  const int nctr = p.tiles * p.tb;
+  const uint64_t pbytes = (uint64_t)p.S * nctr * C::kTileBytes;
+  if (split) {
+    CHECK(nctr <= kSplitMaxCounters, "counters %d", nctr);
+    CHECK(pbytes < (1ull << 31), "partials %llu bytes", (unsigned long long)pbytes);
+    CHECK(dec_workspace_bytes(p, M, N, true) == kSplitCounterBytes + pbytes, "workspace size");
+  }
+  std::vector<uint8_t> pw(split ? pbytes / 16 : 0, 0);
+  std::vector<uint8_t> out((size_t)M * N, 0);
+  for (int z = 0; z < p.tb; ++z)
+    for (int tile = 0; tile < p.tiles; ++tile) {
+      const int ctr = z * p.tiles + tile;
+      for (int tid = 0; tid < 256; ++tid)
+        for (int g = 0; g < C::kNG; ++g) {
+          if (split)
+            for (int s = 0; s < p.S; ++s) {
+              const uint32_t off = ring_partial_off(s, nctr, ctr, g, tid, C::kTileBytes);
+              CHECK(off % 16 == 0 && off + 16 <= pbytes, "partial off %u", off);
+              if (off + 16 <= pbytes) ++pw[off / 16];
+            }
+          const int m = z * 64 + ring_tok<kTok>(tid), n = tile * C::kRows + ring_col<kTok>(tid, g);
+          if (m >= M || n >= N) continue;
+          for (int e = 0; e < std::min(4, N - n); ++e) ++out[(size_t)m * N + n + e];
+        }
+    }
+  for (size_t e = 0; e < out.size(); ++e)
+    if (out[e] != 1) {
+      CHECK(out[e] == 1, "output %zu stored %d times", e, out[e]);
+      break;
+    }
+  for (size_t e = 0; e < pw.size(); ++e)
+    if (pw[e] != 1) {
+      CHECK(pw[e] == 1, "partial slot %zu written %d times", e, pw[e]);
+      break;
+    }
+}
+
 static void decode_shape(const Shape& sh, bool f8) {
   const int M = (int)sh.m, N = (int)sh.n, K = (int)sh.k;
   g_ctx = "decode " + std::to_string(M) + "x" + std::to_string(N) + "x" + std::to_string(K) + (f8 ? " e4m3" : "");
-  if (!decode_suits(sh.m, sh.n, sh.k)) return;
+  if (!decode_suits(sh.m, sh.n, sh.k, f8)) return;
   const DecodePlan p = decode_plan(sh.m, sh.n, sh.k);
+  if (dec_ring(sh.m, f8)) {
+    CHECK(p.S >= 1 && p.tiles == (N + kDecRows - 1) / kDecRows && p.tb == (M + 63) / 64, "plan");
+    if (dec_ring_tok(sh.m) == 32)
+      ring_shape<32>(M, N, K, p);
+    else
+      ring_shape<64>(M, N, K, p);
+    return;
+  }
   const int kMB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   const int kTok = 16 * kMB;
   const int steps = K / kDecStep;
@@ -515,6 +674,8 @@ int main() {
   big_band_checks<192, 8, 4>();
   big_band_checks<256, 8, 2>();
   big_band_checks<256, 8, 4>();
+  ring_config_checks<32>();
+  ring_config_checks<64>();
 
   // the workloads' prefill GEMMs (QKV, gate/up, down, LLM.int8()), replayed
   // at the edge tiles; ragged and split shapes replayed tile by tile
@@ -530,8 +691,9 @@ int main() {
 
   // decode: the workloads' token counts on both MLP projections, and ragged
   const int toks[] = {1, 2, 8, 15, 16, 17, 31, 32, 33, 48, 63, 64, 65, 96, 100, 128, 192, 255, 256};
-  const Shape layers[] = {{0, 14336, 4096}, {0, 4096, 14336}, {0, 6144, 4096}, {0, 512, 256},  {0, 28672, 4096},
-                          {0, 100, 128},    {0, 4100, 1152},  {0, 64, 128},    {0, 1, 128},    {0, 8192, 8192}};
+  const Shape layers[] = {{0, 14336, 4096}, {0, 4096, 14336}, {0, 6144, 4096}, {0, 512, 256},   {0, 28672, 4096},
+                          {0, 100, 128},    {0, 4100, 1152},  {0, 64, 128},    {0, 1, 128},     {0, 8192, 8192},
+                          {0, 28672, 8192}, {0, 16448, 8192}, {0, 14336, 14336}, {0, 8256, 4160}};
   for (int m : toks)
     for (const Shape& l : layers)
       for (int f8 = 0; f8 < 2; ++f8) decode_shape(Shape{m, l.n, l.k}, f8);

@@ -1,8 +1,9 @@
 """Parity of the decode-shaped GEMM (M <= 64 tokens, K a multiple of 128, and
 65..256 tokens where the decode kernel is chosen, one grid layer per 64).
 
-These shapes run the split-K decode kernel: per-slice int32 partial tiles in
-the workspace, ticket counters, the last workgroup of a tile reducing. The
+These shapes run the split-K decode kernel (its unrolled form up to 16
+tokens, its LDS-ring form from 17): per-slice int32 partial tiles in the
+workspace, ticket counters, the last workgroup of a tile reducing. The
 int32 accumulators must equal the oracle's exact integer product; dequantised
 outputs must be within 1 ulp of the oracle. Every call goes through the C ABI.
 """
@@ -51,6 +52,20 @@ def test_decode_int32_exact_wide(m, n, k):
     log("decode i32 wide", m, n, k, "ws", sq.raw["sq_w8a8_linear_workspace_size"](m, n, k))
     xq = workloads.uniform_int8((m, k), seed=m * 3 + n + k, stream=14)
     wq = workloads.uniform_int8((n, k), seed=m * 3 + n + k, stream=15)
+    acc = sq.sq_w8a8_linear(_dev_i8(xq), None, _dev_i8(wq), None, out_dtype=torch.int32)
+    assert np.array_equal(host(acc), oracle.int8_matmul(xq, wq))
+
+
+# K slices longer than the unrolled kernel's 32 steps: more column tiles than
+# the split's ticket counters, so K is not split (the 17..256-token ring form
+# loops over the whole K; fewer tokens route to the tiled kernels); 70B-style
+# layers (28672 x 8192), a ragged 257-tile layer, and two 64-token layers.
+@pytest.mark.parametrize("m,n,k", [(1, 28672, 8192), (8, 28672, 8192), (17, 16448, 8192), (32, 28672, 8192),
+                                   (64, 16448, 8192), (96, 14336, 14336)])
+def test_decode_long_slices_exact(m, n, k):
+    log("decode long slices", m, n, k, "ws", sq.raw["sq_w8a8_linear_workspace_size"](m, n, k))
+    xq = workloads.uniform_int8((m, k), seed=m + n + k, stream=16)
+    wq = workloads.uniform_int8((n, k), seed=m + n + k, stream=17)
     acc = sq.sq_w8a8_linear(_dev_i8(xq), None, _dev_i8(wq), None, out_dtype=torch.int32)
     assert np.array_equal(host(acc), oracle.int8_matmul(xq, wq))
 

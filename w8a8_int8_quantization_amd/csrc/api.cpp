@@ -81,11 +81,11 @@ sq_status quant_then_gemm(Quant quant, const int8_t* wq, const float* w_scale, i
   int8_t* xq = reinterpret_cast<int8_t*>(ws);
   float* dx = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + round_up((size_t)m * (size_t)k));
   void* gws = reinterpret_cast<char*>(ws) + round_up((size_t)m * (size_t)k) + round_up((size_t)m * 4);
-  if (sqh::gemm_decode_suits(m, n, k)) {
+  if (sqh::gemm_decode_suits(m, n, k, false)) {
     // the quantisation launch also clears the GEMM's split-K counters
     uint32_t* counters;
     int64_t ncount;
-    sqh::gemm_decode_counters(m, n, k, gws, &counters, &ncount);
+    sqh::gemm_decode_counters(m, n, k, false, gws, &counters, &ncount);
     hipError_t e = quant(xq, dx, counters, ncount);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(sqh::gemm_i8_decode(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, gws, s));
@@ -180,7 +180,7 @@ sq_status sq_quant_act_per_token(const void* x, sq_dtype xt, int64_t m, int64_t 
 
 size_t sq_w8a8_linear_workspace_size(int64_t m, int64_t n, int64_t k) {
   if (m <= 0 || n <= 0 || k <= 0 || k % 64 != 0) return 0;
-  if (sqh::gemm_decode_suits(m, n, k)) return sqh::gemm_decode_workspace(m, n, k);
+  if (sqh::gemm_decode_suits(m, n, k, false)) return sqh::gemm_decode_workspace(m, n, k, false);
   return sqh::gemm_big_workspace(m, n, k, false);
 }
 
@@ -223,7 +223,7 @@ sq_status sq_w8a8_linear(const int8_t* xq, const float* x_scale, const int8_t* w
   const hipStream_t s = (hipStream_t)stream;
   // decode shapes: the workspace's split-K counters are zero on entry (the
   // caller's contract) and restored to zero by the kernel
-  if (sqh::gemm_decode_suits(m, n, k))
+  if (sqh::gemm_decode_suits(m, n, k, false))
     return hip_status(sqh::gemm_i8_decode(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, ws, s));
   // prefill shapes split over K: the same contract for the tile counters
   return hip_status(sqh::gemm_i8(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, nullptr, ws, s));
@@ -250,7 +250,7 @@ sq_status sq_w8a8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const floa
   const hipStream_t s = (hipStream_t)stream;
   // one token on the weight-streaming path: one launch (the quantisation
   // runs inside the GEMM; the workspace is not touched)
-  if (sqh::gemm_decode_suits(m, n, k) && sqh::decode1_suits(m, n, k, xt))
+  if (sqh::decode1_suits(m, n, k, xt))
     return hip_status(sqh::decode1_linear(x, xt, smooth, wq, w_scale, n, k, y, yt, s));
   auto quant = [&](int8_t* xq, float* dx, uint32_t* zero, int64_t nzero) {
     return sqh::quant_rows(x, xt, m, k, ldx, smooth, nullptr, xq, dx, s, zero, nzero);
@@ -411,7 +411,7 @@ static sq_status check_fp8_gemm(const uint8_t* wq, const float* w_scale, int64_t
 
 size_t sq_fp8_linear_workspace_size(int64_t m, int64_t n, int64_t k) {
   if (m <= 0 || n <= 0 || k <= 0) return 0;
-  if (sqh::gemm_decode_suits(m, n, k)) return sqh::gemm_decode_workspace(m, n, k);
+  if (sqh::gemm_decode_suits(m, n, k, true)) return sqh::gemm_decode_workspace(m, n, k, true);
   return sqh::gemm_big_workspace(m, n, k, true);
 }
 
@@ -429,7 +429,7 @@ sq_status sq_fp8_linear(const uint8_t* xq, const float* x_scale, const uint8_t* 
   const hipStream_t s = (hipStream_t)stream;
   // decode shapes: the workspace's split-K counters are zero on entry (the
   // caller's contract) and restored to zero by the kernel
-  if (sqh::gemm_decode_suits(m, n, k))
+  if (sqh::gemm_decode_suits(m, n, k, true))
     return hip_status(sqh::gemm_f8_decode(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, ws, s));
   return hip_status(sqh::gemm_f8(xq, x_scale, wq, w_scale, m, n, k, y, yt, ldy, ws, s));
 }
@@ -453,11 +453,11 @@ sq_status sq_fp8_linear_dyn(const void* x, sq_dtype xt, int64_t ldx, const uint8
   float* dx = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + round_up((size_t)m * (size_t)k));
   void* gws = reinterpret_cast<char*>(ws) + round_up((size_t)m * (size_t)k) + round_up((size_t)m * 4);
   const hipStream_t s = (hipStream_t)stream;
-  if (sqh::gemm_decode_suits(m, n, k)) {
+  if (sqh::gemm_decode_suits(m, n, k, true)) {
     // the quantisation launch also clears the GEMM's split-K counters
     uint32_t* counters;
     int64_t ncount;
-    sqh::gemm_decode_counters(m, n, k, gws, &counters, &ncount);
+    sqh::gemm_decode_counters(m, n, k, true, gws, &counters, &ncount);
     hipError_t e = sqh::quant_f8_rows(x, xt, m, k, ldx, xq, dx, s, counters, ncount);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(sqh::gemm_f8_decode(xq, dx, wq, w_scale, m, n, k, y, yt, ldy, gws, s));

@@ -1,6 +1,8 @@
 // Decode-shaped int8 GEMM (M <= 64 tokens, and up to 256 where the tiled
 // kernels would cover few CUs): Y = dequant(Xq . Wq^T), where the cost is
-// streaming the weight matrix Wq [N x K] from HBM.
+// streaming the weight matrix Wq [N x K] from HBM. Two forms: the unrolled
+// register-pipeline kernel below (up to 16 tokens, and E4M3 operands), and
+// the LDS-ring kernel further down (int8, 17 tokens and more).
 //
 // The LLM.int8() page, "The architecture: every piece explained" (int8
 // operands, int32 accumulation, dequantisation by the product of the row
@@ -335,6 +337,182 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
   if (tid == 0) __hip_atomic_store(a.counter + ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---- LDS-ring form (int8, 17 tokens and more; index maps: sqi::RingCfg)
+//
+// With 32 or 64 tokens the register form spends its load bandwidth on
+// 64-byte pieces (its operand layout gives each row 4 lanes of 16 bytes per
+// instruction) and re-reads the whole token tile per wave. Here every
+// 128-byte k-step of the 64 Wq rows and the kTok Xq rows is one stage,
+// brought into LDS by direct-to-LDS transfers over whole 128-byte lines;
+// kRing - 1 stages are in flight while the four waves multiply the current
+// one, each wave its own 32-byte quarter of the step. Per stage and wave:
+// one vmcnt wait for the wave's own transfers of the stage, one barrier (all
+// waves' transfers landed; the slot of the stage before is free), the next
+// transfers into that slot, then the fragment reads and MFMAs.
+//
+// The kernel keeps a single LDS array (the ticket word at its end): with a
+// second LDS variable the accesses carry alias scopes, and the compiler then
+// waits for every transfer in flight before each fragment read.
+template <int kN>
+__device__ __forceinline__ void ring_wait_vm() {
+  __builtin_amdgcn_s_waitcnt((kN & 0xF) | ((kN >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// wait until at most `after` stages of kDma transfers are in flight (after
+// is wave-uniform, in [0, kMax])
+template <int kDma, int kMax, int kI = 0>
+__device__ __forceinline__ void ring_wait_stages(int after) {
+  if constexpr (kI >= kMax) {
+    ring_wait_vm<kMax * kDma>();
+  } else {
+    if (after == kI) {
+      ring_wait_vm<kI * kDma>();
+      return;
+    }
+    ring_wait_stages<kDma, kMax, kI + 1>(after);
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void_d;
+
+template <int kTok>
+__global__ __launch_bounds__(256, 1) void gemm_decode_ring_kernel(DecodeArgs a) {
+  using C = sqi::RingCfg<kTok>;
+  constexpr int kR = C::kRing;
+  static_assert((kR - 2) * C::kDma <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[C::kLds + 16];
+  uint32_t& last_ticket = *reinterpret_cast<uint32_t*>(smem + C::kLds);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tile = blockIdx.x, slice = blockIdx.y;
+  const int n0 = tile * C::kRows;
+  const int m0 = (int)blockIdx.z * 64;
+  const int ctr = (int)blockIdx.z * (int)gridDim.x + tile;
+  const sqi::DecSlice sl = sqi::dec_slice(slice, a.slice_steps, a.K);
+  const int nk = sl.nsl;
+
+  const int8_t* src[C::kDma];
+  int dst[C::kDma];
+#pragma unroll
+  for (int i = 0; i < C::kDma; ++i) {
+    const sqi::RingDma d = sqi::ring_dma<kTok>(i, wid, lane);
+    src[i] = d.w ? a.wq + sqi::big_dma_src(n0, d.row, a.N, a.K, sl.step0, d.chunk)
+                 : a.xq + sqi::big_dma_src(m0, d.row, a.M, a.K, sl.step0, d.chunk);
+    dst[i] = d.dst;
+  }
+  // stage s of the slice into ring slot b
+  auto issue = [&](int s, int b) {
+    int8_t* st = smem + b * C::kStage;
+    const int64_t koff = (int64_t)s * kDecStep;
+#pragma unroll
+    for (int i = 0; i < C::kDma; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + koff), (lds_void_d*)(st + dst[i]), 16, 0, 0);
+  };
+
+  int offw[C::kNB], offx[C::kMB];
+#pragma unroll
+  for (int bn = 0; bn < C::kNB; ++bn) offw[bn] = sqi::ring_frag_w<kTok>(bn, wid, lane);
+#pragma unroll
+  for (int bm = 0; bm < C::kMB; ++bm) offx[bm] = sqi::ring_frag_x<kTok>(bm, wid, lane);
+
+  v16i acc[C::kNB][C::kMB];
+#pragma unroll
+  for (int bn = 0; bn < C::kNB; ++bn)
+#pragma unroll
+    for (int bm = 0; bm < C::kMB; ++bm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[bn][bm][r] = 0;
+
+  int ib = 0;  // slot of the next transfer
+  for (int s = 0; s < kR - 1 && s < nk; ++s) {
+    issue(s, ib);
+    ib = ib + 1 == kR ? 0 : ib + 1;
+  }
+  int rb = 0;  // slot of stage s
+  for (int s = 0; s < nk; ++s) {
+    // stages s+1 .. min(s + kR - 2, nk - 1) may stay in flight
+    ring_wait_stages<C::kDma, kR - 2>(sqi::imin(kR - 2, nk - 1 - s));
+    lds_barrier();
+    if (s + kR - 1 < nk) {
+      issue(s + kR - 1, ib);
+      ib = ib + 1 == kR ? 0 : ib + 1;
+    }
+    const int8_t* st = smem + rb * C::kStage;
+    v4i fw[C::kNB], fx[C::kMB];
+#pragma unroll
+    for (int bn = 0; bn < C::kNB; ++bn) fw[bn] = *reinterpret_cast<const v4i*>(st + offw[bn]);
+#pragma unroll
+    for (int bm = 0; bm < C::kMB; ++bm) fx[bm] = *reinterpret_cast<const v4i*>(st + offx[bm]);
+#pragma unroll
+    for (int bn = 0; bn < C::kNB; ++bn)
+#pragma unroll
+      for (int bm = 0; bm < C::kMB; ++bm)
+        acc[bn][bm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[bn], fx[bm], acc[bn][bm], 0, 0, 0);
+    rb = rb + 1 == kR ? 0 : rb + 1;
+  }
+
+  // the four waves' k-quarters, added through LDS (the ring is free once
+  // every transfer has landed and every wave is past its last reads)
+  __syncthreads();
+  int32_t* red = reinterpret_cast<int32_t*>(smem);
+#pragma unroll
+  for (int bn = 0; bn < C::kNB; ++bn)
+#pragma unroll
+    for (int bm = 0; bm < C::kMB; ++bm)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const v4i v = {acc[bn][bm][4 * rg], acc[bn][bm][4 * rg + 1], acc[bn][bm][4 * rg + 2],
+                       acc[bn][bm][4 * rg + 3]};
+        *reinterpret_cast<v4i*>(red + 4 * (wid * C::kSlots + sqi::ring_slot<kTok>(bn, bm, rg, lane))) = v;
+      }
+  __syncthreads();
+  const int ml = sqi::ring_tok<kTok>(tid);
+  v4i sum[C::kNG];
+#pragma unroll
+  for (int g = 0; g < C::kNG; ++g) {
+    const int slot = sqi::ring_read_slot<kTok>(ml, sqi::ring_col<kTok>(tid, g));
+    v4i t = *reinterpret_cast<const v4i*>(red + 4 * slot);
+#pragma unroll
+    for (int w = 1; w < kDecWaves; ++w) t += *reinterpret_cast<const v4i*>(red + 4 * (w * C::kSlots + slot));
+    sum[g] = t;
+  }
+
+  if (a.S > 1) {
+    // Split K: publish this slice's tile, take a ticket; the last workgroup
+    // of the tile adds the other slices (device-coherent accesses, as in the
+    // unrolled kernel; int32 sums are exact in any order, so the own slice
+    // stays in registers)
+    const int nctr = (int)(gridDim.x * gridDim.z);
+    const uint32_t pbytes = (uint32_t)a.S * (uint32_t)nctr * C::kTileBytes;
+    const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(a.partial, (short)0, pbytes, kBufDword3);
+#pragma unroll
+    for (int g = 0; g < C::kNG; ++g)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          sum[g], pr, sqi::ring_partial_off(slice, nctr, ctr, g, tid, C::kTileBytes), 0, kCoherent);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+      last_ticket = __hip_atomic_fetch_add(a.counter + ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (last_ticket != (uint32_t)(a.S - 1)) return;
+    for (int s = 0; s < a.S; ++s) {
+      if (s == slice) continue;
+      v4i part[C::kNG];
+#pragma unroll
+      for (int g = 0; g < C::kNG; ++g)
+        part[g] = __builtin_amdgcn_raw_buffer_load_b128(
+            pr, sqi::ring_partial_off(s, nctr, ctr, g, tid, C::kTileBytes), 0, kCoherent);
+#pragma unroll
+      for (int g = 0; g < C::kNG; ++g) sum[g] += part[g];
+    }
+    // every ticket of this tile has been drawn: restore the counter
+    if (tid == 0) __hip_atomic_store(a.counter + ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int g = 0; g < C::kNG; ++g) {
+    const int32_t t[4] = {sum[g][0], sum[g][1], sum[g][2], sum[g][3]};
+    dec_epilogue<false>(a, m0 + ml, n0 + sqi::ring_col<kTok>(tid, g), t);
+  }
+}
+
 }  // namespace sqk
 
 namespace sqh {
@@ -374,24 +552,34 @@ hipError_t decode_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
     a.partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + kSplitCounterBytes);
   }
   const dim3 grid((unsigned)p.tiles, (unsigned)p.S, (unsigned)p.tb);
+  if (sqi::dec_ring(m, kF8)) {
+    if (sqi::dec_ring_tok(m) == 32)
+      hipLaunchKernelGGL((sqk::gemm_decode_ring_kernel<32>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((sqk::gemm_decode_ring_kernel<64>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   if (m <= 16) return launch_decode<1, kF8>(a, p.ns, grid, s);
-  if (m <= 32) return launch_decode<2, kF8>(a, p.ns, grid, s);
-  return launch_decode<4, kF8>(a, p.ns, grid, s);
+  if constexpr (kF8) {
+    if (m <= 32) return launch_decode<2, true>(a, p.ns, grid, s);
+    return launch_decode<4, true>(a, p.ns, grid, s);
+  }
+  return hipErrorInvalidValue;  // int8 beyond 16 tokens always takes the ring form
 }
 
 }  // namespace
 
-bool gemm_decode_suits(int64_t m, int64_t n, int64_t k) { return sqi::decode_suits(m, n, k); }
+bool gemm_decode_suits(int64_t m, int64_t n, int64_t k, bool f8) { return sqi::decode_suits(m, n, k, f8); }
 
-size_t gemm_decode_workspace(int64_t m, int64_t n, int64_t k) {
-  if (!gemm_decode_suits(m, n, k)) return 0;
-  return sqi::dec_workspace_bytes(decode_plan(m, n, k), m, n);
+size_t gemm_decode_workspace(int64_t m, int64_t n, int64_t k, bool f8) {
+  if (!gemm_decode_suits(m, n, k, f8)) return 0;
+  return sqi::dec_workspace_bytes(decode_plan(m, n, k), m, n, sqi::dec_ring(m, f8));
 }
 
-void gemm_decode_counters(int64_t m, int64_t n, int64_t k, void* ws, uint32_t** counters, int64_t* count) {
+void gemm_decode_counters(int64_t m, int64_t n, int64_t k, bool f8, void* ws, uint32_t** counters, int64_t* count) {
   *counters = nullptr;
   *count = 0;
-  if (!gemm_decode_suits(m, n, k)) return;
+  if (!gemm_decode_suits(m, n, k, f8)) return;
   const DecodePlan p = decode_plan(m, n, k);
   if (p.S == 1) return;
   *counters = reinterpret_cast<uint32_t*>(ws);

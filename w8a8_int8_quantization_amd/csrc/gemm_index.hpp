@@ -322,6 +322,94 @@ SQ_HD uint32_t dec_partial_off(int slice, int M, int N, int m, int n) {
   return (uint32_t)((((size_t)slice * M + m) * N + n) * 4);
 }
 
+// ---- decode, LDS-ring form (int8 operands, more than 16 tokens)
+//
+// A workgroup owns 64 rows of Wq and kTok tokens (32 or 64; one grid layer
+// per 64 tokens as above) over one K slice. Every 128-byte k-step of both
+// tiles is one stage of a ring of kRing LDS buffers, filled by direct-to-LDS
+// transfers whose 8 lanes per row fetch whole 128-byte lines (chunks
+// swizzled with big_swz, as in the prefill kernel); kRing - 1 stages are in
+// flight. The four waves take the four 32-byte k-quarters of every stage
+// (one v_mfma_i32_32x32x32_i8 per 32 x 32 block), and their int32 tiles are
+// added through LDS at the end, where each thread then owns kSpan
+// consecutive outputs of one token.
+constexpr int64_t kRingMinTokens = 17;
+template <int kTok>
+struct RingCfg {
+  static constexpr int kRows = kDecRows;
+  static constexpr int kStageW = kRows * kDecStep;             // Wq part of a stage
+  static constexpr int kStage = (kRows + kTok) * kDecStep;
+  static constexpr int kDmaW = kRows / (8 * kDecWaves);        // 1 KiB transfers per wave and stage
+  static constexpr int kDmaX = kTok / (8 * kDecWaves);
+  static constexpr int kDma = kDmaW + kDmaX;
+  static constexpr int kNB = kRows / 32;                       // 32 x 32 blocks per wave
+  static constexpr int kMB = kTok / 32;
+  static constexpr int kRing = kTok == 64 ? 4 : 6;             // stages in the ring
+  static constexpr int kSlots = kNB * kMB * 4 * 64;            // 16-byte accumulator slots per wave
+  static constexpr int kRedBytes = kDecWaves * kSlots * 16;
+  static constexpr int kLds = kRing * kStage > kRedBytes ? kRing * kStage : kRedBytes;
+  static constexpr int kTpt = 256 / kTok;                      // threads per token in the epilogue
+  static constexpr int kSpan = kRows / kTpt;                   // consecutive outputs per thread
+  static constexpr int kNG = kSpan / 4;                        // 4-output groups per thread
+  static constexpr uint32_t kTileBytes = (uint32_t)kNG * 256 * 16;  // one int32 partial tile
+};
+// Transfer i (0 .. kDma-1) of wave wid, lane: as big_dma, over the stage's
+// 64 Wq rows (w) then its kTok Xq rows.
+struct RingDma {
+  bool w;
+  int row, chunk, dst;
+};
+template <int kTok>
+SQ_HD RingDma ring_dma(int i, int wid, int lane) {
+  using C = RingCfg<kTok>;
+  RingDma d;
+  d.w = i < C::kDmaW;
+  const int blk = (d.w ? i : i - C::kDmaW) * kDecWaves + wid;
+  d.row = blk * 8 + (lane >> 3);
+  d.chunk = (lane & 7) ^ big_swz(d.row);
+  d.dst = (d.w ? 0 : C::kStageW) + blk * 1024;
+  return d;
+}
+// LDS offset within a stage of the fragment of block bn (Wq) or bm (Xq) that
+// lane reads for k-quarter q (its 16 bytes: chunk 2 q + lane / 32 of row
+// lane % 32 of the block).
+template <int kTok>
+SQ_HD int ring_frag_w(int bn, int q, int lane) {
+  return big_lds_off(32 * bn + (lane & 31), 2 * q + (lane >> 5));
+}
+template <int kTok>
+SQ_HD int ring_frag_x(int bm, int q, int lane) {
+  return RingCfg<kTok>::kStageW + big_lds_off(32 * bm + (lane & 31), 2 * q + (lane >> 5));
+}
+// Reduction slot (16 bytes, per wave) of register group rg of block (bn, bm)
+// at lane; it holds outputs n = 32 bn + 8 rg + 4 (lane / 32) .. +3 of token
+// 32 bm + lane % 32.
+template <int kTok>
+SQ_HD int ring_slot(int bn, int bm, int rg, int lane) {
+  return ((bn * RingCfg<kTok>::kMB + bm) * 4 + rg) * 64 + lane;
+}
+// Epilogue thread tid: its token within the tile, and the first of the four
+// outputs (within the tile's 64) of its group g.
+template <int kTok>
+SQ_HD int ring_tok(int tid) { return tid / RingCfg<kTok>::kTpt; }
+template <int kTok>
+SQ_HD int ring_col(int tid, int g) {
+  return (tid % RingCfg<kTok>::kTpt) * RingCfg<kTok>::kSpan + 4 * g;
+}
+// The slot that holds outputs nl .. nl + 3 (nl % 4 == 0) of token ml.
+template <int kTok>
+SQ_HD int ring_read_slot(int ml, int nl) {
+  const int nb = nl & 31;
+  return ring_slot<kTok>(nl >> 5, ml >> 5, nb >> 3, 32 * ((nb >> 2) & 1) + (ml & 31));
+}
+// Split K: partial tiles in thread order (slice, counter index ctr, group g,
+// thread), 16 bytes each, so that every store and load instruction of a
+// wave covers 1 KiB of consecutive bytes; padding rows and tokens travel
+// with the rest and never reach y.
+SQ_HD uint32_t ring_partial_off(int slice, int nctr, int ctr, int g, int tid, uint32_t tile_bytes) {
+  return ((uint32_t)slice * (uint32_t)nctr + (uint32_t)ctr) * tile_bytes + (uint32_t)(g * 256 + tid) * 16;
+}
+
 // ---- decode plan (host)
 
 struct DecodePlan {
@@ -354,19 +442,31 @@ inline DecodePlan decode_plan(int64_t m, int64_t n, int64_t k) {
   if (per > cap) per = cap;
   p.slice_steps = per;
   p.S = (steps + per - 1) / per;
-  // one ticket counter per column tile and token block, in the fixed region
+  // one ticket counter per column tile and token block, in the fixed region;
+  // without room for them K is not split, and the slice may then exceed the
+  // unrolled kernel's step range (see dec_ring / decode_suits)
   if (p.S > 1 && (int64_t)p.tiles * p.tb > kSplitMaxCounters) {
     p.S = 1;
     p.slice_steps = steps;
   }
-  p.ns = (per + kDecWaves - 1) / kDecWaves;
+  p.ns = (p.slice_steps + kDecWaves - 1) / kDecWaves;
   return p;
 }
 
+// Whether the LDS-ring form runs (int8 operands, more than 16 tokens), and
+// its token tile.
+inline bool dec_ring(int64_t m, bool f8) { return !f8 && m >= kRingMinTokens; }
+inline int dec_ring_tok(int64_t m) { return m <= 32 ? 32 : 64; }
+
 // Split-K workspace of a decode plan for m x n outputs: the counter region,
-// then S partial tiles [S][m][n] of int32 / binary32 (0 when not split).
-inline size_t dec_workspace_bytes(const DecodePlan& p, int64_t m, int64_t n) {
+// then the partial tiles (0 when not split): [S][m][n] of int32 / binary32
+// for the unrolled kernel, S x tiles x tb tiles of 64 x kTok int32 in
+// thread order for the ring form.
+inline size_t dec_workspace_bytes(const DecodePlan& p, int64_t m, int64_t n, bool ring = false) {
   if (p.S == 1) return 0;
+  if (ring)
+    return kSplitCounterBytes +
+           (size_t)p.S * (size_t)p.tiles * (size_t)p.tb * (size_t)dec_ring_tok(m) * (size_t)kDecRows * 4;
   return kSplitCounterBytes + (size_t)p.S * (size_t)m * (size_t)n * 4;
 }
 
@@ -388,12 +488,16 @@ inline bool decode_beats_prefill(int64_t m, int64_t n, int64_t k) {
   return units <= 128;
 }
 
-inline bool decode_suits(int64_t m, int64_t n, int64_t k) {
+inline bool decode_suits(int64_t m, int64_t n, int64_t k, bool f8) {
   if (!(m >= 1 && m <= kDecodeMaxM && n >= 1 && n <= INT32_MAX && k % kDecStep == 0)) return false;
-  // the partial tiles must fit 32-bit offsets (with the reducer's eight-slice
-  // rounds)
+  // the partial tiles must fit 32-bit offsets (with the unrolled kernel's
+  // eight-slice reducer rounds)
   const DecodePlan p = decode_plan(m, n, k);
   if ((size_t)(p.S + 7) / 8 * 8 * (size_t)m * (size_t)n * 4 >= ((size_t)1 << 31)) return false;
+  if (dec_workspace_bytes(p, m, n, true) >= ((size_t)1 << 31)) return false;
+  // the unrolled kernel covers at most kDecMaxNS steps per wave (the ring
+  // form loops over any slice)
+  if (!dec_ring(m, f8) && p.ns > kDecMaxNS) return false;
   if (m <= 64) return true;
   // beyond one 64-token block only where the prefill kernels get few tiles
   return decode_beats_prefill(m, n, k);

@@ -102,11 +102,12 @@ bool decode1_suits(int64_t m, int64_t n, int64_t k, sq_dtype xt);
 hipError_t decode1_linear(const void* x, sq_dtype xt, const float* smooth, const int8_t* wq, const float* w_scale,
                           int64_t n, int64_t k, void* y, sq_dtype yt, hipStream_t s);
 
-// Decode GEMM (M <= 64): split-K over workgroups, partial tiles and ticket
-// counters in the workspace. The counters must be zero at launch.
-bool gemm_decode_suits(int64_t m, int64_t n, int64_t k);
-size_t gemm_decode_workspace(int64_t m, int64_t n, int64_t k);
-void gemm_decode_counters(int64_t m, int64_t n, int64_t k, void* ws, uint32_t** counters, int64_t* count);
+// Decode GEMM (up to 256 tokens; f8: E4M3 operands, else int8): split-K over
+// workgroups, partial tiles and ticket counters in the workspace. The
+// counters must be zero at launch.
+bool gemm_decode_suits(int64_t m, int64_t n, int64_t k, bool f8);
+size_t gemm_decode_workspace(int64_t m, int64_t n, int64_t k, bool f8);
+void gemm_decode_counters(int64_t m, int64_t n, int64_t k, bool f8, void* ws, uint32_t** counters, int64_t* count);
 hipError_t gemm_i8_decode(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int64_t m,
                           int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, hipStream_t s);
 // The same decode GEMM on E4M3 operands (binary32 partial tiles in the same workspace layout).
