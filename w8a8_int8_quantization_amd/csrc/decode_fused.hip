@@ -51,26 +51,28 @@ struct Decode1Args {
   int out;              // 0 f32, 1 bf16, 2 f16
 };
 
-// kW waves of kNS 128-byte k-steps each (all loads in flight; K <= 128 kW
-// kNS) over kG 8-row groups of Wq; each thread keeps kC 16-byte vectors of
-// the row (16 / bytes per value, so K <= 64 kW x 16 values).
-template <class In, bool kSmooth, int kW, int kG, int kNS>
+// kW waves of kNS 128-byte k-steps each (all loads of a tile in flight; K <=
+// 128 kW kNS) over kG 8-row groups of Wq per tile, kR tiles one after the
+// other (the row is quantised once per workgroup; the next tile's loads go
+// out before the current tile's products); each thread keeps kC 16-byte
+// vectors of the row (16 / bytes per value, so K <= 64 kW x 16 values).
+template <class In, bool kSmooth, int kW, int kG, int kNS, int kR>
 __global__ __launch_bounds__(64 * kW, 1) void gemv_decode1_kernel(Decode1Args a) {
   constexpr int kT = 64 * kW;
   constexpr int V = In::kVec;
   constexpr int kC = 16 / V;
-  constexpr int kD1Rows = 8 * kG;  // Wq rows (outputs) of the workgroup
+  constexpr int kD1Rows = 8 * kG;  // Wq rows (outputs) of a tile
   constexpr int kD1Steps = kNS;
   constexpr int kMaxK = kT * kC * V;
   __shared__ __attribute__((aligned(16))) int8_t codes[kMaxK];
-  __shared__ int32_t red[kW][kD1Rows];
+  __shared__ int32_t red[2][kW][kD1Rows];
   __shared__ float red_f[kW];
   __shared__ int red_i[kW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
-  const int n0 = (int)blockIdx.x * kD1Rows;
+  const int nfirst = (int)blockIdx.x * kD1Rows * kR;
   const int K = a.K;
   const int nvec = K / V;
   const int nsteps = K / 128;
@@ -94,19 +96,24 @@ __global__ __launch_bounds__(64 * kW, 1) void gemv_decode1_kernel(Decode1Args a)
     }
   }
 
-  // ---- Wq: all kD1Steps steps of this wave for its row groups; steps past
-  // the end reload the last step (valid memory; their products are skipped)
+  // ---- Wq: all kD1Steps steps of this wave for the row groups of tile r
+  // (into register buffer buf); steps past the end reload the last step, and
+  // rows past N the last row (valid memory; their products are not stored)
   const int piece = 16 * (lane & 7);
-  const int8_t* wp[kG];
+  u32x4 wb[kR > 1 ? 2 : 1][kD1Steps][kG];
+  auto wload = [&](int r, int buf) {
+    const int n0 = nfirst + r * kD1Rows;
+    const int8_t* wp[kG];
 #pragma unroll
-  for (int g = 0; g < kG; ++g) wp[g] = a.wq + (int64_t)min(n0 + 8 * g + (lane >> 3), a.N - 1) * K + piece;
-  u32x4 wb[kD1Steps][kG];
+    for (int g = 0; g < kG; ++g) wp[g] = a.wq + (int64_t)min(n0 + 8 * g + (lane >> 3), a.N - 1) * K + piece;
 #pragma unroll
-  for (int i = 0; i < kD1Steps; ++i) {
-    const int64_t off = (int64_t)min(wid + kW * i, nsteps - 1) * 128;
+    for (int i = 0; i < kD1Steps; ++i) {
+      const int64_t off = (int64_t)min(wid + kW * i, nsteps - 1) * 128;
 #pragma unroll
-    for (int g = 0; g < kG; ++g) wb[i][g] = load16(wp[g] + off);
-  }
+      for (int g = 0; g < kG; ++g) wb[buf][i][g] = load16(wp[g] + off);
+    }
+  };
+  wload(0, 0);
   // keep the scheduler from moving the weight loads behind the quantisation
   __builtin_amdgcn_sched_barrier(0);
 
@@ -180,46 +187,81 @@ __global__ __launch_bounds__(64 * kW, 1) void gemv_decode1_kernel(Decode1Args a)
   }
   lds_barrier();
 
-  // ---- dot products: step i of this wave is k-step wid + kW i
-  int acc[kG];
+  // ---- dot products (step i of this wave is k-step wid + kW i), the 8
+  // lanes of a row, then the waves through LDS; with several tiles the next
+  // tile's loads go out first and the LDS partials are double-buffered (one
+  // barrier per tile, none of which waits for the loads in flight). The
+  // single-tile form is kept separate: folded into the loop, the 16-wave
+  // instance spilled a weight register and waited for every load first.
+  auto dots = [&](int buf, int* acc) {
 #pragma unroll
-  for (int g = 0; g < kG; ++g) acc[g] = 0;
+    for (int g = 0; g < kG; ++g) acc[g] = 0;
 #pragma unroll
-  for (int i = 0; i < kD1Steps; ++i) {
-    const int st = wid + kW * i;
-    if (st < nsteps) {
-      const u32x4 xv = *reinterpret_cast<const u32x4*>(&codes[st * 128 + piece]);
+    for (int i = 0; i < kD1Steps; ++i) {
+      const int st = wid + kW * i;
+      if (st < nsteps) {
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(&codes[st * 128 + piece]);
 #pragma unroll
-      for (int g = 0; g < kG; ++g) {
-        acc[g] = __builtin_amdgcn_sdot4((int)wb[i][g].x, (int)xv.x, acc[g], false);
-        acc[g] = __builtin_amdgcn_sdot4((int)wb[i][g].y, (int)xv.y, acc[g], false);
-        acc[g] = __builtin_amdgcn_sdot4((int)wb[i][g].z, (int)xv.z, acc[g], false);
-        acc[g] = __builtin_amdgcn_sdot4((int)wb[i][g].w, (int)xv.w, acc[g], false);
+        for (int g = 0; g < kG; ++g) {
+          acc[g] = __builtin_amdgcn_sdot4((int)wb[buf][i][g].x, (int)xv.x, acc[g], false);
+          acc[g] = __builtin_amdgcn_sdot4((int)wb[buf][i][g].y, (int)xv.y, acc[g], false);
+          acc[g] = __builtin_amdgcn_sdot4((int)wb[buf][i][g].z, (int)xv.z, acc[g], false);
+          acc[g] = __builtin_amdgcn_sdot4((int)wb[buf][i][g].w, (int)xv.w, acc[g], false);
+        }
       }
     }
-  }
-  // the 8 lanes of a row, then the waves
 #pragma unroll
-  for (int g = 0; g < kG; ++g) {
-    acc[g] += __shfl_xor(acc[g], 1);
-    acc[g] += __shfl_xor(acc[g], 2);
-    acc[g] += __shfl_xor(acc[g], 4);
-    if ((lane & 7) == 0) red[wid][8 * g + (lane >> 3)] = acc[g];
-  }
-  __syncthreads();
-  if (tid < kD1Rows) {
-    const int n = n0 + tid;
-    if (n < a.N) {
-      int32_t sum = red[0][tid];
+    for (int g = 0; g < kG; ++g) {
+      acc[g] += __shfl_xor(acc[g], 1);
+      acc[g] += __shfl_xor(acc[g], 2);
+      acc[g] += __shfl_xor(acc[g], 4);
+    }
+  };
+  auto store = [&](int n, int32_t sum) {
+    const float v = __fmul_rn(__fmul_rn((float)sum, d), a.w_scale[n]);
+    if (a.out == 0)
+      reinterpret_cast<float*>(a.y)[n] = v;
+    else if (a.out == 1)
+      reinterpret_cast<uint16_t*>(a.y)[n] = (uint16_t)f32_to_bf16(v);
+    else
+      reinterpret_cast<uint16_t*>(a.y)[n] = (uint16_t)f32_to_f16(v);
+  };
+  if constexpr (kR == 1) {
+    int acc[kG];
+    dots(0, acc);
 #pragma unroll
-      for (int w = 1; w < kW; ++w) sum += red[w][tid];
-      const float v = __fmul_rn(__fmul_rn((float)sum, d), a.w_scale[n]);
-      if (a.out == 0)
-        reinterpret_cast<float*>(a.y)[n] = v;
-      else if (a.out == 1)
-        reinterpret_cast<uint16_t*>(a.y)[n] = (uint16_t)f32_to_bf16(v);
-      else
-        reinterpret_cast<uint16_t*>(a.y)[n] = (uint16_t)f32_to_f16(v);
+    for (int g = 0; g < kG; ++g)
+      if ((lane & 7) == 0) red[0][wid][8 * g + (lane >> 3)] = acc[g];
+    __syncthreads();
+    if (tid < kD1Rows) {
+      const int n = nfirst + tid;
+      if (n < a.N) {
+        int32_t sum = red[0][0][tid];
+#pragma unroll
+        for (int w = 1; w < kW; ++w) sum += red[0][w][tid];
+        store(n, sum);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int buf = r & 1;
+      if (r + 1 < kR) wload(r + 1, buf ^ 1);
+      int acc[kG];
+      dots(buf, acc);
+#pragma unroll
+      for (int g = 0; g < kG; ++g)
+        if ((lane & 7) == 0) red[buf][wid][8 * g + (lane >> 3)] = acc[g];
+      lds_barrier();
+      if (tid < kD1Rows) {
+        const int n = nfirst + r * kD1Rows + tid;
+        if (n < a.N) {
+          int32_t sum = red[buf][0][tid];
+#pragma unroll
+          for (int w = 1; w < kW; ++w) sum += red[buf][w][tid];
+          store(n, sum);
+        }
+      }
     }
   }
 }
@@ -230,29 +272,64 @@ namespace sqh {
 
 namespace {
 
-// 4 waves of 8 steps and 8 rows per workgroup up to K = 4096, 8 waves of 8
-// steps up to 8192, 16 waves of 8 steps and 16 rows up to 16384. Measured on
-// MI355X, us per launch back to back over rotating weight copies, 4096 ->
-// 14336 layer (waves / rows per workgroup / steps per wave): 4/8/8 13.5,
-// 8/8/4 14.2, 8/16/4 13.8, 16/16/2 14.8, 16/32/2 14.2, 16/8/2 18.5; 14336 ->
-// 4096 layer: 16/16/8 15.2, 16/8/8 17.5 (two rounds of workgroups, each
-// quantising the row), 16/24/8 23.7 and 16/32/8 32.8 (registers spilled).
-// Without the quantisation the product alone takes 10.7-11.0 / 11.4 with 8
-// rows, and a plain stream of the same bytes 10.1-10.4: the row's
-// quantisation in every workgroup costs the rest. Publishing the codes from
-// one workgroup to the others through the workspace measured slower (15.6 /
-// 16.1: the publication adds two dependent memory round trips to every other
-// workgroup's path).
+// 4 waves of 8 steps and 8-row tiles up to K = 4096, 8 waves of 8 steps up
+// to 8192, 16 waves of 8 steps and 16-row tiles up to 16384. Measured on
+// MI355X, us per launch back to back over rotating weight copies, one tile
+// per workgroup, 4096 -> 14336 layer (waves / rows per workgroup / steps per
+// wave): 4/8/8 13.5, 8/8/4 14.2, 8/16/4 13.8, 16/16/2 14.8, 16/32/2 14.2,
+// 16/8/2 18.5; 14336 -> 4096 layer: 16/16/8 15.2, 16/8/8 17.5 (two rounds of
+// workgroups, each quantising the row), 16/24/8 23.7 and 16/32/8 32.8
+// (registers spilled). Without the quantisation the product alone takes
+// 10.7-11.0 / 11.4 with 8 rows, and a plain stream of the same bytes
+// 10.1-10.4: the row's quantisation in every workgroup costs the rest.
+// Publishing the codes from one workgroup to the others through the
+// workspace measured slower (15.6 / 16.1: the publication adds two dependent
+// memory round trips to every other workgroup's path).
+//
+// Several tiles per workgroup (the row quantised once, the next tile's loads
+// in flight during the current tile's products), up to K = 8192: kR tiles
+// per workgroup with the grid nearest 448 workgroups measured fastest or
+// within noise of it (us, one tile -> kR): 4096 -> 14336 14.2 -> 12.4 (kR
+// 4; kR 2, 3, 5, 6, 8: 13.5, 14.1, 13.6, 15.0, 14.3), 4096 -> 6144 8.1 ->
+// 7.5 (kR 2), 4096 -> 28672 22.8 -> 22.6 (kR 8), 8192 -> 14336 25.8 ->
+// 23.0 (kR 4), 8192 -> 28672 45.4 -> 41.0 (kR 8). The 16-wave form runs one
+// tile per workgroup (256 workgroups at 4096 columns already fill the CUs
+// once).
+inline int d1_tiles_per_wg(int64_t n, int rows) {
+  const int64_t tiles = (n + rows - 1) / rows;
+  int best = 1;
+  int64_t err = tiles > 448 ? tiles - 448 : 448 - tiles;
+  for (int r = 2; r <= 8; r *= 2) {
+    const int64_t wgs = (tiles + r - 1) / r;
+    const int64_t e = wgs > 448 ? wgs - 448 : 448 - wgs;
+    if (e < err) {
+      best = r;
+      err = e;
+    }
+  }
+  return best;
+}
+
+template <class In, bool kSmooth, int kW>
+void launch_d1_r(const sqk::Decode1Args& a, hipStream_t s) {
+  const int r = d1_tiles_per_wg(a.N, 8);
+  const unsigned grid = (unsigned)((a.N + 8 * r - 1) / (8 * r));
+  switch (r) {
+    case 1: hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, kW, 1, 8, 1>), dim3(grid), dim3(64 * kW), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, kW, 1, 8, 2>), dim3(grid), dim3(64 * kW), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, kW, 1, 8, 4>), dim3(grid), dim3(64 * kW), 0, s, a); break;
+    default: hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, kW, 1, 8, 8>), dim3(grid), dim3(64 * kW), 0, s, a); break;
+  }
+}
+
 template <class In, bool kSmooth>
 void launch_d1(const sqk::Decode1Args& a, hipStream_t s) {
   if (a.K <= 4096)
-    hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, 4, 1, 8>), dim3((unsigned)((a.N + 7) / 8)), dim3(256),
-                       0, s, a);
+    launch_d1_r<In, kSmooth, 4>(a, s);
   else if (a.K <= 8192)
-    hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, 8, 1, 8>), dim3((unsigned)((a.N + 7) / 8)), dim3(512),
-                       0, s, a);
+    launch_d1_r<In, kSmooth, 8>(a, s);
   else if constexpr (In::kVec == 8)  // binary32 rows stop at 8192 (decode1_suits)
-    hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, 16, 2, 8>), dim3((unsigned)((a.N + 15) / 16)),
+    hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, 16, 2, 8, 1>), dim3((unsigned)((a.N + 15) / 16)),
                        dim3(1024), 0, s, a);
 }
 
