@@ -141,11 +141,12 @@ def test_decode_workspace_validation():
 # of 16384). Up to K = 8192 a workgroup runs 1, 2, 4 or 8 tiles of 8 rows
 # (the grid nearest 448 workgroups): 2048 / 4096 columns one tile, 5000 /
 # 6150 two, 9600 / 12290 / 14336 four, 28672 / 28680 eight, ragged last
-# workgroups among them.
+# workgroups among them; beyond K = 8192 (16 waves) as many tiles as keep the
+# grid within 256 workgroups: 2056 / 4096 columns two, 12300 eight.
 ONE_TOKEN = [("bf16", 14336, 4096), ("bf16", 12300, 16384), ("f16", 12290, 1152), ("f32", 14336, 8192),
              ("f32", 12288, 128), ("bf16", 28672, 256), ("bf16", 4096, 14336), ("f16", 300, 1152),
              ("f32", 2050, 16384), ("bf16", 2048, 128), ("f16", 6150, 5120), ("bf16", 28680, 4096),
-             ("f32", 9600, 4096), ("f16", 5000, 8192)]
+             ("f32", 9600, 4096), ("f16", 5000, 8192), ("f16", 2056, 9216)]
 
 
 def _one_token_case(dtype, n, k, seed, smooth_kind):

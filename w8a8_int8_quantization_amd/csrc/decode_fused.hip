@@ -56,7 +56,10 @@ struct Decode1Args {
 // other (the row is quantised once per workgroup; the next tile's loads go
 // out before the current tile's products); each thread keeps kC 16-byte
 // vectors of the row (16 / bytes per value, so K <= 64 kW x 16 values).
-template <class In, bool kSmooth, int kW, int kG, int kNS, int kR>
+// kXFirst: the x and s loads complete before the first weight load goes out
+// (with 1024-thread workgroups the weight requests of every CU otherwise
+// queue in front of them, and the quantisation, which needs them, waits).
+template <class In, bool kSmooth, int kW, int kG, int kNS, int kR, bool kXFirst>
 __global__ __launch_bounds__(64 * kW, 1) void gemv_decode1_kernel(Decode1Args a) {
   constexpr int kT = 64 * kW;
   constexpr int V = In::kVec;
@@ -95,6 +98,8 @@ __global__ __launch_bounds__(64 * kW, 1) void gemv_decode1_kernel(Decode1Args a)
       }
     }
   }
+
+  if constexpr (kXFirst) __builtin_amdgcn_s_waitcnt(0);
 
   // ---- Wq: all kD1Steps steps of this wave for the row groups of tile r
   // (into register buffer buf); steps past the end reload the last step, and
@@ -292,9 +297,11 @@ namespace {
 // within noise of it (us, one tile -> kR): 4096 -> 14336 14.2 -> 12.4 (kR
 // 4; kR 2, 3, 5, 6, 8: 13.5, 14.1, 13.6, 15.0, 14.3), 4096 -> 6144 8.1 ->
 // 7.5 (kR 2), 4096 -> 28672 22.8 -> 22.6 (kR 8), 8192 -> 14336 25.8 ->
-// 23.0 (kR 4), 8192 -> 28672 45.4 -> 41.0 (kR 8). The 16-wave form runs one
-// tile per workgroup (256 workgroups at 4096 columns already fill the CUs
-// once).
+// 23.0 (kR 4), 8192 -> 28672 45.4 -> 41.0 (kR 8). The 16-wave form (one
+// workgroup per CU) takes as many 8-row tiles per workgroup as keep the grid
+// within 256, and waits for x and s before its weight loads: 14336 -> 4096
+// with 16-row tiles 15.0, two 8-row tiles 13.9, and with the x-first wait
+// 13.6 (the wait made no difference at 4096 -> 14336: 12.65 / 12.59).
 inline int d1_tiles_per_wg(int64_t n, int rows) {
   const int64_t tiles = (n + rows - 1) / rows;
   int best = 1;
@@ -310,15 +317,24 @@ inline int d1_tiles_per_wg(int64_t n, int rows) {
   return best;
 }
 
+// The 16-wave form (K above 8192) holds a whole CU: up to 256 workgroups,
+// as few tiles each as that allows.
+inline int d1_tiles_per_wg16(int64_t n) {
+  const int64_t tiles = (n + 7) / 8;
+  int r = 1;
+  while (r < 8 && (tiles + r - 1) / r > 256) r *= 2;
+  return r;
+}
+
 template <class In, bool kSmooth, int kW>
 void launch_d1_r(const sqk::Decode1Args& a, hipStream_t s) {
-  const int r = d1_tiles_per_wg(a.N, 8);
+  const int r = kW == 16 ? d1_tiles_per_wg16(a.N) : d1_tiles_per_wg(a.N, 8);
   const unsigned grid = (unsigned)((a.N + 8 * r - 1) / (8 * r));
   switch (r) {
-    case 1: hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, kW, 1, 8, 1>), dim3(grid), dim3(64 * kW), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, kW, 1, 8, 2>), dim3(grid), dim3(64 * kW), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, kW, 1, 8, 4>), dim3(grid), dim3(64 * kW), 0, s, a); break;
-    default: hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, kW, 1, 8, 8>), dim3(grid), dim3(64 * kW), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, kW, 1, 8, 1, kW == 16>), dim3(grid), dim3(64 * kW), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, kW, 1, 8, 2, kW == 16>), dim3(grid), dim3(64 * kW), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, kW, 1, 8, 4, kW == 16>), dim3(grid), dim3(64 * kW), 0, s, a); break;
+    default: hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, kW, 1, 8, 8, kW == 16>), dim3(grid), dim3(64 * kW), 0, s, a); break;
   }
 }
 
@@ -329,8 +345,7 @@ void launch_d1(const sqk::Decode1Args& a, hipStream_t s) {
   else if (a.K <= 8192)
     launch_d1_r<In, kSmooth, 8>(a, s);
   else if constexpr (In::kVec == 8)  // binary32 rows stop at 8192 (decode1_suits)
-    hipLaunchKernelGGL((sqk::gemv_decode1_kernel<In, kSmooth, 16, 2, 8, 1>), dim3((unsigned)((a.N + 15) / 16)),
-                       dim3(1024), 0, s, a);
+    launch_d1_r<In, kSmooth, 16>(a, s);
 }
 
 template <class In>
