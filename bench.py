@@ -1110,7 +1110,8 @@ def bench_linear(args, dev) -> dict:
 # decode projections at 1 and 64 tokens; the LLM.int8() layer), each timed
 # like the headline with fewer steps and a short oracle sample.
 EXTRA_CONFIGS = [("gateup_prefill", None, 30), ("down_prefill", None, 40), ("decode_up", 1, 200),
-                 ("decode_down", 1, 200), ("decode_up", 64, 200), ("decode_down", 64, 200), ("llm_int8", None, 40)]
+                 ("decode_down", 1, 200), ("decode_up", 8, 200), ("decode_down", 8, 200), ("decode_up", 32, 200),
+                 ("decode_down", 32, 200), ("decode_up", 64, 200), ("decode_down", 64, 200), ("llm_int8", None, 40)]
 
 
 def config_records(args, dev) -> list:
