@@ -222,8 +222,8 @@ __global__ __launch_bounds__(64 * kW, 1) void gemv_decode1_kernel(Decode1Args a)
       acc[g] += __shfl_xor(acc[g], 4);
     }
   };
-  auto store = [&](int n, int32_t sum) {
-    const float v = __fmul_rn(__fmul_rn((float)sum, d), a.w_scale[n]);
+  auto store = [&](int n, int32_t sum, float ws) {
+    const float v = __fmul_rn(__fmul_rn((float)sum, d), ws);
     if (a.out == 0)
       reinterpret_cast<float*>(a.y)[n] = v;
     else if (a.out == 1)
@@ -244,13 +244,17 @@ __global__ __launch_bounds__(64 * kW, 1) void gemv_decode1_kernel(Decode1Args a)
         int32_t sum = red[0][0][tid];
 #pragma unroll
         for (int w = 1; w < kW; ++w) sum += red[0][w][tid];
-        store(n, sum);
+        store(n, sum, a.w_scale[n]);
       }
     }
   } else {
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
       const int buf = r & 1;
+      // the tile's channel scale first: a load issued after the next tile's
+      // weight loads would make the epilogue wait for all of them
+      const int ns = min(nfirst + r * kD1Rows + (tid < kD1Rows ? tid : 0), a.N - 1);
+      const float wsc = a.w_scale[ns];
       if (r + 1 < kR) wload(r + 1, buf ^ 1);
       int acc[kG];
       dots(buf, acc);
@@ -264,7 +268,7 @@ __global__ __launch_bounds__(64 * kW, 1) void gemv_decode1_kernel(Decode1Args a)
           int32_t sum = red[buf][0][tid];
 #pragma unroll
           for (int w = 1; w < kW; ++w) sum += red[buf][w][tid];
-          store(n, sum);
+          store(n, sum, wsc);
         }
       }
     }
