@@ -74,8 +74,8 @@ def decode_steps_per_wave(m: int, n: int, k: int) -> int:
 
 
 def decode_ring(m: int, f8: bool = False) -> bool:
-    """Whether the decode GEMM runs its LDS-ring form (int8, 17 tokens and more)."""
-    return not f8 and m >= 17
+    """Whether the decode GEMM runs its LDS-ring form (17 tokens and more, int8 and E4M3)."""
+    return m >= 17
 
 
 def decode_kernel_runs(m: int, n: int, k: int, f8: bool = False) -> bool:
@@ -606,7 +606,8 @@ def bench_fp8(args, dev):
                 "ops_per_launch": ops}
     # the E4M3 forms of the decode kernel and of the prefill kernel, or the 128 x 128 kernel
     big = big_kernel_suits(c.m, c.n, c.k)
-    kfile, kname = (("gemm_decode.hip", "gemm_decode_kernel<kMB, kNS, kF8=true>") if decode else
+    kfile, kname = (("gemm_decode.hip", "gemm_decode_ring_kernel<kTok, kF8=true>" if decode_ring(c.m, True)
+                     else "gemm_decode_kernel<kMB, kNS, kF8=true>") if decode else
                     ("gemm_big.hip", "gemm_big_kernel<BN, bf16, kVec, kF8=true>") if big else
                     ("gemm_f8.hip", "gemm_f8_kernel"))
     roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": pmc_traffic(args.workload, kfile),

@@ -442,6 +442,59 @@ static void ring_config_checks() {
     }
   for (int v : wseen) CHECK(v == 1, "w chunk read %d times", v);
   for (int v : xseen) CHECK(v == 1, "x chunk read %d times", v);
+  // E4M3 fragments: wave w reads chunks 4 (w & 1) + 2 (lane / 32) + half of
+  // the rows of Wq block w >> 1 (each Wq chunk once) and of every Xq block
+  // (each Xq chunk twice: both Wq blocks' waves)
+  std::fill(wseen.begin(), wseen.end(), 0);
+  std::fill(xseen.begin(), xseen.end(), 0);
+  for (int wid = 0; wid < kDecWaves; ++wid)
+    for (int lane = 0; lane < 64; ++lane)
+      for (int half = 0; half < 2; ++half) {
+        const int chunk = 4 * (wid & 1) + 2 * (lane >> 5) + half;
+        const int offw = ring_f8_frag_w<kTok>(wid, lane, half);
+        CHECK(offw >= 0 && offw + 16 <= C::kStageW && offw % 16 == 0, "f8 w frag off %d", offw);
+        if (offw >= 0 && offw + 16 <= C::kStageW) {
+          const Tag& t = lds[offw / 16];
+          const int row = 32 * (wid >> 1) + (lane & 31);
+          CHECK(t.op == 1 && t.row == row && t.chunk == chunk, "f8 w frag finds (%d,%d,%d)", t.op, t.row, t.chunk);
+          ++wseen[(size_t)row * 8 + chunk];
+        }
+        for (int bm = 0; bm < C::kMB; ++bm) {
+          const int offx = ring_f8_frag_x<kTok>(bm, wid, lane, half);
+          CHECK(offx >= C::kStageW && offx + 16 <= C::kStage && offx % 16 == 0, "f8 x frag off %d", offx);
+          if (offx < C::kStageW || offx + 16 > C::kStage) continue;
+          const Tag& t = lds[offx / 16];
+          const int row = 32 * bm + (lane & 31);
+          CHECK(t.op == 0 && t.row == row && t.chunk == chunk, "f8 x frag finds (%d,%d,%d)", t.op, t.row, t.chunk);
+          ++xseen[(size_t)row * 8 + chunk];
+        }
+      }
+  for (int v : wseen) CHECK(v == 1, "f8 w chunk read %d times", v);
+  for (int v : xseen) CHECK(v == 2, "f8 x chunk read %d times", v);
+  // E4M3 reduction slots: what each holds; outputs read from waves 2 bn, 2 bn + 1
+  std::vector<int> holds8((size_t)kDecWaves * C::kSlotsF8, -1);
+  for (int wid = 0; wid < kDecWaves; ++wid)
+    for (int bm = 0; bm < C::kMB; ++bm)
+      for (int rg = 0; rg < 4; ++rg)
+        for (int lane = 0; lane < 64; ++lane) {
+          const int slot = ring_f8_slot<kTok>(bm, rg, lane);
+          CHECK(slot >= 0 && slot < C::kSlotsF8, "f8 slot %d", slot);
+          if (slot < 0 || slot >= C::kSlotsF8) continue;
+          int& h = holds8[(size_t)wid * C::kSlotsF8 + slot];
+          CHECK(h == -1, "f8 slot written twice");
+          h = (32 * bm + (lane & 31)) * 64 + 32 * (wid >> 1) + 8 * rg + 4 * (lane >> 5);
+        }
+  CHECK(C::kLds >= kDecWaves * C::kSlotsF8 * 16, "f8 reduction fits");
+  for (int tid = 0; tid < 256; ++tid)
+    for (int g = 0; g < C::kNG; ++g) {
+      const int ml = ring_tok<kTok>(tid), nl = ring_col<kTok>(tid, g);
+      const int slot = ring_f8_read_slot<kTok>(ml, nl);
+      const int w0 = 2 * (nl >> 5);
+      CHECK(slot >= 0 && slot < C::kSlotsF8 && w0 + 1 < kDecWaves, "f8 read slot %d", slot);
+      if (slot < 0 || slot >= C::kSlotsF8 || w0 + 1 >= kDecWaves) continue;
+      for (int w = w0; w < w0 + 2; ++w)
+        CHECK(holds8[(size_t)w * C::kSlotsF8 + slot] == ml * 64 + nl, "f8 read slot content");
+    }
   // reduction slots: what each holds, and where the epilogue reads
   std::vector<int> holds(C::kSlots, -1);  // token * 64 + first output
   for (int bn = 0; bn < C::kNB; ++bn)

@@ -1,8 +1,8 @@
 // Decode-shaped int8 GEMM (M <= 64 tokens, and up to 256 where the tiled
 // kernels would cover few CUs): Y = dequant(Xq . Wq^T), where the cost is
 // streaming the weight matrix Wq [N x K] from HBM. Two forms: the unrolled
-// register-pipeline kernel below (up to 16 tokens, and E4M3 operands), and
-// the LDS-ring kernel further down (int8, 17 tokens and more).
+// register-pipeline kernel below (up to 16 tokens), and the LDS-ring kernel
+// further down (17 tokens and more); both take int8 and E4M3 operands.
 //
 // The LLM.int8() page, "The architecture: every piece explained" (int8
 // operands, int32 accumulation, dequantisation by the product of the row
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_kernel(DecodeArgs a) {
   if (tid == 0) __hip_atomic_store(a.counter + ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ---- LDS-ring form (int8, 17 tokens and more; index maps: sqi::RingCfg)
+// ---- LDS-ring form (17 tokens and more; index maps: sqi::RingCfg)
 //
 // With 32 or 64 tokens the register form spends its load bandwidth on
 // 64-byte pieces (its operand layout gives each row 4 lanes of 16 bytes per
@@ -373,8 +373,13 @@ __device__ __forceinline__ void ring_wait_stages(int after) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void_d;
+typedef float v16f_d __attribute__((ext_vector_type(16)));
 
-template <int kTok>
+// kF8: E4M3 operands; each wave takes one 64-byte k-half of every stage for
+// one Wq block (sqi::ring_f8_*), binary32 accumulators. The two k-halves of
+// an output are added in a fixed order (wave 2 bn, then 2 bn + 1), and the
+// S slices' partial tiles in slice order, so results are deterministic.
+template <int kTok, bool kF8>
 __global__ __launch_bounds__(256, 1) void gemm_decode_ring_kernel(DecodeArgs a) {
   using C = sqi::RingCfg<kTok>;
   constexpr int kR = C::kRing;
@@ -407,15 +412,22 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_ring_kernel(DecodeArgs a) 
       __builtin_amdgcn_global_load_lds((const void*)(src[i] + koff), (lds_void_d*)(st + dst[i]), 16, 0, 0);
   };
 
-  int offw[C::kNB], offx[C::kMB];
+  constexpr int kNBW = kF8 ? 1 : C::kNB;  // Wq blocks per wave
+  int offw[kNBW][kF8 ? 2 : 1], offx[C::kMB][kF8 ? 2 : 1];
 #pragma unroll
-  for (int bn = 0; bn < C::kNB; ++bn) offw[bn] = sqi::ring_frag_w<kTok>(bn, wid, lane);
+  for (int h = 0; h < (kF8 ? 2 : 1); ++h) {
 #pragma unroll
-  for (int bm = 0; bm < C::kMB; ++bm) offx[bm] = sqi::ring_frag_x<kTok>(bm, wid, lane);
+    for (int bn = 0; bn < kNBW; ++bn)
+      offw[bn][h] = kF8 ? sqi::ring_f8_frag_w<kTok>(wid, lane, h) : sqi::ring_frag_w<kTok>(bn, wid, lane);
+#pragma unroll
+    for (int bm = 0; bm < C::kMB; ++bm)
+      offx[bm][h] = kF8 ? sqi::ring_f8_frag_x<kTok>(bm, wid, lane, h) : sqi::ring_frag_x<kTok>(bm, wid, lane);
+  }
 
-  v16i acc[C::kNB][C::kMB];
+  using AccT = typename std::conditional<kF8, v16f_d, v16i>::type;
+  AccT acc[kNBW][C::kMB];
 #pragma unroll
-  for (int bn = 0; bn < C::kNB; ++bn)
+  for (int bn = 0; bn < kNBW; ++bn)
 #pragma unroll
     for (int bm = 0; bm < C::kMB; ++bm)
 #pragma unroll
@@ -436,50 +448,78 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_ring_kernel(DecodeArgs a) 
       ib = ib + 1 == kR ? 0 : ib + 1;
     }
     const int8_t* st = smem + rb * C::kStage;
-    v4i fw[C::kNB], fx[C::kMB];
+    if constexpr (kF8) {
+      auto frag = [&](const int* off) {
+        const v4i lo = *reinterpret_cast<const v4i*>(st + off[0]);
+        const v4i hi = *reinterpret_cast<const v4i*>(st + off[1]);
+        return v8i_d{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      };
+      const v8i_d fw = frag(offw[0]);
+      v8i_d fx[C::kMB];
 #pragma unroll
-    for (int bn = 0; bn < C::kNB; ++bn) fw[bn] = *reinterpret_cast<const v4i*>(st + offw[bn]);
-#pragma unroll
-    for (int bm = 0; bm < C::kMB; ++bm) fx[bm] = *reinterpret_cast<const v4i*>(st + offx[bm]);
-#pragma unroll
-    for (int bn = 0; bn < C::kNB; ++bn)
+      for (int bm = 0; bm < C::kMB; ++bm) fx[bm] = frag(offx[bm]);
 #pragma unroll
       for (int bm = 0; bm < C::kMB; ++bm)
-        acc[bn][bm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[bn], fx[bm], acc[bn][bm], 0, 0, 0);
+        acc[0][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw, fx[bm], acc[0][bm], 0, 0, 0, 127, 0, 127);
+    } else {
+      v4i fw[C::kNB], fx[C::kMB];
+#pragma unroll
+      for (int bn = 0; bn < C::kNB; ++bn) fw[bn] = *reinterpret_cast<const v4i*>(st + offw[bn][0]);
+#pragma unroll
+      for (int bm = 0; bm < C::kMB; ++bm) fx[bm] = *reinterpret_cast<const v4i*>(st + offx[bm][0]);
+#pragma unroll
+      for (int bn = 0; bn < C::kNB; ++bn)
+#pragma unroll
+        for (int bm = 0; bm < C::kMB; ++bm)
+          acc[bn][bm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[bn], fx[bm], acc[bn][bm], 0, 0, 0);
+    }
     rb = rb + 1 == kR ? 0 : rb + 1;
   }
 
-  // the four waves' k-quarters, added through LDS (the ring is free once
-  // every transfer has landed and every wave is past its last reads)
+  // the waves' k-parts, added through LDS (the ring is free once every
+  // transfer has landed and every wave is past its last reads): int8, the
+  // four k-quarters of each output; E4M3, its two k-halves in wave order
   __syncthreads();
   int32_t* red = reinterpret_cast<int32_t*>(smem);
+  constexpr int kSlots = kF8 ? C::kSlotsF8 : C::kSlots;
 #pragma unroll
-  for (int bn = 0; bn < C::kNB; ++bn)
+  for (int bn = 0; bn < kNBW; ++bn)
 #pragma unroll
-    for (int bm = 0; bm < C::kMB; ++bm)
+    for (int bm = 0; bm < C::kMB; ++bm) {
+      const v16i bits = __builtin_bit_cast(v16i, acc[bn][bm]);
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const v4i v = {acc[bn][bm][4 * rg], acc[bn][bm][4 * rg + 1], acc[bn][bm][4 * rg + 2],
-                       acc[bn][bm][4 * rg + 3]};
-        *reinterpret_cast<v4i*>(red + 4 * (wid * C::kSlots + sqi::ring_slot<kTok>(bn, bm, rg, lane))) = v;
+        const v4i v = {bits[4 * rg], bits[4 * rg + 1], bits[4 * rg + 2], bits[4 * rg + 3]};
+        const int slot = kF8 ? sqi::ring_f8_slot<kTok>(bm, rg, lane) : sqi::ring_slot<kTok>(bn, bm, rg, lane);
+        *reinterpret_cast<v4i*>(red + 4 * (wid * kSlots + slot)) = v;
       }
+    }
   __syncthreads();
   const int ml = sqi::ring_tok<kTok>(tid);
-  v4i sum[C::kNG];
+  v4i sum[C::kNG];  // int32 sums, or the bits of binary32 sums
 #pragma unroll
   for (int g = 0; g < C::kNG; ++g) {
-    const int slot = sqi::ring_read_slot<kTok>(ml, sqi::ring_col<kTok>(tid, g));
-    v4i t = *reinterpret_cast<const v4i*>(red + 4 * slot);
+    const int nl = sqi::ring_col<kTok>(tid, g);
+    if constexpr (kF8) {
+      const int slot = sqi::ring_f8_read_slot<kTok>(ml, nl);
+      const int w0 = 2 * (nl >> 5);
+      v4f_d t = __builtin_bit_cast(v4f_d, *reinterpret_cast<const v4i*>(red + 4 * (w0 * kSlots + slot)));
+      t += __builtin_bit_cast(v4f_d, *reinterpret_cast<const v4i*>(red + 4 * ((w0 + 1) * kSlots + slot)));
+      sum[g] = __builtin_bit_cast(v4i, t);
+    } else {
+      const int slot = sqi::ring_read_slot<kTok>(ml, nl);
+      v4i t = *reinterpret_cast<const v4i*>(red + 4 * slot);
 #pragma unroll
-    for (int w = 1; w < kDecWaves; ++w) t += *reinterpret_cast<const v4i*>(red + 4 * (w * C::kSlots + slot));
-    sum[g] = t;
+      for (int w = 1; w < kDecWaves; ++w) t += *reinterpret_cast<const v4i*>(red + 4 * (w * kSlots + slot));
+      sum[g] = t;
+    }
   }
 
   if (a.S > 1) {
     // Split K: publish this slice's tile, take a ticket; the last workgroup
-    // of the tile adds the other slices (device-coherent accesses, as in the
+    // of the tile adds the slices (device-coherent accesses, as in the
     // unrolled kernel; int32 sums are exact in any order, so the own slice
-    // stays in registers)
+    // stays in registers; E4M3 partials are added in slice order)
     const int nctr = (int)(gridDim.x * gridDim.z);
     const uint32_t pbytes = (uint32_t)a.S * (uint32_t)nctr * C::kTileBytes;
     const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(a.partial, (short)0, pbytes, kBufDword3);
@@ -493,15 +533,34 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_ring_kernel(DecodeArgs a) 
       last_ticket = __hip_atomic_fetch_add(a.counter + ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (last_ticket != (uint32_t)(a.S - 1)) return;
-    for (int s = 0; s < a.S; ++s) {
-      if (s == slice) continue;
-      v4i part[C::kNG];
+    if constexpr (kF8) {
+      // all S partial tiles in slice order (this slice's from registers)
+      v4f_d tot[C::kNG];
 #pragma unroll
-      for (int g = 0; g < C::kNG; ++g)
-        part[g] = __builtin_amdgcn_raw_buffer_load_b128(
-            pr, sqi::ring_partial_off(s, nctr, ctr, g, tid, C::kTileBytes), 0, kCoherent);
+      for (int g = 0; g < C::kNG; ++g) tot[g] = v4f_d{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < a.S; ++s) {
+        v4i part[C::kNG];
 #pragma unroll
-      for (int g = 0; g < C::kNG; ++g) sum[g] += part[g];
+        for (int g = 0; g < C::kNG; ++g)
+          part[g] = s == slice ? sum[g]
+                               : __builtin_amdgcn_raw_buffer_load_b128(
+                                     pr, sqi::ring_partial_off(s, nctr, ctr, g, tid, C::kTileBytes), 0, kCoherent);
+#pragma unroll
+        for (int g = 0; g < C::kNG; ++g) tot[g] += __builtin_bit_cast(v4f_d, part[g]);
+      }
+#pragma unroll
+      for (int g = 0; g < C::kNG; ++g) sum[g] = __builtin_bit_cast(v4i, tot[g]);
+    } else {
+      for (int s = 0; s < a.S; ++s) {
+        if (s == slice) continue;
+        v4i part[C::kNG];
+#pragma unroll
+        for (int g = 0; g < C::kNG; ++g)
+          part[g] = __builtin_amdgcn_raw_buffer_load_b128(
+              pr, sqi::ring_partial_off(s, nctr, ctr, g, tid, C::kTileBytes), 0, kCoherent);
+#pragma unroll
+        for (int g = 0; g < C::kNG; ++g) sum[g] += part[g];
+      }
     }
     // every ticket of this tile has been drawn: restore the counter
     if (tid == 0) __hip_atomic_store(a.counter + ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -509,7 +568,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_ring_kernel(DecodeArgs a) 
 #pragma unroll
   for (int g = 0; g < C::kNG; ++g) {
     const int32_t t[4] = {sum[g][0], sum[g][1], sum[g][2], sum[g][3]};
-    dec_epilogue<false>(a, m0 + ml, n0 + sqi::ring_col<kTok>(tid, g), t);
+    dec_epilogue<kF8>(a, m0 + ml, n0 + sqi::ring_col<kTok>(tid, g), t);
   }
 }
 
@@ -554,17 +613,13 @@ hipError_t decode_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
   const dim3 grid((unsigned)p.tiles, (unsigned)p.S, (unsigned)p.tb);
   if (sqi::dec_ring(m, kF8)) {
     if (sqi::dec_ring_tok(m) == 32)
-      hipLaunchKernelGGL((sqk::gemm_decode_ring_kernel<32>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((sqk::gemm_decode_ring_kernel<32, kF8>), grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((sqk::gemm_decode_ring_kernel<64>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((sqk::gemm_decode_ring_kernel<64, kF8>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
   }
   if (m <= 16) return launch_decode<1, kF8>(a, p.ns, grid, s);
-  if constexpr (kF8) {
-    if (m <= 32) return launch_decode<2, true>(a, p.ns, grid, s);
-    return launch_decode<4, true>(a, p.ns, grid, s);
-  }
-  return hipErrorInvalidValue;  // int8 beyond 16 tokens always takes the ring form
+  return hipErrorInvalidValue;  // beyond 16 tokens the ring form always runs
 }
 
 }  // namespace

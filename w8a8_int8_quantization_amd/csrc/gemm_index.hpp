@@ -322,7 +322,7 @@ SQ_HD uint32_t dec_partial_off(int slice, int M, int N, int m, int n) {
   return (uint32_t)((((size_t)slice * M + m) * N + n) * 4);
 }
 
-// ---- decode, LDS-ring form (int8 operands, more than 16 tokens)
+// ---- decode, LDS-ring form (more than 16 tokens)
 //
 // A workgroup owns 64 rows of Wq and kTok tokens (32 or 64; one grid layer
 // per 64 tokens as above) over one K slice. Every 128-byte k-step of both
@@ -347,6 +347,7 @@ struct RingCfg {
   static constexpr int kRing = kTok == 64 ? 4 : 6;             // stages in the ring
   static constexpr int kSlots = kNB * kMB * 4 * 64;            // 16-byte accumulator slots per wave
   static constexpr int kRedBytes = kDecWaves * kSlots * 16;
+  static constexpr int kSlotsF8 = kMB * 4 * 64;                // E4M3: one Wq block per wave
   static constexpr int kLds = kRing * kStage > kRedBytes ? kRing * kStage : kRedBytes;
   static constexpr int kTpt = 256 / kTok;                      // threads per token in the epilogue
   static constexpr int kSpan = kRows / kTpt;                   // consecutive outputs per thread
@@ -402,6 +403,31 @@ SQ_HD int ring_read_slot(int ml, int nl) {
   const int nb = nl & 31;
   return ring_slot<kTok>(nl >> 5, ml >> 5, nb >> 3, 32 * ((nb >> 2) & 1) + (ml & 31));
 }
+// E4M3 form: wave w takes the 64-byte k-half kh = w & 1 of every stage for
+// Wq block bn = w >> 1, one v_mfma_scale_f32_32x32x64_f8f6f4 per token
+// block; a lane's 32-byte fragment is chunks 4 kh + 2 (lane / 32) and the
+// next one of row lane % 32 of the block (half 0 / 1).
+SQ_HD int ring_f8_chunk(int wid, int lane, int half) { return 4 * (wid & 1) + 2 * (lane >> 5) + half; }
+template <int kTok>
+SQ_HD int ring_f8_frag_w(int wid, int lane, int half) {
+  return big_lds_off(32 * (wid >> 1) + (lane & 31), ring_f8_chunk(wid, lane, half));
+}
+template <int kTok>
+SQ_HD int ring_f8_frag_x(int bm, int wid, int lane, int half) {
+  return RingCfg<kTok>::kStageW + big_lds_off(32 * bm + (lane & 31), ring_f8_chunk(wid, lane, half));
+}
+// Reduction slot (per wave) of register group rg of token block bm at lane:
+// outputs n = 32 bn + 8 rg + 4 (lane / 32) .. +3 of token 32 bm + lane % 32,
+// bn the wave's Wq block. Outputs nl .. nl + 3 of token ml are the sum of
+// this slot in waves 2 (nl / 32) and 2 (nl / 32) + 1, in that order.
+template <int kTok>
+SQ_HD int ring_f8_slot(int bm, int rg, int lane) { return (bm * 4 + rg) * 64 + lane; }
+template <int kTok>
+SQ_HD int ring_f8_read_slot(int ml, int nl) {
+  const int nb = nl & 31;
+  return ring_f8_slot<kTok>(ml >> 5, nb >> 3, 32 * ((nb >> 2) & 1) + (ml & 31));
+}
+
 // Split K: partial tiles in thread order (slice, counter index ctr, group g,
 // thread), 16 bytes each, so that every store and load instruction of a
 // wave covers 1 KiB of consecutive bytes; padding rows and tokens travel
@@ -453,9 +479,12 @@ inline DecodePlan decode_plan(int64_t m, int64_t n, int64_t k) {
   return p;
 }
 
-// Whether the LDS-ring form runs (int8 operands, more than 16 tokens), and
-// its token tile.
-inline bool dec_ring(int64_t m, bool f8) { return !f8 && m >= kRingMinTokens; }
+// Whether the LDS-ring form runs (more than 16 tokens, int8 or E4M3
+// operands), and its token tile.
+inline bool dec_ring(int64_t m, bool f8) {
+  (void)f8;
+  return m >= kRingMinTokens;
+}
 inline int dec_ring_tok(int64_t m) { return m <= 32 ? 32 : 64; }
 
 // Split-K workspace of a decode plan for m x n outputs: the counter region,
