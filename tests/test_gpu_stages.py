@@ -172,6 +172,39 @@ def test_quant_act_range_fallbacks(dtype):
     assert np.array_equal(host(dx), dx_ref) and np.array_equal(host(xq), xq_ref)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("nvec", [256, 512, 1024])
+@pytest.mark.parametrize("m", [1030, 2050])
+@pytest.mark.parametrize("smooth", [False, True])
+def test_quant_act_full_rows(dtype, nvec, m, smooth):
+    """Prefill rows of exactly 1, 2 or 4 16-byte vectors per thread (the
+    full-row kernel, a workgroup visiting one to three rows): zero rows, rows
+    outside the fast-division range (all tiny; huge), tiny entries inside
+    normal rows, exact .5 quotients, every row checked bit for bit."""
+    k = nvec * (4 if dtype == "f32" else 8)
+    log("quant full rows", dtype, m, k, smooth)
+    rng = np.random.default_rng(m + k + int(smooth))
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    x[:, ::97] *= np.float32(20.0)                          # outlier columns
+    x[1] = 0
+    x[2] *= np.float32(1e-7 if dtype == "f16" else 1e-35)   # whole row tiny: d < 2^-30
+    if dtype != "f16":
+        x[3] *= np.float32(1e25)                            # max > 2^50
+    x[4, ::3] *= np.float32(1e-30 if dtype != "f16" else 1e-6)
+    x[5, :] = 0
+    x[5, 0] = 127.0
+    x[5, 1:9] = [0.5, 1.5, 2.5, -0.5, -2.5, 125.5, -126.5, 64.5]
+    x[m - 1] = 0
+    xr = oracle.round_bf16(x) if dtype == "bf16" else (x.astype(np.float16).astype(np.float32) if dtype == "f16" else x)
+    s_ref = np.exp(rng.uniform(-3, 3, k)).astype(np.float32) if smooth else None
+    if smooth:
+        s_ref[5] = np.float32(1.0)
+    xq, dx = sq.sq_quant_act_per_token(to_dev(xr, dtype), None if s_ref is None else torch.from_numpy(s_ref).to(dev()))
+    xq_ref, dx_ref = oracle.quantize_activations(xr, s_ref)
+    assert np.array_equal(host(dx), dx_ref)
+    assert np.array_equal(host(xq), xq_ref)
+
+
 @pytest.mark.parametrize("k,nout", [(512, 3), (4096, 8), (8192, 0)])
 def test_quant_rows_masked_prefill_kernel(k, nout):
     cfg = workloads.decomp_case(seed=k + nout, m=200, k=k, n=64, n_outlier_cols=nout)

@@ -353,6 +353,151 @@ __global__ __launch_bounds__(kT) void quant_rows_kernel(const uint8_t* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// Rows that fill the workgroup exactly (kCh 16-byte vectors per thread, no
+// outlier mask): the prefill shapes' rows. The same arithmetic as
+// quant_rows_kernel, in fewer instructions per element:
+//  * the row loop is unrolled twice, so the current row and the prefetched
+//    next one live in fixed registers (no copies between rows);
+//  * every load is unconditional (the last row of a workgroup prefetches
+//    itself again), so the compiler's wait counts are exact;
+//  * the row scale d = RN(amax / 127) is Markstein's quotient with the
+//    constant RN(1/127) (exact in the checked range, like every other
+//    quotient here) instead of an IEEE division.
+// Rows outside the fast range take the IEEE path of quant_rows_kernel.
+constexpr float kRcp127 = 0x1.020408p-7f;  // RN(1/127)
+
+template <class In, int kCh, bool kSmooth>
+__global__ __launch_bounds__(256) void quant_rows_full_kernel(const uint8_t* __restrict__ x, int64_t m,
+                                                              int64_t ldx_bytes, const float* __restrict__ smooth,
+                                                              int8_t* __restrict__ xq, float* __restrict__ x_scale,
+                                                              uint32_t* __restrict__ zero, int nzero) {
+  constexpr int kT = 256, kW = 4;
+  constexpr int V = In::kVec;
+  constexpr int64_t k = (int64_t)kCh * kT * V;
+  __shared__ float red[2][kW];
+  __shared__ int any_bad[kW];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int64_t grid = gridDim.x;
+
+  auto load_row = [&](int64_t r, u32x4* raw) {
+    const uint8_t* xr = x + r * ldx_bytes;
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) raw[c] = load16(xr + (int64_t)(tid + kT * c) * 16);
+  };
+  u32x4 buf_a[kCh], buf_b[kCh];
+  load_row(blockIdx.x, buf_a);  // grid <= m
+  if (blockIdx.x == 0)
+    for (int i = tid; i < nzero; i += kT) zero[i] = 0u;
+
+  float sreg[kSmooth ? kCh : 1][V];
+  float rreg[kSmooth ? kCh : 1][V];
+  bool s_ok = true;
+  if constexpr (kSmooth) {
+    int bad = 0;
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) {
+#pragma unroll
+      for (int e = 0; e < V; e += 4) {
+        const u32x4 sv = load16(smooth + (int64_t)(tid + kT * c) * V + e);
+        sreg[c][e] = __uint_as_float(sv.x); sreg[c][e + 1] = __uint_as_float(sv.y);
+        sreg[c][e + 2] = __uint_as_float(sv.z); sreg[c][e + 3] = __uint_as_float(sv.w);
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        rreg[c][e] = rcp_rn(sreg[c][e]);  // used only when every s_j is in the fast range
+        bad |= !(sreg[c][e] >= kFastSMin && sreg[c][e] <= kFastSMax);
+      }
+    }
+    const int wbad = __any(bad);
+    if (lane == 0) any_bad[wid] = wbad;
+    lds_barrier();
+    int anyb = 0;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) anyb |= any_bad[w];
+    s_ok = !anyb;
+  }
+  const bool s_ok_u = __builtin_amdgcn_readfirstlane((int)s_ok) != 0;
+
+  int parity = 0;
+  auto block_amax = [&](float v) {
+    v = wave_max(v);
+    if (lane == 0) red[parity][wid] = v;
+    lds_barrier();
+    float r = red[parity][0];
+#pragma unroll
+    for (int w = 1; w < kW; ++w) r = fmaxf(r, red[parity][w]);
+    parity ^= 1;
+    return r;
+  };
+  // x / s of the row held in raw: Markstein quotients (fast) or IEEE division
+  auto smooth_row = [&](const u32x4* raw, float (*f)[V], bool fast) {
+    float amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) {
+      In::unpack(raw[c], f[c]);
+      if constexpr (kSmooth) {
+        if (fast) {
+#pragma unroll
+          for (int e = 0; e < V; ++e) f[c][e] = div_mk(f[c][e], sreg[c][e], rreg[c][e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < V; ++e) f[c][e] = f[c][e] / sreg[c][e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) amax = fmaxf(amax, fabsf(f[c][e]));
+    }
+    return amax;
+  };
+  auto emit = [&](int8_t* qr, const float (*f)[V], auto quot) {
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) {
+      uint32_t code[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) code[e] = q_code(quot(f[c][e]));
+      int8_t* dst = qr + (int64_t)(tid + kT * c) * V;
+      if constexpr (V == 8)
+        *reinterpret_cast<uint2*>(dst) =
+            make_uint2(pack4(code[0], code[1], code[2], code[3]), pack4(code[4], code[5], code[6], code[7]));
+      else
+        *reinterpret_cast<uint32_t*>(dst) = pack4(code[0], code[1], code[2], code[3]);
+    }
+  };
+  auto body = [&](const u32x4* cur, u32x4* nxt, int64_t row) {
+    load_row(row + grid < m ? row + grid : row, nxt);
+    float f[kCh][V];
+    float amax = block_amax(smooth_row(cur, f, s_ok_u));
+    float d = div_mk(amax, (float)kQMax, kRcp127);
+    const bool fast = s_ok_u && d >= kFastDMin && amax <= kFastAMax;
+    int8_t* qr = xq + row * k;
+    if (fast) {
+      const float rd = rcp_scale(d);
+      emit(qr, f, [&](float v) { return div_mk(v, d, rd); });
+    } else {
+      // the whole row again with IEEE quotients (the Markstein ones may be
+      // inexact outside the checked range)
+      if (s_ok_u && kSmooth) amax = block_amax(smooth_row(cur, f, false));
+      d = amax / (float)kQMax;
+      if (d > 0.f)
+        emit(qr, f, [&](float v) { return v / d; });
+      else
+        emit(qr, f, [](float) { return 0.f; });
+    }
+    if (tid == 0) x_scale[row] = d;
+  };
+  for (int64_t row = blockIdx.x;;) {
+    body(buf_a, buf_b, row);
+    row += grid;
+    if (row >= m) break;
+    body(buf_b, buf_a, row);
+    row += grid;
+    if (row >= m) break;
+  }
+}
+
 }  // namespace sqk
 
 namespace sqh {
@@ -389,6 +534,20 @@ static void launch_quant(const void* x, int64_t m, int64_t k, int64_t ldx, const
     return;
   }
   const int64_t per_thread = (nvec + 255) / 256;
+  // rows of exactly 1, 2 or 4 vectors per thread: the full-row kernel
+  if (!kMask && nvec == per_thread * 256 && (per_thread == 1 || per_thread == 2 || per_thread == 4)) {
+    const int64_t grid = m < 1024 ? m : 1024;
+    if (per_thread == 1)
+      hipLaunchKernelGGL((sqk::quant_rows_full_kernel<In, 1, kSmooth>), dim3((unsigned)grid), dim3(256), 0, s, xb, m,
+                         ldb, smooth, xq, x_scale, zero, nzero);
+    else if (per_thread == 2)
+      hipLaunchKernelGGL((sqk::quant_rows_full_kernel<In, 2, kSmooth>), dim3((unsigned)grid), dim3(256), 0, s, xb, m,
+                         ldb, smooth, xq, x_scale, zero, nzero);
+    else
+      hipLaunchKernelGGL((sqk::quant_rows_full_kernel<In, 4, kSmooth>), dim3((unsigned)grid), dim3(256), 0, s, xb, m,
+                         ldb, smooth, xq, x_scale, zero, nzero);
+    return;
+  }
   if (per_thread <= 1)
     launch_rows<In, 1, 256, kSmooth, kMask>(xb, m, nvec, ldb, smooth, mask, xq, x_scale, s, zero, nzero);
   else if (per_thread <= 2)
