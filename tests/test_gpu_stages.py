@@ -127,7 +127,7 @@ def test_quant_act_prefill_kernel(dtype, k, smooth):
     assert np.array_equal(host(xq), xq_ref)
 
 
-@pytest.mark.parametrize("m,k", [(3, 16384), (1, 4096), (64, 8192), (1100, 4096), (1030, 16384)])
+@pytest.mark.parametrize("m,k", [(3, 16384), (1, 4096), (64, 8192), (1100, 4096), (1030, 16384), (1100, 14336)])
 @pytest.mark.parametrize("hi_exp", [20, 21])
 def test_quant_act_smooth_spread(m, k, hi_exp):
     """Smoothing factors with random significands over every binade of the
@@ -173,12 +173,13 @@ def test_quant_act_range_fallbacks(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
-@pytest.mark.parametrize("nvec", [256, 512, 1024])
+@pytest.mark.parametrize("nvec", [256, 512, 1024, 1792])
 @pytest.mark.parametrize("m", [1030, 2050])
 @pytest.mark.parametrize("smooth", [False, True])
 def test_quant_act_full_rows(dtype, nvec, m, smooth):
-    """Prefill rows of exactly 1, 2 or 4 16-byte vectors per thread (the
-    full-row kernel, a workgroup visiting one to three rows): zero rows, rows
+    """Prefill rows of exactly 1, 2 or 4 16-byte vectors per thread of 256, or
+    4 per thread of 448 (the full-row kernel, a workgroup visiting one to five
+    rows): zero rows, rows
     outside the fast-division range (all tiny; huge), tiny entries inside
     normal rows, exact .5 quotients, every row checked bit for bit."""
     k = nvec * (4 if dtype == "f32" else 8)
