@@ -260,6 +260,16 @@ static void big_shape_checks(const Shape& sh, const BigSplit& p, bool f8, int el
               const int64_t lim = d.a ? a_bytes : b_bytes;
               CHECK(off >= 0 && off + 16 <= lim, "transfer at %lld of %lld (tile %d, stage %d)", (long long)off,
                     (long long)lim, t, kt);
+              // the kernel's form: a buffer resource over the tile's valid
+              // rows, a fixed lane offset and the stage's scalar offset
+              const int tile_row0 = d.a ? m0 : n0;
+              const int valid = big_tile_rows(tile_row0, d.a ? M : N, d.a ? kBigBM : BN);
+              const int64_t voff = big_dma_voff(d.row, valid, K, d.chunk), soff = big_dma_soff(kt);
+              const int64_t rbytes = (int64_t)valid * K;
+              CHECK(valid >= 1 && rbytes < (1ll << 31), "tile resource of %lld bytes", (long long)rbytes);
+              CHECK(voff >= 0 && soff >= 0 && voff + soff + 16 <= rbytes, "buffer transfer at %lld of %lld",
+                    (long long)(voff + soff), (long long)rbytes);
+              CHECK((int64_t)tile_row0 * K + voff + soff == off, "buffer transfer misaddressed (tile %d)", t);
               // a real row reads its own row and stage
               const int row = (d.a ? m0 : n0) + d.row;
               if (row < (d.a ? M : N))

@@ -115,6 +115,14 @@ __device__ __forceinline__ void store4(void* y, int64_t off, const float* v, con
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// 16 bytes per lane from a buffer resource into LDS at M0 + 16 lane (the
+// builtin exists only in the device compilation).
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, lds_void* dst, int voff, int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+#endif
+}
+
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
@@ -157,23 +165,33 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
   const int nk = slice.nk;
 
   // ---- direct-to-LDS transfers: lane L of a 1 KiB transfer fills LDS bytes
-  // [16L, 16L+16) of an 8-row block (sqi::big_dma)
-  const int8_t* src[C::kDma];
+  // [16L, 16L+16) of an 8-row block (sqi::big_dma), read through buffer
+  // resources over the tile's rows of Xq and Wq: the lane's offset is fixed,
+  // the stage is a scalar offset and the LDS destination a scalar (M0), so a
+  // transfer costs no vector instructions (with per-lane 64-bit addresses
+  // and a readfirstlane for M0 each one held up its wave's matrix-core issue)
+  const int uwid = __builtin_amdgcn_readfirstlane(wid);
+  const int rows_a = sqi::big_tile_rows(m0, M, kBigBM), rows_b = sqi::big_tile_rows(n0, N, BN);
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)m0 * K), (short)0, rows_a * K, kBigBufDword3);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(B + (int64_t)n0 * K), (short)0, rows_b * K, kBigBufDword3);
+  int voff[C::kDma];
   int dst[C::kDma];
 #pragma unroll
   for (int i = 0; i < C::kDma; ++i) {
-    const sqi::BigDma d = sqi::big_dma<BN, kW>(i, wid, lane);
-    src[i] = d.a ? A + sqi::big_dma_src(m0, d.row, M, K, kt0, d.chunk) : B + sqi::big_dma_src(n0, d.row, N, K, kt0, d.chunk);
+    const sqi::BigDma d = sqi::big_dma<BN, kW>(i, uwid, lane);
+    voff[i] = sqi::big_dma_voff(d.row, d.a ? rows_a : rows_b, K, d.chunk);
     dst[i] = d.dst;
   }
-  auto kbyte = [&](int kt) -> int64_t { return (int64_t)kt * kBigBK; };
   auto stage_ptr = [&](int kt) { return smem + (kt & 1) * C::kStage; };
+  auto dma_one = [&](int kt, int i) {
+    buffer_load_lds16(i < C::kDmaA ? ra : rb, (lds_void*)(stage_ptr(kt) + dst[i]), voff[i],
+                      sqi::big_dma_soff(kt0 + kt));
+  };
   auto issue = [&](int kt) {
-    int8_t* stage = stage_ptr(kt);
-    const int64_t koff = kbyte(kt);
 #pragma unroll
-    for (int i = 0; i < C::kDma; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(src[i] + koff), (lds_void*)(stage + dst[i]), 16, 0, 0);
+    for (int i = 0; i < C::kDma; ++i) dma_one(kt, i);
   };
 
   AccT acc[C::kFN][C::kFM];
@@ -242,10 +260,6 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
   // per MFMA of the last substep, so the address unit works while the matrix
   // cores do (issued in one burst they stall the wave for hundreds of cycles).
   constexpr int kQ = C::kFN * C::kFM > C::kDma ? C::kFN * C::kFM : C::kDma;
-  auto dma_one = [&](int kt, int i) {
-    __builtin_amdgcn_global_load_lds((const void*)(src[i] + kbyte(kt)), (lds_void*)(stage_ptr(kt) + dst[i]), 16, 0,
-                                     0);
-  };
   auto frag_one = [&](const int8_t* stage, int ks, int q, FragT* xf, FragT* wf) {
     if (q < C::kFM)
       xf[q] = frag(stage, sqi::big_frag_row<BN, kW>(wm, q, frow), ks);

@@ -130,6 +130,16 @@ SQ_HD int64_t big_dma_src(int tile_row0, int row, int rows, int K, int kt, int c
   return (int64_t)imin(tile_row0 + row, rows - 1) * K + (int64_t)kt * kBigBK + chunk * 16;
 }
 
+// The same transfers through a buffer resource over the tile's rows of the
+// operand (based at row tile_row0, valid_rows = big_tile_rows(...) whole rows
+// long): the lane's fixed offset (its row, clamped to the last valid row, and
+// chunk) plus the stage's scalar offset, so the loop advances one scalar per
+// stage. tile_row0 * K + big_dma_voff(...) + big_dma_soff(kt) equals
+// big_dma_src(tile_row0, row, rows, K, kt, chunk).
+SQ_HD int big_tile_rows(int tile_row0, int rows, int tile) { return imin(rows - tile_row0, tile); }
+SQ_HD int big_dma_voff(int row, int valid_rows, int K, int chunk) { return imin(row, valid_rows - 1) * K + chunk * 16; }
+SQ_HD int big_dma_soff(int kt) { return kt * kBigBK; }
+
 // Tile row of fragment i of wave row wm (the lane's row frow = lane % 32).
 template <int BN, int kW>
 SQ_HD int big_frag_row(int wm, int i, int frow) {
