@@ -147,11 +147,13 @@ def parse():
     p.add_argument("--fetch-scale", type=float, default=1.9999,
                    help="FETCH_SIZE scale factor from the copy probe (profiles/hbm_counter_scale_copy.md)")
     p.add_argument("--write-scale", type=float, default=1.0, help="WRITE_SIZE scale factor from the copy probe")
-    p.add_argument("--probe", choices=["mfma", "stream", "lds", "fp8sum"], default=None,
+    p.add_argument("--probe", choices=["mfma", "stream", "lds", "ldsbw", "gemmparts", "fp8sum"], default=None,
                    help="only run one measurement probe (libsq_probes.so) and print its JSON line: mfma = "
                         "int8 matrix-core rate and shader clock with constant and changing operands; stream = "
                         "single-kernel streaming read / read+write ceilings at the workloads' sizes; lds = "
-                        "fragment-read rate of the prefill GEMM's LDS pattern beside the MFMA rate; fp8sum = "
+                        "fragment-read rate of the prefill GEMM's LDS pattern beside the MFMA rate; ldsbw = LDS read "
+                        "throughput by instruction width; gemmparts = the prefill GEMM's main loop taken apart "
+                        "(MFMAs, fragment reads, barriers, stage transfers); fp8sum = "
                         "summation error of the E4M3 matrix instructions against exact sums")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain device-to-device copy of 512 MiB (5 times), the known-size "
@@ -181,7 +183,8 @@ def probe_lib():
     lib = ctypes.CDLL(path)
     P, I, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     for name, argt in (("sqp_mfma_rate", [P, P, I, I, I, P]), ("sqp_stream", [P, L, P, L, P, I, I, P]),
-                       ("sqp_lds_rate", [P, P, I, I, I, P]), ("sqp_fp8_mfma", [P, P, P, I, I, P])):
+                       ("sqp_lds_rate", [P, P, I, I, I, P]), ("sqp_fp8_mfma", [P, P, P, I, I, P]),
+                       ("sqp_lds_bw", [P, P, I, I, I, I, I, I, P]), ("sqp_gemm_parts", [P, P, I, I, I, P, L, P])):
         fn = getattr(lib, name)
         fn.argtypes = argt
         fn.restype = I
@@ -311,6 +314,47 @@ def run_probe(args):
         out["setup"] = (f"{blocks} workgroups x 8 waves (two per SIMD), 64 KiB LDS; per iteration and wave 5 "
                         "ds_read_b128 fragment reads in the prefill GEMM's swizzled 128-byte-row pattern and/or "
                         "6 v_mfma_i32_32x32x32_i8 with constant operands (the kernel's 5 reads per 6 MFMAs)")
+    elif args.probe == "ldsbw":
+        blocks, iters = 256, 4096
+        res = {}
+        for pattern, pname in ((0, "linear"), (1, "gemm_fragments")):
+            for threads in (512, 1024):
+                for nbytes, reads in ((16, 4), (16, 8), (8, 8), (8, 16), (4, 16)):
+                    cyc = torch.zeros(blocks * 16, dtype=torch.int64, device=dev)
+                    sink = torch.zeros(blocks * threads, dtype=torch.int32, device=dev)
+                    launch = lambda: lib.sqp_lds_bw(cyc.data_ptr(), sink.data_ptr(), blocks, threads, iters, nbytes,
+                                                    reads, pattern, stream())
+                    _probe_time(torch, launch, 2)
+                    cmax = float(cyc.view(blocks, 16)[:, : threads // 64].max().item())
+                    per_cu = threads * iters * reads * nbytes
+                    res[f"{pname}_b{nbytes * 8}_reads{reads}_waves{threads // 64}"] = {
+                        "bytes_per_clk_per_cu": per_cu / cmax, "cycles": cmax}
+        out["results"] = res
+        out["setup"] = (f"{blocks} workgroups of 8 or 16 waves, 64 KiB LDS; each lane reads 16, 8 or 4 bytes per "
+                        "instruction, 4 to 16 independent reads in flight per wave and one wait per round; bytes "
+                        "per shader clock per CU from each wave's s_memtime (the slowest wave)")
+    elif args.probe == "gemmparts":
+        blocks, stages = 256, 2000
+        kstage = 57344
+        src = torch.empty(blocks * 16 * kstage, dtype=torch.int8, device=dev).fill_(1)
+        names = ("mfma_only", "plus_fragment_reads", "plus_barrier", "plus_transfers_global_load_lds",
+                 "plus_transfers_buffer_resource", "buffer_transfers_no_l2_reuse")
+        res = {}
+        for mode, name in enumerate(names):
+            cyc = torch.zeros(blocks * 8, dtype=torch.int64, device=dev)
+            sink = torch.zeros(blocks * 512, dtype=torch.int32, device=dev)
+            launch = lambda: lib.sqp_gemm_parts(cyc.data_ptr(), sink.data_ptr(), blocks, stages, mode, src.data_ptr(),
+                                                src.numel(), stream())
+            _probe_time(torch, launch, 2)
+            cmax = float(cyc.max().item())
+            per_mfma = cmax / (2.0 * stages * 24)  # two waves per SIMD, 24 MFMAs per wave and stage
+            res[name] = {"cycles_per_mfma_per_simd": per_mfma, "frac_of_matrix_core_rate": 32.0 / per_mfma}
+        out["results"] = res
+        out["setup"] = (f"{blocks} workgroups x 8 waves (two per SIMD), the prefill GEMM's stage structure at "
+                        "256 x 192 tiles: per 128-byte stage 4 substeps of 6 v_mfma_i32_32x32x32_i8 per wave "
+                        "(32 shader clocks each at the full rate), then fragment reads, one barrier per stage, and "
+                        "the stage's 56 KiB of direct-to-LDS transfers added one at a time; the transfer sources "
+                        "are L2-resident except in the last case")
     else:
         res = {}
         tiles = 4096

@@ -1,7 +1,9 @@
 // Measurement probes of the gfx950 ceilings that bound the int8 path: the
 // matrix-core rate and shader clock with constant or changing operands, a
 // plain streaming read/write kernel, the LDS fragment-read rate beside the
-// MFMA rate, and the summation error of the FP8 (E4M3) matrix instructions.
+// MFMA rate, the LDS read throughput by instruction width, the MFMA rate of
+// the prefill GEMM's main loop taken apart (fragment reads, barriers, stage
+// transfers), and the summation error of the FP8 (E4M3) matrix instructions.
 //
 // None of this is part of the linear layer: the benchmark loads this library
 // (libsq_probes.so) only in its probe modes. Every entry point launches on
@@ -210,6 +212,166 @@ __global__ __launch_bounds__(64) void fp8_mfma_kernel(const uint8_t* __restrict_
   }
 }
 
+// ---- LDS read throughput: every lane reads kB bytes per instruction, kR
+// independent reads per wave in flight, one wait per round; pattern 0: lanes
+// consecutive in a 1 KiB block, 1: the prefill GEMM's fragment reads (32 rows
+// of 128 bytes, chunk XOR (row >> 1) & 7, the lane halves in adjacent chunks).
+// cycles: 16 x blocks (s_memtime per wave), sink: blockDim x blocks.
+template <int kB, int kR>
+__global__ __launch_bounds__(1024) void lds_bw_kernel(int64_t* cycles, int32_t* sink, int iters, int pattern) {
+  __shared__ __attribute__((aligned(16))) int8_t lds[65536];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  for (int i = tid; i < 65536 / 4; i += blockDim.x) reinterpret_cast<uint32_t*>(lds)[i] = mix((uint32_t)i);
+  __syncthreads();
+  int off[kR];
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int blk = (wid * kR + r) & 63;
+    int o;
+    if (pattern == 0) {
+      o = blk * 1024 + lane * kB;
+    } else {
+      const int row = lane & 31, c = (2 * (r & 3) + (lane >> 5)) ^ ((row >> 1) & 7);
+      o = (blk & 15) * 4096 + row * 128 + c * 16;
+    }
+    off[r] = o & 65535;
+  }
+  int acc = 0;
+  __syncthreads();
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+    const int shift = (it & 7) * 64;
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int o = (off[r] + shift) & (65535 & ~(kB - 1));
+      if constexpr (kB == 16) {
+        const v4i v = *reinterpret_cast<const v4i*>(lds + o);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+      } else if constexpr (kB == 8) {
+        const int2 v = *reinterpret_cast<const int2*>(lds + o);
+        acc ^= v.x ^ v.y;
+      } else {
+        acc ^= *reinterpret_cast<const int*>(lds + o);
+      }
+    }
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  if (lane == 0) cycles[blockIdx.x * 16 + wid] = (int64_t)(t1 - t0);
+  sink[blockIdx.x * blockDim.x + tid] = acc;
+}
+
+// ---- The prefill GEMM's main loop taken apart: 8 waves (two per SIMD), per
+// 128-byte stage four substeps of 6 v_mfma_i32_32x32x32_i8 per wave on 6
+// accumulators (the 256 x 192 tile's 64 x 96 wave tiles), with
+//   mode 0: MFMAs only;
+//   mode 1: + 5 fragment reads per substep from LDS in the GEMM's swizzled
+//           pattern, each substep's reads feeding the next one;
+//   mode 2: mode 1 + one workgroup barrier per stage;
+//   mode 3: mode 2 + the stage's 56 KiB of direct-to-LDS transfers (7 per
+//           wave, global_load_lds with per-lane 64-bit addresses) in the last
+//           substep, waited for before the barrier of the next stage;
+//   mode 4: mode 3 with the transfers through a buffer resource (fixed lane
+//           offset, scalar stage offset, scalar LDS base);
+//   mode 5: mode 4 with every stage of every workgroup reading a different
+//           56 KiB (no L2 reuse).
+// Sources: 8 x 16 stages x 56 KiB (modes 3, 4; each XCD's workgroups share
+// theirs, L2-resident) or blocks x 16 x 56 KiB (mode 5).
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void probe_buffer_load_lds16(__amdgpu_buffer_rsrc_t r, lds_void* dst, int voff, int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+#endif
+}
+constexpr int kPartsStage = 57344;  // 448 rows x 128 bytes
+template <int kMode>
+__global__ __launch_bounds__(512) void gemm_parts_kernel(int64_t* cycles, int32_t* sink, int stages,
+                                                         const int8_t* src, int64_t src_bytes) {
+  __shared__ __attribute__((aligned(1024))) int8_t lds[65536 + kPartsStage];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  for (int i = tid; i < 65536 / 16; i += 512)
+    *reinterpret_cast<v4i*>(lds + 16 * i) = v4i{(int)mix(i), i ^ 0x55aa55aa, i * 131, 3 * i};
+  __syncthreads();
+  const int frow = lane & 31, fhalf = lane >> 5;
+  int off[4][5];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      const int r = (wid * 5 + q) * 32 % 448 + frow;
+      const int c = 2 * ks + fhalf;
+      off[ks][q] = r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+    }
+  v4i f[2][5];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int q = 0; q < 5; ++q) f[p][q] = *reinterpret_cast<const v4i*>(lds + off[p][q]);
+  const int uwid = __builtin_amdgcn_readfirstlane(wid);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, (int)src_bytes, 0x00020000);
+  const int8_t* dsrc[7];
+#pragma unroll
+  for (int i = 0; i < 7; ++i) dsrc[i] = src + ((blockIdx.x & 7) * 56 + i * 8 + wid) * 1024 + lane * 16;
+  v16i acc[6];
+#pragma unroll
+  for (int j = 0; j < 6; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0;
+  __syncthreads();
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int st = 0; st < stages; ++st) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int cs = ks & 1, ns = cs ^ 1;
+      if (kMode >= 3 && ks == 3) {
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the previous stage's transfers
+      }
+      if (kMode >= 2 && ks == 3) __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int q = 0; q < 6; ++q) {
+        acc[q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f[cs][q & 1], f[cs][2 + (q >> 1)], acc[q], 0, 0, 0);
+        if (kMode >= 1 && q < 5) f[ns][q] = *reinterpret_cast<const v4i*>(lds + off[(ks + 1) & 3][q]);
+        if (kMode >= 3 && ks == 3 && q < 7) {
+          const int blk = q * 8 + uwid;
+          if (kMode == 3) {
+            __builtin_amdgcn_global_load_lds((const void*)(dsrc[q] + (int64_t)(st & 15) * 8 * kPartsStage),
+                                             (lds_void*)(lds + 65536 + blk * 1024), 16, 0, 0);
+          } else {
+            const int soff = kMode == 4 ? (st & 15) * 8 * kPartsStage + (blockIdx.x & 7) * kPartsStage
+                                        : ((int)blockIdx.x * 16 + (st & 15)) * kPartsStage;
+            probe_buffer_load_lds16(rs, (lds_void*)(lds + 65536 + blk * 1024), blk * 1024 + lane * 16, soff);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (kMode >= 3 && ks == 3 && 6 < 7) {  // the seventh transfer after the substep's MFMAs
+        const int blk = 6 * 8 + uwid;
+        if (kMode == 3) {
+          __builtin_amdgcn_global_load_lds((const void*)(dsrc[6] + (int64_t)(st & 15) * 8 * kPartsStage),
+                                           (lds_void*)(lds + 65536 + blk * 1024), 16, 0, 0);
+        } else {
+          const int soff = kMode == 4 ? (st & 15) * 8 * kPartsStage + (blockIdx.x & 7) * kPartsStage
+                                      : ((int)blockIdx.x * 16 + (st & 15)) * kPartsStage;
+          probe_buffer_load_lds16(rs, (lds_void*)(lds + 65536 + blk * 1024), blk * 1024 + lane * 16, soff);
+        }
+      }
+      if (kMode >= 1) __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    }
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  int s = 0;
+#pragma unroll
+  for (int j = 0; j < 6; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s ^= acc[j][r];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int q = 0; q < 5; ++q) s ^= f[p][q].x;
+  sink[blockIdx.x * 512 + tid] = s;
+  if (lane == 0) cycles[blockIdx.x * 8 + wid] = (int64_t)(t1 - t0);
+}
+
 }  // namespace
 
 extern "C" {
@@ -245,6 +407,43 @@ int sqp_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_byt
 int sqp_lds_rate(int64_t* clocks, int32_t* sink, int blocks, int iters, int mode, hipStream_t s) {
   if (blocks <= 0 || iters <= 0 || mode < 0 || mode > 3) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(lds_rate_kernel, dim3(blocks), dim3(512), 0, s, clocks, sink, iters, mode);
+  return (int)hipGetLastError();
+}
+
+// cycles: 16 x blocks int64 (per wave); sink: threads x blocks int32;
+// bytes: 16, 8 or 4 per lane per read; reads: 4, 8 or 16 in flight per wave;
+// threads: 256, 512 or 1024; pattern 0 (linear) or 1 (GEMM fragments).
+int sqp_lds_bw(int64_t* cycles, int32_t* sink, int blocks, int threads, int iters, int bytes, int reads, int pattern,
+               hipStream_t s) {
+  if (blocks <= 0 || iters <= 0 || (threads != 256 && threads != 512 && threads != 1024) || pattern < 0 ||
+      pattern > 1)
+    return (int)hipErrorInvalidValue;
+#define SQP_LDS_BW(B, R)                                                                                         \
+  if (bytes == B && reads == R) {                                                                              \
+    hipLaunchKernelGGL((lds_bw_kernel<B, R>), dim3(blocks), dim3(threads), 0, s, cycles, sink, iters, pattern); \
+    return (int)hipGetLastError();                                                                             \
+  }
+  SQP_LDS_BW(16, 4) SQP_LDS_BW(16, 8) SQP_LDS_BW(8, 8) SQP_LDS_BW(8, 16) SQP_LDS_BW(4, 16)
+#undef SQP_LDS_BW
+  return (int)hipErrorInvalidValue;
+}
+
+// cycles: 8 x blocks int64 (per wave); sink: 512 x blocks int32; src: at least
+// 8 x 16 x 57344 bytes (modes 3, 4) or blocks x 16 x 57344 bytes (mode 5), and
+// src_bytes < 2^31.
+int sqp_gemm_parts(int64_t* cycles, int32_t* sink, int blocks, int stages, int mode, const int8_t* src,
+                   int64_t src_bytes, hipStream_t s) {
+  if (blocks <= 0 || stages <= 0 || mode < 0 || mode > 5 || src_bytes >= ((int64_t)1 << 31)) return (int)hipErrorInvalidValue;
+  const int64_t need = mode == 5 ? (int64_t)blocks * 16 * kPartsStage : (mode >= 3 ? (int64_t)8 * 16 * kPartsStage : 0);
+  if (src_bytes < need || (need > 0 && !src)) return (int)hipErrorInvalidValue;
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(gemm_parts_kernel<0>, dim3(blocks), dim3(512), 0, s, cycles, sink, stages, src, src_bytes); break;
+    case 1: hipLaunchKernelGGL(gemm_parts_kernel<1>, dim3(blocks), dim3(512), 0, s, cycles, sink, stages, src, src_bytes); break;
+    case 2: hipLaunchKernelGGL(gemm_parts_kernel<2>, dim3(blocks), dim3(512), 0, s, cycles, sink, stages, src, src_bytes); break;
+    case 3: hipLaunchKernelGGL(gemm_parts_kernel<3>, dim3(blocks), dim3(512), 0, s, cycles, sink, stages, src, src_bytes); break;
+    case 4: hipLaunchKernelGGL(gemm_parts_kernel<4>, dim3(blocks), dim3(512), 0, s, cycles, sink, stages, src, src_bytes); break;
+    default: hipLaunchKernelGGL(gemm_parts_kernel<5>, dim3(blocks), dim3(512), 0, s, cycles, sink, stages, src, src_bytes); break;
+  }
   return (int)hipGetLastError();
 }
 
