@@ -257,7 +257,8 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
   // the last substep: wait for the next stage's transfers, retire this wave's
   // LDS reads, barrier (now no wave reads the current buffer any more); the
   // transfers of the stage after next into that buffer are then issued one
-  // per MFMA of the last substep, so the address unit works while the matrix
+  // per MFMA, by half of the waves in the last substep and by the other half
+  // in the next stage's first, so the address unit works while the matrix
   // cores do (issued in one burst they stall the wave for hundreds of cycles).
   constexpr int kQ = C::kFN * C::kFM > C::kDma ? C::kFN * C::kFM : C::kDma;
   auto frag_one = [&](const int8_t* stage, int ks, int q, FragT* xf, FragT* wf) {
@@ -302,7 +303,15 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
             acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[p][j], fx[p][i], acc[j][i], 0, 0, 0);
         }
         if (do_frag && q < C::kFM + C::kFN) frag_one(nstage, nks, q, fx[p ^ 1], fw[p ^ 1]);
-        if (more_dma && q < C::kDma) dma_one(kt + 2, q);
+        // Waves 0 .. kW/2-1 issue their transfers of stage kt + 2 in the last
+        // substep of stage kt, the others in the first substep of stage
+        // kt + 1 (the buffer is free from the barrier before the last
+        // substep of kt; either way the transfers land before the hand-over
+        // of kt + 1 waits for them): the two waves of a SIMD never issue
+        // transfers at the same time, so one of them keeps the matrix core busy.
+        const bool early = uwid < kW / 2;
+        if (early && more_dma && q < C::kDma) dma_one(kt + 2, q);
+        if (!early && ks == 0 && kt >= 1 && kt + 1 < nk && q < C::kDma) dma_one(kt + 1, q);
         __builtin_amdgcn_sched_barrier(0);
       }
       // retire the fragment reads (issued during the MFMAs above) before
