@@ -147,14 +147,17 @@ def parse():
     p.add_argument("--fetch-scale", type=float, default=1.9999,
                    help="FETCH_SIZE scale factor from the copy probe (profiles/hbm_counter_scale_copy.md)")
     p.add_argument("--write-scale", type=float, default=1.0, help="WRITE_SIZE scale factor from the copy probe")
-    p.add_argument("--probe", choices=["mfma", "stream", "lds", "ldsbw", "gemmparts", "fp8sum"], default=None,
+    p.add_argument("--probe", choices=["mfma", "stream", "lds", "ldsbw", "gemmparts", "fp8sum", "quantsitu"],
+                   default=None,
                    help="only run one measurement probe (libsq_probes.so) and print its JSON line: mfma = "
                         "int8 matrix-core rate and shader clock with constant and changing operands; stream = "
                         "single-kernel streaming read / read+write ceilings at the workloads' sizes; lds = "
                         "fragment-read rate of the prefill GEMM's LDS pattern beside the MFMA rate; ldsbw = LDS read "
                         "throughput by instruction width; gemmparts = the prefill GEMM's main loop taken apart "
                         "(MFMAs, fragment reads, barriers, stage transfers); fp8sum = "
-                        "summation error of the E4M3 matrix instructions against exact sums")
+                        "summation error of the E4M3 matrix instructions against exact sums; quantsitu = the "
+                        "activation quantiser (libsq.so) with its input in the last-level cache, evicted by clean "
+                        "reads, and evicted by writes (as after a prefill GEMM's output)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain device-to-device copy of 512 MiB (5 times), the known-size "
                         "reference that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
@@ -225,10 +228,55 @@ def run_probe(args):
     import numpy as np
     import torch
 
-    lib = probe_lib()
     dev = torch.device("cuda:0")
     stream = lambda: ctypes_stream(torch)
     out = {"probe": args.probe, "device": torch.cuda.get_device_name(0)}
+    if args.probe == "quantsitu":
+        # The per-token quantiser of the product library at the prefill sizes,
+        # one launch per measurement (HIP events around it), after: (a) the
+        # same launch (input and output in the 256 MiB last-level cache); (b)
+        # a read of 1 GiB (the cache holds clean lines of other data); (c) a
+        # write of 1 GiB (the cache holds dirty lines, as after a GEMM that
+        # wrote a large output: every miss of the quantiser then also evicts
+        # a dirty line to HBM).
+        import w8a8_int8_quantization_amd as sq
+        q_fn = sq.raw["sq_quant_act_per_token"]
+        big = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(7)
+        res = {}
+        for name, m, k in (("qkv_2048x4096", 2048, 4096), ("gateup_8192x4096", 8192, 4096),
+                           ("down_8192x14336", 8192, 14336)):
+            x = torch.randn(m, k, device=dev).to(torch.bfloat16)
+            s_ = torch.rand(k, device=dev) + 0.5
+            xq = torch.empty(m, k, dtype=torch.int8, device=dev)
+            dx = torch.empty(m, dtype=torch.float32, device=dev)
+            args_ = (x.data_ptr(), sq.SQ_BF16, m, k, k, s_.data_ptr(), xq.data_ptr(), dx.data_ptr(), stream())
+            nbytes = m * k * 2 + 4 * k + m * k + 4 * m
+            for cond in ("cached", "after_clean_reads", "after_writes"):
+                times = []
+                for rep in range(12):
+                    if cond == "after_clean_reads":
+                        big.sum(dtype=torch.int64)
+                    elif cond == "after_writes":
+                        big.fill_(rep & 0xFF)
+                    else:
+                        q_fn(*args_)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    if q_fn(*args_) != 0:
+                        raise SystemExit("quantiser launch failed")
+                    e1.record()
+                    e1.synchronize()
+                    if rep >= 2:
+                        times.append(e0.elapsed_time(e1) * 1e3)
+                us = sorted(times)[len(times) // 2]
+                res[f"{name}_{cond}"] = {"us": us, "tbs_algorithmic": nbytes / us / 1e6, "bytes": nbytes}
+            del x, xq
+        out["results"] = res
+        out["setup"] = ("sq_quant_act_per_token on bf16 rows with smoothing factors, one launch between two HIP "
+                        "events (the launch's dispatch gap included alike in every case), median of 10")
+        print(json.dumps(out), flush=True)
+        return
+    lib = probe_lib()
     if args.probe == "mfma":
         blocks, iters = 256, 20000
         clocks = torch.zeros(blocks * 4, dtype=torch.int64, device=dev)

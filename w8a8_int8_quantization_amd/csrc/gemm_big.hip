@@ -309,7 +309,10 @@ __global__ __launch_bounds__(64 * kW, 1) void gemm_big_kernel(const int8_t* __re
         // substep of kt; either way the transfers land before the hand-over
         // of kt + 1 waits for them): the two waves of a SIMD never issue
         // transfers at the same time, so one of them keeps the matrix core busy.
-        const bool early = uwid < kW / 2;
+        // With two substeps per stage (E4M3) the late half would issue its
+        // transfers only one substep before the hand-over waits for them
+        // (QKV 58 -> 69 us): there every wave issues in the last substep.
+        const bool early = kSub < 4 || uwid < kW / 2;
         if (early && more_dma && q < C::kDma) dma_one(kt + 2, q);
         if (!early && ks == 0 && kt >= 1 && kt + 1 < nk && q < C::kDma) dma_one(kt + 1, q);
         __builtin_amdgcn_sched_barrier(0);
