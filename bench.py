@@ -281,8 +281,10 @@ def run_probe(args):
         blocks, iters = 256, 20000
         clocks = torch.zeros(blocks * 4, dtype=torch.int64, device=dev)
         sink = torch.zeros(blocks * 256, dtype=torch.int32, device=dev)
-        ops = blocks * 4 * iters * 16 * 2 * 32 * 32 * 32
-        for name, rnd in (("constant_operands", 0), ("changing_operands", 1)):
+        ops_i8 = blocks * 4 * iters * 16 * 2 * 32 * 32 * 32
+        for name, rnd in (("constant_operands", 0), ("changing_operands", 1), ("e4m3_constant_operands", 2),
+                          ("e4m3_changing_operands", 3)):
+            ops = ops_i8 * (2 if rnd >= 2 else 1)  # the E4M3 instruction is 32 x 32 x 64
             launch = lambda: lib.sqp_mfma_rate(clocks.data_ptr(), sink.data_ptr(), blocks, iters, rnd, stream())
             _probe_time(torch, launch, 2)
             us = _probe_time(torch, launch, 7)
@@ -292,7 +294,9 @@ def run_probe(args):
                          "pops_at_sclk_per_cu_clk": ops / (real_us * 1e-6) / (ghz * 1e9) / 256}
         out["setup"] = (f"{blocks} workgroups x 4 waves (one per SIMD), {iters} x 16 v_mfma_i32_32x32x32_i8 per wave, "
                         "8 independent accumulators; changing operands: 16 A and 16 B fragments of hashed bytes "
-                        "combined in rotation, so no two consecutive MFMAs share operands")
+                        "combined in rotation, so no two consecutive MFMAs share operands; e4m3: the same with "
+                        "v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales), 8 operand pairs of finite codes "
+                        "(constant: 1.0), frac_of_5_pops against the 5.0 PFLOP/s dense FP8 nameplate")
     elif args.probe == "stream":
         res = {}
         sink = torch.zeros(4096 * 256, dtype=torch.int32, device=dev)

@@ -649,8 +649,17 @@ static void launch_big_f8(const int8_t* xq, const int8_t* wq, int M, int N, int 
 
 }  // namespace sqk
 
+// The host code below is compiled twice (build.py): the int8 entry points,
+// and, with SQ_BIG_E4M3 defined, the E4M3 one. The E4M3 object is built
+// without LLVM's machine-code sinking: with it, the E4M3 main loop's matrix
+// instructions sink past the conditional stage transfers of the hand-over
+// substep, so a stage's twelve MFMAs issue back to back after all of its
+// fragment reads instead of one between each pair (QKV prefill E4M3 GEMM
+// 59.2 -> 48.4 us without the pass); the int8 instances keep the default
+// pipeline.
 namespace sqh {
 
+#ifndef SQ_BIG_E4M3
 bool gemm_big_suits(int64_t m, int64_t n, int64_t k, bool split_ok) { return sqi::big_suits(m, n, k, split_ok); }
 
 namespace {
@@ -711,10 +720,12 @@ hipError_t gemm_i8_big(const int8_t* xq, const float* x_scale, const int8_t* wq,
   return hipGetLastError();
 }
 
+#else  // SQ_BIG_E4M3
+
 hipError_t gemm_f8_big(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int64_t m,
                        int64_t n, int64_t k, void* y, sq_dtype yt, int64_t ldy, void* ws, hipStream_t s) {
   sqk::BigEpi ep{x_scale, w_scale, y, ldy, DecompArgs{}, false, nullptr, nullptr, 1, 0};
-  const BigSplit sp = big_split(m, n, k, true);
+  const sqi::BigSplit sp = sqi::big_split(m, n, k, true, true);
   if (sp.S > 1) {
     ep.S = sp.S;
     ep.slice_stages = sp.slice_stages;
@@ -738,5 +749,7 @@ hipError_t gemm_f8_big(const uint8_t* xq, const float* x_scale, const uint8_t* w
                             out, vec, s);
   return hipGetLastError();
 }
+
+#endif  // SQ_BIG_E4M3
 
 }  // namespace sqh

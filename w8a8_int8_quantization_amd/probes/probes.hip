@@ -83,6 +83,45 @@ __global__ __launch_bounds__(256, 1) void mfma_rate_kernel(int64_t* clocks, int3
   sink[blockIdx.x * 256 + threadIdx.x] = s + lane;
 }
 
+// The same for the E4M3 matrix instruction (v_mfma_scale_f32_32x32x64_f8f6f4,
+// unit scales): 8 operand pairs of 32 bytes per lane (constant 1.0 codes, or
+// hashed bytes with the exponent's low bit cleared, so every code is finite).
+constexpr int kPoolF8 = 8;
+__global__ __launch_bounds__(256, 1) void mfma_rate_f8_kernel(int64_t* clocks, int32_t* sink, int iters, int random) {
+  const int lane = threadIdx.x & 63;
+  v8i a[kPoolF8], b[kPoolF8];
+#pragma unroll
+  for (int p = 0; p < kPoolF8; ++p) {
+    const uint32_t seed = (blockIdx.x * 256u + threadIdx.x) * 64u + (uint32_t)p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[p][e] = random ? (int)(mix(seed * 16u + e) & 0xF7F7F7F7u) : 0x38383838;
+      b[p][e] = random ? (int)(mix(seed * 16u + 8 + e + 0x9e3779b9u) & 0xF7F7F7F7u) : 0x38383838;
+    }
+  }
+  v16f acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  __syncthreads();
+  clock_mark(clocks, 0);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      acc[q & 7] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[q & 7], b[(q * 5 + 3) & 7], acc[q & 7], 0, 0, 0,
+                                                                  127, 0, 127);
+  }
+  __syncthreads();
+  clock_mark(clocks, 1);
+  int32_t s = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s ^= __float_as_int(acc[j][r]);
+  sink[blockIdx.x * 256 + threadIdx.x] = s + lane;
+}
+
 // ---- streaming: each workgroup walks chunks of 256 x kD 16-byte vectors
 // (grid-stride over chunks); thread t loads vectors t, t + 256, ... of a
 // chunk, all kD in flight before their first use, folds them into one word
@@ -379,9 +418,13 @@ extern "C" {
 // clocks: 4 x blocks int64 (start memtime, start realtime, end memtime, end
 // realtime per workgroup); sink: 256 x blocks int32. One 256-thread
 // workgroup (4 waves) per CU for blocks = 256.
+// random: 0 / 1 int8 with constant / changing operands, 2 / 3 the same for E4M3.
 int sqp_mfma_rate(int64_t* clocks, int32_t* sink, int blocks, int iters, int random, hipStream_t s) {
-  if (blocks <= 0 || iters <= 0) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(mfma_rate_kernel, dim3(blocks), dim3(256), 0, s, clocks, sink, iters, random);
+  if (blocks <= 0 || iters <= 0 || random < 0 || random > 3) return (int)hipErrorInvalidValue;
+  if (random >= 2)
+    hipLaunchKernelGGL(mfma_rate_f8_kernel, dim3(blocks), dim3(256), 0, s, clocks, sink, iters, random - 2);
+  else
+    hipLaunchKernelGGL(mfma_rate_kernel, dim3(blocks), dim3(256), 0, s, clocks, sink, iters, random);
   return (int)hipGetLastError();
 }
 
