@@ -708,6 +708,7 @@ def bench_fp8(args, dev):
                     ("gemm_f8.hip", "gemm_f8_kernel"))
     roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": pmc_traffic(args.workload, kfile),
                  "kernel": kname, "launch_us": gemm_ms * 1e3})
+    kernel_only(roof, args.workload, kfile, gemm_bytes if streamed else ops)
     result = {
         "metric": METRIC, "value": ops / (ms * 1e-3) / 1e12, "unit": "TOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -1204,11 +1205,13 @@ def bench_linear(args, dev) -> dict:
 
 # Per-config records of the default run: the other configurations of the
 # workload set (gate/up and down projections at 8192 tokens, alpha 0.5; the
-# decode projections at 1 and 64 tokens; the LLM.int8() layer), each timed
+# decode projections at 1, 8, 32 and 64 tokens; the LLM.int8() layer; the
+# E4M3 variant of the QKV projection), each timed
 # like the headline with fewer steps and a short oracle sample.
 EXTRA_CONFIGS = [("gateup_prefill", None, 30), ("down_prefill", None, 40), ("decode_up", 1, 200),
                  ("decode_down", 1, 200), ("decode_up", 8, 200), ("decode_down", 8, 200), ("decode_up", 32, 200),
-                 ("decode_down", 32, 200), ("decode_up", 64, 200), ("decode_down", 64, 200), ("llm_int8", None, 40)]
+                 ("decode_down", 32, 200), ("decode_up", 64, 200), ("decode_down", 64, 200), ("llm_int8", None, 40),
+                 ("fp8_qkv_prefill", None, 100)]
 
 
 def config_records(args, dev) -> list:
@@ -1220,7 +1223,8 @@ def config_records(args, dev) -> list:
         a.cpu_seconds = min(args.cpu_seconds, 3.0)
         a.one_call = m == 1  # one token: the one-call entry point (the fused step where it applies)
         print(f"[bench] config record {workload} m={m}", file=sys.stderr, flush=True)
-        r = bench_llm_int8(a, dev) if workload == "llm_int8" else bench_linear(a, dev)
+        r = (bench_llm_int8(a, dev) if workload == "llm_int8" else bench_fp8(a, dev) if workload.startswith("fp8_")
+             else bench_linear(a, dev))
         keep = ("value", "unit", "ms_per_step", "steps", "config", "gemm_only_tops", "gemm_us", "quant_us",
                 "gemm_us_back_to_back", "step_gbs_algorithmic", "detect_us", "outlier_columns", "weight_copies",
                 "roofline", "cpu_baseline", "one_call")
