@@ -123,7 +123,8 @@ def parse():
                         "starts from the residual stream: fused RMSNorm with the folded gain + quantisation, "
                         "then the GEMM); silu_down_prefill, silu_decode_down (the step starts from the gate/up "
                         "projection's bf16 outputs: fused SiLU(gate)*up + smoothing + quantisation, then the "
-                        "down projection GEMM); fp8_qkv_prefill, fp8_decode_up (the FP8 E4M3 variant: per-token "
+                        "down projection GEMM); fp8_qkv_prefill, fp8_gateup_prefill, fp8_down_prefill, fp8_decode_up (the FP8 "
+                        "E4M3 variant: per-token "
                         "E4M3 quantisation, then the E4M3 GEMM; no smoothing); gptq_qkv, gptq_down (GPTQ of one "
                         "layer at load time: Hessian of 4096 calibration rows, damping, Cholesky, sweep; "
                         "reports ms per layer)")
@@ -638,7 +639,8 @@ def bench_fp8(args, dev):
     import workloads
     import w8a8_int8_quantization_amd as sq
 
-    base = {"fp8_qkv_prefill": "qkv_prefill", "fp8_decode_up": "decode_up"}[args.workload]
+    base = {"fp8_qkv_prefill": "qkv_prefill", "fp8_decode_up": "decode_up", "fp8_gateup_prefill": "gateup_prefill",
+            "fp8_down_prefill": "down_prefill"}[args.workload]
     c = workloads.linear_case(base, m=args.m)
     to = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
     x, w = to(c.x), to(c.w)
