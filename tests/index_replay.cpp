@@ -731,11 +731,14 @@ int main() {
   big_config_checks<256, 8, false>();
   big_config_checks<128, 8, true>();
   big_config_checks<192, 8, true>();
+  big_config_checks<256, 4, true>();  // E4M3 256-column tiles on four waves
   big_band_checks<128, 8, 2>();
   big_band_checks<128, 8, 4>();
   big_band_checks<192, 8, 2>();
   big_band_checks<192, 8, 4>();
   big_band_checks<256, 8, 2>();
+  big_band_checks<256, 4, 2>();
+  big_band_checks<256, 4, 4>();
   big_band_checks<256, 8, 4>();
   ring_config_checks<32>();
   ring_config_checks<64>();

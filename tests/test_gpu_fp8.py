@@ -120,6 +120,19 @@ def test_fp8_linear_prefill_tiles(m, n, k, out):
     _check_gemm(xq, d, wq, sw, out)
 
 
+# Shapes whose 256-column tiles fill the CUs at least once (and K is not
+# split) run on four waves of 128 x 128 outputs: every output type, ragged
+# tiles in both directions, a single k stage and a longer k.
+@pytest.mark.parametrize("m,n,k,out", [(4096, 4096, 1024, "bf16"), (4352, 4160, 1280, "f32"), (4100, 4200, 128, "f16"),
+                                       (4096, 4096, 3584, "bf16")])
+def test_fp8_linear_prefill_four_wave_tiles(m, n, k, out):
+    log("fp8 prefill gemm, four-wave tiles", m, n, k, out)
+    c = workloads.random_linear_case(m=m, k=k, n=n, seed=5 * m + n + k, dtype="bf16", calib_rows=8)
+    xq, d = oracle.quantize_activations_fp8(c.x)
+    wq, sw = oracle.quantize_weights_fp8(c.w)
+    _check_gemm(xq, d, wq, sw, out)
+
+
 def test_fp8_linear_prefill_random_codes():
     """Every finite E4M3 code in both operands (products from 2^-18 to 448^2),
     on the prefill pipeline."""

@@ -636,6 +636,21 @@ static void launch_big_o(const int8_t* xq, const int8_t* wq, int M, int N, int K
   }
 }
 
+// E4M3 operands, 256-column tiles on four waves (one per SIMD, 128 x 128
+// outputs each: the accumulators and two fragment sets need more registers
+// than a lane has at two waves per SIMD), K not split.
+template <int kOut>
+static void launch_big_f8_w4(const int8_t* xq, const int8_t* wq, int M, int N, int K, const BigEpi& ep, bool vec,
+                             hipStream_t s) {
+  const int tiles = ((M + kBigBM - 1) / kBigBM) * ((N + 255) / 256);
+  if (vec)
+    hipLaunchKernelGGL((gemm_big_kernel<256, 4, kOut, true, true, false>), dim3(tiles), dim3(256), 0, s, xq, wq, M, N,
+                       K, ep);
+  else
+    hipLaunchKernelGGL((gemm_big_kernel<256, 4, kOut, false, true, false>), dim3(tiles), dim3(256), 0, s, xq, wq, M,
+                       N, K, ep);
+}
+
 // E4M3 operands: floating-point outputs only
 template <int BN, int kW = 8>
 static void launch_big_f8(const int8_t* xq, const int8_t* wq, int M, int N, int K, const BigEpi& ep, int out,
@@ -738,10 +753,25 @@ hipError_t gemm_f8_big(const uint8_t* xq, const float* x_scale, const uint8_t* w
                    reinterpret_cast<uintptr_t>(w_scale) % 16 == 0;
   ep.rows16 = (ldy * eb) % 16 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0;
   const int M = (int)m, N = (int)n, K = (int)k;
-  // 192- or 128-column tiles: the E4M3 fragments are twice the int8 ones,
-  // and with 256 columns the accumulators and two fragment sets exceed the
-  // 256 registers a lane has at two waves per SIMD
-  if (sp.bn == 128)
+  // 192- or 128-column tiles on eight waves: the E4M3 fragments are twice
+  // the int8 ones, and with 256 columns the accumulators and two fragment
+  // sets exceed the 256 registers a lane has at two waves per SIMD. Where
+  // 256-column tiles fill the CUs at least once and K is not split, four
+  // waves of 128 x 128 outputs take them instead (one wave per SIMD, 512
+  // registers a lane): 8192 x 4096 -> 28672 903.5 -> 839.1 us, 8192 x 14336
+  // -> 4096 447.0 -> 370.3 us (the same accumulation order per output, so
+  // the same bits); QKV at 2048 tokens (192 such tiles) stays on 192 columns.
+  const int64_t tiles256 = ((m + sqi::kBigBM - 1) / sqi::kBigBM) * ((n + 255) / 256);
+  if (sp.S == 1 && tiles256 >= 256) {
+    const int8_t* a8 = reinterpret_cast<const int8_t*>(xq);
+    const int8_t* b8 = reinterpret_cast<const int8_t*>(wq);
+    if (out == sqk::kBigF32)
+      sqk::launch_big_f8_w4<sqk::kBigF32>(a8, b8, M, N, K, ep, vec, s);
+    else if (out == sqk::kBigBF16)
+      sqk::launch_big_f8_w4<sqk::kBigBF16>(a8, b8, M, N, K, ep, vec, s);
+    else
+      sqk::launch_big_f8_w4<sqk::kBigF16>(a8, b8, M, N, K, ep, vec, s);
+  } else if (sp.bn == 128)
     sqk::launch_big_f8<128>(reinterpret_cast<const int8_t*>(xq), reinterpret_cast<const int8_t*>(wq), M, N, K, ep,
                             out, vec, s);
   else
